@@ -1,0 +1,299 @@
+/*
+ * hisparse.h -- C ABI of the HiSparse swap-in hot path for MI355X (gfx950).
+ *
+ * What the path computes (per decode step, per layer): every request's top-k
+ * token indices from a sparse-attention indexer are resolved against that
+ * request's hot cache in HBM.  A hit returns the token's resident device row.
+ * Misses are deduplicated (across speculative steps in the multi-step call),
+ * given victim slots (LRU for the single-step call, CLOCK for the multi-step
+ * call), and their KV entries are copied from pinned host memory into those
+ * slots; the token->slot table and the policy state are then committed.  The
+ * result is the sparse row (or page) table that decode attention consumes.
+ *
+ * Sources of the operations (page title, section):
+ *   - sglang PR #20343 summary, "Implementation breakdown": the single-step
+ *     swap-in kernel with a token->slot hash table, hit/miss handling and an
+ *     LRU cache; host memory holds the idle KV ("Features and motivation").
+ *   - PR #32162 report "[HiSparse] Support hisparse multi-step swap io
+ *     kernel", "Implementation breakdown" items 1-2: multi-step gather/commit
+ *     over a [batch, steps, top_k] working set with cross-step miss dedup and
+ *     a CLOCK cache; steps limited to 2..4; optional miss_src/miss_dst/
+ *     miss_count plan; "Risks and impact": hot_buffer_size up to 32768.
+ *   - "SGLang HiSparse" blog, section 2.1: swap_in_selected_pages takes
+ *     req_pool_indices, seq_lens, topk_indices and the layer id and returns a
+ *     sparse page table; sections 1.3 and 2.3: token indices become a page
+ *     load list, a token is found by page plus in-page offset.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device pointers unless the name ends in "_h" (host).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Swap and reset calls only enqueue work on `stream`: they never allocate
+ *     and never synchronise the host.  Calls marked "synchronous" wait for
+ *     `stream` to drain.
+ *   - Return value: HISPARSE_OK (0) or a negative HISPARSE_E_* code, decided
+ *     on the host from scalar arguments only.  Problems only the device can
+ *     see (bad indices, a request named twice, page overflow) write -1 to the
+ *     affected outputs and OR a HISPARSE_ERR_* bit into the state's sticky
+ *     error word (hisparse_get_error_flags).
+ *   - A state is used from one stream at a time; the calls that touch it are
+ *     ordered by that stream.
+ *   - All functions are callable from any host thread; no exceptions cross
+ *     the ABI.
+ */
+#ifndef HISPARSE_H_
+#define HISPARSE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Host-side status codes. */
+#define HISPARSE_OK 0
+#define HISPARSE_E_INVAL (-1)       /* an argument is out of range or NULL */
+#define HISPARSE_E_NOMEM (-2)       /* a device or pinned host allocation failed */
+#define HISPARSE_E_HIP (-3)         /* a HIP runtime call failed */
+#define HISPARSE_E_UNSUPPORTED (-4) /* valid request outside what this build supports */
+
+/* Device-side error bits (sticky; see hisparse_get_error_flags). */
+#define HISPARSE_ERR_BAD_INDEX 1u     /* top-k entry outside [0, seq_len), not -1 */
+#define HISPARSE_ERR_DUP_REQUEST 2u   /* one request index twice in one batch */
+#define HISPARSE_ERR_PAGE_OVERFLOW 4u /* a row needs more distinct pages than hot pages */
+#define HISPARSE_ERR_BAD_ROW 8u       /* request index or seq_len out of range */
+
+/* Replacement policies. */
+#define HISPARSE_POLICY_LRU 0   /* single-step calls (PR #20343 summary) */
+#define HISPARSE_POLICY_CLOCK 1 /* multi-step calls (PR #32162 report, item 1) */
+
+/* Limits of this build. */
+#define HISPARSE_MAX_HOT 32768        /* hot_buffer_size bound (PR #32162, "Risks and impact") */
+#define HISPARSE_MIN_STEPS 2          /* multi-step range (PR #32162, item 2) */
+#define HISPARSE_MAX_STEPS 4
+#define HISPARSE_MAX_WORKING_SET 8192 /* top_k (x num_steps) entries per row */
+#define HISPARSE_MAX_SEQ_LEN ((1 << 28) - 2)
+#define HISPARSE_MAX_PAGES_PER_REQUEST (1 << 18)
+
+typedef struct hisparse_state* hisparse_state_t;
+
+/*
+ * Creation parameters (PR #32162 report, "Implementation breakdown" item 2
+ * lists the compile-time knobs block_size, num_top_k, hot_buffer_size,
+ * item_size_bytes, num_steps, record_miss_plan; here they are runtime fields).
+ *
+ *   max_requests     R: request pool size; requests are 0..R-1.
+ *   num_layers       L: layers; each (request, layer) pair is an independent
+ *                    cache instance.
+ *   hot_buffer_size  H: hot slots per instance (pages when page_size > 1),
+ *                    1..HISPARSE_MAX_HOT.
+ *   top_k            K: entries per row and step.  Token LRU needs K <= H.
+ *   max_steps        1 for LRU states; 2..4 for CLOCK states (the largest
+ *                    num_steps a multi-step call may use).
+ *   page_size        P: 1 = token mode; P > 1 = page mode (LRU only), which
+ *                    needs max_seq_len % P == 0.
+ *   item_size_bytes  I: bytes of one token's KV entry, a multiple of 16 (e.g.
+ *                    1152 for a 576-dim bf16 MLA entry, 656 for the fp8 layout).
+ *   max_seq_len      N: host tokens per request.
+ *   policy           HISPARSE_POLICY_LRU or HISPARSE_POLICY_CLOCK.
+ *   max_batch        largest batch of one call, 1..R.
+ *   host_kv          host array of L pointers; layer l's host KV tier,
+ *                    row-major [R][N][I] bytes, in pinned host memory the
+ *                    device can read (hisparse_host_alloc or any hipHostMalloc
+ *                    buffer).  Owned by the caller; must outlive the state and
+ *                    every enqueued call.
+ *   dev_kv           host array of L device pointers; layer l's hot KV
+ *                    buffer: token mode [R][H + X][I] bytes with
+ *                    X = max(0, max_steps*K - H) scratch rows for CLOCK states
+ *                    (0 for LRU); page mode [R][H][P][I] bytes.  Owned by the
+ *                    caller (for example torch tensors).
+ */
+typedef struct hisparse_config {
+  int32_t max_requests;
+  int32_t num_layers;
+  int32_t hot_buffer_size;
+  int32_t top_k;
+  int32_t max_steps;
+  int32_t page_size;
+  int32_t item_size_bytes;
+  int32_t max_seq_len;
+  int32_t policy;
+  int32_t max_batch;
+  const void* const* host_kv;
+  void* const* dev_kv;
+} hisparse_config_t;
+
+/*
+ * Optional miss plan written by a swap call (PR #32162 report, item 2 and
+ * "Risks and impact": the miss_src / miss_dst / miss_count protocol of the
+ * prefetch replay path).  Arrays are device int32 [batch][capacity]; row b's
+ * first miss_count[b] entries are written, the rest are left untouched.
+ *   miss_src  host row copied: r*N + t (token mode) or host page r*(N/P) + p.
+ *   miss_dst  device row written: r*(H+X) + slot, or r*H + page slot.
+ *   victim    key (token or page) evicted from that slot, or -1.
+ * capacity must be >= hisparse_plan_capacity(state).
+ */
+typedef struct hisparse_miss_plan {
+  int32_t* miss_src;
+  int32_t* miss_dst;
+  int32_t* victim;
+  int32_t capacity;
+} hisparse_miss_plan_t;
+
+/* Accumulated kernel timings (see hisparse_profile_enable). */
+typedef struct hisparse_profile {
+  int64_t calls;  /* swap calls timed */
+  double plan_ms; /* summed duration of the lookup/victim/commit kernel */
+  double copy_ms; /* summed duration of the miss-copy kernel */
+} hisparse_profile_t;
+
+/*
+ * Device rows per request of a layer's hot KV buffer for `cfg`: H + X in
+ * token mode, H in page mode (each row then holds P*I bytes).  Returns a
+ * negative HISPARSE_E_* code when `cfg` is invalid.
+ */
+int64_t hisparse_device_rows_per_request(const hisparse_config_t* cfg);
+
+/*
+ * Creates a state on the current HIP device: validates `cfg`, allocates the
+ * per-instance token->slot table, slot->key table, policy state (LRU order and
+ * timestamps, or CLOCK reference bits and hand) and the miss workspace in
+ * HBM, and enqueues their initialisation (every cache empty) on `stream`.
+ * Synchronous.  On success *out owns the device memory it allocated.
+ * Errors: HISPARSE_E_INVAL for a bad field or a host_kv pointer the device
+ * cannot read; HISPARSE_E_NOMEM; HISPARSE_E_HIP.
+ */
+int hisparse_state_create(const hisparse_config_t* cfg, void* stream, hisparse_state_t* out);
+
+/* Frees what the state allocated (not the caller's KV buffers).  The caller
+ * must have drained every stream that used the state.  NULL is a no-op. */
+void hisparse_state_destroy(hisparse_state_t st);
+
+/*
+ * Single-step swap-in of one layer (PR #20343 summary, "Implementation
+ * breakdown"; "SGLang HiSparse" blog, section 2.1).  LRU states only.
+ *
+ *   layer_id          0..L-1.
+ *   batch             rows, 0..max_batch (0 is a no-op).
+ *   req_pool_indices  int32 [batch]: request of each row.
+ *   seq_lens          int32 [batch]: valid token range [0, seq_len) per row.
+ *   topk_indices      int32 [batch][K]: token indices; -1 is padding.
+ *   out_locs          int32 [batch][K], written:
+ *                       token mode: device row r*(H+X) + slot of the token;
+ *                       page mode: j*P + (t mod P), j = index of the token's
+ *                       page among the row's distinct pages (ascending);
+ *                       -1 for padding, invalid entries and rejected rows.
+ *   miss_count        int32 [batch], written: distinct keys (tokens, or pages)
+ *                     of the row that were not resident and were copied.
+ *   page_table        page mode only (NULL in token mode): int32 [batch][H],
+ *                     written: device page row r*H + slot of the j-th distinct
+ *                     page, -1 from num_pages[b] on.
+ *   num_pages         page mode only: int32 [batch], distinct pages per row.
+ *   plan              NULL or a miss plan (see hisparse_miss_plan_t).
+ *
+ * Ordering rules: misses are placed in first-occurrence order of their
+ * tokens (ascending page order in page mode) into victims taken in LRU order
+ * (timestamp, slot) with EMPTY slots first; keys of the call are never
+ * evicted.  A row whose request is out of range or whose seq_len is outside
+ * [0, N] is rejected (ERR_BAD_ROW); a request named by two rows rejects both
+ * (ERR_DUP_REQUEST); page mode with more than H distinct pages rejects the row
+ * (ERR_PAGE_OVERFLOW); rejected rows leave their cache untouched.
+ * Errors: HISPARSE_E_INVAL (NULL pointer, range, policy mismatch, plan
+ * capacity), HISPARSE_E_HIP.
+ */
+int hisparse_swap_in_selected(hisparse_state_t st, int32_t layer_id, int32_t batch,
+                              const int32_t* req_pool_indices, const int32_t* seq_lens,
+                              const int32_t* topk_indices, int32_t* out_locs,
+                              int32_t* miss_count, int32_t* page_table, int32_t* num_pages,
+                              const hisparse_miss_plan_t* plan, void* stream);
+
+/*
+ * Multi-step swap-in of one layer (PR #32162 report, "Implementation
+ * breakdown" items 1-2).  CLOCK states only; token mode.
+ *
+ *   num_steps     S, 2..max_steps.
+ *   topk_indices  int32 [batch][S][K]; -1 is padding.
+ *   out_locs      int32 [batch][S][K], written: device row of each token, a
+ *                 hot slot or, on overflow, a scratch row r*(H+X) + H + j.
+ *   miss_count    int32 [batch]: distinct missing tokens over all S steps.
+ *   plan          NULL or a miss plan; admitted misses first, then scratch.
+ *
+ * The S rows of a request form one working set: duplicates across steps
+ * resolve to one row and one copy.  Resident keys of the call are pinned;
+ * victims come from a CLOCK sweep (reference bit set on hit and insert, hand
+ * persists per instance, stops after the last victim).  When the misses
+ * exceed the unpinned slots, the misses seen in the latest steps are admitted
+ * and the rest are copied to scratch rows without entering the cache (the
+ * pages call this admission approximate; the data of the call stays exact).
+ * Row rejection rules and errors as for hisparse_swap_in_selected.
+ */
+int hisparse_swap_in_spec_multistep(hisparse_state_t st, int32_t layer_id, int32_t batch,
+                                    int32_t num_steps, const int32_t* req_pool_indices,
+                                    const int32_t* seq_lens, const int32_t* topk_indices,
+                                    int32_t* out_locs, int32_t* miss_count,
+                                    const hisparse_miss_plan_t* plan, void* stream);
+
+/*
+ * Empties the caches of `n` requests in every layer (a newly admitted
+ * request).  req_pool_indices: device int32 [n]; out-of-range entries set
+ * ERR_BAD_ROW and are skipped.  Enqueued on `stream`.
+ */
+int hisparse_request_reset(hisparse_state_t st, int32_t n, const int32_t* req_pool_indices,
+                           void* stream);
+
+/* Per-row miss capacity a plan must provide: S*K (token mode) or H (page mode). */
+int32_t hisparse_plan_capacity(hisparse_state_t st);
+
+/*
+ * Copies one instance's state to host memory.  Synchronous.
+ *   slot_key_h  int32 [H]: key held by each slot, -1 if empty.
+ *   policy_h    int32 [H]: LRU timestamp of each slot (-1 if empty), or the
+ *               CLOCK reference bit (0/1).
+ *   ctrl_h      int32 [2]: {LRU call counter, CLOCK hand}.
+ *   key_slot_h  NULL or int32 [N] (token mode) / [N/P] (page mode): slot of
+ *               every key, -1 if not resident.
+ */
+int hisparse_state_export(hisparse_state_t st, int32_t req, int32_t layer, int32_t* slot_key_h,
+                          int32_t* policy_h, int32_t* ctrl_h, int32_t* key_slot_h, void* stream);
+
+/*
+ * Overwrites one instance's state from host memory (same layouts as export;
+ * a resident set built up front, as the pages' tests do).  The caller fills
+ * the matching device KV rows.  Synchronous.  HISPARSE_E_INVAL if a key is
+ * out of range or resident twice, a timestamp is below -1, or an empty slot
+ * carries a timestamp other than -1.
+ */
+int hisparse_state_import(hisparse_state_t st, int32_t req, int32_t layer,
+                          const int32_t* slot_key_h, const int32_t* policy_h,
+                          const int32_t* ctrl_h, void* stream);
+
+/* Reads the sticky error word into *flags_h; clears it when `clear` != 0.
+ * Synchronous. */
+int hisparse_get_error_flags(hisparse_state_t st, uint32_t* flags_h, int32_t clear, void* stream);
+
+/* Static description of a status code. */
+const char* hisparse_strerror(int code);
+
+/*
+ * Pinned, device-readable host memory for the host KV tier (hipHostMalloc,
+ * mapped, non-coherent so the GPU may cache what it reads).  *out_h receives
+ * the host address, usable directly as a host_kv pointer.  Free with
+ * hisparse_host_free.
+ */
+int hisparse_host_alloc(size_t bytes, void** out_h);
+int hisparse_host_free(void* p_h);
+
+/*
+ * Kernel timing with HIP events recorded on the call's stream around the two
+ * kernels of every swap call while enabled.  hisparse_profile_read is
+ * synchronous: it waits for the recorded events, returns the sums since the
+ * last read and resets them.
+ */
+int hisparse_profile_enable(hisparse_state_t st, int32_t enable);
+int hisparse_profile_read(hisparse_state_t st, hisparse_profile_t* out_h);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HISPARSE_H_ */

@@ -1,0 +1,358 @@
+"""Thin ctypes binding of ``libhisparse.so``.
+
+Argument marshalling only: every step of the swap-in path runs in the HIP
+library.  The module-level ``hisparse_*`` functions mirror the C entry points
+one to one (pointers as Python ints); :class:`HiSparseState` and
+:class:`HostKV` are conveniences that pass torch tensors / pinned host buffers
+through them.
+
+torch is imported before the library is loaded so that the library binds to
+the HIP runtime torch already loaded (both export the same soname), and
+streams and device pointers are shared between the two.
+"""
+from __future__ import annotations
+
+import ctypes
+import pathlib
+
+import numpy as np
+import torch
+
+LIB_PATH = pathlib.Path(__file__).resolve().with_name("libhisparse.so")
+
+HISPARSE_OK = 0
+HISPARSE_E_INVAL = -1
+HISPARSE_E_NOMEM = -2
+HISPARSE_E_HIP = -3
+HISPARSE_E_UNSUPPORTED = -4
+
+ERR_BAD_INDEX = 1
+ERR_DUP_REQUEST = 2
+ERR_PAGE_OVERFLOW = 4
+ERR_BAD_ROW = 8
+
+POLICY = {"lru": 0, "clock": 1}
+
+MAX_HOT = 32768
+MAX_WORKING_SET = 8192
+
+c_i32 = ctypes.c_int32
+c_vp = ctypes.c_void_p
+
+
+class HisparseConfig(ctypes.Structure):
+    _fields_ = [
+        ("max_requests", c_i32), ("num_layers", c_i32), ("hot_buffer_size", c_i32),
+        ("top_k", c_i32), ("max_steps", c_i32), ("page_size", c_i32),
+        ("item_size_bytes", c_i32), ("max_seq_len", c_i32), ("policy", c_i32),
+        ("max_batch", c_i32), ("host_kv", ctypes.POINTER(c_vp)),
+        ("dev_kv", ctypes.POINTER(c_vp)),
+    ]
+
+
+class HisparseMissPlan(ctypes.Structure):
+    _fields_ = [("miss_src", c_vp), ("miss_dst", c_vp), ("victim", c_vp), ("capacity", c_i32)]
+
+
+class HisparseProfile(ctypes.Structure):
+    _fields_ = [("calls", ctypes.c_int64), ("plan_ms", ctypes.c_double),
+                ("copy_ms", ctypes.c_double)]
+
+
+_SIGNATURES = {
+    "hisparse_device_rows_per_request": (ctypes.c_int64, [ctypes.POINTER(HisparseConfig)]),
+    "hisparse_state_create": (ctypes.c_int, [ctypes.POINTER(HisparseConfig), c_vp,
+                                             ctypes.POINTER(c_vp)]),
+    "hisparse_state_destroy": (None, [c_vp]),
+    "hisparse_swap_in_selected": (ctypes.c_int, [c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp,
+                                                 c_vp, c_vp, c_vp,
+                                                 ctypes.POINTER(HisparseMissPlan), c_vp]),
+    "hisparse_swap_in_spec_multistep": (ctypes.c_int, [c_vp, c_i32, c_i32, c_i32, c_vp, c_vp,
+                                                       c_vp, c_vp, c_vp,
+                                                       ctypes.POINTER(HisparseMissPlan),
+                                                       c_vp]),
+    "hisparse_request_reset": (ctypes.c_int, [c_vp, c_i32, c_vp, c_vp]),
+    "hisparse_plan_capacity": (c_i32, [c_vp]),
+    "hisparse_state_export": (ctypes.c_int, [c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "hisparse_state_import": (ctypes.c_int, [c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]),
+    "hisparse_get_error_flags": (ctypes.c_int, [c_vp, ctypes.POINTER(ctypes.c_uint32), c_i32,
+                                                c_vp]),
+    "hisparse_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "hisparse_host_alloc": (ctypes.c_int, [ctypes.c_size_t, ctypes.POINTER(c_vp)]),
+    "hisparse_host_free": (ctypes.c_int, [c_vp]),
+    "hisparse_profile_enable": (ctypes.c_int, [c_vp, c_i32]),
+    "hisparse_profile_read": (ctypes.c_int, [c_vp, ctypes.POINTER(HisparseProfile)]),
+}
+
+EXPORTED = tuple(_SIGNATURES)
+
+_lib = None
+
+
+class HiSparseError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {strerror(code)} ({code})")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m sparse_attention_kv_request_amd.build`")
+        handle = ctypes.CDLL(str(LIB_PATH))
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().hisparse_strerror(code).decode()
+
+
+def _check(code: int, what: str) -> int:
+    if code != HISPARSE_OK:
+        raise HiSparseError(code, what)
+    return code
+
+
+# -- one-to-one wrappers of the C entry points ---------------------------------
+
+def hisparse_device_rows_per_request(cfg: HisparseConfig) -> int:
+    return lib().hisparse_device_rows_per_request(ctypes.byref(cfg))
+
+
+def hisparse_state_create(cfg: HisparseConfig, stream: int) -> int:
+    out = c_vp()
+    _check(lib().hisparse_state_create(ctypes.byref(cfg), stream, ctypes.byref(out)),
+           "hisparse_state_create")
+    return out.value
+
+
+def hisparse_state_destroy(st: int) -> None:
+    lib().hisparse_state_destroy(st)
+
+
+def hisparse_swap_in_selected(st, layer_id, batch, req_pool_indices, seq_lens, topk_indices,
+                              out_locs, miss_count, page_table, num_pages, plan, stream) -> int:
+    return lib().hisparse_swap_in_selected(st, layer_id, batch, req_pool_indices, seq_lens,
+                                           topk_indices, out_locs, miss_count, page_table,
+                                           num_pages, plan, stream)
+
+
+def hisparse_swap_in_spec_multistep(st, layer_id, batch, num_steps, req_pool_indices, seq_lens,
+                                    topk_indices, out_locs, miss_count, plan, stream) -> int:
+    return lib().hisparse_swap_in_spec_multistep(st, layer_id, batch, num_steps,
+                                                 req_pool_indices, seq_lens, topk_indices,
+                                                 out_locs, miss_count, plan, stream)
+
+
+def hisparse_request_reset(st, n, req_pool_indices, stream) -> int:
+    return lib().hisparse_request_reset(st, n, req_pool_indices, stream)
+
+
+def hisparse_plan_capacity(st) -> int:
+    return lib().hisparse_plan_capacity(st)
+
+
+def hisparse_state_export(st, req, layer, slot_key_h, policy_h, ctrl_h, key_slot_h, stream):
+    return lib().hisparse_state_export(st, req, layer, slot_key_h, policy_h, ctrl_h,
+                                       key_slot_h, stream)
+
+
+def hisparse_state_import(st, req, layer, slot_key_h, policy_h, ctrl_h, stream):
+    return lib().hisparse_state_import(st, req, layer, slot_key_h, policy_h, ctrl_h, stream)
+
+
+def hisparse_get_error_flags(st, clear: bool, stream) -> int:
+    v = ctypes.c_uint32()
+    _check(lib().hisparse_get_error_flags(st, ctypes.byref(v), int(clear), stream),
+           "hisparse_get_error_flags")
+    return v.value
+
+
+def hisparse_host_alloc(nbytes: int) -> int:
+    p = c_vp()
+    _check(lib().hisparse_host_alloc(nbytes, ctypes.byref(p)), "hisparse_host_alloc")
+    return p.value
+
+
+def hisparse_host_free(ptr: int) -> None:
+    _check(lib().hisparse_host_free(ptr), "hisparse_host_free")
+
+
+def hisparse_profile_enable(st, enable: bool) -> None:
+    _check(lib().hisparse_profile_enable(st, int(enable)), "hisparse_profile_enable")
+
+
+def hisparse_profile_read(st) -> dict:
+    p = HisparseProfile()
+    _check(lib().hisparse_profile_read(st, ctypes.byref(p)), "hisparse_profile_read")
+    return {"calls": p.calls, "plan_ms": p.plan_ms, "copy_ms": p.copy_ms}
+
+
+# -- conveniences ----------------------------------------------------------------
+
+class HostKV:
+    """Pinned, device-readable host buffer of one layer: uint8 [R, N, item]."""
+
+    def __init__(self, requests: int, seq_len: int, unit_bytes: int):
+        self.shape = (requests, seq_len, unit_bytes)
+        self.nbytes = requests * seq_len * unit_bytes
+        self.ptr = hisparse_host_alloc(self.nbytes)
+        raw = (ctypes.c_uint8 * self.nbytes).from_address(self.ptr)
+        self.array = np.ctypeslib.as_array(raw).reshape(self.shape)
+
+    def tensor(self) -> torch.Tensor:
+        """A CPU torch view sharing the pinned memory."""
+        return torch.from_numpy(self.array)
+
+    def free(self):
+        if self.ptr:
+            self.array = None
+            hisparse_host_free(self.ptr)
+            self.ptr = 0
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: torch.Tensor | None, dtype=torch.int32) -> int:
+    if t is None:
+        return 0
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"expected a contiguous {dtype} CUDA tensor")
+    return t.data_ptr()
+
+
+class HiSparseState:
+    """Owns a library state plus (optionally) the device KV buffers of every layer.
+
+    ``host_kv``: list of :class:`HostKV` (one per layer).  ``dev_kv``: list of
+    uint8 CUDA tensors ``[R, rows, item]`` (token) or ``[R, H, P * item]``
+    (page); allocated here when omitted.
+    """
+
+    def __init__(self, *, max_requests, num_layers, hot_buffer_size, top_k, item_size_bytes,
+                 max_seq_len, host_kv, max_steps=1, page_size=1, policy="lru",
+                 max_batch=None, dev_kv=None, stream=None):
+        self.cfg = HisparseConfig(
+            max_requests=max_requests, num_layers=num_layers, hot_buffer_size=hot_buffer_size,
+            top_k=top_k, max_steps=max_steps, page_size=page_size,
+            item_size_bytes=item_size_bytes, max_seq_len=max_seq_len, policy=POLICY[policy],
+            max_batch=max_batch or max_requests)
+        rows = hisparse_device_rows_per_request(self.cfg)
+        if rows < 0:
+            raise HiSparseError(rows, "hisparse_device_rows_per_request")
+        self.rows = rows
+        self.policy = policy
+        self.page_size = page_size
+        self.host_kv = host_kv
+        unit = item_size_bytes * page_size
+        if dev_kv is None:
+            dev_kv = [torch.zeros((max_requests, rows, unit), dtype=torch.uint8, device="cuda")
+                      for _ in range(num_layers)]
+        self.dev_kv = dev_kv
+        self._host_ptrs = (c_vp * num_layers)(*[h.ptr for h in host_kv])
+        self._dev_ptrs = (c_vp * num_layers)(*[d.data_ptr() for d in dev_kv])
+        self.cfg.host_kv = ctypes.cast(self._host_ptrs, ctypes.POINTER(c_vp))
+        self.cfg.dev_kv = ctypes.cast(self._dev_ptrs, ctypes.POINTER(c_vp))
+        self.handle = hisparse_state_create(self.cfg, _stream(stream))
+        self.capacity = hisparse_plan_capacity(self.handle)
+
+    # shapes
+    @property
+    def hot(self):
+        return self.cfg.hot_buffer_size
+
+    @property
+    def nkeys(self):
+        return self.cfg.max_seq_len // self.page_size
+
+    def close(self):
+        if getattr(self, "handle", None):
+            torch.cuda.synchronize()
+            hisparse_state_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @staticmethod
+    def _plan(plan):
+        if plan is None:
+            return None
+        src, dst, vic = plan
+        return ctypes.byref(HisparseMissPlan(_ptr(src), _ptr(dst), _ptr(vic), src.shape[-1]))
+
+    def swap_in_selected(self, layer_id, req_pool_indices, seq_lens, topk_indices, out_locs,
+                         miss_count, page_table=None, num_pages=None, plan=None, stream=None):
+        batch = int(req_pool_indices.shape[0])
+        rc = hisparse_swap_in_selected(
+            self.handle, layer_id, batch, _ptr(req_pool_indices), _ptr(seq_lens),
+            _ptr(topk_indices), _ptr(out_locs), _ptr(miss_count), _ptr(page_table),
+            _ptr(num_pages), self._plan(plan), _stream(stream))
+        return _check(rc, "hisparse_swap_in_selected")
+
+    def swap_in_spec_multistep(self, layer_id, req_pool_indices, seq_lens, topk_indices,
+                               out_locs, miss_count, plan=None, stream=None):
+        batch = int(req_pool_indices.shape[0])
+        num_steps = int(topk_indices.shape[1])
+        rc = hisparse_swap_in_spec_multistep(
+            self.handle, layer_id, batch, num_steps, _ptr(req_pool_indices), _ptr(seq_lens),
+            _ptr(topk_indices), _ptr(out_locs), _ptr(miss_count), self._plan(plan),
+            _stream(stream))
+        return _check(rc, "hisparse_swap_in_spec_multistep")
+
+    def request_reset(self, req_pool_indices: torch.Tensor, stream=None):
+        rc = hisparse_request_reset(self.handle, int(req_pool_indices.shape[0]),
+                                    _ptr(req_pool_indices), _stream(stream))
+        return _check(rc, "hisparse_request_reset")
+
+    def export(self, req: int, layer: int, with_map: bool = False, stream=None) -> dict:
+        H = self.hot
+        slot_key = np.empty(H, np.int32)
+        policy = np.empty(H, np.int32)
+        ctrl = np.empty(2, np.int32)
+        key_slot = np.empty(self.nkeys, np.int32) if with_map else None
+        rc = hisparse_state_export(
+            self.handle, req, layer, slot_key.ctypes.data, policy.ctypes.data, ctrl.ctypes.data,
+            key_slot.ctypes.data if with_map else None, _stream(stream))
+        _check(rc, "hisparse_state_export")
+        out = {"slot_key": slot_key, "ctrl": ctrl, "key_slot": key_slot}
+        out["ts" if self.policy == "lru" else "ref"] = policy
+        return out
+
+    def import_(self, req: int, layer: int, slot_key, policy, ctrl, stream=None):
+        slot_key = np.ascontiguousarray(slot_key, np.int32)
+        policy = np.ascontiguousarray(policy, np.int32)
+        ctrl = np.ascontiguousarray(ctrl, np.int32)
+        rc = hisparse_state_import(self.handle, req, layer, slot_key.ctypes.data,
+                                   policy.ctypes.data, ctrl.ctypes.data, _stream(stream))
+        return _check(rc, "hisparse_state_import")
+
+    def error_flags(self, clear: bool = True, stream=None) -> int:
+        return hisparse_get_error_flags(self.handle, clear, _stream(stream))
+
+    def profile(self, enable: bool):
+        hisparse_profile_enable(self.handle, enable)
+
+    def profile_read(self) -> dict:
+        return hisparse_profile_read(self.handle)

@@ -1,0 +1,59 @@
+"""Builds ``libhisparse.so`` (C ABI + HIP kernels for gfx950) in place.
+
+Usage: ``python -m sparse_attention_kv_request_amd.build`` (or ``build()``).
+Each source compiles to an object under ``_build/`` in parallel, then one
+link produces the shared library next to this file.
+"""
+from __future__ import annotations
+
+import concurrent.futures
+import os
+import pathlib
+import shutil
+import subprocess
+
+PKG = pathlib.Path(__file__).resolve().parent
+ROOT = PKG.parent
+CSRC = PKG / "csrc"
+INCLUDE = ROOT / "include"
+LIB = PKG / "libhisparse.so"
+BUILD = ROOT / "_build"
+
+HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    # packed fp32 instructions are kept out of every kernel
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}",
+]
+
+
+def sources():
+    return sorted(list(CSRC.glob("*.hip")) + list(CSRC.glob("*.cpp")))
+
+
+def _compile(src: pathlib.Path) -> pathlib.Path:
+    obj = BUILD / (src.name + ".o")
+    cmd = [HIPCC, *FLAGS, "-c", str(src), "-o", str(obj)]
+    if src.suffix == ".cpp":
+        cmd[1:1] = ["-x", "hip"]
+    subprocess.run(cmd, check=True)
+    return obj
+
+
+def build(verbose: bool = False) -> pathlib.Path:
+    BUILD.mkdir(exist_ok=True)
+    srcs = sources()
+    with concurrent.futures.ThreadPoolExecutor(min(8, os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    tmp = LIB.with_suffix(".so.tmp")
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC",
+                    *[str(o) for o in objs], "-o", str(tmp)], check=True)
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

@@ -1,0 +1,115 @@
+// Device helpers shared by the swap-in kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hisparse.h"
+
+namespace hisparse {
+
+constexpr int kWave = 64;
+constexpr int32_t kEmpty = -1;
+
+// Key words of the LDS working-set hash: (token + 1) in the low 28 bits, 0 =
+// empty bucket; bits 28..31 record which speculative steps named the token.
+constexpr uint32_t kKeyBits = 28;
+constexpr uint32_t kKeyMask = (1u << kKeyBits) - 1u;
+
+// Everything a plan (lookup / victim / commit) kernel needs.  One workgroup
+// handles one batch row = one (request, layer) cache instance.
+struct PlanArgs {
+  // persistent state of the layer's instances, instance q = layer * R + r
+  int16_t* key_slot;    // [L*R][nkeys]  key -> slot, -1 = not resident
+  int32_t* slot_key;    // [L*R][H]      slot -> key, -1 = empty
+  int32_t* ts;          // [L*R][H]      LRU timestamp (-1 = empty)
+  int16_t* order;       // [L*R][H]      LRU order of slots, least recent first
+  uint32_t* refbits;    // [L*R][Hw]     CLOCK reference bits
+  int32_t* ctrl;        // [L*R][2]      {LRU call counter, CLOCK hand}
+  uint32_t* err;        // sticky error word
+  int32_t R, H, Hw, K, S, N, P, nkeys, rows, layer;
+  // the call
+  int32_t batch;
+  const int32_t* req;
+  const int32_t* seq;
+  const int32_t* topk;
+  int32_t* out_locs;
+  int32_t* miss_count;
+  int32_t* page_table;
+  int32_t* num_pages;
+  int32_t* miss_src;    // [batch][cap]
+  int32_t* miss_dst;
+  int32_t* victim;
+  int32_t cap;
+  int32_t hash_size;    // LDS hash buckets
+};
+
+// Exclusive prefix sum over the NT threads of a workgroup.  `scratch` holds
+// NT/64 + 1 ints of LDS.  Returns the exclusive prefix; *total receives the
+// sum.  Contains barriers: every thread of the block must call it.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
+  static_assert(NT % kWave == 0 && NT / kWave <= kWave, "block shape");
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    int y = __shfl_up(x, d, kWave);
+    if (lane >= d) x += y;
+  }
+  if (lane == kWave - 1) scratch[wid] = x;
+  __syncthreads();
+  if (wid == 0) {
+    int w = lane < NT / kWave ? scratch[lane] : 0;
+    int s = w;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      int y = __shfl_up(s, d, kWave);
+      if (lane >= d) s += y;
+    }
+    if (lane < NT / kWave) scratch[lane] = s - w;
+    if (lane == NT / kWave - 1) scratch[NT / kWave] = s;
+  }
+  __syncthreads();
+  const int excl = scratch[wid] + x - v;
+  *total = scratch[NT / kWave];
+  __syncthreads();
+  return excl;
+}
+
+__device__ __forceinline__ bool bit_test(const uint32_t* bm, int i) {
+  return (bm[i >> 5] >> (i & 31)) & 1u;
+}
+__device__ __forceinline__ void bit_set_atomic(uint32_t* bm, int i) {
+  atomicOr(&bm[i >> 5], 1u << (i & 31));
+}
+__device__ __forceinline__ void bit_clear_atomic(uint32_t* bm, int i) {
+  atomicAnd(&bm[i >> 5], ~(1u << (i & 31)));
+}
+
+// Bucket of a token in an LDS hash of `size` buckets (multiplicative hash
+// scaled to the table size, any size).
+__device__ __forceinline__ int hash_bucket(int32_t t, int size) {
+  const uint32_t h = static_cast<uint32_t>(t) * 2654435761u;
+  return static_cast<int>((static_cast<uint64_t>(h) * static_cast<uint32_t>(size)) >> 32);
+}
+
+// Inserts token t (0 <= t < 2^28 - 1) into the open-addressing LDS table
+// `keys` (0 = empty) and returns its bucket.  The table is sized above the
+// number of distinct keys, so the probe terminates.
+__device__ __forceinline__ int hash_insert(uint32_t* keys, int size, int32_t t) {
+  const uint32_t want = static_cast<uint32_t>(t) + 1u;
+  int h = hash_bucket(t, size);
+  while (true) {
+    const uint32_t old = atomicCAS(&keys[h], 0u, want);
+    if (old == 0u || (old & kKeyMask) == want) return h;
+    h = (h + 1 == size) ? 0 : h + 1;
+  }
+}
+
+__device__ __forceinline__ void raise_error(uint32_t* err, uint32_t bits) {
+  atomicOr(err, bits);
+}
+
+}  // namespace hisparse

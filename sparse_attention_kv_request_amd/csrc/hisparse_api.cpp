@@ -1,0 +1,553 @@
+// C ABI of the HiSparse swap-in path: validation, state memory, launches.
+//
+// Every swap call enqueues exactly two kernels on the caller's stream (the
+// plan kernel, then the miss copy), allocates nothing and never synchronises
+// the host; this keeps the pages' stream-ordering lesson (PR #20343 summary,
+// "Review highlights": an overlap race fixed by a stream wait) structural --
+// there is no side stream to wait for.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <numeric>
+#include <vector>
+
+#include "internal.h"
+
+using namespace hisparse;
+
+namespace {
+
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int dev) {
+    int cur = -1;
+    if (hipGetDevice(&cur) == hipSuccess && cur != dev && hipSetDevice(dev) == hipSuccess)
+      prev = cur;
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+struct Derived {
+  int32_t rows = 0;
+  int32_t scratch = 0;
+  int32_t nkeys = 0;
+  int32_t hw = 0;
+  int32_t cap = 0;
+};
+
+// Scalar validation of a configuration; pointer arrays are checked by create.
+int derive(const hisparse_config_t* c, Derived* d) {
+  if (c == nullptr) return HISPARSE_E_INVAL;
+  const bool lru = c->policy == HISPARSE_POLICY_LRU;
+  const bool clock = c->policy == HISPARSE_POLICY_CLOCK;
+  if (!lru && !clock) return HISPARSE_E_INVAL;
+  if (c->max_requests < 1 || c->num_layers < 1 || c->top_k < 1 || c->page_size < 1)
+    return HISPARSE_E_INVAL;
+  if (c->hot_buffer_size < 1 || c->hot_buffer_size > HISPARSE_MAX_HOT) return HISPARSE_E_INVAL;
+  if (c->item_size_bytes < 16 || c->item_size_bytes % 16) return HISPARSE_E_INVAL;
+  if (c->max_seq_len < 1) return HISPARSE_E_INVAL;
+  if (c->max_seq_len > HISPARSE_MAX_SEQ_LEN) return HISPARSE_E_UNSUPPORTED;
+  if (c->max_batch < 1 || c->max_batch > c->max_requests) return HISPARSE_E_INVAL;
+  const int64_t H = c->hot_buffer_size, K = c->top_k, P = c->page_size;
+  if (lru) {
+    if (c->max_steps != 1) return HISPARSE_E_INVAL;
+    if (K > HISPARSE_MAX_WORKING_SET) return HISPARSE_E_UNSUPPORTED;
+    if (P == 1) {
+      if (K > H) return HISPARSE_E_INVAL;  // a row's distinct tokens must fit
+    } else {
+      if (c->max_seq_len % P) return HISPARSE_E_INVAL;
+      if (c->max_seq_len / P > HISPARSE_MAX_PAGES_PER_REQUEST) return HISPARSE_E_UNSUPPORTED;
+      if (H > kMaxPageModeHot) return HISPARSE_E_UNSUPPORTED;
+    }
+  } else {
+    if (P != 1) return HISPARSE_E_INVAL;
+    if (c->max_steps < HISPARSE_MIN_STEPS || c->max_steps > HISPARSE_MAX_STEPS)
+      return HISPARSE_E_INVAL;
+    if (c->max_steps * K > HISPARSE_MAX_WORKING_SET) return HISPARSE_E_UNSUPPORTED;
+  }
+  d->scratch = clock ? static_cast<int32_t>(std::max<int64_t>(0, c->max_steps * K - H)) : 0;
+  d->rows = P > 1 ? static_cast<int32_t>(H) : static_cast<int32_t>(H + d->scratch);
+  d->nkeys = P > 1 ? c->max_seq_len / c->page_size : c->max_seq_len;
+  d->hw = static_cast<int32_t>((H + 31) / 32);
+  d->cap = P > 1 ? static_cast<int32_t>(H) : static_cast<int32_t>(c->max_steps * K);
+  // host rows, device rows and plan entries are int32
+  const int64_t R = c->max_requests;
+  if (R * d->nkeys >= (int64_t{1} << 31) || R * d->rows >= (int64_t{1} << 31))
+    return HISPARSE_E_UNSUPPORTED;
+  return HISPARSE_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t{255}; }
+
+int status_of(hipError_t e) {
+  if (e == hipSuccess) return HISPARSE_OK;
+  if (e == hipErrorOutOfMemory) return HISPARSE_E_NOMEM;
+  return HISPARSE_E_HIP;
+}
+
+PlanArgs plan_args(const hisparse_state* st, int32_t layer, int32_t batch, int32_t steps,
+                   const int32_t* req, const int32_t* seq, const int32_t* topk, int32_t* out,
+                   int32_t* miss_count, int32_t* page_table, int32_t* num_pages,
+                   const hisparse_miss_plan_t* plan) {
+  PlanArgs a{};
+  a.key_slot = st->key_slot;
+  a.slot_key = st->slot_key;
+  a.ts = st->ts;
+  a.order = st->order;
+  a.refbits = st->refbits;
+  a.ctrl = st->ctrl;
+  a.err = st->err;
+  a.R = st->cfg.max_requests;
+  a.H = st->cfg.hot_buffer_size;
+  a.Hw = st->hw;
+  a.K = st->cfg.top_k;
+  a.S = steps;
+  a.N = st->cfg.max_seq_len;
+  a.P = st->cfg.page_size;
+  a.nkeys = st->nkeys;
+  a.rows = st->rows;
+  a.layer = layer;
+  a.batch = batch;
+  a.req = req;
+  a.seq = seq;
+  a.topk = topk;
+  a.out_locs = out;
+  a.miss_count = miss_count;
+  a.page_table = page_table;
+  a.num_pages = num_pages;
+  if (plan != nullptr) {
+    a.miss_src = plan->miss_src;
+    a.miss_dst = plan->miss_dst;
+    a.victim = plan->victim;
+    a.cap = plan->capacity;
+  } else {
+    a.miss_src = st->ws_src;
+    a.miss_dst = st->ws_dst;
+    a.victim = st->ws_victim;
+    a.cap = st->cap;
+  }
+  return a;
+}
+
+// Accumulated profile of drained event triples.
+struct ProfileSums {
+  int64_t calls = 0;
+  double plan_ms = 0, copy_ms = 0;
+};
+
+hipError_t drain_events(hisparse_state* st, ProfileSums* sums) {
+  hipError_t err = hipSuccess;
+  for (size_t i = 0; i + 2 < st->ev_pending.size(); i += 3) {
+    hipEvent_t e0 = st->ev_pending[i], e1 = st->ev_pending[i + 1], e2 = st->ev_pending[i + 2];
+    hipError_t e = hipEventSynchronize(e2);
+    float t1 = 0, t2 = 0;
+    if (e == hipSuccess) e = hipEventElapsedTime(&t1, e0, e1);
+    if (e == hipSuccess) e = hipEventElapsedTime(&t2, e1, e2);
+    if (e == hipSuccess) {
+      sums->calls += 1;
+      sums->plan_ms += t1;
+      sums->copy_ms += t2;
+    } else {
+      err = e;
+    }
+    st->ev_free.push_back(e0);
+    st->ev_free.push_back(e1);
+    st->ev_free.push_back(e2);
+  }
+  st->ev_pending.clear();
+  return err;
+}
+
+hipEvent_t take_event(hisparse_state* st) {
+  if (st->ev_free.empty()) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDefault) != hipSuccess) return nullptr;
+    return e;
+  }
+  hipEvent_t e = st->ev_free.back();
+  st->ev_free.pop_back();
+  return e;
+}
+
+struct ProfiledState : hisparse_state {
+  ProfileSums sums;
+};
+
+void record(hisparse_state* st, hipStream_t s) {
+  if (!st->profiling) return;
+  hipEvent_t e = take_event(st);
+  if (e == nullptr) return;
+  if (hipEventRecord(e, s) != hipSuccess) {
+    st->ev_free.push_back(e);
+    return;
+  }
+  st->ev_pending.push_back(e);
+}
+
+int run_swap(hisparse_state* st, const PlanArgs& a, bool multistep, hipStream_t s) {
+  auto* ps = static_cast<ProfiledState*>(st);
+  if (st->profiling && st->ev_pending.size() >= 3 * 4096) (void)drain_events(st, &ps->sums);
+  const size_t mark = st->ev_pending.size();
+  record(st, s);
+  hipError_t e;
+  if (multistep)
+    e = launch_clock_plan(a, s);
+  else if (st->cfg.page_size > 1)
+    e = launch_lru_page_plan(a, s);
+  else
+    e = launch_lru_token_plan(a, s);
+  if (e != hipSuccess) return status_of(e);
+  record(st, s);
+  CopyArgs c{};
+  c.miss_count = a.miss_count;
+  c.src = a.miss_src;
+  c.dst = a.miss_dst;
+  c.batch = a.batch;
+  c.cap = a.cap;
+  c.host = st->host_kv[a.layer];
+  c.dev = st->dev_kv[a.layer];
+  const int64_t unit = static_cast<int64_t>(st->cfg.item_size_bytes) * st->cfg.page_size;
+  c.unit_bytes = unit;
+  c.unit16 = static_cast<int32_t>(unit / 16);
+  e = launch_miss_copy(c, s);
+  if (e != hipSuccess) return status_of(e);
+  record(st, s);
+  if (st->profiling && st->ev_pending.size() - mark != 3) {
+    // an event could not be taken: drop this call's partial triple
+    while (st->ev_pending.size() > mark) {
+      st->ev_free.push_back(st->ev_pending.back());
+      st->ev_pending.pop_back();
+    }
+  }
+  return HISPARSE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t hisparse_device_rows_per_request(const hisparse_config_t* cfg) {
+  Derived d;
+  const int rc = derive(cfg, &d);
+  return rc == HISPARSE_OK ? d.rows : rc;
+}
+
+int hisparse_state_create(const hisparse_config_t* cfg, void* stream, hisparse_state_t* out) {
+  if (out == nullptr) return HISPARSE_E_INVAL;
+  *out = nullptr;
+  Derived d;
+  int rc = derive(cfg, &d);
+  if (rc != HISPARSE_OK) return rc;
+  if (cfg->host_kv == nullptr || cfg->dev_kv == nullptr) return HISPARSE_E_INVAL;
+  const int L = cfg->num_layers, R = cfg->max_requests, H = cfg->hot_buffer_size;
+  const bool lru = cfg->policy == HISPARSE_POLICY_LRU;
+  int device = 0;
+  if (hipGetDevice(&device) != hipSuccess) return HISPARSE_E_HIP;
+
+  auto* st = new (std::nothrow) ProfiledState();
+  if (st == nullptr) return HISPARSE_E_NOMEM;
+  st->cfg = *cfg;
+  st->cfg.host_kv = nullptr;
+  st->cfg.dev_kv = nullptr;
+  st->device = device;
+  st->rows = d.rows;
+  st->scratch = d.scratch;
+  st->nkeys = d.nkeys;
+  st->hw = d.hw;
+  st->cap = d.cap;
+  for (int l = 0; l < L; ++l) {
+    hipPointerAttribute_t attr{};
+    const void* hp = cfg->host_kv[l];
+    void* dp = cfg->dev_kv[l];
+    if (hp == nullptr || dp == nullptr ||
+        hipPointerGetAttributes(&attr, hp) != hipSuccess || attr.type != hipMemoryTypeHost ||
+        attr.devicePointer == nullptr) {
+      (void)hipGetLastError();
+      delete st;
+      return HISPARSE_E_INVAL;
+    }
+    st->host_kv.push_back(static_cast<const uint8_t*>(attr.devicePointer));
+    hipPointerAttribute_t dattr{};
+    if (hipPointerGetAttributes(&dattr, dp) != hipSuccess || dattr.type != hipMemoryTypeDevice ||
+        dattr.device != device) {
+      (void)hipGetLastError();
+      delete st;
+      return HISPARSE_E_INVAL;
+    }
+    st->dev_kv.push_back(static_cast<uint8_t*>(dp));
+  }
+
+  const size_t inst = static_cast<size_t>(L) * R;
+  size_t off = 0;
+  const size_t o_key_slot = off; off += align256(inst * d.nkeys * sizeof(int16_t));
+  const size_t o_slot_key = off; off += align256(inst * H * sizeof(int32_t));
+  const size_t o_ts = off;       off += lru ? align256(inst * H * sizeof(int32_t)) : 0;
+  const size_t o_order = off;    off += lru ? align256(inst * H * sizeof(int16_t)) : 0;
+  const size_t o_ref = off;      off += lru ? 0 : align256(inst * d.hw * sizeof(uint32_t));
+  const size_t o_ctrl = off;     off += align256(inst * 2 * sizeof(int32_t));
+  const size_t ws = align256(static_cast<size_t>(cfg->max_batch) * d.cap * sizeof(int32_t));
+  const size_t o_src = off;      off += ws;
+  const size_t o_dst = off;      off += ws;
+  const size_t o_vic = off;      off += ws;
+  const size_t o_err = off;      off += 256;
+  hipError_t e = hipMalloc(&st->arena, off);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    delete st;
+    return status_of(e);
+  }
+  auto* base = static_cast<uint8_t*>(st->arena);
+  st->key_slot = reinterpret_cast<int16_t*>(base + o_key_slot);
+  st->slot_key = reinterpret_cast<int32_t*>(base + o_slot_key);
+  st->ts = lru ? reinterpret_cast<int32_t*>(base + o_ts) : nullptr;
+  st->order = lru ? reinterpret_cast<int16_t*>(base + o_order) : nullptr;
+  st->refbits = lru ? nullptr : reinterpret_cast<uint32_t*>(base + o_ref);
+  st->ctrl = reinterpret_cast<int32_t*>(base + o_ctrl);
+  st->ws_src = reinterpret_cast<int32_t*>(base + o_src);
+  st->ws_dst = reinterpret_cast<int32_t*>(base + o_dst);
+  st->ws_victim = reinterpret_cast<int32_t*>(base + o_vic);
+  st->err = reinterpret_cast<uint32_t*>(base + o_err);
+
+  auto s = static_cast<hipStream_t>(stream);
+  e = hipMemsetAsync(st->err, 0, sizeof(uint32_t), s);
+  if (e == hipSuccess) {
+    ResetArgs ra{nullptr, st->key_slot, st->slot_key, st->ts, st->order, st->refbits,
+                 st->ctrl, st->err, R, H, d.hw, d.nkeys};
+    e = launch_reset(ra, R, L, s);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    (void)hipFree(st->arena);
+    delete st;
+    return status_of(e);
+  }
+  *out = st;
+  return HISPARSE_OK;
+}
+
+void hisparse_state_destroy(hisparse_state_t st) {
+  if (st == nullptr) return;
+  DeviceGuard g(st->device);
+  for (hipEvent_t e : st->ev_pending) (void)hipEventDestroy(e);
+  for (hipEvent_t e : st->ev_free) (void)hipEventDestroy(e);
+  (void)hipFree(st->arena);
+  delete static_cast<ProfiledState*>(st);
+}
+
+int32_t hisparse_plan_capacity(hisparse_state_t st) { return st ? st->cap : HISPARSE_E_INVAL; }
+
+int hisparse_swap_in_selected(hisparse_state_t st, int32_t layer_id, int32_t batch,
+                              const int32_t* req_pool_indices, const int32_t* seq_lens,
+                              const int32_t* topk_indices, int32_t* out_locs,
+                              int32_t* miss_count, int32_t* page_table, int32_t* num_pages,
+                              const hisparse_miss_plan_t* plan, void* stream) {
+  if (st == nullptr || st->cfg.policy != HISPARSE_POLICY_LRU) return HISPARSE_E_INVAL;
+  if (layer_id < 0 || layer_id >= st->cfg.num_layers) return HISPARSE_E_INVAL;
+  if (batch < 0 || batch > st->cfg.max_batch) return HISPARSE_E_INVAL;
+  if (batch == 0) return HISPARSE_OK;
+  if (!req_pool_indices || !seq_lens || !topk_indices || !out_locs || !miss_count)
+    return HISPARSE_E_INVAL;
+  const bool page = st->cfg.page_size > 1;
+  if (page && (page_table == nullptr || num_pages == nullptr)) return HISPARSE_E_INVAL;
+  if (plan && (!plan->miss_src || !plan->miss_dst || !plan->victim || plan->capacity < st->cap))
+    return HISPARSE_E_INVAL;
+  DeviceGuard g(st->device);
+  PlanArgs a = plan_args(st, layer_id, batch, 1, req_pool_indices, seq_lens, topk_indices,
+                         out_locs, miss_count, page ? page_table : nullptr,
+                         page ? num_pages : nullptr, plan);
+  a.hash_size = page ? 0 : hash_size_for(a.K);
+  return run_swap(st, a, false, static_cast<hipStream_t>(stream));
+}
+
+int hisparse_swap_in_spec_multistep(hisparse_state_t st, int32_t layer_id, int32_t batch,
+                                    int32_t num_steps, const int32_t* req_pool_indices,
+                                    const int32_t* seq_lens, const int32_t* topk_indices,
+                                    int32_t* out_locs, int32_t* miss_count,
+                                    const hisparse_miss_plan_t* plan, void* stream) {
+  if (st == nullptr || st->cfg.policy != HISPARSE_POLICY_CLOCK) return HISPARSE_E_INVAL;
+  if (layer_id < 0 || layer_id >= st->cfg.num_layers) return HISPARSE_E_INVAL;
+  if (num_steps < HISPARSE_MIN_STEPS || num_steps > st->cfg.max_steps) return HISPARSE_E_INVAL;
+  if (batch < 0 || batch > st->cfg.max_batch) return HISPARSE_E_INVAL;
+  if (batch == 0) return HISPARSE_OK;
+  if (!req_pool_indices || !seq_lens || !topk_indices || !out_locs || !miss_count)
+    return HISPARSE_E_INVAL;
+  if (plan && (!plan->miss_src || !plan->miss_dst || !plan->victim || plan->capacity < st->cap))
+    return HISPARSE_E_INVAL;
+  DeviceGuard g(st->device);
+  PlanArgs a = plan_args(st, layer_id, batch, num_steps, req_pool_indices, seq_lens,
+                         topk_indices, out_locs, miss_count, nullptr, nullptr, plan);
+  const int E = num_steps * a.K;
+  a.hash_size = std::max(64, ((3 * E / 2 + 64) + 63) / 64 * 64);
+  return run_swap(st, a, true, static_cast<hipStream_t>(stream));
+}
+
+int hisparse_request_reset(hisparse_state_t st, int32_t n, const int32_t* req_pool_indices,
+                           void* stream) {
+  if (st == nullptr || n < 0) return HISPARSE_E_INVAL;
+  if (n == 0) return HISPARSE_OK;
+  if (req_pool_indices == nullptr) return HISPARSE_E_INVAL;
+  DeviceGuard g(st->device);
+  ResetArgs ra{req_pool_indices, st->key_slot, st->slot_key, st->ts, st->order, st->refbits,
+               st->ctrl, st->err, st->cfg.max_requests, st->cfg.hot_buffer_size, st->hw,
+               st->nkeys};
+  return status_of(launch_reset(ra, n, st->cfg.num_layers, static_cast<hipStream_t>(stream)));
+}
+
+int hisparse_state_export(hisparse_state_t st, int32_t req, int32_t layer, int32_t* slot_key_h,
+                          int32_t* policy_h, int32_t* ctrl_h, int32_t* key_slot_h,
+                          void* stream) {
+  if (st == nullptr || !slot_key_h || !policy_h || !ctrl_h) return HISPARSE_E_INVAL;
+  if (req < 0 || req >= st->cfg.max_requests || layer < 0 || layer >= st->cfg.num_layers)
+    return HISPARSE_E_INVAL;
+  DeviceGuard g(st->device);
+  auto s = static_cast<hipStream_t>(stream);
+  const size_t q = static_cast<size_t>(layer) * st->cfg.max_requests + req;
+  const int H = st->cfg.hot_buffer_size;
+  std::vector<uint32_t> bits(st->hw);
+  std::vector<int16_t> ks(key_slot_h ? st->nkeys : 0);
+  hipError_t e = hipMemcpyAsync(slot_key_h, st->slot_key + q * H, H * sizeof(int32_t),
+                                hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) {
+    if (st->ts)
+      e = hipMemcpyAsync(policy_h, st->ts + q * H, H * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+    else
+      e = hipMemcpyAsync(bits.data(), st->refbits + q * st->hw, st->hw * sizeof(uint32_t),
+                         hipMemcpyDeviceToHost, s);
+  }
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(ctrl_h, st->ctrl + 2 * q, 2 * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess && key_slot_h)
+    e = hipMemcpyAsync(ks.data(), st->key_slot + q * st->nkeys, st->nkeys * sizeof(int16_t),
+                       hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return status_of(e);
+  if (!st->ts)
+    for (int i = 0; i < H; ++i) policy_h[i] = (bits[i >> 5] >> (i & 31)) & 1u;
+  if (key_slot_h)
+    for (int i = 0; i < st->nkeys; ++i) key_slot_h[i] = ks[i];
+  return HISPARSE_OK;
+}
+
+int hisparse_state_import(hisparse_state_t st, int32_t req, int32_t layer,
+                          const int32_t* slot_key_h, const int32_t* policy_h,
+                          const int32_t* ctrl_h, void* stream) {
+  if (st == nullptr || !slot_key_h || !policy_h || !ctrl_h) return HISPARSE_E_INVAL;
+  if (req < 0 || req >= st->cfg.max_requests || layer < 0 || layer >= st->cfg.num_layers)
+    return HISPARSE_E_INVAL;
+  const int H = st->cfg.hot_buffer_size;
+  const bool lru = st->ts != nullptr;
+  std::vector<int16_t> ks(st->nkeys, static_cast<int16_t>(kEmpty));
+  for (int s = 0; s < H; ++s) {
+    const int32_t k = slot_key_h[s];
+    if (k == kEmpty) {
+      if (lru && policy_h[s] != -1) return HISPARSE_E_INVAL;
+      continue;
+    }
+    if (k < 0 || k >= st->nkeys || ks[k] != kEmpty) return HISPARSE_E_INVAL;
+    ks[k] = static_cast<int16_t>(s);
+    if (lru && (policy_h[s] < 0 || policy_h[s] >= ctrl_h[0])) return HISPARSE_E_INVAL;
+  }
+  std::vector<int16_t> order;
+  std::vector<uint32_t> bits;
+  if (lru) {
+    if (ctrl_h[0] < 0) return HISPARSE_E_INVAL;
+    std::vector<int32_t> idx(H);
+    std::iota(idx.begin(), idx.end(), 0);
+    std::stable_sort(idx.begin(), idx.end(),
+                     [&](int32_t x, int32_t y) { return policy_h[x] < policy_h[y]; });
+    order.assign(idx.begin(), idx.end());
+  } else {
+    if (ctrl_h[1] < 0 || ctrl_h[1] >= H) return HISPARSE_E_INVAL;
+    bits.assign(st->hw, 0u);
+    for (int s = 0; s < H; ++s) {
+      if (policy_h[s] != 0 && policy_h[s] != 1) return HISPARSE_E_INVAL;
+      if (policy_h[s]) bits[s >> 5] |= 1u << (s & 31);
+    }
+  }
+  DeviceGuard g(st->device);
+  auto s = static_cast<hipStream_t>(stream);
+  const size_t q = static_cast<size_t>(layer) * st->cfg.max_requests + req;
+  hipError_t e = hipMemcpyAsync(st->slot_key + q * H, slot_key_h, H * sizeof(int32_t),
+                                hipMemcpyHostToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(st->key_slot + q * st->nkeys, ks.data(), st->nkeys * sizeof(int16_t),
+                       hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && lru)
+    e = hipMemcpyAsync(st->ts + q * H, policy_h, H * sizeof(int32_t), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && lru)
+    e = hipMemcpyAsync(st->order + q * H, order.data(), H * sizeof(int16_t),
+                       hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && !lru)
+    e = hipMemcpyAsync(st->refbits + q * st->hw, bits.data(), st->hw * sizeof(uint32_t),
+                       hipMemcpyHostToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(st->ctrl + 2 * q, ctrl_h, 2 * sizeof(int32_t), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return status_of(e);
+}
+
+int hisparse_get_error_flags(hisparse_state_t st, uint32_t* flags_h, int32_t clear,
+                             void* stream) {
+  if (st == nullptr || flags_h == nullptr) return HISPARSE_E_INVAL;
+  DeviceGuard g(st->device);
+  auto s = static_cast<hipStream_t>(stream);
+  uint32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, st->err, sizeof(uint32_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess && clear) e = hipMemsetAsync(st->err, 0, sizeof(uint32_t), s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return status_of(e);
+  *flags_h = v;
+  return HISPARSE_OK;
+}
+
+const char* hisparse_strerror(int code) {
+  switch (code) {
+    case HISPARSE_OK: return "success";
+    case HISPARSE_E_INVAL: return "invalid argument";
+    case HISPARSE_E_NOMEM: return "out of memory";
+    case HISPARSE_E_HIP: return "HIP runtime error";
+    case HISPARSE_E_UNSUPPORTED: return "outside the limits of this build";
+    default: return "unknown status";
+  }
+}
+
+int hisparse_host_alloc(size_t bytes, void** out_h) {
+  if (out_h == nullptr || bytes == 0) return HISPARSE_E_INVAL;
+  *out_h = nullptr;
+  hipError_t e = hipHostMalloc(out_h, bytes, hipHostMallocMapped);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    *out_h = nullptr;
+    return status_of(e) == HISPARSE_E_HIP ? HISPARSE_E_NOMEM : status_of(e);
+  }
+  return HISPARSE_OK;
+}
+
+int hisparse_host_free(void* p_h) {
+  if (p_h == nullptr) return HISPARSE_OK;
+  return status_of(hipHostFree(p_h));
+}
+
+int hisparse_profile_enable(hisparse_state_t st, int32_t enable) {
+  if (st == nullptr) return HISPARSE_E_INVAL;
+  st->profiling = enable != 0;
+  return HISPARSE_OK;
+}
+
+int hisparse_profile_read(hisparse_state_t st, hisparse_profile_t* out_h) {
+  if (st == nullptr || out_h == nullptr) return HISPARSE_E_INVAL;
+  DeviceGuard g(st->device);
+  auto* ps = static_cast<ProfiledState*>(st);
+  const hipError_t e = drain_events(st, &ps->sums);
+  out_h->calls = ps->sums.calls;
+  out_h->plan_ms = ps->sums.plan_ms;
+  out_h->copy_ms = ps->sums.copy_ms;
+  ps->sums = ProfileSums{};
+  return status_of(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,85 @@
+// Internal declarations shared by the ABI implementation and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "device_common.h"
+#include "hisparse.h"
+
+namespace hisparse {
+
+constexpr int kPlanThreads = 1024;  // one workgroup (16 waves) per batch row
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;      // 16-byte loads in flight per lane
+constexpr int kCopyBlocks = 1024;   // 4 workgroups per CU on 256 CUs
+constexpr int kMaxPageModeHot = 4096;
+
+// Miss copy: rows of `unit_bytes` from the host tier to the hot buffer.
+struct CopyArgs {
+  const int32_t* miss_count;  // [batch]
+  const int32_t* src;         // [batch][cap] host row
+  const int32_t* dst;         // [batch][cap] device row
+  int32_t batch;
+  int32_t cap;
+  const uint8_t* host;        // device-visible address of the host tier
+  uint8_t* dev;
+  int32_t unit16;             // 16-byte chunks per row
+  int64_t unit_bytes;
+};
+
+struct ResetArgs {
+  const int32_t* reqs;  // NULL = requests 0..n-1
+  int16_t* key_slot;
+  int32_t* slot_key;
+  int32_t* ts;
+  int16_t* order;
+  uint32_t* refbits;
+  int32_t* ctrl;
+  uint32_t* err;
+  int32_t R, H, Hw, nkeys;
+};
+
+int hash_size_for(int entries);
+size_t lru_token_lds_bytes(const PlanArgs& a);
+size_t lru_page_lds_bytes(const PlanArgs& a);
+size_t clock_lds_bytes(const PlanArgs& a);
+
+hipError_t launch_lru_token_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_lru_page_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_clock_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_miss_copy(const CopyArgs& a, hipStream_t s);
+hipError_t launch_reset(const ResetArgs& a, int n, int layers, hipStream_t s);
+
+}  // namespace hisparse
+
+struct hisparse_state {
+  hisparse_config_t cfg{};
+  std::vector<const uint8_t*> host_kv;  // device-visible addresses
+  std::vector<uint8_t*> dev_kv;
+  int device = 0;
+  int32_t rows = 0;     // device rows per request
+  int32_t scratch = 0;  // CLOCK scratch rows per request
+  int32_t nkeys = 0;    // keys per request (tokens or pages)
+  int32_t hw = 0;       // 32-bit words of an H-bit mask
+  int32_t cap = 0;      // plan capacity per row
+  // device memory, one allocation
+  void* arena = nullptr;
+  int16_t* key_slot = nullptr;
+  int32_t* slot_key = nullptr;
+  int32_t* ts = nullptr;
+  int16_t* order = nullptr;
+  uint32_t* refbits = nullptr;
+  int32_t* ctrl = nullptr;
+  int32_t* ws_src = nullptr;
+  int32_t* ws_dst = nullptr;
+  int32_t* ws_victim = nullptr;
+  uint32_t* err = nullptr;
+  // profiling
+  bool profiling = false;
+  std::vector<hipEvent_t> ev_free;
+  std::vector<hipEvent_t> ev_pending;  // triples: before plan, after plan, after copy
+};

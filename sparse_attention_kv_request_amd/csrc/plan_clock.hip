@@ -1,0 +1,337 @@
+// Multi-step CLOCK swap-in: one working set over all speculative steps.
+//
+// PR #32162 report, "Implementation breakdown" item 1: the top-k rows of all
+// MTP steps of a request are flattened, looked up once, their misses are
+// deduplicated across steps, and one CLOCK update places them; "Risks and
+// impact": once the misses exceed the cache, admission favours the recent
+// steps while the data of the call stays exact (here: the rest go to
+// per-request scratch rows).
+//
+// One workgroup per batch row.  The sequential CLOCK hand walk becomes two
+// prefix selections over the circular slot order starting at the hand:
+//   lap 1: unpinned slots with reference bit 0, in hand order;
+//   lap 2 (only if lap 1 has too few): unpinned slots whose bit was 1.
+// A slot the hand passes with bit 1 loses it; in lap-2 calls every unpinned
+// bit is cleared.  This reproduces the textbook sweep exactly.
+#include "internal.h"
+
+namespace hisparse {
+
+namespace {
+
+template <int NT>
+__device__ __forceinline__ uint32_t multistep_row_check(const PlanArgs& a, int b, int r, int sl) {
+  if (!(r >= 0 && r < a.R && sl >= 0 && sl <= a.N)) return HISPARSE_ERR_BAD_ROW;
+  int dup = 0;
+  for (int bb = threadIdx.x; bb < a.batch; bb += NT) dup |= (bb != b && a.req[bb] == r);
+  return __syncthreads_or(dup) ? HISPARSE_ERR_DUP_REQUEST : 0u;
+}
+
+template <int NT, int EPT, int EPH>
+__global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
+  extern __shared__ uint32_t lds[];
+  const int T = a.hash_size;
+  const int E = a.S * a.K;
+  uint32_t* hkey = lds;                                         // [T] key | step bits
+  int32_t* hval = reinterpret_cast<int32_t*>(hkey + T);         // [T] first pos, then row
+  uint32_t* pinned = reinterpret_cast<uint32_t*>(hval + T);     // [Hw]
+  uint32_t* refl = pinned + a.Hw;                               // [Hw] reference bits
+  int* scan = reinterpret_cast<int*>(refl + a.Hw);              // [NT/64+1]
+  int16_t* miss_h = reinterpret_cast<int16_t*>(scan + NT / kWave + 1);  // [E]
+  __shared__ int s_cnt[HISPARSE_MAX_STEPS];
+  __shared__ int s_klast;
+  __shared__ int s_last_slot;
+
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int r = a.req[b];
+  const int sl = a.seq[b];
+  const uint32_t code = multistep_row_check<NT>(a, b, r, sl);
+  if (code) {
+    int32_t* out = a.out_locs + static_cast<size_t>(b) * E;
+    for (int i = tid; i < E; i += NT) out[i] = -1;
+    if (tid == 0) {
+      a.miss_count[b] = 0;
+      raise_error(a.err, code);
+    }
+    return;
+  }
+  const size_t q = static_cast<size_t>(a.layer) * a.R + r;
+  int16_t* ks = a.key_slot + q * a.nkeys;
+  int32_t* sk = a.slot_key + q * a.H;
+  uint32_t* refq = a.refbits + q * a.Hw;
+  const int hand = a.ctrl[2 * q + 1];
+
+  for (int i = tid; i < T; i += NT) {
+    hkey[i] = 0u;
+    hval[i] = 0x7fffffff;
+  }
+  for (int i = tid; i < a.Hw; i += NT) {
+    pinned[i] = 0u;
+    refl[i] = refq[i];
+  }
+  if (tid < HISPARSE_MAX_STEPS) s_cnt[tid] = 0;
+  __syncthreads();
+
+  // 1. flatten [S][K] step-major; insert with the step bit
+  const int32_t* row = a.topk + static_cast<size_t>(b) * E;
+  int32_t tok[EPT];
+  int hpos[EPT];
+  bool bad_index = false;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int i = tid * EPT + e;
+    const int32_t t = i < E ? row[i] : -1;
+    const bool valid = t >= 0 && t < sl;
+    bad_index |= (!valid && t != -1);
+    tok[e] = valid ? t : -1;
+    hpos[e] = 0;
+  }
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    if (tok[e] >= 0) {
+      const int i = tid * EPT + e;
+      hpos[e] = hash_insert(hkey, T, tok[e]);
+      atomicMin(&hval[hpos[e]], i);
+      atomicOr(&hkey[hpos[e]], 1u << (kKeyBits + i / a.K));
+    }
+  }
+  __syncthreads();
+
+  // 2. representatives look up; hits are pinned and referenced
+  bool rep[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) rep[e] = tok[e] >= 0 && hval[hpos[e]] == tid * EPT + e;
+  __syncthreads();
+  int slot[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) slot[e] = rep[e] ? static_cast<int>(ks[tok[e]]) : -1;
+  int packed = 0;  // misses | hits << 16
+  int last[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    last[e] = 0;
+    if (!rep[e]) continue;
+    if (slot[e] >= 0) {
+      bit_set_atomic(pinned, slot[e]);
+      bit_set_atomic(refl, slot[e]);
+      hval[hpos[e]] = slot[e];
+      packed += 1 << 16;
+    } else {
+      last[e] = 31 - __clz(hkey[hpos[e]] >> kKeyBits);
+      atomicAdd(&s_cnt[last[e]], 1);
+      packed += 1;
+    }
+  }
+  int tot;
+  const int pre = block_exclusive_scan<NT>(packed, scan, &tot);
+  const int m = tot & 0xffff;
+  const int nhits = tot >> 16;
+  const int room = a.H - nhits;
+
+  // admitted misses: all, or (overflow) the latest last steps first
+  int ma = m;
+  int sstar = -1, take_eq = 0;
+  if (m > room) {
+    int acc = 0;
+    for (int s = a.S - 1; s >= 0; --s) {
+      if (acc + s_cnt[s] >= room) {
+        sstar = s;
+        take_eq = room - acc;
+        break;
+      }
+      acc += s_cnt[s];
+    }
+  }
+  bool adm[EPT];
+  int ja[EPT];
+  int jm[EPT];
+  {
+    int j = pre & 0xffff;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const bool miss = rep[e] && slot[e] < 0;
+      jm[e] = miss ? j : -1;
+      j += miss;
+    }
+  }
+  if (m > room) {
+    int neq = 0;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) neq += (jm[e] >= 0 && last[e] == sstar);
+    int eq_tot;
+    int req = block_exclusive_scan<NT>(neq, scan, &eq_tot);
+    int nadm = 0;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      adm[e] = false;
+      if (jm[e] < 0) continue;
+      if (last[e] > sstar) {
+        adm[e] = true;
+      } else if (last[e] == sstar) {
+        adm[e] = req < take_eq;
+        ++req;
+      }
+      nadm += adm[e];
+    }
+    int pa = block_exclusive_scan<NT>(nadm, scan, &ma);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      ja[e] = pa;
+      pa += adm[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      adm[e] = jm[e] >= 0;
+      ja[e] = jm[e];
+    }
+  }
+  int32_t* msrc = a.miss_src + static_cast<size_t>(b) * a.cap;
+  int32_t* mdst = a.miss_dst + static_cast<size_t>(b) * a.cap;
+  int32_t* mvic = a.victim + static_cast<size_t>(b) * a.cap;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    if (jm[e] < 0) continue;
+    if (adm[e]) {
+      miss_h[ja[e]] = static_cast<int16_t>(hpos[e]);
+    } else {  // scratch row H + jo, outside the cache
+      const int jo = jm[e] - ja[e];
+      hval[hpos[e]] = a.H + jo;
+      msrc[ma + jo] = r * a.nkeys + tok[e];
+      mdst[ma + jo] = r * a.rows + a.H + jo;
+      mvic[ma + jo] = -1;
+    }
+  }
+  __syncthreads();
+
+  // 3. CLOCK sweep over circular positions k (slot = (hand + k) mod H)
+  int sl_of[EPH];
+  bool pin[EPH], rf[EPH];
+  int n1 = 0;
+#pragma unroll
+  for (int e = 0; e < EPH; ++e) {
+    const int k = tid * EPH + e;
+    int s = hand + k;
+    if (s >= a.H) s -= a.H;
+    sl_of[e] = k < a.H ? s : -1;
+    pin[e] = k < a.H ? bit_test(pinned, s) : true;
+    rf[e] = k < a.H ? bit_test(refl, s) : false;
+    n1 += (!pin[e] && !rf[e]);
+  }
+  int e1_tot;
+  int r1 = block_exclusive_scan<NT>(n1, scan, &e1_tot);
+  int vrank[EPH];
+#pragma unroll
+  for (int e = 0; e < EPH; ++e) {
+    vrank[e] = -1;
+    if (!pin[e] && !rf[e]) {
+      if (r1 < ma) vrank[e] = r1;
+      ++r1;
+    }
+  }
+  if (e1_tot >= ma) {
+    if (ma > 0) {
+#pragma unroll
+      for (int e = 0; e < EPH; ++e)
+        if (vrank[e] == ma - 1) {
+          s_klast = tid * EPH + e;
+          s_last_slot = sl_of[e];
+        }
+    }
+    __syncthreads();
+    if (ma > 0) {
+      const int klast = s_klast;
+#pragma unroll
+      for (int e = 0; e < EPH; ++e)
+        if (!pin[e] && rf[e] && tid * EPH + e < klast) bit_clear_atomic(refl, sl_of[e]);
+    }
+  } else {
+    int n2 = 0;
+#pragma unroll
+    for (int e = 0; e < EPH; ++e) n2 += (!pin[e] && rf[e]);
+    int e2_tot;
+    int r2 = block_exclusive_scan<NT>(n2, scan, &e2_tot);
+#pragma unroll
+    for (int e = 0; e < EPH; ++e) {
+      if (!pin[e] && rf[e]) {
+        if (e1_tot + r2 < ma) vrank[e] = e1_tot + r2;
+        ++r2;
+        bit_clear_atomic(refl, sl_of[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EPH; ++e)
+      if (vrank[e] == ma - 1) s_last_slot = sl_of[e];
+  }
+  __syncthreads();
+
+  // 4. commit admitted misses into their victims
+#pragma unroll
+  for (int e = 0; e < EPH; ++e) {
+    if (vrank[e] < 0) continue;
+    const int j = vrank[e];
+    const int s = sl_of[e];
+    const int h = miss_h[j];
+    const int32_t key = static_cast<int32_t>(hkey[h] & kKeyMask) - 1;
+    const int32_t old = sk[s];
+    if (old >= 0) ks[old] = static_cast<int16_t>(kEmpty);
+    sk[s] = key;
+    ks[key] = static_cast<int16_t>(s);
+    bit_set_atomic(refl, s);
+    hval[h] = s;
+    msrc[j] = r * a.nkeys + key;
+    mdst[j] = r * a.rows + s;
+    mvic[j] = old;
+  }
+  __syncthreads();
+
+  for (int i = tid; i < a.Hw; i += NT) refq[i] = refl[i];
+  int32_t* out = a.out_locs + static_cast<size_t>(b) * E;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int i = tid * EPT + e;
+    if (i >= E) continue;
+    out[i] = tok[e] >= 0 ? r * a.rows + hval[hpos[e]] : -1;
+  }
+  if (tid == 0) {
+    a.miss_count[b] = m;
+    if (ma > 0) {
+      const int nh = s_last_slot + 1;
+      a.ctrl[2 * q + 1] = nh == a.H ? 0 : nh;
+    }
+  }
+  if (bad_index) raise_error(a.err, HISPARSE_ERR_BAD_INDEX);
+}
+
+}  // namespace
+
+size_t clock_lds_bytes(const PlanArgs& a) {
+  return (2 * static_cast<size_t>(a.hash_size) + 2 * a.Hw + kPlanThreads / kWave + 1) * 4 +
+         static_cast<size_t>(a.S) * a.K * 2;
+}
+
+hipError_t launch_clock_plan(const PlanArgs& a, hipStream_t s) {
+  const size_t lds = clock_lds_bytes(a);
+  const int E = a.S * a.K;
+  auto go = [&](auto kernel) -> hipError_t {
+    if (lds > 64 * 1024) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         static_cast<int>(lds));
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kernel, dim3(a.batch), dim3(kPlanThreads), lds, s, a);
+    return hipGetLastError();
+  };
+  if (E <= 2 * kPlanThreads) {
+    if (a.H <= 4 * kPlanThreads) return go(clock_plan<kPlanThreads, 2, 4>);
+    if (a.H <= 8 * kPlanThreads) return go(clock_plan<kPlanThreads, 2, 8>);
+    return go(clock_plan<kPlanThreads, 2, 32>);
+  }
+  if (a.H <= 4 * kPlanThreads) return go(clock_plan<kPlanThreads, 8, 4>);
+  if (a.H <= 8 * kPlanThreads) return go(clock_plan<kPlanThreads, 8, 8>);
+  return go(clock_plan<kPlanThreads, 8, 32>);
+}
+
+}  // namespace hisparse

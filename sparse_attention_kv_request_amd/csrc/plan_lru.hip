@@ -1,0 +1,437 @@
+// Single-step LRU swap-in: lookup, dedup, victim selection and commit.
+//
+// One workgroup resolves one batch row, i.e. one (request, layer) cache
+// instance (PR #20343 summary, "Implementation breakdown": hash lookup,
+// hit/miss handling and LRU update; "SGLang HiSparse" blog, section 2.1).
+//
+// Layout choices (gfx950):
+//  * key_slot is a direct-address table over the request's keys (int16 per
+//    token or page).  It plays the role of the pages' token->slot hash with a
+//    perfect hash: one 2-byte read per lookup, no probing, no tombstones.
+//  * The LRU order is an explicit slot list, least recent first, ties in
+//    slot order.  A call moves every slot it used to the back in slot order,
+//    so the list always equals the (timestamp, slot) order and the victims
+//    are its first m unused slots: two block scans, no sort.
+//  * Duplicates inside the row are found with an LDS hash (first occurrence
+//    wins by atomicMin of the position); misses are ranked in position order
+//    with block scans, so the result does not depend on thread timing.
+#include "internal.h"
+
+namespace hisparse {
+
+namespace {
+
+// Row checks shared by the single-step kernels: returns nonzero (and the
+// error bit) when the row must be rejected.  Uniform over the block.
+template <int NT>
+__device__ __forceinline__ uint32_t row_check(const PlanArgs& a, int b, int r, int sl) {
+  if (!(r >= 0 && r < a.R && sl >= 0 && sl <= a.N)) return HISPARSE_ERR_BAD_ROW;
+  int dup = 0;
+  for (int bb = threadIdx.x; bb < a.batch; bb += NT) dup |= (bb != b && a.req[bb] == r);
+  return __syncthreads_or(dup) ? HISPARSE_ERR_DUP_REQUEST : 0u;
+}
+
+template <int NT>
+__device__ void reject_row(const PlanArgs& a, int b, int entries, uint32_t code, bool page_mode) {
+  int32_t* out = a.out_locs + static_cast<size_t>(b) * entries;
+  for (int i = threadIdx.x; i < entries; i += NT) out[i] = -1;
+  if (page_mode) {
+    int32_t* pt = a.page_table + static_cast<size_t>(b) * a.H;
+    for (int j = threadIdx.x; j < a.H; j += NT) pt[j] = -1;
+  }
+  if (threadIdx.x == 0) {
+    a.miss_count[b] = 0;
+    if (page_mode) a.num_pages[b] = 0;
+    raise_error(a.err, code);
+  }
+}
+
+// Victim selection over the LRU order, commit of the m misses and rewrite of
+// the order.  `o` holds order positions tid*EPH .. tid*EPH+EPH-1.  `used` has
+// the bits of the slots hit by this call; victims are added to it.  Miss j
+// (key miss_key[j]) goes to vslot[j].
+template <int NT, int EPH>
+__device__ void lru_select_commit(const PlanArgs& a, int b, int r, int now, int m,
+                                  const int (&o)[EPH], uint32_t* used, const int32_t* miss_key,
+                                  int32_t* vslot, int* scan, int16_t* ks, int32_t* sk,
+                                  int32_t* tsq, int16_t* ord) {
+  const int tid = threadIdx.x;
+  bool avail[EPH];
+  int navail = 0;
+#pragma unroll
+  for (int e = 0; e < EPH; ++e) {
+    avail[e] = o[e] >= 0 && !bit_test(used, o[e]);
+    navail += avail[e];
+  }
+  int total_avail;
+  int rk = block_exclusive_scan<NT>(navail, scan, &total_avail);
+  int rank[EPH];
+#pragma unroll
+  for (int e = 0; e < EPH; ++e) {
+    rank[e] = rk;
+    rk += avail[e];
+  }
+  // commit: the owner of a victim slot replaces its key
+  int32_t* msrc = a.miss_src + static_cast<size_t>(b) * a.cap;
+  int32_t* mdst = a.miss_dst + static_cast<size_t>(b) * a.cap;
+  int32_t* mvic = a.victim + static_cast<size_t>(b) * a.cap;
+#pragma unroll
+  for (int e = 0; e < EPH; ++e) {
+    if (avail[e] && rank[e] < m) {
+      const int j = rank[e];
+      const int s = o[e];
+      const int32_t key = miss_key[j];
+      const int32_t old = sk[s];
+      if (old >= 0) ks[old] = static_cast<int16_t>(kEmpty);
+      sk[s] = key;
+      ks[key] = static_cast<int16_t>(s);
+      tsq[s] = now;
+      vslot[j] = s;
+      bit_set_atomic(used, s);
+      msrc[j] = r * a.nkeys + key;
+      mdst[j] = r * a.rows + s;
+      mvic[j] = old;
+    }
+  }
+  __syncthreads();
+  // untouched slots keep their relative order at the front
+#pragma unroll
+  for (int e = 0; e < EPH; ++e)
+    if (avail[e] && rank[e] >= m) ord[rank[e] - m] = static_cast<int16_t>(o[e]);
+  // slots used by this call (timestamp = now) go to the back in slot order
+  const int wpt = (a.Hw + NT - 1) / NT;
+  const int w0 = tid * wpt;
+  int cnt = 0;
+  for (int w = w0; w < w0 + wpt && w < a.Hw; ++w) cnt += __popc(used[w]);
+  int ntouched;
+  int pos = block_exclusive_scan<NT>(cnt, scan, &ntouched);
+  pos += a.H - ntouched;
+  for (int w = w0; w < w0 + wpt && w < a.Hw; ++w) {
+    uint32_t bits = used[w];
+    while (bits) {
+      const int bit = __ffs(bits) - 1;
+      bits &= bits - 1u;
+      ord[pos++] = static_cast<int16_t>(w * 32 + bit);
+    }
+  }
+}
+
+// -------------------------------------------------------------------------
+// Token mode
+// -------------------------------------------------------------------------
+template <int NT, int EPT, int EPH>
+__global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
+  extern __shared__ uint32_t lds[];
+  const int T = a.hash_size;
+  uint32_t* hkey = lds;                                            // [T]
+  int32_t* hval = reinterpret_cast<int32_t*>(hkey + T);            // [T]
+  uint32_t* used = reinterpret_cast<uint32_t*>(hval + T);          // [Hw]
+  int32_t* miss_key = reinterpret_cast<int32_t*>(used + a.Hw);     // [K]
+  int32_t* vslot = miss_key + a.K;                                 // [K]
+  int* scan = vslot + a.K;                                         // [NT/64+1]
+
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int r = a.req[b];
+  const int sl = a.seq[b];
+  const uint32_t code = row_check<NT>(a, b, r, sl);
+  if (code) {
+    reject_row<NT>(a, b, a.K, code, false);
+    return;
+  }
+  const size_t q = static_cast<size_t>(a.layer) * a.R + r;
+  int16_t* ks = a.key_slot + q * a.nkeys;
+  int32_t* sk = a.slot_key + q * a.H;
+  int32_t* tsq = a.ts + q * a.H;
+  int16_t* ord = a.order + q * a.H;
+  const int now = a.ctrl[2 * q];
+
+  // the LRU order is independent of the row: fetch it first
+  int o[EPH];
+#pragma unroll
+  for (int e = 0; e < EPH; ++e) {
+    const int k = tid * EPH + e;
+    o[e] = k < a.H ? static_cast<int>(ord[k]) : -1;
+  }
+  for (int i = tid; i < T; i += NT) {
+    hkey[i] = 0u;
+    hval[i] = 0x7fffffff;
+  }
+  for (int i = tid; i < a.Hw; i += NT) used[i] = 0u;
+  __syncthreads();
+
+  // 1. validate and insert every entry; the first occurrence keeps its position
+  const int32_t* row = a.topk + static_cast<size_t>(b) * a.K;
+  int32_t tok[EPT];
+  int hpos[EPT];
+  bool bad_index = false;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int i = tid * EPT + e;
+    const int32_t t = i < a.K ? row[i] : -1;
+    const bool valid = t >= 0 && t < sl;
+    bad_index |= (!valid && t != -1);
+    tok[e] = valid ? t : -1;
+    hpos[e] = 0;
+  }
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    if (tok[e] >= 0) {
+      hpos[e] = hash_insert(hkey, T, tok[e]);
+      atomicMin(&hval[hpos[e]], tid * EPT + e);
+    }
+  }
+  __syncthreads();
+
+  // 2. representatives look their key up
+  bool rep[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) rep[e] = tok[e] >= 0 && hval[hpos[e]] == tid * EPT + e;
+  __syncthreads();
+  int slot[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) slot[e] = rep[e] ? static_cast<int>(ks[tok[e]]) : -1;
+  int nmiss = 0;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    if (!rep[e]) continue;
+    if (slot[e] >= 0) {
+      bit_set_atomic(used, slot[e]);
+      tsq[slot[e]] = now;
+      hval[hpos[e]] = slot[e];
+    } else {
+      ++nmiss;
+    }
+  }
+  int m;
+  int j = block_exclusive_scan<NT>(nmiss, scan, &m);
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    if (rep[e] && slot[e] < 0) {
+      hval[hpos[e]] = -(j + 1);
+      miss_key[j] = tok[e];
+      ++j;
+    }
+  }
+  __syncthreads();
+
+  // 3. victims, commit, new order
+  lru_select_commit<NT, EPH>(a, b, r, now, m, o, used, miss_key, vslot, scan, ks, sk, tsq, ord);
+  __syncthreads();
+
+  // 4. outputs
+  int32_t* out = a.out_locs + static_cast<size_t>(b) * a.K;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int i = tid * EPT + e;
+    if (i >= a.K) continue;
+    int loc = -1;
+    if (tok[e] >= 0) {
+      const int v = hval[hpos[e]];
+      loc = r * a.rows + (v >= 0 ? v : vslot[-v - 1]);
+    }
+    out[i] = loc;
+  }
+  if (tid == 0) {
+    a.miss_count[b] = m;
+    a.ctrl[2 * q] = now + 1;
+  }
+  if (bad_index) raise_error(a.err, HISPARSE_ERR_BAD_INDEX);
+}
+
+// -------------------------------------------------------------------------
+// Page mode ("SGLang HiSparse" blog, sections 1.3 and 2.3)
+// -------------------------------------------------------------------------
+template <int NT, int EPT, int EPH>
+__global__ __launch_bounds__(NT) void lru_page_plan(PlanArgs a) {
+  extern __shared__ uint32_t lds[];
+  const int npw = (a.nkeys + 31) / 32;
+  uint32_t* pbits = lds;                                           // [npw] pages named
+  int32_t* wpre = reinterpret_cast<int32_t*>(pbits + npw);         // [npw] pages before word
+  uint32_t* used = reinterpret_cast<uint32_t*>(wpre + npw);        // [Hw]
+  int32_t* pslot = reinterpret_cast<int32_t*>(used + a.Hw);        // [H] page list, then slot
+  int32_t* miss_key = pslot + a.H;                                 // [H]
+  int32_t* vslot = miss_key + a.H;                                 // [H]
+  int* scan = vslot + a.H;                                         // [NT/64+1]
+
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int r = a.req[b];
+  const int sl = a.seq[b];
+  const uint32_t code = row_check<NT>(a, b, r, sl);
+  if (code) {
+    reject_row<NT>(a, b, a.K, code, true);
+    return;
+  }
+  const size_t q = static_cast<size_t>(a.layer) * a.R + r;
+  int16_t* ks = a.key_slot + q * a.nkeys;
+  int32_t* sk = a.slot_key + q * a.H;
+  int32_t* tsq = a.ts + q * a.H;
+  int16_t* ord = a.order + q * a.H;
+  const int now = a.ctrl[2 * q];
+
+  int o[EPH];
+#pragma unroll
+  for (int e = 0; e < EPH; ++e) {
+    const int k = tid * EPH + e;
+    o[e] = k < a.H ? static_cast<int>(ord[k]) : -1;
+  }
+  for (int i = tid; i < npw; i += NT) pbits[i] = 0u;
+  for (int i = tid; i < a.Hw; i += NT) used[i] = 0u;
+  __syncthreads();
+
+  // 1. tokens -> pages named by the row
+  const int32_t* row = a.topk + static_cast<size_t>(b) * a.K;
+  int32_t tok[EPT];
+  bool bad_index = false;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int i = tid * EPT + e;
+    const int32_t t = i < a.K ? row[i] : -1;
+    const bool valid = t >= 0 && t < sl;
+    bad_index |= (!valid && t != -1);
+    tok[e] = valid ? t : -1;
+    if (valid) bit_set_atomic(pbits, t / a.P);
+  }
+  __syncthreads();
+
+  // 2. distinct pages in ascending order
+  const int wpt = (npw + NT - 1) / NT;
+  const int w0 = tid * wpt;
+  int cnt = 0;
+  for (int w = w0; w < w0 + wpt && w < npw; ++w) cnt += __popc(pbits[w]);
+  int npages;
+  int pre = block_exclusive_scan<NT>(cnt, scan, &npages);
+  if (npages > a.H) {  // uniform over the block
+    if (bad_index) raise_error(a.err, HISPARSE_ERR_BAD_INDEX);
+    reject_row<NT>(a, b, a.K, HISPARSE_ERR_PAGE_OVERFLOW, true);
+    return;
+  }
+  for (int w = w0; w < w0 + wpt && w < npw; ++w) {
+    wpre[w] = pre;
+    uint32_t bits = pbits[w];
+    while (bits) {
+      const int bit = __ffs(bits) - 1;
+      bits &= bits - 1u;
+      pslot[pre++] = w * 32 + bit;
+    }
+  }
+  __syncthreads();
+
+  // 3. look every distinct page up; rank misses in page order
+  int m = 0;
+  for (int base = 0; base < npages; base += NT) {
+    const int jp = base + tid;
+    const bool active = jp < npages;
+    const int p = active ? pslot[jp] : 0;
+    const int s = active ? static_cast<int>(ks[p]) : -1;
+    const bool miss = active && s < 0;
+    if (active && s >= 0) {
+      bit_set_atomic(used, s);
+      tsq[s] = now;
+    }
+    int round_misses;
+    int jm = block_exclusive_scan<NT>(miss ? 1 : 0, scan, &round_misses) + m;
+    if (active) {
+      if (miss) {
+        miss_key[jm] = p;
+        pslot[jp] = -(jm + 1);
+      } else {
+        pslot[jp] = s;
+      }
+    }
+    m += round_misses;
+  }
+  __syncthreads();
+
+  // 4. victims, commit, new order
+  lru_select_commit<NT, EPH>(a, b, r, now, m, o, used, miss_key, vslot, scan, ks, sk, tsq, ord);
+  __syncthreads();
+
+  // 5. outputs: page table, page count, token locations (page index, offset)
+  int32_t* pt = a.page_table + static_cast<size_t>(b) * a.H;
+  for (int jp = tid; jp < a.H; jp += NT) {
+    int v = -1;
+    if (jp < npages) {
+      const int x = pslot[jp];
+      v = r * a.rows + (x >= 0 ? x : vslot[-x - 1]);
+    }
+    pt[jp] = v;
+  }
+  int32_t* out = a.out_locs + static_cast<size_t>(b) * a.K;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int i = tid * EPT + e;
+    if (i >= a.K) continue;
+    int loc = -1;
+    if (tok[e] >= 0) {
+      const int p = tok[e] / a.P;
+      const uint32_t below = pbits[p >> 5] & ((1u << (p & 31)) - 1u);
+      const int jp = wpre[p >> 5] + __popc(below);
+      loc = jp * a.P + (tok[e] - p * a.P);
+    }
+    out[i] = loc;
+  }
+  if (tid == 0) {
+    a.miss_count[b] = m;
+    a.num_pages[b] = npages;
+    a.ctrl[2 * q] = now + 1;
+  }
+  if (bad_index) raise_error(a.err, HISPARSE_ERR_BAD_INDEX);
+}
+
+template <typename K>
+hipError_t launch_plan(K kernel, const PlanArgs& a, size_t lds, hipStream_t s) {
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kernel, dim3(a.batch), dim3(kPlanThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int hash_size_for(int entries) {
+  // about 2 buckets per entry, rounded to a multiple of 64
+  return ((2 * entries + 63) / 64) * 64;
+}
+
+size_t lru_token_lds_bytes(const PlanArgs& a) {
+  return (2 * static_cast<size_t>(a.hash_size) + a.Hw + 2 * static_cast<size_t>(a.K) +
+          kPlanThreads / kWave + 1) * 4;
+}
+
+size_t lru_page_lds_bytes(const PlanArgs& a) {
+  const size_t npw = (a.nkeys + 31) / 32;
+  return (2 * npw + a.Hw + 3 * static_cast<size_t>(a.H) + kPlanThreads / kWave + 1) * 4;
+}
+
+// Entries per thread (EPT) and order positions per thread (EPH) are compile
+// time so the per-thread arrays stay in registers.
+#define HS_DISPATCH_EPH(KERNEL, EPTV)                                                 \
+  if (a.H <= 4 * kPlanThreads)                                                        \
+    return launch_plan(KERNEL<kPlanThreads, EPTV, 4>, a, lds, s);                     \
+  if (a.H <= 8 * kPlanThreads)                                                        \
+    return launch_plan(KERNEL<kPlanThreads, EPTV, 8>, a, lds, s);                     \
+  return launch_plan(KERNEL<kPlanThreads, EPTV, 32>, a, lds, s);
+
+hipError_t launch_lru_token_plan(const PlanArgs& a, hipStream_t s) {
+  const size_t lds = lru_token_lds_bytes(a);
+  if (a.K <= 2 * kPlanThreads) {
+    HS_DISPATCH_EPH(lru_token_plan, 2)
+  }
+  HS_DISPATCH_EPH(lru_token_plan, 8)
+}
+
+hipError_t launch_lru_page_plan(const PlanArgs& a, hipStream_t s) {
+  const size_t lds = lru_page_lds_bytes(a);
+  if (a.K <= 2 * kPlanThreads) {
+    HS_DISPATCH_EPH(lru_page_plan, 2)
+  }
+  HS_DISPATCH_EPH(lru_page_plan, 8)
+}
+
+}  // namespace hisparse

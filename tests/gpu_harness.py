@@ -1,0 +1,131 @@
+"""GPU-vs-oracle parity harness (used by the ``gpu`` tests).
+
+A :class:`Pair` drives one library state (through the C ABI) and one oracle
+state with the same seeded host KV bytes and the same calls, and compares,
+after every call:
+
+* ``out_locs``, ``miss_count`` (and ``page_table`` / ``num_pages``);
+* the ordered miss plan ``(miss_src, miss_dst, victim)`` of every row;
+* the sticky error word;
+* optionally the whole device KV buffer against the oracle's shadow buffer
+  (which also catches stray writes) and every touched instance's exported
+  state (slot->key, timestamps or reference bits, call counter or hand, and
+  the key->slot table).
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from oracle import hisparse_oracle as ora
+from sparse_attention_kv_request_amd import binding
+
+DEV = torch.device("cuda", 0)
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def t32(x):
+    return torch.as_tensor(np.ascontiguousarray(x, np.int32)).to(DEV)
+
+
+class Pair:
+    def __init__(self, *, R, L, H, K, N, I, S=1, P=1, policy="lru", seed=0, max_batch=None,
+                 shadow=True, host_fill=None):
+        self.R, self.L, self.H, self.K, self.N, self.I, self.S, self.P = R, L, H, K, N, I, S, P
+        self.policy = policy
+        rng = np.random.default_rng(seed)
+        self.host = [binding.HostKV(R, N, I) for _ in range(L)]
+        for l, h in enumerate(self.host):
+            if host_fill is None:
+                h.array[...] = rng.integers(0, 256, h.shape, dtype=np.uint8)
+            else:
+                host_fill(l, h.array)
+        self.gpu = binding.HiSparseState(
+            max_requests=R, num_layers=L, hot_buffer_size=H, top_k=K, item_size_bytes=I,
+            max_seq_len=N, max_steps=S, page_size=P, policy=policy,
+            max_batch=max_batch or R, host_kv=self.host)
+        self.shadow = shadow
+        self.cpu = ora.OracleState(
+            max_requests=R, num_layers=L, hot=H, top_k=K, item_bytes=I, max_seq_len=N,
+            max_steps=S, page_size=P, policy=policy,
+            host_kv=[h.array for h in self.host] if shadow else None)
+        self.rows = self.cpu.rows
+        assert self.gpu.rows == self.rows
+
+    def close(self):
+        self.gpu.close()
+        for h in self.host:
+            h.free()
+
+    # -- calls -------------------------------------------------------------------
+    def call(self, layer, req, seq, topk, check_bytes=True, check_state=True):
+        req = np.asarray(req, np.int32)
+        seq = np.asarray(seq, np.int32)
+        topk = np.asarray(topk, np.int32)
+        B = req.shape[0]
+        multi = topk.ndim == 3
+        cap = self.gpu.capacity
+        out = torch.full(topk.shape, -7, dtype=torch.int32, device=DEV)
+        mc = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+        plan = tuple(torch.full((B, cap), -7, dtype=torch.int32, device=DEV) for _ in range(3))
+        if multi:
+            self.gpu.swap_in_spec_multistep(layer, t32(req), t32(seq), t32(topk), out, mc,
+                                            plan=plan)
+            want = self.cpu.swap_in_spec_multistep(layer, req, seq, topk)
+        else:
+            pt = nump = None
+            if self.P > 1:
+                pt = torch.full((B, self.H), -7, dtype=torch.int32, device=DEV)
+                nump = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+            self.gpu.swap_in_selected(layer, t32(req), t32(seq), t32(topk), out, mc,
+                                      page_table=pt, num_pages=nump, plan=plan)
+            want = self.cpu.swap_in_selected(layer, req, seq, topk)
+        torch.cuda.synchronize()
+        got_out = out.cpu().numpy()
+        got_mc = mc.cpu().numpy()
+        assert np.array_equal(got_mc, want["miss_count"]), (got_mc, want["miss_count"])
+        if not np.array_equal(got_out, want["out_locs"]):
+            bad = np.argwhere(got_out != want["out_locs"])[:5]
+            raise AssertionError(f"out_locs differ at {bad.tolist()}: "
+                                 f"gpu {got_out[tuple(bad[0])]} oracle "
+                                 f"{want['out_locs'][tuple(bad[0])]}")
+        if self.P > 1 and not multi:
+            assert np.array_equal(pt.cpu().numpy(), want["page_table"])
+            assert np.array_equal(nump.cpu().numpy(), want["num_pages"])
+        src, dst, vic = (p.cpu().numpy() for p in plan)
+        for b in range(B):
+            m = int(got_mc[b])
+            got_plan = list(zip(src[b, :m].tolist(), dst[b, :m].tolist(), vic[b, :m].tolist()))
+            assert got_plan == [tuple(x) for x in want["plan"][b]], f"plan of row {b} differs"
+            assert np.all(src[b, m:] == -7), "plan written beyond miss_count"
+        flags = self.gpu.error_flags(clear=True)
+        assert flags == self.cpu.error_flags, (flags, self.cpu.error_flags)
+        self.cpu.error_flags = 0
+        if check_bytes and self.shadow:
+            for l in range(self.L):
+                assert torch.equal(self.gpu.dev_kv[l].cpu(),
+                                   torch.from_numpy(self.cpu.dev_kv[l])), "device KV differs"
+        if check_state:
+            for r in sorted(set(int(x) for x in req if 0 <= x < self.R)):
+                self.compare_state(r, layer)
+        return got_out, got_mc, want
+
+    def compare_state(self, r, layer):
+        g = self.gpu.export(r, layer, with_map=True)
+        c = self.cpu.export(r, layer)
+        assert g["slot_key"].tolist() == c["slot_key"], f"slot_key of ({r},{layer})"
+        if self.policy == "lru":
+            assert g["ts"].tolist() == c["ts"], f"ts of ({r},{layer})"
+            assert int(g["ctrl"][0]) == c["now"]
+        else:
+            assert g["ref"].tolist() == c["ref"], f"ref of ({r},{layer})"
+            assert int(g["ctrl"][1]) == c["hand"]
+        ks = g["key_slot"]
+        resident = np.flatnonzero(ks >= 0)
+        assert {int(k): int(ks[k]) for k in resident} == c["map"], f"map of ({r},{layer})"

@@ -1,0 +1,273 @@
+"""GPU (HIP path through the C ABI) against the CPU oracle, element by element.
+
+Sizes are small enough for the oracle to finish in seconds yet span several
+thread tiles with ragged tails (K and H not multiples of the 1024-thread
+workgroup or of 32-bit mask words), and every call is compared on outputs,
+plan, error word, the whole device KV buffer and the touched instances' state.
+"""
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_harness import Pair, log
+
+pytestmark = pytest.mark.gpu
+
+
+def make_rows(rng, B, K, N, prev=None, reuse=0.6, pad=0.02, dup=0.03, bad=0.0):
+    """Top-k rows with step-to-step reuse, padding, in-row duplicates and
+    (optionally) out-of-range entries."""
+    rows = np.empty((B, K), np.int64)
+    for b in range(B):
+        if prev is not None and reuse > 0:
+            keep = rng.choice(prev[b][prev[b] >= 0], size=min(int(reuse * K), int((prev[b] >= 0).sum())),
+                              replace=False)
+        else:
+            keep = np.empty(0, np.int64)
+        mask = np.zeros(N, bool)
+        mask[keep] = True
+        fresh = rng.choice(np.flatnonzero(~mask), size=K - keep.size, replace=False)
+        rows[b] = rng.permutation(np.concatenate([keep, fresh]))
+    u = rng.random((B, K))
+    src = rng.integers(0, K, (B, K))
+    rows = np.where(u < dup, np.take_along_axis(rows, src, 1), rows)
+    rows = np.where((u >= dup) & (u < dup + pad), -1, rows)
+    if bad:
+        v = rng.random((B, K))
+        rows = np.where(v < bad / 2, N + rng.integers(0, 5, (B, K)), rows)
+        rows = np.where((v >= bad / 2) & (v < bad), -2 - rng.integers(0, 5, (B, K)), rows)
+    return rows.astype(np.int32)
+
+
+LRU_SHAPES = [
+    # (H, K, N, I) -- ragged tiles, K == H, cfg-1-like bf16 rows, EPH = 8 variant
+    (3000, 1500, 6000, 48),
+    (100, 37, 300, 16),
+    (300, 300, 1000, 32),
+    (4096, 2048, 8192, 1152),
+    (8000, 2048, 20000, 656),
+    (5000, 3000, 9000, 32),      # K > 2048: 8 entries per thread
+]
+
+
+@pytest.mark.parametrize("H,K,N,I", LRU_SHAPES)
+def test_lru_token_parity(H, K, N, I):
+    log(f"lru token H={H} K={K} N={N} I={I}")
+    rng = np.random.default_rng(H + K)
+    R, L, B = 5, 2, 4
+    p = Pair(R=R, L=L, H=H, K=K, N=N, I=I, seed=H)
+    prev = {}
+    try:
+        for call in range(10):
+            layer = call % L
+            req = rng.permutation(R)[:B]
+            rows = make_rows(rng, B, K, N, prev=prev.get(layer))
+            prev[layer] = rows
+            p.call(layer, req, np.full(B, N), rows)
+    finally:
+        p.close()
+
+
+PAGE_SHAPES = [
+    # (P, pages per request, H pages, K tokens, I)
+    (16, 150, 64, 300, 32),
+    (256, 64, 64, 512, 656),
+    (4, 1000, 200, 700, 16),
+]
+
+
+@pytest.mark.parametrize("P,NP,H,K,I", PAGE_SHAPES)
+def test_lru_page_parity(P, NP, H, K, I):
+    log(f"lru page P={P} NP={NP} H={H} K={K} I={I}")
+    rng = np.random.default_rng(P * 7 + K)
+    R, L, B = 4, 1, 3
+    N = P * NP
+    p = Pair(R=R, L=L, H=H, K=K, N=N, I=I, P=P, seed=P)
+    try:
+        for call in range(10):
+            req = rng.permutation(R)[:B]
+            rows = np.empty((B, K), np.int64)
+            for b in range(B):   # clustered tokens: a few page windows
+                centres = rng.integers(0, N, 4)
+                width = max(P * 3, 8)
+                toks = np.clip(centres[rng.integers(0, 4, K)] + rng.integers(-width, width, K),
+                               0, N - 1)
+                rows[b] = toks
+            if call == 4:        # one row naming more pages than the hot cache holds
+                rows[0] = rng.choice(N, K, replace=False)
+            rows[:, ::17] = -1
+            p.call(0, req, np.full(B, N), rows.astype(np.int32))
+    finally:
+        p.close()
+
+
+CLOCK_SHAPES = [
+    # (H, K, N, I, S)
+    (1000, 700, 5000, 32, 2),
+    (1000, 700, 5000, 32, 4),
+    (50, 100, 400, 16, 3),       # overflow every call
+    (4096, 2048, 32768, 656, 4),  # S * K = 8192 entries per row
+    (3000, 1024, 9000, 48, 3),
+]
+
+
+@pytest.mark.parametrize("H,K,N,I,S", CLOCK_SHAPES)
+def test_clock_multistep_parity(H, K, N, I, S):
+    log(f"clock H={H} K={K} N={N} I={I} S={S}")
+    rng = np.random.default_rng(H + 3 * K + S)
+    R, L, B = 4, 2, 3
+    p = Pair(R=R, L=L, H=H, K=K, N=N, I=I, S=S, policy="clock", seed=K)
+    prev = {}
+    try:
+        for call in range(8):
+            layer = call % L
+            req = rng.permutation(R)[:B]
+            base = make_rows(rng, B, K, N, prev=prev.get(layer), reuse=0.5)
+            prev[layer] = base
+            steps = [base]
+            for s in range(1, S):  # later steps share most of the first step's entries
+                nxt = make_rows(rng, B, K, N, prev=base, reuse=0.8)
+                steps.append(nxt)
+            topk = np.stack(steps, axis=1)
+            p.call(layer, req, np.full(B, N), topk)
+    finally:
+        p.close()
+
+
+def test_clock_with_fewer_steps_than_max():
+    rng = np.random.default_rng(5)
+    p = Pair(R=3, L=1, H=200, K=64, N=1000, I=16, S=4, policy="clock", seed=5)
+    try:
+        for call in range(8):
+            S = 2 + call % 3
+            topk = rng.integers(-1, 1000, (2, S, 64))
+            p.call(0, rng.permutation(3)[:2], [1000, 1000], topk)
+    finally:
+        p.close()
+
+
+def test_row_errors_and_padding():
+    rng = np.random.default_rng(11)
+    R, H, K, N = 6, 64, 40, 500
+    p = Pair(R=R, L=1, H=H, K=K, N=N, I=16, seed=11)
+    try:
+        rows = make_rows(rng, 5, K, N, bad=0.1)
+        rows[3] = -1                                            # all padding
+        # rows 0 and 4 name the same request; row 2 has an out-of-range request
+        p.call(0, [1, 2, 9, 3, 1], [N, 300, N, N, N], rows)
+        rows = make_rows(rng, 4, K, N, bad=0.05)
+        p.call(0, [0, 1, 2, 3], [N, 0, N + 1, -1], rows)         # seq_len 0, too long, negative
+        rows = make_rows(rng, 3, K, N)
+        p.call(0, [1, 2, 3], [N, N, N], rows)                    # clean call afterwards
+    finally:
+        p.close()
+
+
+def test_request_reset_then_reuse():
+    rng = np.random.default_rng(12)
+    R, H, K, N = 4, 128, 100, 1000
+    p = Pair(R=R, L=2, H=H, K=K, N=N, I=32, seed=12)
+    try:
+        for call in range(4):
+            p.call(call % 2, [0, 1, 2], [N] * 3, make_rows(rng, 3, K, N))
+        p.gpu.request_reset(torch.tensor([1, 7], dtype=torch.int32, device="cuda"))
+        torch.cuda.synchronize()
+        p.cpu.request_reset([1])
+        assert p.gpu.error_flags() == 8                           # request 7 is out of range
+        for r in range(R):
+            for l in range(2):
+                p.compare_state(r, l)
+        for call in range(4):
+            p.call(call % 2, [2, 1, 3], [N] * 3, make_rows(rng, 3, K, N))
+    finally:
+        p.close()
+
+
+def test_import_export_roundtrip():
+    rng = np.random.default_rng(13)
+    R, H, K, N, I = 2, 300, 120, 2000, 32
+    p = Pair(R=R, L=1, H=H, K=K, N=N, I=I, seed=13)
+    try:
+        keys = rng.choice(N, H - 40, replace=False)
+        slot_key = np.full(H, -1, np.int32)
+        where = rng.choice(H, keys.size, replace=False)
+        slot_key[where] = keys
+        ts = np.where(slot_key >= 0, rng.integers(0, 5, H), -1).astype(np.int32)
+        ctrl = np.array([5, 0], np.int32)
+        p.gpu.import_(1, 0, slot_key, ts, ctrl)
+        p.cpu.import_(1, 0, slot_key, ts=ts, now=5)
+        dev = p.gpu.dev_kv[0]
+        for s in np.flatnonzero(slot_key >= 0):                   # resident rows hold their bytes
+            dev[1, s] = torch.from_numpy(p.host[0].array[1, slot_key[s]])
+        p.compare_state(1, 0)
+        for _ in range(5):
+            p.call(0, [1], [N], make_rows(rng, 1, K, N, prev=None), check_bytes=True)
+        with pytest.raises(Exception):
+            bad = slot_key.copy()
+            bad[0] = bad[1] = 3
+            p.gpu.import_(1, 0, bad, ts, ctrl)
+    finally:
+        p.close()
+
+
+def test_hot_buffer_upper_bound():
+    """hot_buffer_size at the pages' upper limit of 32768 slots."""
+    rng = np.random.default_rng(14)
+    H, K, N = 32768, 2048, 65536
+    p = Pair(R=2, L=1, H=H, K=K, N=N, I=16, seed=14)
+    try:
+        prev = None
+        for call in range(20):
+            rows = make_rows(rng, 2, K, N, prev=prev, reuse=0.3)
+            prev = rows
+            p.call(0, [0, 1], [N, N], rows, check_state=(call % 5 == 4))
+    finally:
+        p.close()
+
+
+def test_host_side_argument_errors():
+    p = Pair(R=2, L=1, H=64, K=16, N=100, I=16, seed=15)
+    dev = torch.device("cuda", 0)
+    i32 = dict(dtype=torch.int32, device=dev)
+    req = torch.zeros(1, **i32)
+    seq = torch.full((1,), 100, **i32)
+    topk = torch.zeros((1, 16), **i32)
+    out = torch.zeros((1, 16), **i32)
+    mc = torch.zeros(1, **i32)
+    from sparse_attention_kv_request_amd import binding as bd
+    try:
+        h = p.gpu.handle
+        assert bd.hisparse_swap_in_selected(h, 1, 1, req.data_ptr(), seq.data_ptr(),
+                                            topk.data_ptr(), out.data_ptr(), mc.data_ptr(),
+                                            0, 0, None, 0) == bd.HISPARSE_E_INVAL   # layer
+        assert bd.hisparse_swap_in_selected(h, 0, 3, req.data_ptr(), seq.data_ptr(),
+                                            topk.data_ptr(), out.data_ptr(), mc.data_ptr(),
+                                            0, 0, None, 0) == bd.HISPARSE_E_INVAL   # batch
+        assert bd.hisparse_swap_in_selected(h, 0, 1, 0, seq.data_ptr(), topk.data_ptr(),
+                                            out.data_ptr(), mc.data_ptr(), 0, 0, None,
+                                            0) == bd.HISPARSE_E_INVAL               # NULL
+        assert bd.hisparse_swap_in_spec_multistep(h, 0, 1, 2, req.data_ptr(), seq.data_ptr(),
+                                                  topk.data_ptr(), out.data_ptr(),
+                                                  mc.data_ptr(), None,
+                                                  0) == bd.HISPARSE_E_INVAL         # policy
+        assert bd.hisparse_swap_in_selected(h, 0, 0, 0, 0, 0, 0, 0, 0, 0, None,
+                                            0) == bd.HISPARSE_OK                    # empty batch
+        small = bd.HisparseMissPlan(out.data_ptr(), out.data_ptr(), out.data_ptr(), 15)
+        import ctypes
+        assert bd.hisparse_swap_in_selected(h, 0, 1, req.data_ptr(), seq.data_ptr(),
+                                            topk.data_ptr(), out.data_ptr(), mc.data_ptr(),
+                                            0, 0, ctypes.byref(small),
+                                            0) == bd.HISPARSE_E_INVAL               # capacity
+        # a pageable host buffer is not a valid host tier
+        cfg = bd.HisparseConfig(max_requests=2, num_layers=1, hot_buffer_size=64, top_k=16,
+                                max_steps=1, page_size=1, item_size_bytes=16, max_seq_len=100,
+                                policy=0, max_batch=2)
+        pageable = np.zeros(2 * 100 * 16, np.uint8)
+        hp = (ctypes.c_void_p * 1)(pageable.ctypes.data)
+        dp = (ctypes.c_void_p * 1)(p.gpu.dev_kv[0].data_ptr())
+        cfg.host_kv = ctypes.cast(hp, ctypes.POINTER(ctypes.c_void_p))
+        cfg.dev_kv = ctypes.cast(dp, ctypes.POINTER(ctypes.c_void_p))
+        with pytest.raises(bd.HiSparseError):
+            bd.hisparse_state_create(cfg, 0)
+    finally:
+        p.close()
