@@ -62,6 +62,7 @@ extern "C" {
 #define HISPARSE_ERR_DUP_REQUEST 2u   /* one request index twice in one batch */
 #define HISPARSE_ERR_PAGE_OVERFLOW 4u /* a row needs more distinct pages than hot pages */
 #define HISPARSE_ERR_BAD_ROW 8u       /* request index or seq_len out of range */
+#define HISPARSE_ERR_BAD_PLAN 16u     /* a replayed plan entry outside the buffers */
 
 /* Replacement policies. */
 #define HISPARSE_POLICY_LRU 0   /* single-step calls (PR #20343 summary) */
@@ -232,6 +233,22 @@ int hisparse_swap_in_spec_multistep(hisparse_state_t st, int32_t layer_id, int32
                                     const int32_t* seq_lens, const int32_t* topk_indices,
                                     int32_t* out_locs, int32_t* miss_count,
                                     const hisparse_miss_plan_t* plan, void* stream);
+
+/*
+ * Replays a miss plan: for every row b < batch, copies the first
+ * min(miss_count[b], plan->capacity) pairs (miss_src, miss_dst) of `plan`
+ * from layer `layer_id`'s host tier into its hot KV buffer -- the copy half
+ * of a swap call on its own, so a plan recorded by a swap call can be
+ * replayed later or on another stream (PR #32162 report, item 2 and "Risks
+ * and impact": the plan stays compatible with the prefetch replay path).
+ * The victim array is not read.  Entries outside the layer's host rows
+ * ([0, R*N) tokens or [0, R*N/P) pages) or device rows are skipped and raise
+ * HISPARSE_ERR_BAD_PLAN.  miss_count: device int32 [batch].  Enqueued on
+ * `stream`; errors: HISPARSE_E_INVAL, HISPARSE_E_HIP.
+ */
+int hisparse_copy_planned(hisparse_state_t st, int32_t layer_id, int32_t batch,
+                          const int32_t* miss_count, const hisparse_miss_plan_t* plan,
+                          void* stream);
 
 /*
  * Empties the caches of `n` requests in every layer (a newly admitted

@@ -30,6 +30,7 @@ ERR_BAD_INDEX = 1
 ERR_DUP_REQUEST = 2
 ERR_PAGE_OVERFLOW = 4
 ERR_BAD_ROW = 8
+ERR_BAD_PLAN = 16
 
 POLICY = {"lru": 0, "clock": 1}
 
@@ -71,6 +72,8 @@ _SIGNATURES = {
                                                        c_vp, c_vp, c_vp,
                                                        ctypes.POINTER(HisparseMissPlan),
                                                        c_vp]),
+    "hisparse_copy_planned": (ctypes.c_int, [c_vp, c_i32, c_i32, c_vp,
+                                             ctypes.POINTER(HisparseMissPlan), c_vp]),
     "hisparse_request_reset": (ctypes.c_int, [c_vp, c_i32, c_vp, c_vp]),
     "hisparse_plan_capacity": (c_i32, [c_vp]),
     "hisparse_state_export": (ctypes.c_int, [c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
@@ -150,6 +153,10 @@ def hisparse_swap_in_spec_multistep(st, layer_id, batch, num_steps, req_pool_ind
     return lib().hisparse_swap_in_spec_multistep(st, layer_id, batch, num_steps,
                                                  req_pool_indices, seq_lens, topk_indices,
                                                  out_locs, miss_count, plan, stream)
+
+
+def hisparse_copy_planned(st, layer_id, batch, miss_count, plan, stream) -> int:
+    return lib().hisparse_copy_planned(st, layer_id, batch, miss_count, plan, stream)
 
 
 def hisparse_request_reset(st, n, req_pool_indices, stream) -> int:
@@ -320,6 +327,13 @@ class HiSparseState:
             _ptr(topk_indices), _ptr(out_locs), _ptr(miss_count), self._plan(plan),
             _stream(stream))
         return _check(rc, "hisparse_swap_in_spec_multistep")
+
+    def copy_planned(self, layer_id, miss_count, plan, stream=None):
+        """Replays ``plan = (miss_src, miss_dst, victim)`` int32 [batch, cap]."""
+        batch = int(miss_count.shape[0])
+        rc = hisparse_copy_planned(self.handle, layer_id, batch, _ptr(miss_count),
+                                   self._plan(plan), _stream(stream))
+        return _check(rc, "hisparse_copy_planned")
 
     def request_reset(self, req_pool_indices: torch.Tensor, stream=None):
         rc = hisparse_request_reset(self.handle, int(req_pool_indices.shape[0]),

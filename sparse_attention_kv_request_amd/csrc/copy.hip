@@ -28,7 +28,7 @@ __global__ __launch_bounds__(NT) void miss_copy(CopyArgs a) {
   int running = 0;
   for (int base = 0; base < a.batch; base += NT) {
     const int b = base + tid;
-    const int v = b < a.batch ? max(a.miss_count[b], 0) : 0;
+    const int v = b < a.batch ? min(max(a.miss_count[b], 0), a.cap) : 0;
     int tot;
     const int x = block_exclusive_scan<NT>(v, scan, &tot);
     if (b < a.batch) pre[b] = running + x;
@@ -71,6 +71,10 @@ __global__ __launch_bounds__(NT) void miss_copy(CopyArgs a) {
       const size_t slot = static_cast<size_t>(lo) * a.cap + j;
       const int64_t srow = a.src[slot];
       const int64_t drow = a.dst[slot];
+      if (srow < 0 || srow >= a.src_rows || drow < 0 || drow >= a.dst_rows) {
+        if (off == 0) raise_error(a.err, HISPARSE_ERR_BAD_PLAN);
+        continue;
+      }
       const u32x4* sp = reinterpret_cast<const u32x4*>(a.host + srow * a.unit_bytes) + off;
       dst[u] = reinterpret_cast<u32x4*>(a.dev + drow * a.unit_bytes) + off;
       v[u] = __builtin_nontemporal_load(sp);

@@ -188,6 +188,25 @@ void record(hisparse_state* st, hipStream_t s) {
   st->ev_pending.push_back(e);
 }
 
+CopyArgs copy_args(const hisparse_state* st, int layer, int batch, const int32_t* miss_count,
+                   const int32_t* src, const int32_t* dst, int cap) {
+  CopyArgs c{};
+  c.miss_count = miss_count;
+  c.src = src;
+  c.dst = dst;
+  c.batch = batch;
+  c.cap = cap;
+  c.host = st->host_kv[layer];
+  c.dev = st->dev_kv[layer];
+  const int64_t unit = static_cast<int64_t>(st->cfg.item_size_bytes) * st->cfg.page_size;
+  c.unit_bytes = unit;
+  c.unit16 = static_cast<int32_t>(unit / 16);
+  c.src_rows = static_cast<int64_t>(st->cfg.max_requests) * st->nkeys;
+  c.dst_rows = static_cast<int64_t>(st->cfg.max_requests) * st->rows;
+  c.err = st->err;
+  return c;
+}
+
 int run_swap(hisparse_state* st, const PlanArgs& a, bool multistep, hipStream_t s) {
   auto* ps = static_cast<ProfiledState*>(st);
   if (st->profiling && st->ev_pending.size() >= 3 * 4096) (void)drain_events(st, &ps->sums);
@@ -202,17 +221,7 @@ int run_swap(hisparse_state* st, const PlanArgs& a, bool multistep, hipStream_t 
     e = launch_lru_token_plan(a, s);
   if (e != hipSuccess) return status_of(e);
   record(st, s);
-  CopyArgs c{};
-  c.miss_count = a.miss_count;
-  c.src = a.miss_src;
-  c.dst = a.miss_dst;
-  c.batch = a.batch;
-  c.cap = a.cap;
-  c.host = st->host_kv[a.layer];
-  c.dev = st->dev_kv[a.layer];
-  const int64_t unit = static_cast<int64_t>(st->cfg.item_size_bytes) * st->cfg.page_size;
-  c.unit_bytes = unit;
-  c.unit16 = static_cast<int32_t>(unit / 16);
+  const CopyArgs c = copy_args(st, a.layer, a.batch, a.miss_count, a.miss_src, a.miss_dst, a.cap);
   e = launch_miss_copy(c, s);
   if (e != hipSuccess) return status_of(e);
   record(st, s);
@@ -383,6 +392,19 @@ int hisparse_swap_in_spec_multistep(hisparse_state_t st, int32_t layer_id, int32
   const int E = num_steps * a.K;
   a.hash_size = std::max(64, ((3 * E / 2 + 64) + 63) / 64 * 64);
   return run_swap(st, a, true, static_cast<hipStream_t>(stream));
+}
+
+int hisparse_copy_planned(hisparse_state_t st, int32_t layer_id, int32_t batch,
+                          const int32_t* miss_count, const hisparse_miss_plan_t* plan,
+                          void* stream) {
+  if (st == nullptr || plan == nullptr || miss_count == nullptr) return HISPARSE_E_INVAL;
+  if (layer_id < 0 || layer_id >= st->cfg.num_layers || batch < 0) return HISPARSE_E_INVAL;
+  if (!plan->miss_src || !plan->miss_dst || plan->capacity < 1) return HISPARSE_E_INVAL;
+  if (batch == 0) return HISPARSE_OK;
+  DeviceGuard g(st->device);
+  const CopyArgs c = copy_args(st, layer_id, batch, miss_count, plan->miss_src, plan->miss_dst,
+                               plan->capacity);
+  return status_of(launch_miss_copy(c, static_cast<hipStream_t>(stream)));
 }
 
 int hisparse_request_reset(hisparse_state_t st, int32_t n, const int32_t* req_pool_indices,

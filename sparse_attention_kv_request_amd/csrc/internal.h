@@ -29,6 +29,9 @@ struct CopyArgs {
   uint8_t* dev;
   int32_t unit16;             // 16-byte chunks per row
   int64_t unit_bytes;
+  int64_t src_rows;           // valid host rows [0, src_rows)
+  int64_t dst_rows;           // valid device rows [0, dst_rows)
+  uint32_t* err;
 };
 
 struct ResetArgs {

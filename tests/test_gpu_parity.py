@@ -271,3 +271,41 @@ def test_host_side_argument_errors():
             bd.hisparse_state_create(cfg, 0)
     finally:
         p.close()
+
+
+def test_copy_planned_replays_the_plan():
+    """Replaying the plan of a swap call reproduces its copies; an entry outside
+    the buffers is skipped and flagged instead of being written."""
+    rng = np.random.default_rng(16)
+    R, H, K, N, I = 3, 200, 150, 1000, 32
+    p = Pair(R=R, L=1, H=H, K=K, N=N, I=I, seed=16)
+    dev = torch.device("cuda", 0)
+    try:
+        p.call(0, [0, 2], [N, N], make_rows(rng, 2, K, N))
+        cap = p.gpu.capacity
+        plan = tuple(torch.full((2, cap), -1, dtype=torch.int32, device=dev) for _ in range(3))
+        mc = torch.empty(2, dtype=torch.int32, device=dev)
+        out = torch.empty((2, K), dtype=torch.int32, device=dev)
+        rows = torch.from_numpy(make_rows(rng, 2, K, N)).to(dev)
+        p.gpu.swap_in_selected(0, torch.tensor([0, 2], dtype=torch.int32, device=dev),
+                               torch.full((2,), N, dtype=torch.int32, device=dev), rows, out, mc,
+                               plan=plan)
+        torch.cuda.synchronize()
+        p.gpu.dev_kv[0].zero_()
+        p.gpu.copy_planned(0, mc, plan)
+        torch.cuda.synchronize()
+        host = torch.from_numpy(p.host[0].array).reshape(-1, I)
+        flat = p.gpu.dev_kv[0].reshape(-1, I).cpu()
+        src, dst = plan[0].cpu(), plan[1].cpu()
+        n = mc.cpu()
+        for b in range(2):
+            for j in range(int(n[b])):
+                assert torch.equal(flat[dst[b, j]], host[src[b, j]])
+        assert p.gpu.error_flags() == 0
+        bad_src = plan[0].clone()
+        bad_src[0, 0] = R * N + 5
+        p.gpu.copy_planned(0, mc, (bad_src, plan[1], plan[2]))
+        torch.cuda.synchronize()
+        assert p.gpu.error_flags() == 16
+    finally:
+        p.close()
