@@ -1,0 +1,55 @@
+"""Summarise a rocprofv3 kernel-trace database as a short markdown table.
+
+``python -m sparse_attention_kv_request_amd.profile_summary RESULTS.db
+--skip N --command "..."`` prints, per kernel, the launch count and the
+average duration over all launches and over the launches after the first
+``N`` of that kernel (the warm-up launches a benchmark does not time), so the
+figure matches what the benchmark measures live.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import re
+import sqlite3
+
+
+def short(name: str) -> str:
+    m = re.search(r"::(\w+)(<[^()]*>)?\(", name)
+    if m:
+        return m.group(1) + (m.group(2) or "")
+    return name.split("(")[0][:60]
+
+
+def summarize(db_path: str, skip: int):
+    db = sqlite3.connect(db_path)
+    rows = db.execute("select name, duration from kernels order by start").fetchall()
+    by = collections.OrderedDict()
+    for name, dur in rows:
+        by.setdefault(short(name), []).append(dur / 1e3)  # ns -> us
+    out = []
+    for k, v in by.items():
+        timed = v[skip:] if len(v) > skip else v
+        out.append((k, len(v), sum(v) / len(v), len(timed), sum(timed) / len(timed), sum(v)))
+    out.sort(key=lambda r: -r[5])
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("db")
+    ap.add_argument("--skip", type=int, default=0)
+    ap.add_argument("--command", default="")
+    ap.add_argument("--title", default="rocprofv3 kernel trace")
+    a = ap.parse_args()
+    print(f"# {a.title}\n")
+    if a.command:
+        print(f"Command: `{a.command}`\n")
+    print(f"| kernel | launches | avg us (all) | launches timed | avg us (timed, first {a.skip} skipped) | total us |")
+    print("|---|---|---|---|---|---|")
+    for k, n, avg, nt, avg_t, tot in summarize(a.db, a.skip):
+        print(f"| `{k}` | {n} | {avg:.2f} | {nt} | {avg_t:.2f} | {tot:.1f} |")
+
+
+if __name__ == "__main__":
+    main()
