@@ -77,7 +77,11 @@ __global__ __launch_bounds__(NT) void miss_copy(CopyArgs a) {
       }
       const u32x4* sp = reinterpret_cast<const u32x4*>(a.host + srow * a.unit_bytes) + off;
       dst[u] = reinterpret_cast<u32x4*>(a.dev + drow * a.unit_bytes) + off;
+#if HISPARSE_COPY_NT_LOAD
       v[u] = __builtin_nontemporal_load(sp);
+#else
+      v[u] = *sp;
+#endif
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)

@@ -42,6 +42,12 @@ struct PlanArgs {
   int32_t* victim;
   int32_t cap;
   int32_t hash_size;    // LDS hash buckets
+  // copy list: the same misses in ascending host-row order (rows of one
+  // request that are adjacent in host memory then share their 128-byte lines)
+  int32_t* copy_src;    // [batch][ccap]
+  int32_t* copy_dst;
+  int32_t ccap;
+  int32_t sort_words;   // words of the LDS miss bitmap; 0 = no copy list
 };
 
 // Exclusive prefix sum over the NT threads of a workgroup.  `scratch` holds
@@ -106,6 +112,28 @@ __device__ __forceinline__ int hash_insert(uint32_t* keys, int size, int32_t t) 
     if (old == 0u || (old & kKeyMask) == want) return h;
     h = (h + 1 == size) ? 0 : h + 1;
   }
+}
+
+// Exclusive prefix of set bits over a bitmap of `words` words: wpre[w] =
+// bits set in words [0, w).  Threads own contiguous words.  Block-wide.
+template <int NT>
+__device__ __forceinline__ void bitmap_word_prefix(const uint32_t* bits, int32_t* wpre,
+                                                   int words, int* scan) {
+  const int wpt = (words + NT - 1) / NT;
+  const int w0 = threadIdx.x * wpt;
+  int cnt = 0;
+  for (int w = w0; w < w0 + wpt && w < words; ++w) cnt += __popc(bits[w]);
+  int total;
+  int pre = block_exclusive_scan<NT>(cnt, scan, &total);
+  for (int w = w0; w < w0 + wpt && w < words; ++w) {
+    wpre[w] = pre;
+    pre += __popc(bits[w]);
+  }
+}
+
+// Rank of key k among the set bits of `bits` (after bitmap_word_prefix).
+__device__ __forceinline__ int bitmap_rank(const uint32_t* bits, const int32_t* wpre, int k) {
+  return wpre[k >> 5] + __popc(bits[k >> 5] & ((1u << (k & 31)) - 1u));
 }
 
 __device__ __forceinline__ void raise_error(uint32_t* err, uint32_t bits) {

@@ -17,6 +17,10 @@
 
 using namespace hisparse;
 
+#ifndef HISPARSE_HOST_ALLOC_FLAGS
+#define HISPARSE_HOST_ALLOC_FLAGS hipHostMallocMapped
+#endif
+
 namespace {
 
 struct DeviceGuard {
@@ -119,6 +123,10 @@ PlanArgs plan_args(const hisparse_state* st, int32_t layer, int32_t batch, int32
   a.miss_count = miss_count;
   a.page_table = page_table;
   a.num_pages = num_pages;
+  a.copy_src = st->cp_src;
+  a.copy_dst = st->cp_dst;
+  a.ccap = st->cap;
+  a.sort_words = 0;
   if (plan != nullptr) {
     a.miss_src = plan->miss_src;
     a.miss_dst = plan->miss_dst;
@@ -188,6 +196,13 @@ void record(hisparse_state* st, hipStream_t s) {
   st->ev_pending.push_back(e);
 }
 
+// Turns on the ascending-host-row copy list when its LDS bitmap fits.
+void enable_copy_sort(const hisparse_state* st, PlanArgs* a, size_t (*lds_bytes)(const PlanArgs&)) {
+  if (st->nkeys > kMaxSortedKeys) return;
+  a->sort_words = (st->nkeys + 31) / 32;
+  if (lds_bytes(*a) > st->max_lds) a->sort_words = 0;
+}
+
 CopyArgs copy_args(const hisparse_state* st, int layer, int batch, const int32_t* miss_count,
                    const int32_t* src, const int32_t* dst, int cap) {
   CopyArgs c{};
@@ -221,7 +236,11 @@ int run_swap(hisparse_state* st, const PlanArgs& a, bool multistep, hipStream_t 
     e = launch_lru_token_plan(a, s);
   if (e != hipSuccess) return status_of(e);
   record(st, s);
-  const CopyArgs c = copy_args(st, a.layer, a.batch, a.miss_count, a.miss_src, a.miss_dst, a.cap);
+  const CopyArgs c = a.sort_words
+                         ? copy_args(st, a.layer, a.batch, a.miss_count, a.copy_src, a.copy_dst,
+                                     a.ccap)
+                         : copy_args(st, a.layer, a.batch, a.miss_count, a.miss_src, a.miss_dst,
+                                     a.cap);
   e = launch_miss_copy(c, s);
   if (e != hipSuccess) return status_of(e);
   record(st, s);
@@ -256,6 +275,10 @@ int hisparse_state_create(const hisparse_config_t* cfg, void* stream, hisparse_s
   const bool lru = cfg->policy == HISPARSE_POLICY_LRU;
   int device = 0;
   if (hipGetDevice(&device) != hipSuccess) return HISPARSE_E_HIP;
+  int max_lds = 0;
+  if (hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, device) !=
+      hipSuccess)
+    return HISPARSE_E_HIP;
 
   auto* st = new (std::nothrow) ProfiledState();
   if (st == nullptr) return HISPARSE_E_NOMEM;
@@ -268,6 +291,7 @@ int hisparse_state_create(const hisparse_config_t* cfg, void* stream, hisparse_s
   st->nkeys = d.nkeys;
   st->hw = d.hw;
   st->cap = d.cap;
+  st->max_lds = static_cast<size_t>(max_lds);
   for (int l = 0; l < L; ++l) {
     hipPointerAttribute_t attr{};
     const void* hp = cfg->host_kv[l];
@@ -302,6 +326,8 @@ int hisparse_state_create(const hisparse_config_t* cfg, void* stream, hisparse_s
   const size_t o_src = off;      off += ws;
   const size_t o_dst = off;      off += ws;
   const size_t o_vic = off;      off += ws;
+  const size_t o_cps = off;      off += ws;
+  const size_t o_cpd = off;      off += ws;
   const size_t o_err = off;      off += 256;
   hipError_t e = hipMalloc(&st->arena, off);
   if (e != hipSuccess) {
@@ -319,6 +345,8 @@ int hisparse_state_create(const hisparse_config_t* cfg, void* stream, hisparse_s
   st->ws_src = reinterpret_cast<int32_t*>(base + o_src);
   st->ws_dst = reinterpret_cast<int32_t*>(base + o_dst);
   st->ws_victim = reinterpret_cast<int32_t*>(base + o_vic);
+  st->cp_src = reinterpret_cast<int32_t*>(base + o_cps);
+  st->cp_dst = reinterpret_cast<int32_t*>(base + o_cpd);
   st->err = reinterpret_cast<uint32_t*>(base + o_err);
 
   auto s = static_cast<hipStream_t>(stream);
@@ -369,6 +397,9 @@ int hisparse_swap_in_selected(hisparse_state_t st, int32_t layer_id, int32_t bat
                          out_locs, miss_count, page ? page_table : nullptr,
                          page ? num_pages : nullptr, plan);
   a.hash_size = page ? 0 : hash_size_for(a.K);
+  if (!page) enable_copy_sort(st, &a, lru_token_lds_bytes);
+  if ((page ? lru_page_lds_bytes(a) : lru_token_lds_bytes(a)) > st->max_lds)
+    return HISPARSE_E_UNSUPPORTED;
   return run_swap(st, a, false, static_cast<hipStream_t>(stream));
 }
 
@@ -391,6 +422,8 @@ int hisparse_swap_in_spec_multistep(hisparse_state_t st, int32_t layer_id, int32
                          topk_indices, out_locs, miss_count, nullptr, nullptr, plan);
   const int E = num_steps * a.K;
   a.hash_size = std::max(64, ((3 * E / 2 + 64) + 63) / 64 * 64);
+  enable_copy_sort(st, &a, clock_lds_bytes);
+  if (clock_lds_bytes(a) > st->max_lds) return HISPARSE_E_UNSUPPORTED;
   return run_swap(st, a, true, static_cast<hipStream_t>(stream));
 }
 
@@ -540,7 +573,7 @@ const char* hisparse_strerror(int code) {
 int hisparse_host_alloc(size_t bytes, void** out_h) {
   if (out_h == nullptr || bytes == 0) return HISPARSE_E_INVAL;
   *out_h = nullptr;
-  hipError_t e = hipHostMalloc(out_h, bytes, hipHostMallocMapped);
+  hipError_t e = hipHostMalloc(out_h, bytes, HISPARSE_HOST_ALLOC_FLAGS);
   if (e != hipSuccess) {
     (void)hipGetLastError();
     *out_h = nullptr;

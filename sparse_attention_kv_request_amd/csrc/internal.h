@@ -12,10 +12,24 @@
 
 namespace hisparse {
 
+// Launch shape of the miss copy; the macros let a build sweep other shapes.
+#ifndef HISPARSE_COPY_THREADS
+#define HISPARSE_COPY_THREADS 256
+#endif
+#ifndef HISPARSE_COPY_UNROLL
+#define HISPARSE_COPY_UNROLL 4
+#endif
+#ifndef HISPARSE_COPY_BLOCKS
+#define HISPARSE_COPY_BLOCKS 1024
+#endif
+#ifndef HISPARSE_COPY_NT_LOAD
+#define HISPARSE_COPY_NT_LOAD 0
+#endif
+
 constexpr int kPlanThreads = 1024;  // one workgroup (16 waves) per batch row
-constexpr int kCopyThreads = 256;
-constexpr int kCopyUnroll = 4;      // 16-byte loads in flight per lane
-constexpr int kCopyBlocks = 1024;   // 4 workgroups per CU on 256 CUs
+constexpr int kCopyThreads = HISPARSE_COPY_THREADS;
+constexpr int kCopyUnroll = HISPARSE_COPY_UNROLL;  // 16-byte loads in flight per lane
+constexpr int kCopyBlocks = HISPARSE_COPY_BLOCKS;  // 4 workgroups per CU on 256 CUs
 constexpr int kMaxPageModeHot = 4096;
 
 // Miss copy: rows of `unit_bytes` from the host tier to the hot buffer.
@@ -47,6 +61,7 @@ struct ResetArgs {
 };
 
 int hash_size_for(int entries);
+constexpr int kMaxSortedKeys = 1 << 18;  // keys per request with a sorted copy list
 size_t lru_token_lds_bytes(const PlanArgs& a);
 size_t lru_page_lds_bytes(const PlanArgs& a);
 size_t clock_lds_bytes(const PlanArgs& a);
@@ -80,7 +95,10 @@ struct hisparse_state {
   int32_t* ws_src = nullptr;
   int32_t* ws_dst = nullptr;
   int32_t* ws_victim = nullptr;
+  int32_t* cp_src = nullptr;  // copy list in ascending host-row order
+  int32_t* cp_dst = nullptr;
   uint32_t* err = nullptr;
+  size_t max_lds = 0;         // dynamic LDS a workgroup may use
   // profiling
   bool profiling = false;
   std::vector<hipEvent_t> ev_free;

@@ -37,7 +37,10 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
   uint32_t* pinned = reinterpret_cast<uint32_t*>(hval + T);     // [Hw]
   uint32_t* refl = pinned + a.Hw;                               // [Hw] reference bits
   int* scan = reinterpret_cast<int*>(refl + a.Hw);              // [NT/64+1]
-  int16_t* miss_h = reinterpret_cast<int16_t*>(scan + NT / kWave + 1);  // [E]
+  const int sw = a.sort_words;
+  uint32_t* mbits = reinterpret_cast<uint32_t*>(scan + NT / kWave + 1);  // [sw] miss keys
+  int32_t* mwpre = reinterpret_cast<int32_t*>(mbits + sw);              // [sw]
+  int16_t* miss_h = reinterpret_cast<int16_t*>(mwpre + sw);             // [E]
   __shared__ int s_cnt[HISPARSE_MAX_STEPS];
   __shared__ int s_klast;
   __shared__ int s_last_slot;
@@ -70,6 +73,7 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
     pinned[i] = 0u;
     refl[i] = refq[i];
   }
+  for (int i = tid; i < sw; i += NT) mbits[i] = 0u;
   if (tid < HISPARSE_MAX_STEPS) s_cnt[tid] = 0;
   __syncthreads();
 
@@ -120,6 +124,7 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
     } else {
       last[e] = 31 - __clz(hkey[hpos[e]] >> kKeyBits);
       atomicAdd(&s_cnt[last[e]], 1);
+      if (sw) bit_set_atomic(mbits, tok[e]);
       packed += 1;
     }
   }
@@ -204,6 +209,10 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
     }
   }
   __syncthreads();
+  if (sw) {
+    bitmap_word_prefix<NT>(mbits, mwpre, sw, scan);
+    __syncthreads();
+  }
 
   // 3. CLOCK sweep over circular positions k (slot = (hand + k) mod H)
   int sl_of[EPH];
@@ -283,6 +292,20 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
     msrc[j] = r * a.nkeys + key;
     mdst[j] = r * a.rows + s;
     mvic[j] = old;
+    if (sw) {
+      const size_t c = static_cast<size_t>(b) * a.ccap + bitmap_rank(mbits, mwpre, key);
+      a.copy_src[c] = r * a.nkeys + key;
+      a.copy_dst[c] = r * a.rows + s;
+    }
+  }
+  if (sw) {  // scratch-row misses join the copy list too
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      if (jm[e] < 0 || adm[e]) continue;
+      const size_t c = static_cast<size_t>(b) * a.ccap + bitmap_rank(mbits, mwpre, tok[e]);
+      a.copy_src[c] = r * a.nkeys + tok[e];
+      a.copy_dst[c] = r * a.rows + a.H + (jm[e] - ja[e]);
+    }
   }
   __syncthreads();
 
@@ -307,8 +330,8 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
 }  // namespace
 
 size_t clock_lds_bytes(const PlanArgs& a) {
-  return (2 * static_cast<size_t>(a.hash_size) + 2 * a.Hw + kPlanThreads / kWave + 1) * 4 +
-         static_cast<size_t>(a.S) * a.K * 2;
+  return (2 * static_cast<size_t>(a.hash_size) + 2 * a.Hw + kPlanThreads / kWave + 1 +
+          2 * static_cast<size_t>(a.sort_words)) * 4 + static_cast<size_t>(a.S) * a.K * 2;
 }
 
 hipError_t launch_clock_plan(const PlanArgs& a, hipStream_t s) {

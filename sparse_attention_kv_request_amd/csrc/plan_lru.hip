@@ -54,7 +54,8 @@ template <int NT, int EPH>
 __device__ void lru_select_commit(const PlanArgs& a, int b, int r, int now, int m,
                                   const int (&o)[EPH], uint32_t* used, const int32_t* miss_key,
                                   int32_t* vslot, int* scan, int16_t* ks, int32_t* sk,
-                                  int32_t* tsq, int16_t* ord) {
+                                  int32_t* tsq, int16_t* ord, const uint32_t* mbits,
+                                  const int32_t* mwpre) {
   const int tid = threadIdx.x;
   bool avail[EPH];
   int navail = 0;
@@ -91,6 +92,11 @@ __device__ void lru_select_commit(const PlanArgs& a, int b, int r, int now, int 
       msrc[j] = r * a.nkeys + key;
       mdst[j] = r * a.rows + s;
       mvic[j] = old;
+      if (mbits != nullptr) {
+        const size_t c = static_cast<size_t>(b) * a.ccap + bitmap_rank(mbits, mwpre, key);
+        a.copy_src[c] = r * a.nkeys + key;
+        a.copy_dst[c] = r * a.rows + s;
+      }
     }
   }
   __syncthreads();
@@ -129,6 +135,9 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
   int32_t* miss_key = reinterpret_cast<int32_t*>(used + a.Hw);     // [K]
   int32_t* vslot = miss_key + a.K;                                 // [K]
   int* scan = vslot + a.K;                                         // [NT/64+1]
+  const int sw = a.sort_words;
+  uint32_t* mbits = reinterpret_cast<uint32_t*>(scan + NT / kWave + 1);  // [sw] miss keys
+  int32_t* mwpre = reinterpret_cast<int32_t*>(mbits + sw);              // [sw]
 
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -158,6 +167,7 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
     hval[i] = 0x7fffffff;
   }
   for (int i = tid; i < a.Hw; i += NT) used[i] = 0u;
+  for (int i = tid; i < sw; i += NT) mbits[i] = 0u;
   __syncthreads();
 
   // 1. validate and insert every entry; the first occurrence keeps its position
@@ -210,13 +220,19 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
     if (rep[e] && slot[e] < 0) {
       hval[hpos[e]] = -(j + 1);
       miss_key[j] = tok[e];
+      if (sw) bit_set_atomic(mbits, tok[e]);
       ++j;
     }
   }
   __syncthreads();
+  if (sw) {
+    bitmap_word_prefix<NT>(mbits, mwpre, sw, scan);
+    __syncthreads();
+  }
 
   // 3. victims, commit, new order
-  lru_select_commit<NT, EPH>(a, b, r, now, m, o, used, miss_key, vslot, scan, ks, sk, tsq, ord);
+  lru_select_commit<NT, EPH>(a, b, r, now, m, o, used, miss_key, vslot, scan, ks, sk, tsq, ord,
+                             sw ? mbits : nullptr, mwpre);
   __syncthreads();
 
   // 4. outputs
@@ -344,8 +360,9 @@ __global__ __launch_bounds__(NT) void lru_page_plan(PlanArgs a) {
   }
   __syncthreads();
 
-  // 4. victims, commit, new order
-  lru_select_commit<NT, EPH>(a, b, r, now, m, o, used, miss_key, vslot, scan, ks, sk, tsq, ord);
+  // 4. victims, commit, new order (pages are already in ascending order)
+  lru_select_commit<NT, EPH>(a, b, r, now, m, o, used, miss_key, vslot, scan, ks, sk, tsq, ord,
+                             nullptr, nullptr);
   __syncthreads();
 
   // 5. outputs: page table, page count, token locations (page index, offset)
@@ -401,7 +418,7 @@ int hash_size_for(int entries) {
 
 size_t lru_token_lds_bytes(const PlanArgs& a) {
   return (2 * static_cast<size_t>(a.hash_size) + a.Hw + 2 * static_cast<size_t>(a.K) +
-          kPlanThreads / kWave + 1) * 4;
+          kPlanThreads / kWave + 1 + 2 * static_cast<size_t>(a.sort_words)) * 4;
 }
 
 size_t lru_page_lds_bytes(const PlanArgs& a) {

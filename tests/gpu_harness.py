@@ -64,13 +64,13 @@ class Pair:
             h.free()
 
     # -- calls -------------------------------------------------------------------
-    def call(self, layer, req, seq, topk, check_bytes=True, check_state=True):
+    def call(self, layer, req, seq, topk, check_bytes=True, check_state=True, plan_extra=0):
         req = np.asarray(req, np.int32)
         seq = np.asarray(seq, np.int32)
         topk = np.asarray(topk, np.int32)
         B = req.shape[0]
         multi = topk.ndim == 3
-        cap = self.gpu.capacity
+        cap = self.gpu.capacity + plan_extra
         out = torch.full(topk.shape, -7, dtype=torch.int32, device=DEV)
         mc = torch.full((B,), -7, dtype=torch.int32, device=DEV)
         plan = tuple(torch.full((B, cap), -7, dtype=torch.int32, device=DEV) for _ in range(3))

@@ -63,7 +63,7 @@ def test_lru_token_parity(H, K, N, I):
             req = rng.permutation(R)[:B]
             rows = make_rows(rng, B, K, N, prev=prev.get(layer))
             prev[layer] = rows
-            p.call(layer, req, np.full(B, N), rows)
+            p.call(layer, req, np.full(B, N), rows, plan_extra=7 * (call % 2))
     finally:
         p.close()
 
@@ -129,7 +129,7 @@ def test_clock_multistep_parity(H, K, N, I, S):
                 nxt = make_rows(rng, B, K, N, prev=base, reuse=0.8)
                 steps.append(nxt)
             topk = np.stack(steps, axis=1)
-            p.call(layer, req, np.full(B, N), topk)
+            p.call(layer, req, np.full(B, N), topk, plan_extra=5 * (call % 2))
     finally:
         p.close()
 
