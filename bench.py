@@ -1,16 +1,19 @@
 #!/usr/bin/env python3
 """Benchmark of the HiSparse swap-in hot path on one MI355X.
 
-Workload (single-step LRU): 64 requests x 8 layers, every (request, layer) an
-independent hot cache of 4096 slots over 32768 host tokens of 656 bytes (fp8
-MLA layout: 512 e4m3 latent + 4 fp32 scales + 64 bf16 rope), top-k 2048 per
-row and layer, 70 % step-to-step reuse with a Zipf(1.1) recency bias.  One
-step is one decode step: the 8 per-layer swap calls (lookup/victim/commit
-kernel + miss-copy kernel each) on one stream.
+Default workload (single-step LRU, the bench line): 64 requests x 8 layers,
+every (request, layer) an independent hot cache of 4096 slots over 32768 host
+tokens of 656 bytes (fp8 MLA layout: 512 e4m3 latent + 4 fp32 scales + 64
+bf16 rope), top-k 2048 per row and layer, 70 % step-to-step reuse with a
+Zipf(1.1) recency bias.  One step is one decode step: the 8 per-layer swap
+calls (plan kernel + miss-copy kernel each) on one stream.
 
-Inputs (top-k traces) are resident in HBM and the host KV tier is in pinned
-host memory before the timed region; reading the host tier over PCIe is the
-method's own miss copy.  Prints one JSON line.
+``--workload 1|3|4|5`` measures the other workload shapes the same way
+(1: B=1 bf16 rows; 3: multi-step CLOCK, also against S sequential LRU calls;
+4: miss-heavy long context; 5: page mode).  Inputs (top-k traces) are resident
+in HBM and the host KV tier in pinned host memory before the timed region;
+reading the host tier over PCIe is the method's own miss copy.  Prints one
+JSON line.
 """
 from __future__ import annotations
 
@@ -39,6 +42,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--num-steps", type=int, default=4, help="MTP steps of workload 3")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -46,17 +51,36 @@ def parse():
     return ap.parse_args()
 
 
-def state_bytes_per_row(K, H, m):
-    """Algorithmic HBM bytes of the plan kernel for one row of the workload
-    (every row holds K distinct tokens, m of them misses): top-k read and
-    output write (4 + 4 B per entry), key->slot probe (2 B per key), hit
-    timestamp (4 B), LRU order read + write (2 + 2 B per slot), call counter
-    (8 B), and per miss slot->key read + write, key->slot delete + insert,
-    timestamp and the three plan words (4+4+2+2+4+12 B)."""
-    return 8 * K + 2 * K + 4 * (K - m) + 4 * H + 8 + 28 * m
+def state_bytes_per_row(w, m, distinct):
+    """Algorithmic HBM bytes of the plan kernel for one row with `distinct`
+    keys of which m miss: top-k read and output write (4 + 4 B per entry),
+    key->slot probe (2 B per key), hit policy update (4 B), LRU order read +
+    write (2 + 2 B per slot; CLOCK: reference bits read + write, H/4 B),
+    control word (8 B), and per miss slot->key read + write, key->slot delete
+    + insert, policy word and the three plan words (4+4+2+2+4+12 B) plus the
+    two copy-list words (8 B)."""
+    entries = w.num_steps * w.top_k
+    policy = 4 * w.hot if w.policy == "lru" else w.hot // 4
+    return 8 * entries + 2 * distinct + 4 * (distinct - m) + policy + 8 + 36 * m
 
 
-def link_probes(torch, binding, st, host, w, rows):
+def distinct_keys(w, trace):
+    """Distinct keys per row of every call: tokens over all MTP steps, or
+    pages in page mode.  trace: [L, steps, B, S, K] -> [L, steps, B]."""
+    import numpy as np
+
+    L, T, B = trace.shape[:3]
+    out = np.empty((L, T, B), np.int64)
+    for l in range(L):
+        for t in range(T):
+            for b in range(B):
+                keys = trace[l, t, b].reshape(-1)
+                keys = keys[keys >= 0] // w.page_size
+                out[l, t, b] = np.unique(keys).size
+    return out
+
+
+def link_probes(torch, st, w, rows):
     """Host->HBM link: (i) hipMemcpyAsync of 1 GiB from pinned memory, (ii) the
     miss-copy kernel replaying a plan of consecutive host rows, (iii) the same
     kernel over a random row order (the gather pattern of real misses)."""
@@ -75,8 +99,9 @@ def link_probes(torch, binding, st, host, w, rows):
         best = max(best, (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9)
     res["memcpy_h2d_GBps"] = round(best, 2)
     del src, dst
-    B, N, H, I = w.batch, w.seq_len, w.hot, w.item_bytes
-    per = N // 2
+    B, N, H = w.batch, w.seq_len // w.page_size, w.hot
+    unit = w.item_bytes * w.page_size
+    per = min(N // 2, max(1, (1 << 30) // (B * unit)))
     mc = torch.full((B,), per, dtype=torch.int32, device=dev)
     j = torch.arange(per, dtype=torch.int32, device=dev)
     r = torch.arange(B, dtype=torch.int32, device=dev)[:, None]
@@ -96,31 +121,40 @@ def link_probes(torch, binding, st, host, w, rows):
             st.copy_planned(0, mc, plan)
             e1.record()
             torch.cuda.synchronize()
-            best = max(best, B * per * I / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+            best = max(best, B * per * unit / (e0.elapsed_time(e1) * 1e-3) / 1e9)
         res[name] = round(best, 2)
     # the probe overwrote device rows: empty the caches again
-    st.request_reset(torch.arange(B, dtype=torch.int32, device=dev))
+    st.request_reset(torch.arange(w.requests, dtype=torch.int32, device=dev))
     torch.cuda.synchronize()
     return res
 
 
 def cpu_baseline(w, host, trace, budget_s):
     """The oracle as it stands, timed on one host core over whole instances
-    (request r, layer 0, every step of the trace) until the budget is spent."""
+    (request r, layer l, every step of the trace) until the budget is spent."""
     from oracle import hisparse_oracle as ora
 
-    st = ora.OracleState(max_requests=w.batch, num_layers=1, hot=w.hot, top_k=w.top_k,
-                         item_bytes=w.item_bytes, max_seq_len=w.seq_len,
-                         host_kv=[host[0].array])
-    entries = 0
-    insts = 0
+    st = ora.OracleState(max_requests=w.requests, num_layers=w.layers, hot=w.hot,
+                         top_k=w.top_k, item_bytes=w.item_bytes, max_seq_len=w.seq_len,
+                         max_steps=w.num_steps, page_size=w.page_size, policy=w.policy,
+                         host_kv=[h.array for h in host])
+    entries = insts = 0
     t0 = time.perf_counter()
-    for r in range(w.batch):
-        for s in range(trace.shape[1]):
-            st.swap_in_selected(0, [r], [w.seq_len], trace[0, s, r:r + 1, 0])
-            entries += w.top_k
-        insts += 1
-        if time.perf_counter() - t0 >= budget_s:
+    done = False
+    for l in range(w.layers):
+        for r in range(w.batch):
+            for s in range(trace.shape[1]):
+                rows = trace[l, s, r:r + 1]
+                if w.policy == "clock":
+                    st.swap_in_spec_multistep(l, [r], [w.seq_len], rows)
+                else:
+                    st.swap_in_selected(l, [r], [w.seq_len], rows[:, 0])
+                entries += w.num_steps * w.top_k
+            insts += 1
+            if time.perf_counter() - t0 >= budget_s:
+                done = True
+                break
+        if done:
             break
     dt = time.perf_counter() - t0
     return {"value": round(entries / dt, 1), "unit": "entries/s", "cores": 1, "kind": "oracle",
@@ -134,16 +168,114 @@ def copy_kernel_hash():
     return hashlib.sha256(src).hexdigest()[:16]
 
 
-def traffic_from_profiles():
+def traffic_from_profiles(workload):
     """HBM bytes per copy launch from the committed counter summary, if it was
-    taken on the current copy kernel source."""
+    taken on the current copy kernel source and this workload."""
     p = ROOT / "profiles" / "miss_copy_counters.json"
     if not p.exists():
         return None
     d = json.loads(p.read_text())
     if d.get("copy_kernel_sha256_16") != copy_kernel_hash():
         return None
-    return d.get("traffic_bytes_per_launch")
+    return d.get("traffic_bytes_per_launch", {}).get(str(workload))
+
+
+WORKLOAD_TEXT = {
+    1: "single-step LRU swap-in: 1 request, top_k 2048, hot 4096, 8192 host tokens x 1152 B (bf16)",
+    2: ("single-step LRU swap-in: 64 requests x 8 layers, top_k 2048, hot buffer 4096 slots, "
+        "32768 host tokens x 656 B (fp8 MLA), 70% reuse + Zipf(1.1) recency"),
+    3: ("multi-step CLOCK swap-in: 64 requests, {S} MTP steps x top_k 2048, hot 4096, "
+        "32768 host tokens x 656 B, 80% intra-call share, 60% call-to-call reuse"),
+    4: "single-step LRU swap-in: 128 requests, top_k 2048, hot 8192, 131072 host tokens x 656 B, 30% reuse",
+    5: ("page-mode LRU swap-in: 32 requests, 256-token pages, 512 clustered tokens, "
+        "64 hot pages, 65536 host tokens x 656 B"),
+}
+
+
+class Runner:
+    """One workload on the GPU: host tier, traces, state, per-step calls."""
+
+    def __init__(self, torch, binding, workloads, w, policy=None):
+        import numpy as np
+
+        self.torch, self.w = torch, w
+        self.np = np
+        self.dev = torch.device("cuda", 0)
+        self.policy = policy or w.policy
+        t0 = time.perf_counter()
+        self.host = [binding.HostKV(w.requests, w.seq_len, w.item_bytes) for _ in range(w.layers)]
+        workloads.fill_host_kv(w, [h.array for h in self.host], threads=16)
+        log(f"host KV {w.layers} x {self.host[0].nbytes / 2**30:.2f} GiB in "
+            f"{time.perf_counter() - t0:.1f} s")
+        t0 = time.perf_counter()
+        self.trace = workloads.batch_trace(w, threads=16)     # [L, steps, B, S, K]
+        log(f"trace {self.trace.shape} in {time.perf_counter() - t0:.1f} s")
+        self.topk = torch.from_numpy(np.ascontiguousarray(
+            self.trace.transpose(1, 0, 2, 3, 4))).to(self.dev)  # [steps, L, B, S, K]
+        # per-MTP-step rows for the sequential comparator: [steps, L, S, B, K]
+        self.topk_seq = (self.topk.permute(0, 1, 3, 2, 4).contiguous()
+                         if self.policy != "clock" and w.num_steps > 1 else None)
+        B = w.batch
+        self.req = torch.arange(B, dtype=torch.int32, device=self.dev)
+        self.seq = torch.full((B,), w.seq_len, dtype=torch.int32, device=self.dev)
+        multi = self.policy == "clock"
+        self.st = binding.HiSparseState(
+            max_requests=w.requests, num_layers=w.layers, hot_buffer_size=w.hot,
+            top_k=w.top_k, item_size_bytes=w.item_bytes, max_seq_len=w.seq_len,
+            max_steps=w.num_steps if multi else 1, page_size=w.page_size, policy=self.policy,
+            host_kv=self.host)
+        S = w.num_steps
+        self.outs = [torch.empty((B, S, w.top_k) if multi else (B, w.top_k), dtype=torch.int32,
+                                 device=self.dev) for _ in range(w.layers)]
+        calls_per_step = 1 if (multi or S == 1) else S
+        self.miss = torch.zeros((w.steps, w.layers, calls_per_step, B), dtype=torch.int32,
+                                device=self.dev)
+        self.pt = self.npg = None
+        if w.page_size > 1:
+            self.pt = torch.empty((B, w.hot), dtype=torch.int32, device=self.dev)
+            self.npg = torch.empty(B, dtype=torch.int32, device=self.dev)
+
+    def step(self, s):
+        st, w = self.st, self.w
+        for l in range(w.layers):
+            if self.policy == "clock":
+                st.swap_in_spec_multistep(l, self.req, self.seq, self.topk[s, l], self.outs[l],
+                                          self.miss[s, l, 0])
+            elif w.num_steps == 1:
+                st.swap_in_selected(l, self.req, self.seq, self.topk[s, l, :, 0], self.outs[l],
+                                    self.miss[s, l, 0], page_table=self.pt, num_pages=self.npg)
+            else:  # sequential comparator: one single-step call per MTP step
+                for k in range(w.num_steps):
+                    st.swap_in_selected(l, self.req, self.seq, self.topk_seq[s, l, k],
+                                        self.outs[l], self.miss[s, l, k])
+
+    def timed(self, W, K):
+        torch = self.torch
+        for s in range(W):
+            self.step(s)
+        torch.cuda.synchronize()
+        self.st.profile(True)
+        self.st.profile_read()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for s in range(W, W + K):
+            self.step(s)
+        e1.record()
+        torch.cuda.synchronize()
+        elapsed = e0.elapsed_time(e1) * 1e-3
+        prof = self.st.profile_read()
+        self.st.profile(False)
+        flags = self.st.error_flags()
+        if flags:
+            raise SystemExit(f"device error flags {flags} during the benchmark")
+        m = self.miss[W:W + K].cpu().numpy().astype(self.np.int64)
+        return elapsed, prof, m
+
+    def close(self):
+        self.st.close()
+        for h in self.host:
+            h.free()
 
 
 def main():
@@ -155,111 +287,86 @@ def main():
               "the path would shard). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     from sparse_attention_kv_request_amd import binding, workloads
 
     torch.cuda.set_device(0)
-    dev = torch.device("cuda", 0)
     W, K = args.warmup, args.steps
-    w = workloads.config(2, steps=W + K)
-    B, L, H, N, I, TK = w.batch, w.layers, w.hot, w.seq_len, w.item_bytes, w.top_k
-
-    t0 = time.perf_counter()
-    host = [binding.HostKV(B, N, I) for _ in range(L)]
-    workloads.fill_host_kv(w, [h.array for h in host], threads=16)
-    log(f"host KV {L} x {host[0].nbytes / 2**30:.2f} GiB filled in {time.perf_counter() - t0:.1f} s")
-    t0 = time.perf_counter()
-    trace = workloads.batch_trace(w, threads=16)          # [L, steps, B, 1, K]
-    log(f"trace {trace.shape} in {time.perf_counter() - t0:.1f} s")
-    topk = torch.from_numpy(np.ascontiguousarray(trace[:, :, :, 0].transpose(1, 0, 2, 3))).to(dev)
-    req = torch.arange(B, dtype=torch.int32, device=dev)
-    seq = torch.full((B,), N, dtype=torch.int32, device=dev)
-
-    st = binding.HiSparseState(max_requests=B, num_layers=L, hot_buffer_size=H, top_k=TK,
-                               item_size_bytes=I, max_seq_len=N, host_kv=host)
-    link = {} if args.no_link_probe else link_probes(torch, binding, st, host, w, st.rows)
+    over = {"steps": W + K}
+    if args.workload == 3:
+        over["num_steps"] = args.num_steps
+    w = workloads.config(args.workload, **over)
+    run = Runner(torch, binding, workloads, w)
+    link = {} if args.no_link_probe else link_probes(torch, run.st, w, run.st.rows)
     if link:
         log(f"link probes {link}")
+    elapsed, prof, m = run.timed(W, K)
 
-    outs = [torch.empty((B, TK), dtype=torch.int32, device=dev) for _ in range(L)]
-    miss = torch.zeros((W + K, L, B), dtype=torch.int32, device=dev)
-
-    def step(s):
-        for l in range(L):
-            st.swap_in_selected(l, req, seq, topk[s, l], outs[l], miss[s, l])
-
-    for s in range(W):
-        step(s)
-    torch.cuda.synchronize()
-    st.profile(True)
-    st.profile_read()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for s in range(W, W + K):
-        step(s)
-    e1.record()
-    torch.cuda.synchronize()
-    elapsed_s = e0.elapsed_time(e1) * 1e-3
-    prof = st.profile_read()
-    st.profile(False)
-    flags = st.error_flags()
-    if flags:
-        raise SystemExit(f"device error flags {flags} during the benchmark")
-
-    m = miss[W:].cpu().numpy().astype(np.int64)            # [K, L, B]
-    miss_bytes = int(m.sum()) * I
+    unit = w.item_bytes * w.page_size
+    miss_bytes = int(m.sum()) * unit
     entries = K * w.entries_per_step
-    calls = K * L
-    copy_s = prof["copy_ms"] * 1e-3
-    plan_s = prof["plan_ms"] * 1e-3
-    copy_gbps = miss_bytes / copy_s / 1e9
-    measured_link = max([v for v in link.values()], default=None)
-    state_bytes = int(sum(state_bytes_per_row(TK, H, int(x)) for x in m.reshape(-1)))
+    calls = prof["calls"]
+    copy_gbps = miss_bytes / (prof["copy_ms"] * 1e-3) / 1e9
+    measured_link = max(link.values(), default=None)
+    dist = distinct_keys(w, run.trace[:, W:W + K])           # [L, K, B]
+    state_bytes = sum(state_bytes_per_row(w, int(x), int(d))
+                      for x, d in zip(m[:, :, 0, :].transpose(1, 0, 2).reshape(-1),
+                                      dist.reshape(-1)))
+    plan_kernel = {"lru": "lru_page_plan" if w.page_size > 1 else "lru_token_plan",
+                   "clock": "clock_plan"}[w.policy]
+    cfg = {"workload": WORKLOAD_TEXT[args.workload].format(S=w.num_steps),
+           "batch": w.batch, "layers": w.layers, "num_steps": w.num_steps, "top_k": w.top_k,
+           "hot_buffer_size": w.hot, "seq_len": w.seq_len, "item_size_bytes": w.item_bytes,
+           "page_size": w.page_size, "policy": w.policy}
     res = {
         "metric": METRIC,
-        "value": round(entries / elapsed_s, 1),
+        "value": round(entries / elapsed, 1),
         "unit": "entries/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
-        "ms_per_step": round(elapsed_s * 1e3 / K, 4),
+        "ms_per_step": round(elapsed * 1e3 / K, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int32",
         "data": "synthetic",
-        "config": {"workload": "single-step LRU swap-in: 64 requests x 8 layers, top_k 2048, "
-                               "hot buffer 4096 slots, 32768 host tokens x 656 B (fp8 MLA), "
-                               "70% reuse + Zipf(1.1) recency",
-                   "batch": B, "layers": L, "top_k": TK, "hot_buffer_size": H,
-                   "seq_len": N, "item_size_bytes": I, "policy": "lru"},
-        "miss_copy": {"GBps_per_step": round(miss_bytes / elapsed_s / 1e9, 2),
+        "config": cfg,
+        "miss_copy": {"GBps_per_step": round(miss_bytes / elapsed / 1e9, 2),
                       "bytes_per_step": miss_bytes // K,
                       "misses_per_step": int(m.sum()) // K},
         "roofline": {"bound": "pcie", "kernel": "miss_copy",
                      "achieved": round(copy_gbps, 2), "peak": PCIE5_X16_GBPS, "unit": "GB/s",
                      "frac": round(copy_gbps / PCIE5_X16_GBPS, 4),
-                     "traffic": traffic_from_profiles(),
-                     "avg_launch_us": round(prof["copy_ms"] * 1e3 / max(prof["calls"], 1), 2),
-                     "bytes_per_launch": miss_bytes // calls,
+                     "traffic": traffic_from_profiles(args.workload),
+                     "avg_launch_us": round(prof["copy_ms"] * 1e3 / max(calls, 1), 2),
+                     "bytes_per_launch": miss_bytes // max(calls, 1),
                      "measured_link_GBps": measured_link,
                      "frac_of_measured_link": (round(copy_gbps / measured_link, 4)
                                                if measured_link else None)},
-        "state_roofline": {"bound": "hbm", "kernel": "lru_token_plan",
-                           "achieved": round(state_bytes / plan_s / 1e9, 2),
+        "state_roofline": {"bound": "hbm", "kernel": plan_kernel,
+                           "achieved": round(state_bytes / (prof["plan_ms"] * 1e-3) / 1e9, 2),
                            "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                           "frac": round(state_bytes / plan_s / 1e9 / HBM_PEAK_GBPS, 5),
-                           "avg_launch_us": round(prof["plan_ms"] * 1e3 / max(prof["calls"], 1), 2),
-                           "bytes_per_launch": state_bytes // calls},
+                           "frac": round(state_bytes / (prof["plan_ms"] * 1e-3) / 1e9
+                                         / HBM_PEAK_GBPS, 5),
+                           "avg_launch_us": round(prof["plan_ms"] * 1e3 / max(calls, 1), 2),
+                           "bytes_per_launch": state_bytes // max(calls, 1)},
         "link": link,
     }
+    if args.workload == 3:
+        # the per-step path the multi-step call replaces: S single-step LRU calls
+        seq_run = Runner(torch, binding, workloads, w, policy="lru")
+        seq_elapsed, _, _ = seq_run.timed(W, K)
+        seq_run.close()
+        res["sequential_lru"] = {
+            "ms_per_call_multistep": round(elapsed * 1e3 / (K * w.layers), 4),
+            "ms_per_call_sequential": round(seq_elapsed * 1e3 / (K * w.layers), 4),
+            "latency_reduction": round(1 - elapsed / seq_elapsed, 4)}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
-        res["cpu_baseline"] = cpu_baseline(w, host, trace, args.cpu_seconds)
-    st.close()
+        res["cpu_baseline"] = cpu_baseline(w, run.host, run.trace, args.cpu_seconds)
+    run.close()
     print(json.dumps(res), flush=True)
 
 
