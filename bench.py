@@ -163,9 +163,16 @@ def cpu_baseline(w, host, trace, budget_s):
                        f"into a shadow device buffer), {dt:.1f} s on one core")}
 
 
+COPY_SOURCES = ("copy.hip", "plan_lru.hip", "internal.h")
+
+
 def copy_kernel_hash():
-    src = (ROOT / "sparse_attention_kv_request_amd" / "csrc" / "copy.hip").read_bytes()
-    return hashlib.sha256(src).hexdigest()[:16]
+    """Hash of the sources that decide the copy kernel's launches (the kernel,
+    its launch shape and the copy list the plan kernel writes)."""
+    m = hashlib.sha256()
+    for name in COPY_SOURCES:
+        m.update((ROOT / "sparse_attention_kv_request_amd" / "csrc" / name).read_bytes())
+    return m.hexdigest()[:16]
 
 
 def traffic_from_profiles(workload):

@@ -21,7 +21,7 @@ def short(name: str) -> str:
     return name.split("(")[0][:60]
 
 
-def summarize(db_path: str, skip: int):
+def summarize(db_path: str, skip: int, limit: int = 0):
     db = sqlite3.connect(db_path)
     rows = db.execute("select name, duration from kernels order by start").fetchall()
     by = collections.OrderedDict()
@@ -30,6 +30,8 @@ def summarize(db_path: str, skip: int):
     out = []
     for k, v in by.items():
         timed = v[skip:] if len(v) > skip else v
+        if limit:
+            timed = timed[:limit]
         out.append((k, len(v), sum(v) / len(v), len(timed), sum(timed) / len(timed), sum(v)))
     out.sort(key=lambda r: -r[5])
     return out
@@ -39,6 +41,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("db")
     ap.add_argument("--skip", type=int, default=0)
+    ap.add_argument("--limit", type=int, default=0,
+                    help="use at most this many launches per kernel after the skipped ones")
     ap.add_argument("--command", default="")
     ap.add_argument("--title", default="rocprofv3 kernel trace")
     a = ap.parse_args()
@@ -47,7 +51,7 @@ def main():
         print(f"Command: `{a.command}`\n")
     print(f"| kernel | launches | avg us (all) | launches timed | avg us (timed, first {a.skip} skipped) | total us |")
     print("|---|---|---|---|---|---|")
-    for k, n, avg, nt, avg_t, tot in summarize(a.db, a.skip):
+    for k, n, avg, nt, avg_t, tot in summarize(a.db, a.skip, a.limit):
         print(f"| `{k}` | {n} | {avg:.2f} | {nt} | {avg_t:.2f} | {tot:.1f} |")
 
 
