@@ -31,6 +31,8 @@ constexpr int kCopyThreads = HISPARSE_COPY_THREADS;
 constexpr int kCopyUnroll = HISPARSE_COPY_UNROLL;  // 16-byte loads in flight per lane
 constexpr int kCopyBlocks = HISPARSE_COPY_BLOCKS;  // 4 workgroups per CU on 256 CUs
 constexpr int kMaxPageModeHot = 4096;
+static_assert((HISPARSE_MAX_HOT + 31) / 32 <= kPlanThreads,
+              "one thread per word of an H-bit mask in the plan kernels");
 
 // Miss copy: rows of `unit_bytes` from the host tier to the hot buffer.
 struct CopyArgs {

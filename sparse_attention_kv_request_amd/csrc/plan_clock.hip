@@ -49,6 +49,21 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
   const int tid = threadIdx.x;
   const int r = a.req[b];
   const int sl = a.seq[b];
+  // Loads that need only the instance go out before the row checks so they
+  // share one round trip (a rejected row discards them).
+  const size_t q = static_cast<size_t>(a.layer) * a.R + (r >= 0 && r < a.R ? r : 0);
+  int16_t* ks = a.key_slot + q * a.nkeys;
+  int32_t* sk = a.slot_key + q * a.H;
+  uint32_t* refq = a.refbits + q * a.Hw;
+  const int hand = a.ctrl[2 * q + 1];
+  const int32_t* row = a.topk + static_cast<size_t>(b) * E;
+  int32_t raw[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int i = tid * EPT + e;
+    raw[e] = i < E ? row[i] : -1;
+  }
+  const uint32_t ref_word = tid < a.Hw ? refq[tid] : 0u;  // Hw <= NT
   const uint32_t code = multistep_row_check<NT>(a, b, r, sl);
   if (code) {
     int32_t* out = a.out_locs + static_cast<size_t>(b) * E;
@@ -59,33 +74,36 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
     }
     return;
   }
-  const size_t q = static_cast<size_t>(a.layer) * a.R + r;
-  int16_t* ks = a.key_slot + q * a.nkeys;
-  int32_t* sk = a.slot_key + q * a.H;
-  uint32_t* refq = a.refbits + q * a.Hw;
-  const int hand = a.ctrl[2 * q + 1];
-
+  // circular sweep positions of this thread and their slot->key words
+  int sl_of[EPH];
+  int oldk[EPH];
+#pragma unroll
+  for (int e = 0; e < EPH; ++e) {
+    const int k = tid * EPH + e;
+    int s = hand + k;
+    if (s >= a.H) s -= a.H;
+    sl_of[e] = k < a.H ? s : -1;
+    oldk[e] = k < a.H ? sk[s] : kEmpty;
+  }
   for (int i = tid; i < T; i += NT) {
     hkey[i] = 0u;
     hval[i] = 0x7fffffff;
   }
-  for (int i = tid; i < a.Hw; i += NT) {
-    pinned[i] = 0u;
-    refl[i] = refq[i];
+  if (tid < a.Hw) {
+    pinned[tid] = 0u;
+    refl[tid] = ref_word;
   }
   for (int i = tid; i < sw; i += NT) mbits[i] = 0u;
   if (tid < HISPARSE_MAX_STEPS) s_cnt[tid] = 0;
   __syncthreads();
 
   // 1. flatten [S][K] step-major; insert with the step bit
-  const int32_t* row = a.topk + static_cast<size_t>(b) * E;
   int32_t tok[EPT];
   int hpos[EPT];
   bool bad_index = false;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
-    const int i = tid * EPT + e;
-    const int32_t t = i < E ? row[i] : -1;
+    const int32_t t = raw[e];
     const bool valid = t >= 0 && t < sl;
     bad_index |= (!valid && t != -1);
     tok[e] = valid ? t : -1;
@@ -215,17 +233,13 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
   }
 
   // 3. CLOCK sweep over circular positions k (slot = (hand + k) mod H)
-  int sl_of[EPH];
   bool pin[EPH], rf[EPH];
   int n1 = 0;
 #pragma unroll
   for (int e = 0; e < EPH; ++e) {
-    const int k = tid * EPH + e;
-    int s = hand + k;
-    if (s >= a.H) s -= a.H;
-    sl_of[e] = k < a.H ? s : -1;
-    pin[e] = k < a.H ? bit_test(pinned, s) : true;
-    rf[e] = k < a.H ? bit_test(refl, s) : false;
+    const int s = sl_of[e];
+    pin[e] = s >= 0 ? bit_test(pinned, s) : true;
+    rf[e] = s >= 0 ? bit_test(refl, s) : false;
     n1 += (!pin[e] && !rf[e]);
   }
   int e1_tot;
@@ -283,7 +297,7 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
     const int s = sl_of[e];
     const int h = miss_h[j];
     const int32_t key = static_cast<int32_t>(hkey[h] & kKeyMask) - 1;
-    const int32_t old = sk[s];
+    const int32_t old = oldk[e];  // slot_key[s], fetched at kernel start
     if (old >= 0) ks[old] = static_cast<int16_t>(kEmpty);
     sk[s] = key;
     ks[key] = static_cast<int16_t>(s);
@@ -309,7 +323,7 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
   }
   __syncthreads();
 
-  for (int i = tid; i < a.Hw; i += NT) refq[i] = refl[i];
+  if (tid < a.Hw) refq[tid] = refl[tid];
   int32_t* out = a.out_locs + static_cast<size_t>(b) * E;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {

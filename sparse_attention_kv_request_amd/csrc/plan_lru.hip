@@ -55,7 +55,7 @@ __device__ void lru_select_commit(const PlanArgs& a, int b, int r, int now, int 
                                   const int (&o)[EPH], uint32_t* used, const int32_t* miss_key,
                                   int32_t* vslot, int* scan, int16_t* ks, int32_t* sk,
                                   int32_t* tsq, int16_t* ord, const uint32_t* mbits,
-                                  const int32_t* mwpre) {
+                                  const int32_t* mwpre, const int (&oldk)[EPH]) {
   const int tid = threadIdx.x;
   bool avail[EPH];
   int navail = 0;
@@ -82,7 +82,7 @@ __device__ void lru_select_commit(const PlanArgs& a, int b, int r, int now, int 
       const int j = rank[e];
       const int s = o[e];
       const int32_t key = miss_key[j];
-      const int32_t old = sk[s];
+      const int32_t old = oldk[e];  // slot_key[s], fetched at kernel start
       if (old >= 0) ks[old] = static_cast<int16_t>(kEmpty);
       sk[s] = key;
       ks[key] = static_cast<int16_t>(s);
@@ -143,25 +143,36 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
   const int tid = threadIdx.x;
   const int r = a.req[b];
   const int sl = a.seq[b];
-  const uint32_t code = row_check<NT>(a, b, r, sl);
-  if (code) {
-    reject_row<NT>(a, b, a.K, code, false);
-    return;
-  }
-  const size_t q = static_cast<size_t>(a.layer) * a.R + r;
+  // Loads that need only the instance go out before the row checks so they
+  // share one round trip (a rejected row discards them).
+  const size_t q = static_cast<size_t>(a.layer) * a.R + (r >= 0 && r < a.R ? r : 0);
   int16_t* ks = a.key_slot + q * a.nkeys;
   int32_t* sk = a.slot_key + q * a.H;
   int32_t* tsq = a.ts + q * a.H;
   int16_t* ord = a.order + q * a.H;
   const int now = a.ctrl[2 * q];
-
-  // the LRU order is independent of the row: fetch it first
   int o[EPH];
 #pragma unroll
   for (int e = 0; e < EPH; ++e) {
     const int k = tid * EPH + e;
     o[e] = k < a.H ? static_cast<int>(ord[k]) : -1;
   }
+  const int32_t* row = a.topk + static_cast<size_t>(b) * a.K;
+  int32_t raw[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int i = tid * EPT + e;
+    raw[e] = i < a.K ? row[i] : -1;
+  }
+  const uint32_t code = row_check<NT>(a, b, r, sl);
+  if (code) {
+    reject_row<NT>(a, b, a.K, code, false);
+    return;
+  }
+  // slot->key of every order position, for the victims' commit
+  int oldk[EPH];
+#pragma unroll
+  for (int e = 0; e < EPH; ++e) oldk[e] = o[e] >= 0 ? sk[o[e]] : kEmpty;
   for (int i = tid; i < T; i += NT) {
     hkey[i] = 0u;
     hval[i] = 0x7fffffff;
@@ -171,14 +182,12 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
   __syncthreads();
 
   // 1. validate and insert every entry; the first occurrence keeps its position
-  const int32_t* row = a.topk + static_cast<size_t>(b) * a.K;
   int32_t tok[EPT];
   int hpos[EPT];
   bool bad_index = false;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
-    const int i = tid * EPT + e;
-    const int32_t t = i < a.K ? row[i] : -1;
+    const int32_t t = raw[e];
     const bool valid = t >= 0 && t < sl;
     bad_index |= (!valid && t != -1);
     tok[e] = valid ? t : -1;
@@ -232,7 +241,7 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
 
   // 3. victims, commit, new order
   lru_select_commit<NT, EPH>(a, b, r, now, m, o, used, miss_key, vslot, scan, ks, sk, tsq, ord,
-                             sw ? mbits : nullptr, mwpre);
+                             sw ? mbits : nullptr, mwpre, oldk);
   __syncthreads();
 
   // 4. outputs
@@ -274,36 +283,43 @@ __global__ __launch_bounds__(NT) void lru_page_plan(PlanArgs a) {
   const int tid = threadIdx.x;
   const int r = a.req[b];
   const int sl = a.seq[b];
-  const uint32_t code = row_check<NT>(a, b, r, sl);
-  if (code) {
-    reject_row<NT>(a, b, a.K, code, true);
-    return;
-  }
-  const size_t q = static_cast<size_t>(a.layer) * a.R + r;
+  const size_t q = static_cast<size_t>(a.layer) * a.R + (r >= 0 && r < a.R ? r : 0);
   int16_t* ks = a.key_slot + q * a.nkeys;
   int32_t* sk = a.slot_key + q * a.H;
   int32_t* tsq = a.ts + q * a.H;
   int16_t* ord = a.order + q * a.H;
   const int now = a.ctrl[2 * q];
-
   int o[EPH];
 #pragma unroll
   for (int e = 0; e < EPH; ++e) {
     const int k = tid * EPH + e;
     o[e] = k < a.H ? static_cast<int>(ord[k]) : -1;
   }
+  const int32_t* row = a.topk + static_cast<size_t>(b) * a.K;
+  int32_t raw[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int i = tid * EPT + e;
+    raw[e] = i < a.K ? row[i] : -1;
+  }
+  const uint32_t code = row_check<NT>(a, b, r, sl);
+  if (code) {
+    reject_row<NT>(a, b, a.K, code, true);
+    return;
+  }
+  int oldk[EPH];
+#pragma unroll
+  for (int e = 0; e < EPH; ++e) oldk[e] = o[e] >= 0 ? sk[o[e]] : kEmpty;
   for (int i = tid; i < npw; i += NT) pbits[i] = 0u;
   for (int i = tid; i < a.Hw; i += NT) used[i] = 0u;
   __syncthreads();
 
   // 1. tokens -> pages named by the row
-  const int32_t* row = a.topk + static_cast<size_t>(b) * a.K;
   int32_t tok[EPT];
   bool bad_index = false;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
-    const int i = tid * EPT + e;
-    const int32_t t = i < a.K ? row[i] : -1;
+    const int32_t t = raw[e];
     const bool valid = t >= 0 && t < sl;
     bad_index |= (!valid && t != -1);
     tok[e] = valid ? t : -1;
@@ -362,7 +378,7 @@ __global__ __launch_bounds__(NT) void lru_page_plan(PlanArgs a) {
 
   // 4. victims, commit, new order (pages are already in ascending order)
   lru_select_commit<NT, EPH>(a, b, r, now, m, o, used, miss_key, vslot, scan, ks, sk, tsq, ord,
-                             nullptr, nullptr);
+                             nullptr, nullptr, oldk);
   __syncthreads();
 
   // 5. outputs: page table, page count, token locations (page index, offset)
