@@ -333,3 +333,46 @@ def fill_host_kv(w: Workload, layer_arrays, threads: int = 16) -> None:
 
     with ThreadPoolExecutor(threads) as ex:
         list(ex.map(run, jobs))
+
+
+# -- inputs of the decode-attention consumer -----------------------------------
+
+MLA_LATENT, MLA_ROPE = 512, 64
+
+
+def _to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    b = x.astype(np.float32).view(np.uint32)
+    return ((b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1)))
+            >> np.uint32(16)).astype(np.uint16)
+
+
+def mla_kv_rows(rng: np.random.Generator, n: int, item_bytes: int) -> np.ndarray:
+    """``n`` MLA KV rows with N(0,1) latent and rope values, as stored bytes.
+
+    1152 B: 576 bfloat16.  656 B: 512 fp8 e4m3fn latent values quantised per
+    128-dim tile with scale = max|x| / 448 (float32), the 4 scales, then 64
+    bfloat16 rope values.
+    """
+    lat = rng.standard_normal((n, MLA_LATENT)).astype(np.float32)
+    rope = rng.standard_normal((n, MLA_ROPE)).astype(np.float32)
+    if item_bytes == 2 * (MLA_LATENT + MLA_ROPE):
+        return _to_bf16_bits(np.concatenate([lat, rope], 1)).view(np.uint8).reshape(n, -1)
+    if item_bytes == MLA_LATENT + 16 + 2 * MLA_ROPE:
+        import torch
+
+        tiles = lat.reshape(n, 4, 128)
+        scale = (np.abs(tiles).max(axis=2) / np.float32(448.0)).astype(np.float32)
+        scale = np.where(scale > 0, scale, np.float32(1.0))
+        q = torch.from_numpy(tiles / scale[:, :, None]).to(torch.float8_e4m3fn)
+        codes = q.view(torch.uint8).numpy().reshape(n, MLA_LATENT)
+        out = np.empty((n, item_bytes), np.uint8)
+        out[:, :MLA_LATENT] = codes
+        out[:, MLA_LATENT:MLA_LATENT + 16] = scale.view(np.uint8).reshape(n, 16)
+        out[:, MLA_LATENT + 16:] = _to_bf16_bits(rope).view(np.uint8).reshape(n, -1)
+        return out
+    raise ValueError(item_bytes)
+
+
+def mla_queries(rng: np.random.Generator, batch: int, heads: int) -> np.ndarray:
+    """bfloat16 bits [batch, heads, 576] of N(0,1) queries."""
+    return _to_bf16_bits(rng.standard_normal((batch, heads, MLA_LATENT + MLA_ROPE)))
