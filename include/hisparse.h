@@ -251,6 +251,42 @@ int hisparse_copy_planned(hisparse_state_t st, int32_t layer_id, int32_t batch,
                           void* stream);
 
 /*
+ * Sparse MLA decode attention over the rows a swap call returned ("SGLang
+ * HiSparse" blog, section 1: attention is exact over the selected positions;
+ * section 2.1: the sparse table goes straight to decode attention).  For
+ * batch row b and head h, over the valid entries i of locs[b]:
+ *   s_i = softmax_scale * (q[b][h][0:512] . c_i + q[b][h][512:576] . r_i)
+ *   out[b][h] = sum_i softmax(s)_i * c_i,   lse[b][h] = ln sum_i exp(s_i)
+ * where c_i (512-dim latent, also the value) and r_i (64-dim rope key) are
+ * decoded from the KV row of location i in layer `layer_id`'s hot buffer.
+ * Row formats by item_size_bytes: 1152 = 576 bf16; 656 = 512 fp8 e4m3fn
+ * latent, 4 fp32 scales (one per 128 latent dims), 64 bf16 rope.  Other
+ * item sizes: HISPARSE_E_UNSUPPORTED.
+ *
+ *   q           bf16 [batch][num_heads][576] (device).
+ *   locs        int32 [batch][n_locs]: token mode, device rows as returned in
+ *               out_locs; page mode, j*P + offset with page_table.  -1 entries
+ *               are skipped; an entry that resolves outside the buffer is
+ *               skipped and raises HISPARSE_ERR_BAD_INDEX.
+ *   page_table  page mode only: int32 [batch][H] as returned; NULL otherwise.
+ *   out         fp32 [batch][num_heads][512]; a row with no valid entry gets 0.
+ *   lse         fp32 [batch][num_heads] (natural log; -inf when empty), or NULL.
+ *   workspace   device scratch of at least
+ *               hisparse_sparse_mla_workspace_bytes(st, batch, num_heads,
+ *               n_locs) bytes (split partials), NULL when that is 0.
+ * Computes in bf16 MFMA with fp32 accumulation; the softmax weights are
+ * rounded to bf16 before the weighted sum.  Enqueued on `stream`; allocates
+ * nothing.  Errors: HISPARSE_E_INVAL, HISPARSE_E_UNSUPPORTED, HISPARSE_E_HIP.
+ */
+size_t hisparse_sparse_mla_workspace_bytes(hisparse_state_t st, int32_t batch, int32_t num_heads,
+                                           int32_t n_locs);
+int hisparse_sparse_mla_decode(hisparse_state_t st, int32_t layer_id, int32_t batch,
+                               int32_t num_heads, int32_t n_locs, const void* q,
+                               const int32_t* locs, const int32_t* page_table,
+                               float softmax_scale, float* out, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
  * Empties the caches of `n` requests in every layer (a newly admitted
  * request).  req_pool_indices: device int32 [n]; out-of-range entries set
  * ERR_BAD_ROW and are skipped.  Enqueued on `stream`.

@@ -74,6 +74,10 @@ _SIGNATURES = {
                                                        c_vp]),
     "hisparse_copy_planned": (ctypes.c_int, [c_vp, c_i32, c_i32, c_vp,
                                              ctypes.POINTER(HisparseMissPlan), c_vp]),
+    "hisparse_sparse_mla_workspace_bytes": (ctypes.c_size_t, [c_vp, c_i32, c_i32, c_i32]),
+    "hisparse_sparse_mla_decode": (ctypes.c_int, [c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp,
+                                                  c_vp, ctypes.c_float, c_vp, c_vp, c_vp,
+                                                  ctypes.c_size_t, c_vp]),
     "hisparse_request_reset": (ctypes.c_int, [c_vp, c_i32, c_vp, c_vp]),
     "hisparse_plan_capacity": (c_i32, [c_vp]),
     "hisparse_state_export": (ctypes.c_int, [c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
@@ -157,6 +161,18 @@ def hisparse_swap_in_spec_multistep(st, layer_id, batch, num_steps, req_pool_ind
 
 def hisparse_copy_planned(st, layer_id, batch, miss_count, plan, stream) -> int:
     return lib().hisparse_copy_planned(st, layer_id, batch, miss_count, plan, stream)
+
+
+def hisparse_sparse_mla_workspace_bytes(st, batch, num_heads, n_locs) -> int:
+    return lib().hisparse_sparse_mla_workspace_bytes(st, batch, num_heads, n_locs)
+
+
+def hisparse_sparse_mla_decode(st, layer_id, batch, num_heads, n_locs, q, locs, page_table,
+                               softmax_scale, out, lse, workspace, workspace_bytes,
+                               stream) -> int:
+    return lib().hisparse_sparse_mla_decode(st, layer_id, batch, num_heads, n_locs, q, locs,
+                                            page_table, softmax_scale, out, lse, workspace,
+                                            workspace_bytes, stream)
 
 
 def hisparse_request_reset(st, n, req_pool_indices, stream) -> int:
@@ -334,6 +350,27 @@ class HiSparseState:
         rc = hisparse_copy_planned(self.handle, layer_id, batch, _ptr(miss_count),
                                    self._plan(plan), _stream(stream))
         return _check(rc, "hisparse_copy_planned")
+
+    def sparse_mla_decode(self, layer_id, q, locs, out, lse=None, page_table=None,
+                          softmax_scale=None, workspace=None, stream=None):
+        """Decode attention of ``q`` (bf16 [B, heads, 576]) over ``locs``
+        (int32 [B, n]) into ``out`` (float32 [B, heads, 512]) and ``lse``."""
+        B, heads, dim = q.shape
+        n = int(locs.shape[1])
+        if q.dtype != torch.bfloat16 or dim != 576 or not q.is_contiguous():
+            raise ValueError("q must be a contiguous bfloat16 [B, heads, 576] tensor")
+        if out.dtype != torch.float32 or not out.is_contiguous():
+            raise ValueError("out must be a contiguous float32 tensor")
+        need = hisparse_sparse_mla_workspace_bytes(self.handle, B, heads, n)
+        if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        scale = softmax_scale if softmax_scale is not None else 576 ** -0.5
+        wptr = workspace.data_ptr() if (need and workspace is not None) else 0
+        rc = hisparse_sparse_mla_decode(
+            self.handle, layer_id, B, heads, n, q.data_ptr(), _ptr(locs), _ptr(page_table),
+            scale, out.data_ptr(), lse.data_ptr() if lse is not None else 0, wptr,
+            need, _stream(stream))
+        return _check(rc, "hisparse_sparse_mla_decode")
 
     def request_reset(self, req_pool_indices: torch.Tensor, stream=None):
         rc = hisparse_request_reset(self.handle, int(req_pool_indices.shape[0]),

@@ -275,9 +275,11 @@ int hisparse_state_create(const hisparse_config_t* cfg, void* stream, hisparse_s
   const bool lru = cfg->policy == HISPARSE_POLICY_LRU;
   int device = 0;
   if (hipGetDevice(&device) != hipSuccess) return HISPARSE_E_HIP;
-  int max_lds = 0;
+  int max_lds = 0, num_cus = 0;
   if (hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, device) !=
-      hipSuccess)
+          hipSuccess ||
+      hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, device) !=
+          hipSuccess)
     return HISPARSE_E_HIP;
 
   auto* st = new (std::nothrow) ProfiledState();
@@ -292,6 +294,7 @@ int hisparse_state_create(const hisparse_config_t* cfg, void* stream, hisparse_s
   st->hw = d.hw;
   st->cap = d.cap;
   st->max_lds = static_cast<size_t>(max_lds);
+  st->num_cus = num_cus;
   for (int l = 0; l < L; ++l) {
     hipPointerAttribute_t attr{};
     const void* hp = cfg->host_kv[l];
@@ -438,6 +441,50 @@ int hisparse_copy_planned(hisparse_state_t st, int32_t layer_id, int32_t batch,
   const CopyArgs c = copy_args(st, layer_id, batch, miss_count, plan->miss_src, plan->miss_dst,
                                plan->capacity);
   return status_of(launch_miss_copy(c, static_cast<hipStream_t>(stream)));
+}
+
+size_t hisparse_sparse_mla_workspace_bytes(hisparse_state_t st, int32_t batch, int32_t num_heads,
+                                           int32_t n_locs) {
+  if (st == nullptr || batch < 1 || num_heads < 1 || n_locs < 1) return 0;
+  return mla_workspace_bytes(batch, num_heads, n_locs, st->num_cus);
+}
+
+int hisparse_sparse_mla_decode(hisparse_state_t st, int32_t layer_id, int32_t batch,
+                               int32_t num_heads, int32_t n_locs, const void* q,
+                               const int32_t* locs, const int32_t* page_table,
+                               float softmax_scale, float* out, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (st == nullptr || layer_id < 0 || layer_id >= st->cfg.num_layers) return HISPARSE_E_INVAL;
+  if (batch < 0 || num_heads < 1 || num_heads > 1024 || n_locs < 1) return HISPARSE_E_INVAL;
+  if (batch == 0) return HISPARSE_OK;
+  if (q == nullptr || locs == nullptr || out == nullptr) return HISPARSE_E_INVAL;
+  const int I = st->cfg.item_size_bytes;
+  if (I != 1152 && I != 656) return HISPARSE_E_UNSUPPORTED;
+  const bool page = st->cfg.page_size > 1;
+  if (page != (page_table != nullptr)) return HISPARSE_E_INVAL;
+  if (workspace_bytes < mla_workspace_bytes(batch, num_heads, n_locs, st->num_cus) ||
+      (workspace_bytes > 0 && workspace == nullptr))
+    return HISPARSE_E_INVAL;
+  DeviceGuard g(st->device);
+  MlaDecodeCall c{};
+  c.q = q;
+  c.locs = locs;
+  c.page_table = page ? page_table : nullptr;
+  c.kv = st->dev_kv[layer_id];
+  c.kv_rows = static_cast<int64_t>(st->cfg.max_requests) * st->rows * st->cfg.page_size;
+  c.item_bytes = I;
+  c.page_size = st->cfg.page_size;
+  c.pt_stride = st->cfg.hot_buffer_size;
+  c.batch = batch;
+  c.heads = num_heads;
+  c.n_locs = n_locs;
+  c.num_cus = st->num_cus;
+  c.scale = softmax_scale;
+  c.out = out;
+  c.lse = lse;
+  c.workspace = workspace;
+  c.err = st->err;
+  return status_of(launch_mla_decode(c, static_cast<hipStream_t>(stream)));
 }
 
 int hisparse_request_reset(hisparse_state_t st, int32_t n, const int32_t* req_pool_indices,

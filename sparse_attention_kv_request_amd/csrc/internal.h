@@ -62,6 +62,25 @@ struct ResetArgs {
   int32_t R, H, Hw, nkeys;
 };
 
+// One sparse MLA decode-attention call (see hisparse_sparse_mla_decode).
+struct MlaDecodeCall {
+  const void* q;
+  const int32_t* locs;
+  const int32_t* page_table;
+  const uint8_t* kv;
+  int64_t kv_rows;
+  int32_t item_bytes, page_size, pt_stride;
+  int32_t batch, heads, n_locs, num_cus;
+  float scale;
+  float* out;
+  float* lse;
+  void* workspace;
+  uint32_t* err;
+};
+int mla_splits(int batch, int heads, int n_locs, int num_cus);
+size_t mla_workspace_bytes(int batch, int heads, int n_locs, int num_cus);
+hipError_t launch_mla_decode(const MlaDecodeCall& c, hipStream_t s);
+
 int hash_size_for(int entries);
 constexpr int kMaxSortedKeys = 1 << 18;  // keys per request with a sorted copy list
 size_t lru_token_lds_bytes(const PlanArgs& a);
@@ -101,6 +120,7 @@ struct hisparse_state {
   int32_t* cp_dst = nullptr;
   uint32_t* err = nullptr;
   size_t max_lds = 0;         // dynamic LDS a workgroup may use
+  int num_cus = 0;
   // profiling
   bool profiling = false;
   std::vector<hipEvent_t> ev_free;

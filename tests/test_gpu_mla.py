@@ -1,0 +1,135 @@
+"""Sparse MLA decode attention (HIP, through the C ABI) against the float64
+oracle, on rows that a swap call placed in the hot buffer.
+
+Tolerance, per (row, head), from the arithmetic of the kernel:
+* scores use bf16 q and bf16 keys (fp8 rows are dequantised and rounded to
+  bf16: |k^ - k| <= 2^-9 |k|) with fp32 accumulation, so
+  |s^_i - s_i| <= d = scale * (2^-9 [fp8 only] + 2^-20) * max_i sum_d |q_d k_id|;
+* each softmax weight is rounded to bf16 (relative 2^-9) and moves by at most
+  exp(2d) - 1 through the scores, so every normalised weight moves by a
+  relative e = 2 * (exp(2d) - 1 + 2^-9);
+* values are the same bf16 latents (fp8: rounded, relative 2^-9).
+Hence |out^ - out| <= max_i |c_i| * (e + 2^-9 [fp8]) and |lse^ - lse| <= d + 2^-8.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import sparse_mla_oracle as mla
+from sparse_attention_kv_request_amd import binding, workloads
+from tests.gpu_harness import DEV, log
+
+pytestmark = pytest.mark.gpu
+
+
+def tolerances(q_bits, locs_host, host_rows, scale, fp8):
+    B, H, _ = q_bits.shape
+    tol_out = np.zeros((B, H))
+    tol_lse = np.zeros((B, H))
+    for b in range(B):
+        rows = [int(x) for x in locs_host[b] if x >= 0]
+        if not rows:
+            continue
+        lat, rope = mla.decode_rows(host_rows[rows])
+        k = np.abs(np.concatenate([lat, rope], 1))
+        q = np.abs(mla.bf16_to_f64(q_bits[b]))
+        d = scale * ((2.0 ** -9 if fp8 else 0.0) + 2.0 ** -20) * (q @ k.T).max(axis=1)
+        e = 2 * (np.expm1(2 * d) + 2.0 ** -9)
+        vmax = np.abs(lat).max()
+        tol_out[b] = vmax * (e + (2.0 ** -9 if fp8 else 0.0)) + 1e-6
+        tol_lse[b] = d + 2.0 ** -8 + 1e-6
+    return tol_out, tol_lse
+
+
+def run_case(*, R, B, H, K, N, item, heads, P=1, seed=0, pad_row=None, calls=2):
+    rng = np.random.default_rng(seed)
+    host = binding.HostKV(R, N, item)
+    for r in range(R):
+        host.array[r] = workloads.mla_kv_rows(rng, N, item)
+    st = binding.HiSparseState(max_requests=R, num_layers=1, hot_buffer_size=H, top_k=K,
+                               item_size_bytes=item, max_seq_len=N, page_size=P,
+                               host_kv=[host])
+    scale = mla.default_scale()
+    worst = 0.0
+    try:
+        for call in range(calls):
+            req = rng.permutation(R)[:B].astype(np.int32)
+            span = N if P == 1 else min(N, H * P)             # page mode: fits the hot pages
+            topk = np.stack([rng.choice(span, K, replace=False) for _ in range(B)]).astype(np.int32)
+            topk[:, ::7] = -1                                 # padding entries
+            topk[:, 1] = topk[:, 2]                           # a duplicate entry
+            if pad_row is not None:
+                topk[pad_row] = -1
+            out_locs = torch.empty((B, K), dtype=torch.int32, device=DEV)
+            mc = torch.empty(B, dtype=torch.int32, device=DEV)
+            pt = nump = None
+            if P > 1:
+                pt = torch.empty((B, H), dtype=torch.int32, device=DEV)
+                nump = torch.empty(B, dtype=torch.int32, device=DEV)
+            t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+            st.swap_in_selected(0, t(req), t(np.full(B, N, np.int32)), t(topk), out_locs, mc,
+                                page_table=pt, num_pages=nump)
+            q_bits = workloads.mla_queries(rng, B, heads)
+            q = torch.from_numpy(q_bits.view(np.int16)).view(torch.bfloat16).to(DEV)
+            out = torch.full((B, heads, 512), float("nan"), dtype=torch.float32, device=DEV)
+            lse = torch.full((B, heads), float("nan"), dtype=torch.float32, device=DEV)
+            st.sparse_mla_decode(0, q, out_locs, out, lse, page_table=pt, softmax_scale=scale)
+            torch.cuda.synchronize()
+            assert st.error_flags() == 0
+            # the oracle reads the host tier by token: row r*N + t
+            locs_host = np.where(topk >= 0, req[:, None].astype(np.int64) * N + topk, -1)
+            host_rows = host.array.reshape(R * N, item)
+            ref_out, ref_lse = mla.sparse_mla_decode(q_bits, locs_host, host_rows, scale)
+            tol_out, tol_lse = tolerances(q_bits, locs_host, host_rows, scale, item == 656)
+            got_out = out.cpu().numpy().astype(np.float64)
+            got_lse = lse.cpu().numpy().astype(np.float64)
+            err = np.abs(got_out - ref_out).max(axis=2)
+            assert np.all(err <= tol_out), f"out error {err.max()} > {tol_out[err > tol_out].min()}"
+            both_inf = np.isneginf(got_lse) & np.isneginf(ref_lse)
+            lerr = np.where(both_inf, 0.0, np.abs(got_lse - ref_lse))
+            assert np.all(lerr <= tol_lse), f"lse error {lerr.max()}"
+            if pad_row is not None:
+                assert np.all(got_out[pad_row] == 0) and np.all(np.isneginf(got_lse[pad_row]))
+            live = tol_out > 0
+            worst = max(worst, float((err[live] / tol_out[live]).max()))
+        log(f"mla item={item} P={P} heads={heads} B={B} K={K}: worst error / bound = {worst:.3g}")
+    finally:
+        st.close()
+        host.free()
+
+
+@pytest.mark.parametrize("item", [1152, 656])
+def test_mla_token_rows_many_splits(item):
+    """Small batch: the location list is split over many workgroups and merged."""
+    run_case(R=3, B=2, H=2048, K=1000, N=4000, item=item, heads=128, seed=item, pad_row=1)
+
+
+@pytest.mark.parametrize("item", [1152, 656])
+def test_mla_token_rows_large_batch(item):
+    run_case(R=40, B=40, H=600, K=300, N=1500, item=item, heads=64, seed=item + 1, calls=1)
+
+
+def test_mla_ragged_heads_and_locations():
+    """Heads not a multiple of 16 and a location count not a multiple of 32."""
+    run_case(R=4, B=3, H=128, K=77, N=500, item=1152, heads=24, seed=5)
+
+
+@pytest.mark.parametrize("item", [1152, 656])
+def test_mla_page_mode(item):
+    run_case(R=3, B=3, H=40, K=200, N=16 * 64, item=item, heads=32, P=16, seed=item + 2)
+
+
+def test_mla_rejects_bad_arguments():
+    host = binding.HostKV(2, 64, 48)
+    st = binding.HiSparseState(max_requests=2, num_layers=1, hot_buffer_size=64, top_k=8,
+                               item_size_bytes=48, max_seq_len=64, host_kv=[host])
+    try:
+        q = torch.zeros((1, 16, 576), dtype=torch.bfloat16, device=DEV)
+        locs = torch.zeros((1, 8), dtype=torch.int32, device=DEV)
+        out = torch.zeros((1, 16, 512), dtype=torch.float32, device=DEV)
+        with pytest.raises(binding.HiSparseError) as e:
+            st.sparse_mla_decode(0, q, locs, out)              # 48-byte rows: no MLA layout
+        assert e.value.code == binding.HISPARSE_E_UNSUPPORTED
+    finally:
+        st.close()
+        host.free()
