@@ -48,6 +48,12 @@ def parse():
                     help="wall-clock budget of the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-link-probe", action="store_true")
+    ap.add_argument("--attention", action="store_true",
+                    help="time the sparse MLA decode attention over the swapped-in rows "
+                         "instead of the swap step")
+    ap.add_argument("--heads", type=int, default=128, help="attention heads (--attention)")
+    ap.add_argument("--item", type=int, default=0,
+                    help="KV row bytes for --attention (1152 bf16 or 656 fp8; default: workload's)")
     return ap.parse_args()
 
 
@@ -285,6 +291,79 @@ class Runner:
             h.free()
 
 
+BF16_MFMA_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+
+
+def attention_bench(args, torch, binding, workloads):
+    """Sparse MLA decode attention over the rows the swap step left in the hot
+    buffer: per row 2048 locations x `heads` heads; FLOPs 2 * (576 + 512)
+    per (row, head, location); bytes = KV rows + q + out + lse + locations."""
+    import numpy as np
+
+    W, K = args.warmup, args.steps
+    w = workloads.config(args.workload, steps=W + 1)
+    if args.item:
+        w = w.replace(item_bytes=args.item)
+    item = w.item_bytes
+    run = Runner(torch, binding, workloads, w)
+    for s in range(W + 1):
+        run.step(s)
+    torch.cuda.synchronize()
+    # valid MLA rows in the hot buffer: overwrite the random bytes with
+    # well-formed latent/rope rows (the attention reads only what was copied)
+    rng = np.random.default_rng(9)
+    for l in range(w.layers):
+        dev = run.st.dev_kv[l]
+        flat = dev.reshape(-1, item)
+        rows = torch.from_numpy(workloads.mla_kv_rows(rng, 4096, item)).to(dev.device)
+        idx = torch.arange(flat.shape[0], device=dev.device) % 4096
+        flat.copy_(rows[idx])
+    B, H = w.batch, args.heads
+    q = torch.from_numpy(workloads.mla_queries(rng, B, H).view(np.int16)).view(
+        torch.bfloat16).to(run.dev)
+    out = torch.empty((B, H, 512), dtype=torch.float32, device=run.dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=run.dev)
+    need = binding.hisparse_sparse_mla_workspace_bytes(run.st.handle, B, H, w.top_k)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=run.dev)
+    locs = [run.outs[l] for l in range(w.layers)]
+    for l in range(w.layers):
+        run.st.sparse_mla_decode(l, q, locs[l], out, lse, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        for l in range(w.layers):
+            run.st.sparse_mla_decode(l, q, locs[l], out, lse, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    calls = K * w.layers
+    per_call = e0.elapsed_time(e1) * 1e-3 / calls
+    valid = int(sum(int((x >= 0).sum()) for x in locs)) // w.layers
+    flops = 2.0 * (576 + 512) * H * valid
+    byts = valid * item + B * H * (576 * 2 + 512 * 4 + 4) + B * w.top_k * 4
+    splits = (need // (B * H * 514 * 4)) if need else 1
+    run.close()
+    tflops = flops / per_call / 1e12
+    gbps = byts / per_call / 1e9
+    return {
+        "metric": "sparse MLA decode attention over swapped-in rows, TFLOP/s",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(per_call * 1e3 * w.layers, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"decode attention, {B} rows x {H} heads x {w.top_k} locations, "
+                               f"{item}-B rows ({'fp8' if item == 656 else 'bf16'})",
+                   "batch": B, "heads": H, "locations": w.top_k, "item_size_bytes": item,
+                   "layers": w.layers, "splits": splits},
+        "roofline": {"bound": "mfma" if flops / byts > BF16_MFMA_TFLOPS / 8.0 else "hbm",
+                     "achieved_tflops": round(tflops, 2), "peak_tflops": BF16_MFMA_TFLOPS,
+                     "frac_mfma": round(tflops / BF16_MFMA_TFLOPS, 4),
+                     "achieved_GBps": round(gbps, 1), "peak_GBps": HBM_PEAK_GBPS,
+                     "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4),
+                     "us_per_call": round(per_call * 1e6, 2),
+                     "flops_per_call": flops, "bytes_per_call": byts},
+    }
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -299,6 +378,9 @@ def main():
     from sparse_attention_kv_request_amd import binding, workloads
 
     torch.cuda.set_device(0)
+    if args.attention:
+        print(json.dumps(attention_bench(args, torch, binding, workloads)), flush=True)
+        return
     W, K = args.warmup, args.steps
     over = {"steps": W + K}
     if args.workload == 3:

@@ -462,6 +462,9 @@ int hisparse_sparse_mla_decode(hisparse_state_t st, int32_t layer_id, int32_t ba
   if (I != 1152 && I != 656) return HISPARSE_E_UNSUPPORTED;
   const bool page = st->cfg.page_size > 1;
   if (page != (page_table != nullptr)) return HISPARSE_E_INVAL;
+  if (n_locs > mla_max_locations()) return HISPARSE_E_UNSUPPORTED;
+  const int64_t kv_rows = static_cast<int64_t>(st->cfg.max_requests) * st->rows * st->cfg.page_size;
+  if (kv_rows >= (int64_t{1} << 31)) return HISPARSE_E_UNSUPPORTED;
   if (workspace_bytes < mla_workspace_bytes(batch, num_heads, n_locs, st->num_cus) ||
       (workspace_bytes > 0 && workspace == nullptr))
     return HISPARSE_E_INVAL;
@@ -471,7 +474,7 @@ int hisparse_sparse_mla_decode(hisparse_state_t st, int32_t layer_id, int32_t ba
   c.locs = locs;
   c.page_table = page ? page_table : nullptr;
   c.kv = st->dev_kv[layer_id];
-  c.kv_rows = static_cast<int64_t>(st->cfg.max_requests) * st->rows * st->cfg.page_size;
+  c.kv_rows = kv_rows;
   c.item_bytes = I;
   c.page_size = st->cfg.page_size;
   c.pt_stride = st->cfg.hot_buffer_size;

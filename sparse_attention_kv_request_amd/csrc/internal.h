@@ -78,6 +78,7 @@ struct MlaDecodeCall {
   uint32_t* err;
 };
 int mla_splits(int batch, int heads, int n_locs, int num_cus);
+int mla_max_locations();
 size_t mla_workspace_bytes(int batch, int heads, int n_locs, int num_cus);
 hipError_t launch_mla_decode(const MlaDecodeCall& c, hipStream_t s);
 

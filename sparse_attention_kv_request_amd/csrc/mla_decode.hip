@@ -7,12 +7,14 @@
 //   s_i = scale * (q_h[:512].c_i + q_h[512:].r_i),  out_h = softmax(s) . c,
 //   lse_h = log sum exp(s).
 //
-// Work split: one workgroup = 4 waves = 64 heads of one batch row over one
+// Work split: one workgroup = 8 waves = 128 heads of one batch row over one
 // range of its locations (split-K over locations when the batch is small;
-// a second kernel merges the splits by their log-sum-exp).  Tiles of 32 rows
-// are gathered into LDS as bf16 (fp8 rows are dequantised on the way).  Each
+// a second kernel merges the splits by their log-sum-exp).  The rows of the
+// whole range are resolved once; tiles of 32 rows are gathered into LDS as
+// bf16 (fp8 rows dequantised on the way), the next tile's loads in flight in
+// registers while the current one is computed.  Each
 // wave owns 16 heads and computes with MFMA 16x16x32 bf16:
-//   S^T (tokens x heads) = K (tokens x 576) . Q^T   -- Q^T lives in registers
+//   S^T (tokens x heads) = K (tokens x 576) . Q^T   -- the wave's Q^T in registers
 //   O^T (dims x heads)  += V^T (dims x tokens) . P^T
 // With heads as the N dimension every lane's accumulators belong to one head,
 // so the online-softmax rescale is a per-lane scalar, and the C layout of S^T
@@ -35,12 +37,16 @@ constexpr int kLatent = 512;
 constexpr int kRope = 64;
 constexpr int kDim = kLatent + kRope;     // 576
 constexpr int kTile = 32;                 // rows per LDS tile
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * kWave;  // 256
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * kWave;  // 512
 constexpr int kHeadsPerGroup = 16 * kWaves;
-constexpr int kRowElems = kDim + 16;      // LDS row pitch in bf16 (1184 B)
+constexpr int kRowElems = kDim + 8;       // LDS row pitch in bf16: 292 dwords, so 16
+                                          // consecutive rows hit distinct bank groups
 constexpr int kKSteps = kDim / 32;        // 18
+constexpr int kVtPitch = kTile + 4;       // dim-major latent row: 18 dwords
+constexpr int kMaxPerSplit = 2048;        // locations one workgroup handles
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLazy = 8.f;              // log2 headroom of the lazy softmax rescale
 
 struct MlaArgs {
   const uint16_t* q;          // bf16 bits [B][Hq][576]
@@ -66,6 +72,11 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
+// Two floats rounded to bf16 (nearest even), low one in the low half.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return static_cast<uint32_t>(bf16_bits(lo)) | (static_cast<uint32_t>(bf16_bits(hi)) << 16);
+}
+
 // Token row of location `loc` of batch row b, or -1.
 __device__ __forceinline__ int64_t token_row(const MlaArgs& a, int b, int32_t loc) {
   if (loc < 0) return -1;
@@ -82,74 +93,107 @@ __device__ __forceinline__ int64_t token_row(const MlaArgs& a, int b, int32_t lo
   return row < a.kv_rows ? row : -1;
 }
 
-// Gathers rows [t0, t0 + kTile) of batch row b into the LDS tile as bf16.
-__device__ void load_tile(const MlaArgs& a, int b, int t0, int t_end, uint16_t* tile,
-                          int* tvalid) {
+// Per-thread register staging of one tile's rows: the loads for tile t+1
+// are issued before tile t is computed and written to LDS after it.  Thread
+// t stages the latent of tokens 2*(t/32) and +1 (bf16 rows: 16-dim chunk t%32
+// as two 16-byte words; fp8 rows: 16 codes plus their scale) and, for t < 256,
+// rope chunk t%8 of token t/8; it then writes one latent dim of its 2 tokens
+// as one 4-byte word of the dim-major copy.
+struct Staged {
+  u32x4 lat[4];      // bf16: [token x][half c] at 2x+c; fp8: codes of token x at x
+  u32x4 rope;
+  float scale[2];
+};
+
+__device__ __forceinline__ void fetch_tile(const MlaArgs& a, const int32_t* rows, int nrows,
+                                           int t0, Staged& st) {
   const int tid = threadIdx.x;
-  __shared__ int64_t s_row[kTile];
-  if (tid < kTile) {
-    const int t = t0 + tid;
-    int64_t row = -1;
-    if (t < t_end) {
-      row = token_row(a, b, a.locs[static_cast<size_t>(b) * a.n_locs + t]);
-      if (row < 0 && a.locs[static_cast<size_t>(b) * a.n_locs + t] >= 0)
-        raise_error(a.err, HISPARSE_ERR_BAD_INDEX);
-    }
-    s_row[tid] = row;
-    tvalid[tid] = row >= 0;
-  }
-  __syncthreads();
-  if (a.item_bytes == 2 * kDim) {
-    // bf16 rows: 72 chunks of 16 bytes each
-    for (int c = tid; c < kTile * 72; c += kThreads) {
-      const int r = c / 72, col = c - r * 72;
-      const int64_t row = s_row[r];
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row >= 0)
-        v = *reinterpret_cast<const u32x4*>(a.kv + row * a.item_bytes + col * 16);
-      *reinterpret_cast<u32x4*>(tile + r * kRowElems + col * 8) = v;
-    }
-  } else {
-    // fp8 rows: 32 latent chunks of 16 codes (dequantised with their tile's
-    // scale) and 8 rope chunks of 8 bf16
-    for (int c = tid; c < kTile * 40; c += kThreads) {
-      const int r = c / 40, col = c - r * 40;
-      const int64_t row = s_row[r];
-      const uint8_t* src = a.kv + row * a.item_bytes;
-      if (col < 32) {
-        u16x8 lo = {0, 0, 0, 0, 0, 0, 0, 0}, hi = lo;
-        if (row >= 0) {
-          const u32x4 codes = *reinterpret_cast<const u32x4*>(src + col * 16);
-          const float scale = *reinterpret_cast<const float*>(src + kLatent + (col >> 3) * 4);
+  const int tp = tid >> 5, cp = tid & 31;
+  const bool bf16 = a.item_bytes == 2 * kDim;
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const f32x2 x0 = __builtin_amdgcn_cvt_pk_f32_fp8(codes[w], false);
-            const f32x2 x1 = __builtin_amdgcn_cvt_pk_f32_fp8(codes[w], true);
-            const uint16_t e0 = bf16_bits(x0[0] * scale), e1 = bf16_bits(x0[1] * scale);
-            const uint16_t e2 = bf16_bits(x1[0] * scale), e3 = bf16_bits(x1[1] * scale);
-            if (w < 2) {
-              lo[4 * w] = e0; lo[4 * w + 1] = e1; lo[4 * w + 2] = e2; lo[4 * w + 3] = e3;
-            } else {
-              hi[4 * (w - 2)] = e0; hi[4 * (w - 2) + 1] = e1;
-              hi[4 * (w - 2) + 2] = e2; hi[4 * (w - 2) + 3] = e3;
-            }
-          }
-        }
-        *reinterpret_cast<u16x8*>(tile + r * kRowElems + col * 16) = lo;
-        *reinterpret_cast<u16x8*>(tile + r * kRowElems + col * 16 + 8) = hi;
-      } else {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (row >= 0)
-          v = *reinterpret_cast<const u32x4*>(src + kLatent + 16 + (col - 32) * 16);
-        *reinterpret_cast<u32x4*>(tile + r * kRowElems + kLatent + (col - 32) * 8) = v;
-      }
+  for (int x = 0; x < 2; ++x) {
+    const int t = t0 + 2 * tp + x;
+    const int row = t < nrows ? rows[t] : -1;
+    const uint8_t* src = a.kv + static_cast<int64_t>(row) * a.item_bytes;
+    if (bf16) {
+      st.lat[2 * x] = row >= 0 ? *reinterpret_cast<const u32x4*>(src + 32 * cp) : u32x4{0u, 0u, 0u, 0u};
+      st.lat[2 * x + 1] =
+          row >= 0 ? *reinterpret_cast<const u32x4*>(src + 32 * cp + 16) : u32x4{0u, 0u, 0u, 0u};
+    } else {
+      st.lat[x] = row >= 0 ? *reinterpret_cast<const u32x4*>(src + 16 * cp) : u32x4{0u, 0u, 0u, 0u};
+      st.scale[x] = row >= 0 ? *reinterpret_cast<const float*>(src + kLatent + (cp >> 3) * 4) : 0.f;
     }
   }
+  st.rope = u32x4{0u, 0u, 0u, 0u};
+  if (tid < kTile * 8) {
+    const int t = t0 + (tid >> 3);
+    const int row = t < nrows ? rows[t] : -1;
+    const int rope_off = bf16 ? 2 * kLatent : kLatent + 16;
+    if (row >= 0)
+      st.rope = *reinterpret_cast<const u32x4*>(a.kv + static_cast<int64_t>(row) * a.item_bytes +
+                                                rope_off + 16 * (tid & 7));
+  }
+}
+
+// Column of the 4-token group tg in row d of the dim-major latent copy: the
+// group index is XOR-swizzled by (d / 16) mod 8 so that the staging threads'
+// stores (rows 16 apart) spread over the banks; readers of one MFMA operand
+// all share one d / 16 and stay conflict-free.
+__device__ __forceinline__ int vt_col(int d, int tg) { return 4 * (tg ^ ((d >> 4) & 7)); }
+
+// fp8 rows: turn the staged codes of token x (16 latent dims) into packed
+// bf16 pairs in place, lat[2x] = dims 0..7, lat[2x+1] = dims 8..15, the
+// register format bf16 rows are staged in.
+__device__ __forceinline__ void dequant_fp8(Staged& st) {
+#pragma unroll
+  for (int x = 1; x >= 0; --x) {
+    const u32x4 codes = st.lat[x];
+    const float sc = st.scale[x];
+    u32x4 out[2];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const f32x2 x0 = __builtin_amdgcn_cvt_pk_f32_fp8(codes[w], false);
+      const f32x2 x1 = __builtin_amdgcn_cvt_pk_f32_fp8(codes[w], true);
+      out[w >> 1][2 * (w & 1)] = pack_bf16(x0[0] * sc, x0[1] * sc);
+      out[w >> 1][2 * (w & 1) + 1] = pack_bf16(x1[0] * sc, x1[1] * sc);
+    }
+    st.lat[2 * x] = out[0];
+    st.lat[2 * x + 1] = out[1];
+  }
+}
+
+// Writes the staged tile: token-major rows (all 576 dims) and the dim-major
+// latent copy vt[dim][token].  Each 4-byte vt word holds one dim of the
+// thread's 2 tokens, assembled with a byte permute of the packed registers.
+__device__ __forceinline__ void store_tile(const MlaArgs& a, Staged& st, uint16_t* tile,
+                                           uint16_t* vt) {
+  const int tid = threadIdx.x;
+  const int tp = tid >> 5, cp = tid & 31;
+  if (a.item_bytes != 2 * kDim) dequant_fp8(st);
+  const int d0 = 16 * cp;
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    uint16_t* dst = tile + (2 * tp + x) * kRowElems + d0;
+    *reinterpret_cast<u32x4*>(dst) = st.lat[2 * x];
+    *reinterpret_cast<u32x4*>(dst + 8) = st.lat[2 * x + 1];
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int c = e >> 3, w = (e & 7) >> 1;
+    // low halves (even dim) or high halves (odd dim) of the two tokens' words
+    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+    const uint32_t v = __builtin_amdgcn_perm(st.lat[2 + c][w], st.lat[c][w], sel);
+    const int d = d0 + e;
+    *reinterpret_cast<uint32_t*>(vt + d * kVtPitch + vt_col(d, tp >> 1) + 2 * (tp & 1)) = v;
+  }
+  if (tid < kTile * 8)
+    *reinterpret_cast<u32x4*>(tile + (tid >> 3) * kRowElems + kLatent + 8 * (tid & 7)) = st.rope;
 }
 
 __global__ __launch_bounds__(kThreads) void mla_decode(MlaArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[kTile * kRowElems];
-  __shared__ int tvalid[kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[kLatent * kVtPitch];
+  __shared__ int32_t rows[kMaxPerSplit];
 
   // XCD-aware mapping: the head groups of one (row, split) unit run on the
   // same XCD (workgroups are dealt to the 8 XCDs round robin) and share its
@@ -163,10 +207,19 @@ __global__ __launch_bounds__(kThreads) void mla_decode(MlaArgs a) {
   const int b = unit / a.splits;
   const int split = unit - b * a.splits;
   const int t_begin = split * a.per_split;
-  const int t_end = min(a.n_locs, t_begin + a.per_split);
+  const int nrows = max(0, min(a.n_locs, t_begin + a.per_split) - t_begin);
+  const int tid = threadIdx.x;
 
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  // rows of this split's locations (-1 = skipped)
+  for (int t = tid; t < nrows; t += kThreads) {
+    const int32_t loc = a.locs[static_cast<size_t>(b) * a.n_locs + t_begin + t];
+    const int64_t row = token_row(a, b, loc);
+    if (row < 0 && loc >= 0) raise_error(a.err, HISPARSE_ERR_BAD_INDEX);
+    rows[t] = static_cast<int32_t>(row);
+  }
+
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
   const int g = lane >> 4;       // lane group
   const int n = lane & 15;       // head within the wave / row within a 16-tile
   const int head = hg * kHeadsPerGroup + wave * 16 + n;
@@ -183,15 +236,20 @@ __global__ __launch_bounds__(kThreads) void mla_decode(MlaArgs a) {
       qreg[ks] = as_bf16x8(v);
     }
   }
+  __syncthreads();
+
   f32x4 acc[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY;  // running max of scaled scores, log2 units
-  float l_run = 0.f;        // running sum of exp2(score - m_run)
+  float l_run = 0.f;        // running sum of the (bf16-rounded) weights
 
-  for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
-    load_tile(a, b, t0, t_end, tile, tvalid);
+  Staged stage;
+  if (nrows > 0) fetch_tile(a, rows, nrows, 0, stage);
+  for (int t0 = 0; t0 < nrows; t0 += kTile) {
+    store_tile(a, stage, tile, vt);
     __syncthreads();
+    if (t0 + kTile < nrows) fetch_tile(a, rows, nrows, t0 + kTile, stage);
 
     // S^T for tokens [0,16) and [16,32) of the tile
     f32x4 s[2];
@@ -212,14 +270,20 @@ __global__ __launch_bounds__(kThreads) void mla_decode(MlaArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int tok = (i < 4 ? 0 : 16) + 4 * g + (i & 3);
-      const float v = tvalid[tok] ? s[i >> 2][i & 3] * a.scale_log2 : -INFINITY;
+      const bool valid = t0 + tok < nrows && rows[t0 + tok] >= 0;
+      const float v = valid ? s[i >> 2][i & 3] * a.scale_log2 : -INFINITY;
       sc[i] = v;
       tmax = fmaxf(tmax, v);
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+    // The weights are taken relative to a reference m_run that only moves
+    // when the maximum grows by more than kLazy (log2 units): weights stay
+    // below 2^kLazy, and the accumulators are rescaled only on those rare
+    // moves (the result is the same; only the common factor differs).
+    const bool move = tmax > m_run + kLazy;
+    const float m_new = move ? tmax : m_run;
+    const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
     float psum = 0.f;
     u16x8 pbits;
 #pragma unroll
@@ -231,36 +295,36 @@ __global__ __launch_bounds__(kThreads) void mla_decode(MlaArgs a) {
     }
     psum += __shfl_xor(psum, 16);
     psum += __shfl_xor(psum, 32);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    if (__any(move)) {   // some head of the wave moved its reference
+      l_run *= alpha;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) acc[i] *= alpha;
+      for (int i = 0; i < 32; ++i) acc[i] *= alpha;
+    }
+    l_run += psum;
+    m_run = m_new;
     const bf16x8 pop = __builtin_bit_cast(bf16x8, pbits);
 
-    // O^T += V^T . P^T; quad u covers dims 64u .. 64u+63, lane row n <-> dims
-    // 64u + 4n + j for the four sub-tiles j
+    // O^T += V^T . P^T.  Sub-tile (u, j) covers dims 64u + 16j + [0,16); its
+    // A operand row n is dim 64u + 16j + n and its k-slots are the lane's
+    // 8 tokens 4g..4g+3 and 16+4g..16+4g+3 (token groups g and 4+g), two
+    // 8-byte reads of vt.
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      u16x4 v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int tok = (i < 4 ? 0 : 16) + 4 * g + (i & 3);
-        v[i] = *reinterpret_cast<const u16x4*>(tile + tok * kRowElems + 64 * u + 4 * n);
-      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        u16x8 col;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) col[i] = v[i][j];
-        acc[4 * u + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, col), pop, acc[4 * u + j], 0, 0, 0);
+        const int d = 64 * u + 16 * j + n;
+        const uint16_t* vrow = vt + d * kVtPitch;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + vt_col(d, g));
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + vt_col(d, 4 + g));
+        const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
+        acc[4 * u + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w), pop,
+                                                                 acc[4 * u + j], 0, 0, 0);
       }
     }
     __syncthreads();
   }
 
-  if (!head_ok) return;
-  // lane holds head `head`, dims 64u + 16g + 4i + j  (sub-tile (u, j), C row 4g + i)
+  if (head >= a.heads) return;
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   float* dst;
   if (a.splits == 1) {
@@ -276,14 +340,12 @@ __global__ __launch_bounds__(kThreads) void mla_decode(MlaArgs a) {
       a.part_ml[2 * ps + 1] = l_run;
     }
   }
+  // sub-tile (u, j), C row 4g + i  <->  dim 64u + 16j + 4g + i
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f32x4 o = {acc[4 * u][i] * inv, acc[4 * u + 1][i] * inv, acc[4 * u + 2][i] * inv,
-                 acc[4 * u + 3][i] * inv};
-      *reinterpret_cast<f32x4*>(dst + 64 * u + 16 * g + 4 * i) = o;
-    }
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<f32x4*>(dst + 64 * u + 16 * j + 4 * g) = acc[4 * u + j] * inv;
   }
 }
 
@@ -316,15 +378,19 @@ __global__ __launch_bounds__(128) void mla_combine(MlaArgs a) {
 
 }  // namespace
 
-// Splits of the location list per batch row: enough workgroups to cover the
-// CUs twice, at least 128 locations per split.
+// Splits of the location list per batch row: about one workgroup per CU
+// (the kernel runs one workgroup per CU), at least one 32-row tile and at
+// most kMaxPerSplit locations per split.
 int mla_splits(int batch, int heads, int n_locs, int num_cus) {
   const int groups = (heads + kHeadsPerGroup - 1) / kHeadsPerGroup;
   const int units = batch * groups;
-  int splits = (2 * num_cus + units - 1) / units;
-  splits = min(splits, max(1, n_locs / 128));
-  return max(1, min(splits, 64));
+  int splits = (num_cus + units - 1) / units;
+  splits = min(splits, (n_locs + kTile - 1) / kTile);
+  splits = max(splits, (n_locs + kMaxPerSplit - 1) / kMaxPerSplit);
+  return max(1, splits);
 }
+
+int mla_max_locations() { return 64 * kMaxPerSplit; }
 
 size_t mla_workspace_bytes(int batch, int heads, int n_locs, int num_cus) {
   const int splits = mla_splits(batch, heads, n_locs, num_cus);
