@@ -7,19 +7,23 @@
 //   s_i = scale * (q_h[:512].c_i + q_h[512:].r_i),  out_h = softmax(s) . c,
 //   lse_h = log sum exp(s).
 //
-// Work split: one workgroup = 8 waves = 128 heads of one batch row over one
-// range of its locations (split-K over locations when the batch is small;
-// a second kernel merges the splits by their log-sum-exp).  The rows of the
-// whole range are resolved once; tiles of 32 rows are gathered into LDS as
-// bf16 (fp8 rows dequantised on the way), the next tile's loads in flight in
-// registers while the current one is computed.  Each
-// wave owns 16 heads and computes with MFMA 16x16x32 bf16:
-//   S^T (tokens x heads) = K (tokens x 576) . Q^T   -- the wave's Q^T in registers
-//   O^T (dims x heads)  += V^T (dims x tokens) . P^T
+// Work split: one workgroup = 4 waves (one per SIMD) = 128 heads of one batch
+// row over one range of its locations (split-K over locations when the batch
+// is small; a second kernel merges the splits by their log-sum-exp).  The
+// rows of the range are resolved once.  Tiles of 32 rows are gathered from
+// the hot buffer straight into LDS with 16-byte global->LDS loads (no VGPR
+// staging), double buffered so the next tile streams in while the current
+// one is computed; fp8 rows land in a raw buffer and are dequantised to bf16
+// by the whole workgroup.  Each wave owns 32 heads (two 16-head blocks) and
+// computes with MFMA 16x16x32 bf16:
+//   S^T (tokens x heads) = K (tokens x 576) . Q^T    -- Q^T held in VGPRs
+//   O^T (dims x heads)  += V^T (dims x tokens) . P^T -- O^T in AGPRs
+// One K operand read from LDS feeds both head blocks.  V^T operands come from
+// the same token-major tile through the transposing LDS read: a 16-lane group
+// that reads a 4-token x 16-dim block hands every lane the 4 tokens of one dim.
 // With heads as the N dimension every lane's accumulators belong to one head,
 // so the online-softmax rescale is a per-lane scalar, and the C layout of S^T
-// is directly the B operand of the P.V product (the 8 tokens a lane holds
-// are used as its 8 k-slots, and V^T is read with the same token order).
+// is directly the B operand of the P.V product.
 #include "internal.h"
 
 namespace hisparse {
@@ -27,26 +31,53 @@ namespace hisparse {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
 
 constexpr int kLatent = 512;
 constexpr int kRope = 64;
 constexpr int kDim = kLatent + kRope;     // 576
 constexpr int kTile = 32;                 // rows per LDS tile
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * kWave;  // 512
-constexpr int kHeadsPerGroup = 16 * kWaves;
-constexpr int kRowElems = kDim + 8;       // LDS row pitch in bf16: 292 dwords, so 16
-                                          // consecutive rows hit distinct bank groups
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;  // 256
+constexpr int kHeadsPerWave = 32;
+constexpr int kHeadsPerGroup = kHeadsPerWave * kWaves;
 constexpr int kKSteps = kDim / 32;        // 18
-constexpr int kVtPitch = kTile + 4;       // dim-major latent row: 18 dwords
+constexpr int kDimBlocks = kLatent / 16;  // 32
 constexpr int kMaxPerSplit = 2048;        // locations one workgroup handles
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kLazy = 8.f;              // log2 headroom of the lazy softmax rescale
+constexpr int kQkAhead = 2;               // k-steps of K operands read ahead
+constexpr int kPvAhead = 4;               // dim blocks of V operands read ahead
+constexpr int kSchedMfma = 0x008;         // scheduling-group masks: MFMA
+constexpr int kSchedDsRead = 0x100;       // LDS read
+constexpr float kRefSlack = 64.f;         // log2 headroom of the weights over their reference
+
+// bf16 tile: row pitch 584 elements = 1168 B = 73 16-byte slots (292 dwords:
+// 16 consecutive rows start in distinct 4-bank groups).  A global->LDS load
+// instruction fills 64 consecutive slots, so a tile takes 37 of them and its
+// buffer is rounded up to 37 KiB.
+constexpr int kPitch = kDim + 8;
+constexpr int kRowSlots = kPitch / 8;                                  // 73
+constexpr int kTileInstr = (kTile * kRowSlots + kWave - 1) / kWave;    // 37
+constexpr int kTileBytes = kTileInstr * kWave * 16;                    // 37888
+// raw fp8 tile: rows of 656 B = 41 slots back to back
+constexpr int kFp8Row = kLatent + 16 + 2 * kRope;                      // 656
+constexpr int kFp8Slots = kFp8Row / 16;                                // 41
+constexpr int kRawInstr = (kTile * kFp8Slots + kWave - 1) / kWave;     // 21
+constexpr int kRawBytes = kRawInstr * kWave * 16;                      // 21504
+// LDS: bf16 rows use two tile buffers; fp8 rows two raw buffers + one tile
+constexpr int kStageBytes = (2 * kTileBytes > kTileBytes + 2 * kRawBytes)
+                                ? 2 * kTileBytes : kTileBytes + 2 * kRawBytes;
+
+// Source of the loads of rows that are absent (padding, skipped locations,
+// the tail of the last tile): zeros, so that their zero weights meet zero
+// values rather than whatever the hot buffer holds.
+__device__ __attribute__((aligned(256))) uint8_t g_zero_row[2 * kDim];
 
 struct MlaArgs {
   const uint16_t* q;          // bf16 bits [B][Hq][576]
@@ -93,122 +124,126 @@ __device__ __forceinline__ int64_t token_row(const MlaArgs& a, int b, int32_t lo
   return row < a.kv_rows ? row : -1;
 }
 
-// Per-thread register staging of one tile's rows: the loads for tile t+1
-// are issued before tile t is computed and written to LDS after it.  Thread
-// t stages the latent of tokens 2*(t/32) and +1 (bf16 rows: 16-dim chunk t%32
-// as two 16-byte words; fp8 rows: 16 codes plus their scale) and, for t < 256,
-// rope chunk t%8 of token t/8; it then writes one latent dim of its 2 tokens
-// as one 4-byte word of the dim-major copy.
-struct Staged {
-  u32x4 lat[4];      // bf16: [token x][half c] at 2x+c; fp8: codes of token x at x
-  u32x4 rope;
-  float scale[2];
-};
-
-__device__ __forceinline__ void fetch_tile(const MlaArgs& a, const int32_t* rows, int nrows,
-                                           int t0, Staged& st) {
-  const int tid = threadIdx.x;
-  const int tp = tid >> 5, cp = tid & 31;
-  const bool bf16 = a.item_bytes == 2 * kDim;
+// Issues this wave's share of the global->LDS loads of tile rows
+// [t0, t0 + 32): instruction i fills slots 64i .. 64i + 63 of the buffer, lane
+// l slot 64i + l.  All row numbers are read from LDS before the first load is
+// issued (one wait, not one per instruction).  Returns the tile's valid-row
+// mask (bit t: row t0 + t exists and is present).
+template <int kSlots, int kInstr>
+__device__ __forceinline__ uint32_t load_tile(const MlaArgs& a, const int32_t* rows, int nrows,
+                                              int t0, uint8_t* buf, int wave, int lane) {
+  constexpr int row_bytes = kSlots == kFp8Slots ? kFp8Row : 2 * kDim;
+  constexpr int kPerWave = (kInstr + kWaves - 1) / kWaves;
+  // Opaque copy of the lane index: keeps the (tile-invariant) per-slot
+  // address math here instead of letting it be hoisted out of the tile loop
+  // into dozens of live registers.
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  int row[kPerWave];
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int t = t0 + 2 * tp + x;
-    const int row = t < nrows ? rows[t] : -1;
-    const uint8_t* src = a.kv + static_cast<int64_t>(row) * a.item_bytes;
-    if (bf16) {
-      st.lat[2 * x] = row >= 0 ? *reinterpret_cast<const u32x4*>(src + 32 * cp) : u32x4{0u, 0u, 0u, 0u};
-      st.lat[2 * x + 1] =
-          row >= 0 ? *reinterpret_cast<const u32x4*>(src + 32 * cp + 16) : u32x4{0u, 0u, 0u, 0u};
-    } else {
-      st.lat[x] = row >= 0 ? *reinterpret_cast<const u32x4*>(src + 16 * cp) : u32x4{0u, 0u, 0u, 0u};
-      st.scale[x] = row >= 0 ? *reinterpret_cast<const float*>(src + kLatent + (cp >> 3) * 4) : 0.f;
+  for (int k = 0; k < kPerWave; ++k) {
+    const int r = (kWave * (wave + kWaves * k) + ln) / kSlots;
+    row[k] = (r < kTile && t0 + r < nrows) ? rows[t0 + r] : -1;
+  }
+  const int own = t0 + (ln & (kTile - 1));
+  const bool present = ln < kTile && own < nrows && rows[min(own, nrows - 1)] >= 0;
+#pragma unroll
+  for (int k = 0; k < kPerWave; ++k) {
+    const int i = wave + kWaves * k;
+    if (i < kInstr) {
+      const int s = kWave * i + ln;
+      const int c = s - (s / kSlots) * kSlots;
+      // slots past a row's bytes (the bf16 pitch pad) read zeros
+      const int cc = min(c, row_bytes / 16 - 1);
+      const uint8_t* src = (row[k] >= 0 && 16 * c < row_bytes)
+                               ? a.kv + static_cast<int64_t>(row[k]) * row_bytes + 16 * c
+                               : g_zero_row + 16 * cc;
+      __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(buf + i * kWave * 16), 16, 0, 0);
     }
   }
-  st.rope = u32x4{0u, 0u, 0u, 0u};
-  if (tid < kTile * 8) {
-    const int t = t0 + (tid >> 3);
-    const int row = t < nrows ? rows[t] : -1;
-    const int rope_off = bf16 ? 2 * kLatent : kLatent + 16;
-    if (row >= 0)
-      st.rope = *reinterpret_cast<const u32x4*>(a.kv + static_cast<int64_t>(row) * a.item_bytes +
-                                                rope_off + 16 * (tid & 7));
-  }
+  return static_cast<uint32_t>(__ballot(present));
 }
 
-// Column of the 4-token group tg in row d of the dim-major latent copy: the
-// group index is XOR-swizzled by (d / 16) mod 8 so that the staging threads'
-// stores (rows 16 apart) spread over the banks; readers of one MFMA operand
-// all share one d / 16 and stay conflict-free.
-__device__ __forceinline__ int vt_col(int d, int tg) { return 4 * (tg ^ ((d >> 4) & 7)); }
-
-// fp8 rows: turn the staged codes of token x (16 latent dims) into packed
-// bf16 pairs in place, lat[2x] = dims 0..7, lat[2x+1] = dims 8..15, the
-// register format bf16 rows are staged in.
-__device__ __forceinline__ void dequant_fp8(Staged& st) {
+// fp8 rows: the raw tile (codes, 4 scales, bf16 rope per row) -> bf16 tile.
+// Job j = 8 latent codes of one row (2048 jobs) or one 16-byte rope chunk
+// (256 jobs); consecutive lanes take consecutive chunks of a row.
+__device__ __forceinline__ void dequant_tile(const uint8_t* raw, uint16_t* tile) {
+  const int tid = threadIdx.x;
+#pragma unroll 4
+  for (int k = 0; k < kTile * (kLatent / 8) / kThreads; ++k) {
+    const int j = tid + kThreads * k;
+    const int r = j >> 6, c = j & 63;
+    const uint8_t* src = raw + r * kFp8Row;
+    const u32x2 codes = *reinterpret_cast<const u32x2*>(src + 8 * c);
+    const float sc = *reinterpret_cast<const float*>(src + kLatent + 4 * (c >> 4));
+    u32x4 o;
 #pragma unroll
-  for (int x = 1; x >= 0; --x) {
-    const u32x4 codes = st.lat[x];
-    const float sc = st.scale[x];
-    u32x4 out[2];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < 2; ++w) {
       const f32x2 x0 = __builtin_amdgcn_cvt_pk_f32_fp8(codes[w], false);
       const f32x2 x1 = __builtin_amdgcn_cvt_pk_f32_fp8(codes[w], true);
-      out[w >> 1][2 * (w & 1)] = pack_bf16(x0[0] * sc, x0[1] * sc);
-      out[w >> 1][2 * (w & 1) + 1] = pack_bf16(x1[0] * sc, x1[1] * sc);
+      o[2 * w] = pack_bf16(x0[0] * sc, x0[1] * sc);
+      o[2 * w + 1] = pack_bf16(x1[0] * sc, x1[1] * sc);
     }
-    st.lat[2 * x] = out[0];
-    st.lat[2 * x + 1] = out[1];
+    *reinterpret_cast<u32x4*>(tile + r * kPitch + 8 * c) = o;
+  }
+  {
+    const int r = tid >> 3, c = tid & 7;
+    *reinterpret_cast<u32x4*>(tile + r * kPitch + kLatent + 8 * c) =
+        *reinterpret_cast<const u32x4*>(raw + r * kFp8Row + kLatent + 16 + 16 * c);
   }
 }
 
-// Writes the staged tile: token-major rows (all 576 dims) and the dim-major
-// latent copy vt[dim][token].  Each 4-byte vt word holds one dim of the
-// thread's 2 tokens, assembled with a byte permute of the packed registers.
-__device__ __forceinline__ void store_tile(const MlaArgs& a, Staged& st, uint16_t* tile,
-                                           uint16_t* vt) {
-  const int tid = threadIdx.x;
-  const int tp = tid >> 5, cp = tid & 31;
-  if (a.item_bytes != 2 * kDim) dequant_fp8(st);
-  const int d0 = 16 * cp;
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    uint16_t* dst = tile + (2 * tp + x) * kRowElems + d0;
-    *reinterpret_cast<u32x4*>(dst) = st.lat[2 * x];
-    *reinterpret_cast<u32x4*>(dst + 8) = st.lat[2 * x + 1];
-  }
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int c = e >> 3, w = (e & 7) >> 1;
-    // low halves (even dim) or high halves (odd dim) of the two tokens' words
-    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-    const uint32_t v = __builtin_amdgcn_perm(st.lat[2 + c][w], st.lat[c][w], sel);
-    const int d = d0 + e;
-    *reinterpret_cast<uint32_t*>(vt + d * kVtPitch + vt_col(d, tp >> 1) + 2 * (tp & 1)) = v;
-  }
-  if (tid < kTile * 8)
-    *reinterpret_cast<u32x4*>(tile + (tid >> 3) * kRowElems + kLatent + 8 * (tid & 7)) = st.rope;
+// Value of lane l ^ 32 / l ^ 16 (gfx950 row swaps: with both operands x,
+// permlane32_swap returns (x of lanes 0-31 twice, x of lanes 32-63 twice),
+// so lane l holds x[l] in one result and x[l ^ 32] in the other; permlane16
+// does the same for the 16-lane rows 0/1 and 2/3).
+__device__ __forceinline__ float xor32(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float xor16(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (threadIdx.x & 16) ? r[0] : r[1]);
 }
 
-__global__ __launch_bounds__(kThreads) void mla_decode(MlaArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kTile * kRowElems];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kLatent * kVtPitch];
+// K operand of k-step ks for tokens 16 st + [0, 16): base = tile row n, dim 8g.
+__device__ __forceinline__ bf16x8 k_operand(const uint16_t* base, int ks, int st) {
+  return as_bf16x8(*reinterpret_cast<const u32x4*>(base + st * 16 * kPitch + 32 * ks));
+}
+
+// V^T operand of dim block [d0, d0 + 16): two transposing reads at p (rows
+// 4g + n/4) and p + 16 rows, giving k-slots 0..3 and 4..7.
+__device__ __forceinline__ bf16x8 v_operand(const uint16_t* p) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(p));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(p + 16 * kPitch));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+}
+
+template <bool fp8>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_decode(MlaArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t stage[kStageBytes];
   __shared__ int32_t rows[kMaxPerSplit];
+  __shared__ int32_t restart_at[2];
 
   // XCD-aware mapping: the head groups of one (row, split) unit run on the
   // same XCD (workgroups are dealt to the 8 XCDs round robin) and share its
   // rows through that XCD's L2.
   const int id = blockIdx.x;
   const int xcd = id & 7;
-  const int k = id >> 3;
-  const int hg = k % a.groups;
-  const int unit = (k / a.groups) * 8 + xcd;
+  const int kx = id >> 3;
+  const int hg = kx % a.groups;
+  const int unit = (kx / a.groups) * 8 + xcd;
   if (unit >= a.units) return;
   const int b = unit / a.splits;
   const int split = unit - b * a.splits;
   const int t_begin = split * a.per_split;
   const int nrows = max(0, min(a.n_locs, t_begin + a.per_split) - t_begin);
   const int tid = threadIdx.x;
+  if (tid < 2) restart_at[tid] = -2;
 
   // rows of this split's locations (-1 = skipped)
   for (int t = tid; t < nrows; t += kThreads) {
@@ -221,131 +256,213 @@ __global__ __launch_bounds__(kThreads) void mla_decode(MlaArgs a) {
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int g = lane >> 4;       // lane group
-  const int n = lane & 15;       // head within the wave / row within a 16-tile
-  const int head = hg * kHeadsPerGroup + wave * 16 + n;
-  const bool head_ok = head < a.heads;
+  const int n = lane & 15;       // head within a block / row within a 16-row tile
 
-  // Q^T operand: lane holds q[head][32*ks + 8*g .. +8] for every k-step
-  bf16x8 qreg[kKSteps];
-  {
-    const uint16_t* qh = a.q + (static_cast<size_t>(b) * a.heads + (head_ok ? head : 0)) * kDim;
+  // Q^T operands: lane holds q[head][32*ks + 8*g .. +8] of its head in each
+  // of the wave's two 16-head blocks
+  bf16x8 qreg[2][kKSteps];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const int head = hg * kHeadsPerGroup + wave * kHeadsPerWave + hb * 16 + n;
+    const bool ok = head < a.heads;
+    const uint16_t* qh = a.q + (static_cast<size_t>(b) * a.heads + (ok ? head : 0)) * kDim;
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
       u32x4 v = *reinterpret_cast<const u32x4*>(qh + 32 * ks + 8 * g);
-      if (!head_ok) v = u32x4{0u, 0u, 0u, 0u};
-      qreg[ks] = as_bf16x8(v);
+      if (!ok) v = u32x4{0u, 0u, 0u, 0u};
+      qreg[hb][ks] = as_bf16x8(v);
     }
   }
-  __syncthreads();
+  __syncthreads();  // rows[] complete
 
-  f32x4 acc[32];
+  f32x4 acc[2][kDimBlocks];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;  // running max of scaled scores, log2 units
-  float l_run = 0.f;        // running sum of the (bf16-rounded) weights
-
-  Staged stage;
-  if (nrows > 0) fetch_tile(a, rows, nrows, 0, stage);
-  for (int t0 = 0; t0 < nrows; t0 += kTile) {
-    store_tile(a, stage, tile, vt);
-    __syncthreads();
-    if (t0 + kTile < nrows) fetch_tile(a, rows, nrows, t0 + kTile, stage);
-
-    // S^T for tokens [0,16) and [16,32) of the tile
-    f32x4 s[2];
+  for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      f32x4 c = {0.f, 0.f, 0.f, 0.f};
-      const uint16_t* krow = tile + (st * 16 + n) * kRowElems + 8 * g;
+    for (int i = 0; i < kDimBlocks; ++i) acc[hb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref[2] = {-INFINITY, -INFINITY};  // reference of the weights, log2 units
+  float l_run[2] = {0.f, 0.f};              // sum of the (bf16-rounded) weights
+
+  // buffers: bf16 rows -> tiles at stage + {0, kTileBytes};
+  //          fp8 rows  -> tile at stage, raw tiles at stage + kTileBytes + {0, kRawBytes}
+  auto issue = [&](int it, int buf) -> uint32_t {
+    const int t0 = it * kTile;
+    if constexpr (fp8)
+      return load_tile<kFp8Slots, kRawInstr>(a, rows, nrows, t0,
+                                             stage + kTileBytes + buf * kRawBytes, wave, lane);
+    else
+      return load_tile<kRowSlots, kTileInstr>(a, rows, nrows, t0, stage + buf * kTileBytes, wave,
+                                              lane);
+  };
+  const int ntiles = (nrows + kTile - 1) / kTile;
+  uint32_t valid_next = ntiles > 0 ? issue(0, 0) : 0u;  // valid rows of the tile in flight
+  // The weights are exp2(s - m_ref) with m_ref fixed per head at the first
+  // tile's maximum, so the accumulators are never rescaled (they sit in
+  // AGPRs, where a read-modify-write would cost more than the whole tile).
+  // Weights may exceed 1 by up to 2^kRefSlack; a tile whose maximum goes
+  // beyond that asks for a restart: it raises the wave's reference and
+  // posts the phase in restart_at[phase & 1].  After the next barrier every
+  // wave reads the request, fetches the first tile again instead of the next
+  // one and, one phase later, replays the range from the start with zeroed
+  // sums and accumulators (a write-only reset; the tile computed in between
+  // is discarded with the rest).
+  int it = 0;          // tile in buffer `cur`
+  bool fresh = false;  // this phase starts the sums over
+  for (int phase = 0; it < ntiles; ++phase) {
+    const int cur = phase & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // this phase's tile is in LDS; every wave is done with the last one
+    const bool replay = restart_at[cur ^ 1] == phase - 1;
+    const int next = replay ? 0 : it + 1;
+    const uint32_t valid = valid_next;  // bit t: row t of this tile is present
+    if (next < ntiles) valid_next = issue(next, cur ^ 1);
+    const int t0 = it * kTile;
+    const uint16_t* tile;
+    if constexpr (fp8) {
+      dequant_tile(stage + kTileBytes + cur * kRawBytes, reinterpret_cast<uint16_t*>(stage));
+      __syncthreads();
+      tile = reinterpret_cast<const uint16_t*>(stage);
+    } else {
+      tile = reinterpret_cast<const uint16_t*>(stage + cur * kTileBytes);
+    }
+    // S^T for tokens [0,16) and [16,32) of the tile, both head blocks
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 s[2][2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) s[hb][st] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Software pipeline: the K operands of k-step ks + kQkAhead are read
+    // while the MFMAs of k-step ks run (one wave per SIMD: nothing else hides
+    // the LDS latency), the interleave pinned by scheduling-group barriers.
+    {
+      const uint16_t* kbase = tile + n * kPitch + 8 * g;
+      bf16x8 kf[kQkAhead + 1][2];
+#pragma unroll
+      for (int j = 0; j < kQkAhead; ++j)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) kf[j][st] = k_operand(kbase, j, st);
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
-        const bf16x8 kv = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 32 * ks));
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qreg[ks], c, 0, 0, 0);
+        if (ks + kQkAhead < kKSteps) {
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+            kf[(ks + kQkAhead) % (kQkAhead + 1)][st] = k_operand(kbase, ks + kQkAhead, st);
+        }
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb)
+            s[hb][st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks % (kQkAhead + 1)][st],
+                                                                qreg[hb][ks], s[hb][st], 0, 0, 0);
       }
-      s[st] = c;
-    }
-    // online softmax for this lane's head; lane holds tokens 4g+i and 16+4g+i
-    float sc[8];
-    float tmax = -INFINITY;
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kQkAhead, 0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int tok = (i < 4 ? 0 : 16) + 4 * g + (i & 3);
-      const bool valid = t0 + tok < nrows && rows[t0 + tok] >= 0;
-      const float v = valid ? s[i >> 2][i & 3] * a.scale_log2 : -INFINITY;
-      sc[i] = v;
-      tmax = fmaxf(tmax, v);
+      for (int ks = 0; ks < kKSteps; ++ks) {
+        if (ks + kQkAhead < kKSteps) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    // The weights are taken relative to a reference m_run that only moves
-    // when the maximum grows by more than kLazy (log2 units): weights stay
-    // below 2^kLazy, and the accumulators are rescaled only on those rare
-    // moves (the result is the same; only the common factor differs).
-    const bool move = tmax > m_run + kLazy;
-    const float m_new = move ? tmax : m_run;
-    const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
-    float psum = 0.f;
-    u16x8 pbits;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p = m_new == -INFINITY ? 0.f : exp2f(sc[i] - m_new);
-      const uint16_t pb = bf16_bits(p);
-      pbits[i] = pb;
-      psum += __builtin_bit_cast(float, static_cast<uint32_t>(pb) << 16);
-    }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
-    if (__any(move)) {   // some head of the wave moved its reference
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) acc[i] *= alpha;
-    }
-    l_run += psum;
-    m_run = m_new;
-    const bf16x8 pop = __builtin_bit_cast(bf16x8, pbits);
 
-    // O^T += V^T . P^T.  Sub-tile (u, j) covers dims 64u + 16j + [0,16); its
-    // A operand row n is dim 64u + 16j + n and its k-slots are the lane's
-    // 8 tokens 4g..4g+3 and 16+4g..16+4g+3 (token groups g and 4+g), two
-    // 8-byte reads of vt.
+    // weights per head block; lane holds tokens 4g+i and 16+4g+i
+    bf16x8 pop[2];
+    bool restart = false;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int hb = 0; hb < 2; ++hb) {
+      float sc[8];
+      float tmax = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = 64 * u + 16 * j + n;
-        const uint16_t* vrow = vt + d * kVtPitch;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + vt_col(d, g));
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + vt_col(d, 4 + g));
-        const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
-        acc[4 * u + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w), pop,
-                                                                 acc[4 * u + j], 0, 0, 0);
+      for (int i = 0; i < 8; ++i) {
+        const int tok = (i < 4 ? 0 : 16) + 4 * g + (i & 3);
+        const float v = (valid >> tok) & 1u ? s[hb][i >> 2][i & 3] * a.scale_log2 : -INFINITY;
+        sc[i] = v;
+        tmax = fmaxf(tmax, v);
       }
+      tmax = fmaxf(tmax, xor16(tmax));
+      tmax = fmaxf(tmax, xor32(tmax));
+      const bool beyond = tmax > m_ref[hb] + kRefSlack;
+      restart |= beyond && m_ref[hb] != -INFINITY;
+      if (beyond) m_ref[hb] = tmax;
+      // no reference yet means no valid row yet: every sc is -inf, every p 0
+      const float mr = m_ref[hb] == -INFINITY ? 0.f : m_ref[hb];
+      float psum = 0.f;
+      u16x8 pbits;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float p = exp2f(sc[i] - mr);
+        const uint16_t pb = bf16_bits(p);
+        pbits[i] = pb;
+        psum += __builtin_bit_cast(float, static_cast<uint32_t>(pb) << 16);
+      }
+      psum += xor16(psum);
+      psum += xor32(psum);
+      l_run[hb] = fresh ? psum : l_run[hb] + psum;
+      pop[hb] = __builtin_bit_cast(bf16x8, pbits);
     }
-    __syncthreads();
+    if (__any(restart) && lane == 0) restart_at[cur] = phase;
+
+    // O^T += V^T . P^T.  Dim block db covers dims 16db + [0,16).  Its A
+    // operand (lane: dim 16db + n, k-slots = tokens 4g..4g+3 and
+    // 16+4g..16+4g+3, the token order of P^T) is two transposing reads: lane
+    // n of group g points at row 4g + n/4 (then 16 + 4g + n/4), dims
+    // 16db + 4(n%4) .. +3.
+    const uint16_t* vbase = tile + (4 * g + (n >> 2)) * kPitch + 4 * (n & 3);
+    __builtin_amdgcn_sched_barrier(0);
+    if (fresh) {  // replay: the sums start over
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int db = 0; db < kDimBlocks; ++db) acc[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    {
+      bf16x8 vf[kPvAhead + 1];
+#pragma unroll
+      for (int j = 0; j < kPvAhead; ++j) vf[j] = v_operand(vbase + 16 * j);
+#pragma unroll
+      for (int db = 0; db < kDimBlocks; ++db) {
+        if (db + kPvAhead < kDimBlocks)
+          vf[(db + kPvAhead) % (kPvAhead + 1)] = v_operand(vbase + 16 * (db + kPvAhead));
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+          acc[hb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db % (kPvAhead + 1)], pop[hb],
+                                                                acc[hb][db], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPvAhead, 0);
+#pragma unroll
+      for (int db = 0; db < kDimBlocks; ++db) {
+        if (db + kPvAhead < kDimBlocks) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    fresh = replay;
+    it = next;
   }
 
-  if (head >= a.heads) return;
-  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-  float* dst;
-  if (a.splits == 1) {
-    dst = a.out + (static_cast<size_t>(b) * a.heads + head) * kLatent;
-    if (a.lse != nullptr && g == 0)
-      a.lse[static_cast<size_t>(b) * a.heads + head] =
-          l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
-  } else {
-    const size_t ps = (static_cast<size_t>(b) * a.splits + split) * a.heads + head;
-    dst = a.part_out + ps * kLatent;
-    if (g == 0) {
-      a.part_ml[2 * ps] = m_run;
-      a.part_ml[2 * ps + 1] = l_run;
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const int head = hg * kHeadsPerGroup + wave * kHeadsPerWave + hb * 16 + n;
+    if (head >= a.heads) continue;
+    const float inv = l_run[hb] > 0.f ? 1.f / l_run[hb] : 0.f;
+    float* dst;
+    if (a.splits == 1) {
+      dst = a.out + (static_cast<size_t>(b) * a.heads + head) * kLatent;
+      if (a.lse != nullptr && g == 0)
+        a.lse[static_cast<size_t>(b) * a.heads + head] =
+            l_run[hb] > 0.f ? (m_ref[hb] + log2f(l_run[hb])) * kLn2 : -INFINITY;
+    } else {
+      const size_t ps = (static_cast<size_t>(b) * a.splits + split) * a.heads + head;
+      dst = a.part_out + ps * kLatent;
+      if (g == 0) {
+        a.part_ml[2 * ps] = m_ref[hb];
+        a.part_ml[2 * ps + 1] = l_run[hb];
+      }
     }
-  }
-  // sub-tile (u, j), C row 4g + i  <->  dim 64u + 16j + 4g + i
+    // dim block db, C row 4g + i  <->  dim 16db + 4g + i
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<f32x4*>(dst + 64 * u + 16 * j + 4 * g) = acc[4 * u + j] * inv;
+    for (int db = 0; db < kDimBlocks; ++db)
+      *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * g) = acc[hb][db] * inv;
   }
 }
 
@@ -424,7 +541,10 @@ hipError_t launch_mla_decode(const MlaDecodeCall& c, hipStream_t s) {
     a.part_ml = a.part_out + static_cast<size_t>(c.batch) * a.splits * c.heads * kLatent;
   }
   const int padded_units = (a.units + 7) / 8 * 8;
-  hipLaunchKernelGGL(mla_decode, dim3(padded_units * a.groups), dim3(kThreads), 0, s, a);
+  if (c.item_bytes == 2 * kDim)
+    hipLaunchKernelGGL(mla_decode<false>, dim3(padded_units * a.groups), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(mla_decode<true>, dim3(padded_units * a.groups), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   hipLaunchKernelGGL(mla_combine, dim3(c.batch * c.heads), dim3(128), 0, s, a);

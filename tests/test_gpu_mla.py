@@ -41,7 +41,21 @@ def tolerances(q_bits, locs_host, host_rows, scale, fp8):
     return tol_out, tol_lse
 
 
-def run_case(*, R, B, H, K, N, item, heads, P=1, seed=0, pad_row=None, calls=2):
+def boost_rows(host, item, req_row, tokens, factor):
+    """Multiplies the latent of the given host rows by `factor` (bf16 rows:
+    re-rounded to bf16; fp8 rows: through their four scales, exactly)."""
+    rows = host.array[req_row]
+    for t in tokens:
+        if item == mla.BF16_ROW:
+            v = rows[t].view(np.uint16)[:mla.LATENT].astype(np.uint32) << 16
+            f = v.view(np.float32) * np.float32(factor)
+            rows[t].view(np.uint16)[:mla.LATENT] = (f.view(np.uint32) >> 16).astype(np.uint16)
+        else:
+            sc = rows[t, mla.LATENT:mla.LATENT + 16].view(np.float32)
+            sc *= np.float32(factor)
+
+
+def run_case(*, R, B, H, K, N, item, heads, P=1, seed=0, pad_row=None, calls=2, boost=None):
     rng = np.random.default_rng(seed)
     host = binding.HostKV(R, N, item)
     for r in range(R):
@@ -60,6 +74,8 @@ def run_case(*, R, B, H, K, N, item, heads, P=1, seed=0, pad_row=None, calls=2):
             topk[:, 1] = topk[:, 2]                           # a duplicate entry
             if pad_row is not None:
                 topk[pad_row] = -1
+            for b, pos, factor in boost or ():
+                boost_rows(host, item, req[b], [topk[b, pos]], factor)
             out_locs = torch.empty((B, K), dtype=torch.int32, device=DEV)
             mc = torch.empty(B, dtype=torch.int32, device=DEV)
             pt = nump = None
@@ -90,6 +106,18 @@ def run_case(*, R, B, H, K, N, item, heads, P=1, seed=0, pad_row=None, calls=2):
             assert np.all(lerr <= tol_lse), f"lse error {lerr.max()}"
             if pad_row is not None:
                 assert np.all(got_out[pad_row] == 0) and np.all(np.isneginf(got_lse[pad_row]))
+            for b, pos, factor in boost or ():
+                # the boosted row's score exceeds every unboosted score of its
+                # batch row (so the first tile of its split) by far more than
+                # the weights' 2^64 headroom, for some head
+                keep = locs_host[b] >= 0
+                lat, rope = mla.decode_rows(host_rows[locs_host[b][keep]])
+                qd = mla.bf16_to_f64(q_bits[b])
+                sc = scale * (qd[:, :512] @ lat.T + qd[:, 512:] @ rope.T) / np.log(2)
+                boosted = {int(np.count_nonzero(keep[:pp])) for bb, pp, _ in boost if bb == b}
+                plain = [i for i in range(sc.shape[1]) if i not in boosted]
+                i_big = int(np.count_nonzero(keep[:pos]))
+                assert (sc[:, i_big] - sc[:, plain].max(axis=1)).max() > 64
             live = tol_out > 0
             worst = max(worst, float((err[live] / tol_out[live]).max()))
         log(f"mla item={item} P={P} heads={heads} B={B} K={K}: worst error / bound = {worst:.3g}")
@@ -117,6 +145,14 @@ def test_mla_ragged_heads_and_locations():
 @pytest.mark.parametrize("item", [1152, 656])
 def test_mla_page_mode(item):
     run_case(R=3, B=3, H=40, K=200, N=16 * 64, item=item, heads=32, P=16, seed=item + 2)
+
+
+@pytest.mark.parametrize("item", [1152, 656])
+def test_mla_replay_after_large_score_jump(item):
+    """Rows far above the first tile's scores (latent x2000, then x5000) in
+    later tiles of a split: the split restarts with a raised reference."""
+    run_case(R=64, B=64, H=400, K=300, N=1200, item=item, heads=128, seed=item + 3, calls=1,
+             boost=[(0, 50, 2000.0), (0, 80, 5000.0), (7, 230, 3000.0)])
 
 
 def test_mla_rejects_bad_arguments():
