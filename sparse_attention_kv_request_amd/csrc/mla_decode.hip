@@ -186,7 +186,7 @@ __device__ __forceinline__ void dequant_tile(const uint8_t* raw, uint16_t* tile)
     }
     *reinterpret_cast<u32x4*>(tile + r * kPitch + 8 * c) = o;
   }
-  {
+  if (tid < kTile * 8) {
     const int r = tid >> 3, c = tid & 7;
     *reinterpret_cast<u32x4*>(tile + r * kPitch + kLatent + 8 * c) =
         *reinterpret_cast<const u32x4*>(raw + r * kFp8Row + kLatent + 16 + 16 * c);
