@@ -52,6 +52,9 @@ def parse():
                     help="time the sparse MLA decode attention over the swapped-in rows "
                          "instead of the swap step")
     ap.add_argument("--heads", type=int, default=128, help="attention heads (--attention)")
+    ap.add_argument("--topk", action="store_true",
+                    help="time the fused top-k selection + paged index table on the "
+                         "batch/sequence shape of --workload (2: 64 x 32768, 4: 128 x 131072)")
     ap.add_argument("--item", type=int, default=0,
                     help="KV row bytes for --attention (1152 bf16 or 656 fp8; default: workload's)")
     return ap.parse_args()
@@ -364,6 +367,68 @@ def attention_bench(args, torch, binding, workloads):
     }
 
 
+def topk_bench(args, torch, binding, workloads):
+    """Fused top-k selection + PAGED index table over synthetic indexer scores:
+    one plan per step, one build per layer (8 layers, different scores each).
+    Bytes per call = scores read + indices and locations written + the page
+    table entries of the selected positions."""
+    import time
+
+    import numpy as np
+
+    W, K = args.warmup, args.steps
+    w = workloads.config(args.workload)
+    B, N, k, P, L = w.batch, w.seq_len, w.top_k, 64, 8
+    rng = np.random.default_rng(17)
+    lens = np.full(B, N, np.int32)
+    dev = torch.device("cuda", 0)
+    logits = [torch.from_numpy(workloads.indexer_logits(rng, B, N)).to(dev) for _ in range(L)]
+    pt = torch.from_numpy(rng.permutation(B * (N // P)).astype(np.int32).reshape(B, N // P)).to(dev)
+    sl = torch.from_numpy(lens).to(dev)
+    bld = binding.TopkIndexBuilder(B, N, k, device=dev)
+    idx = torch.empty((B, k), dtype=torch.int32, device=dev)
+    locs = torch.empty((B, k), dtype=torch.int32, device=dev)
+    bld.plan(sl)
+    for _ in range(W):
+        for l in range(L):
+            bld.build(logits[l], sl, idx, locs, mode="paged", page_table=pt, page_size=P)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        bld.plan(sl)
+        for l in range(L):
+            bld.build(logits[l], sl, idx, locs, mode="paged", page_table=pt, page_size=P)
+    e1.record()
+    torch.cuda.synchronize()
+    per_call = e0.elapsed_time(e1) * 1e-3 / (K * L)
+    assert bld.error_flags() == 0
+    byts = int(lens.sum()) * 4 + B * k * 12
+    res = {
+        "metric": "fused top-k selection + paged index table, rows/s",
+        "value": round(B / per_call, 1), "unit": "rows/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(per_call * 1e3 * L, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"top-{k} of {B} rows x {N} indexer scores, paged table P={P}",
+                   "batch": B, "seq_len": N, "top_k": k, "layers": L, "page_size": P},
+        "roofline": {"bound": "hbm", "achieved": round(byts / per_call / 1e9, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(byts / per_call / 1e9 / HBM_PEAK_GBPS, 4),
+                     "us_per_call": round(per_call * 1e6, 2), "bytes_per_call": byts},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import topk_oracle
+        host = logits[0].cpu().numpy()
+        t0, rows = time.perf_counter(), 0
+        while rows < B and time.perf_counter() - t0 < args.cpu_seconds:
+            topk_oracle.topk_row(host[rows], N, k)
+            rows += 1
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(rows / dt, 2), "unit": "rows/s", "cores": 1,
+                               "kind": "oracle", "sample": f"{rows} rows of {N} scores, k={k}"}
+    return res
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -380,6 +445,9 @@ def main():
     torch.cuda.set_device(0)
     if args.attention:
         print(json.dumps(attention_bench(args, torch, binding, workloads)), flush=True)
+        return
+    if args.topk:
+        print(json.dumps(topk_bench(args, torch, binding, workloads)), flush=True)
         return
     W, K = args.warmup, args.steps
     over = {"steps": W + K}

@@ -287,6 +287,88 @@ int hisparse_sparse_mla_decode(hisparse_state_t st, int32_t layer_id, int32_t ba
                                size_t workspace_bytes, void* stream);
 
 /*
+ * ---- Top-k selection fused with the index-table build ----
+ * ("SGLang HiSparse" blog, section 2.2: a plan computed once per decode step
+ * from the sequence lengths alone, then one kernel per layer that selects
+ * the top-k positions from the indexer scores and builds the index table in
+ * the same pass; section 2.3: PAGED and RAGGED index tables.)
+ *
+ * Selection: for row b, the min(k, seq_lens[b]) positions of
+ * [0, seq_lens[b]) with the largest logits; equal logits go to the lower
+ * position; NaN ranks below every number.  `indices[b]` lists them in
+ * ascending position order, then -1 up to k: the top-k input of
+ * hisparse_swap_in_selected.  A row with seq_lens[b] < 0 or > max_len gets
+ * all -1 and raises HISPARSE_ERR_BAD_ROW.
+ * Index table (`locs`, same shape and order):
+ *   HISPARSE_INDEX_PAGED   locs = page_table[b][p / page_size] * page_size
+ *                          + p % page_size; a position whose page entry is
+ *                          negative or at or beyond pt_stride gets -1 and
+ *                          raises HISPARSE_ERR_BAD_INDEX;
+ *   HISPARSE_INDEX_RAGGED  locs = row_offsets[b] + p;
+ *   HISPARSE_INDEX_NONE    locs unused (may be NULL).
+ * -1 entries of `indices` give -1 in `locs`.
+ */
+#define HISPARSE_INDEX_NONE 0
+#define HISPARSE_INDEX_PAGED 1
+#define HISPARSE_INDEX_RAGGED 2
+#define HISPARSE_TOPK_CHUNK 32768     /* positions per workgroup; longer rows are split */
+#define HISPARSE_TOPK_MAX_CHUNKS 32   /* max_len <= 32 * 32768 */
+
+typedef struct hisparse_topk_call {
+  int32_t batch;               /* rows, >= 1 */
+  int32_t max_len;             /* logits row length (stride), 1 .. 2^20 */
+  int32_t k;                   /* >= 1; ceil(max_len / 32768) * k <= 32768 */
+  const float* logits;         /* device fp32 [batch][max_len], caller-owned */
+  const int32_t* seq_lens;     /* device int32 [batch] */
+  int32_t* plan;               /* device plan from hisparse_topk_plan for the same
+                                  batch, max_len and seq_lens; its per-row ticket
+                                  words are used and left at 0, so calls sharing a
+                                  plan must be ordered on one stream */
+  size_t plan_ints;            /* size of `plan` in int32 */
+  int32_t mode;                /* HISPARSE_INDEX_* */
+  const int32_t* page_table;   /* PAGED: device int32 [batch][pt_stride] */
+  int32_t pt_stride;           /* PAGED: >= 1 */
+  int32_t page_size;           /* PAGED: >= 1 */
+  const int32_t* row_offsets;  /* RAGGED: device int32 [batch] */
+  int32_t* indices;            /* device int32 [batch][k], written */
+  int32_t* locs;               /* device int32 [batch][k], written (PAGED/RAGGED) */
+  void* workspace;             /* device scratch of hisparse_topk_workspace_bytes
+                                  (NULL when that is 0) */
+  size_t workspace_bytes;
+  uint32_t* error_word;        /* device uint32; HISPARSE_ERR_* bits are OR-ed in */
+} hisparse_topk_call_t;
+
+/*
+ * Plan of the work split: int32 words needed for `batch` rows of length up
+ * to max_len, and the plan itself (device seq_lens in, device plan out:
+ * n_items, max_len, per row (first item, n_chunks), per item (row, chunk,
+ * start, length), per row a ticket word set to 0).  A row of s positions is
+ * split into n = max(1, ceil(s / 32768)) chunks of 1024 * ceil(ceil(s / n) /
+ * 1024) positions (the last shorter); rows outside [0, max_len] get one empty
+ * chunk.  The plan depends on seq_lens only: one plan serves every layer of a
+ * decode step.  Enqueued on `stream`; allocates nothing.
+ * Errors: HISPARSE_E_INVAL (bad sizes, NULL pointers, plan_ints too small),
+ * HISPARSE_E_UNSUPPORTED (max_len above 2^20), HISPARSE_E_HIP.
+ */
+size_t hisparse_topk_plan_ints(int32_t batch, int32_t max_len);
+int hisparse_topk_plan(int32_t batch, int32_t max_len, const int32_t* seq_lens, int32_t* plan,
+                       size_t plan_ints, void* stream);
+/*
+ * Scratch bytes for hisparse_topk_index_build: 0 when no row can be split
+ * (max_len <= 32768), else 8 * k + 4 bytes per plan item for the chunks'
+ * candidates.
+ */
+size_t hisparse_topk_workspace_bytes(int32_t batch, int32_t max_len, int32_t k);
+/*
+ * One layer's selection and index table (see above) in one kernel launch on
+ * `stream`; reads each logit once.  Allocates nothing.
+ * Errors: HISPARSE_E_INVAL (NULL pointers, bad sizes or mode, plan or
+ * workspace too small), HISPARSE_E_UNSUPPORTED (k or max_len beyond the
+ * limits above), HISPARSE_E_HIP.
+ */
+int hisparse_topk_index_build(const hisparse_topk_call_t* call, void* stream);
+
+/*
  * Empties the caches of `n` requests in every layer (a newly admitted
  * request).  req_pool_indices: device int32 [n]; out-of-range entries set
  * ERR_BAD_ROW and are skipped.  Enqueued on `stream`.

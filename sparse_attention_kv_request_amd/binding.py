@@ -55,6 +55,20 @@ class HisparseMissPlan(ctypes.Structure):
     _fields_ = [("miss_src", c_vp), ("miss_dst", c_vp), ("victim", c_vp), ("capacity", c_i32)]
 
 
+class HisparseTopkCall(ctypes.Structure):
+    _fields_ = [
+        ("batch", c_i32), ("max_len", c_i32), ("k", c_i32), ("logits", c_vp),
+        ("seq_lens", c_vp), ("plan", c_vp), ("plan_ints", ctypes.c_size_t), ("mode", c_i32),
+        ("page_table", c_vp), ("pt_stride", c_i32), ("page_size", c_i32),
+        ("row_offsets", c_vp), ("indices", c_vp), ("locs", c_vp), ("workspace", c_vp),
+        ("workspace_bytes", ctypes.c_size_t), ("error_word", c_vp),
+    ]
+
+
+INDEX_MODE = {"none": 0, "paged": 1, "ragged": 2}
+TOPK_CHUNK = 32768
+
+
 class HisparseProfile(ctypes.Structure):
     _fields_ = [("calls", ctypes.c_int64), ("plan_ms", ctypes.c_double),
                 ("copy_ms", ctypes.c_double)]
@@ -78,6 +92,10 @@ _SIGNATURES = {
     "hisparse_sparse_mla_decode": (ctypes.c_int, [c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp,
                                                   c_vp, ctypes.c_float, c_vp, c_vp, c_vp,
                                                   ctypes.c_size_t, c_vp]),
+    "hisparse_topk_plan_ints": (ctypes.c_size_t, [c_i32, c_i32]),
+    "hisparse_topk_plan": (ctypes.c_int, [c_i32, c_i32, c_vp, c_vp, ctypes.c_size_t, c_vp]),
+    "hisparse_topk_workspace_bytes": (ctypes.c_size_t, [c_i32, c_i32, c_i32]),
+    "hisparse_topk_index_build": (ctypes.c_int, [ctypes.POINTER(HisparseTopkCall), c_vp]),
     "hisparse_request_reset": (ctypes.c_int, [c_vp, c_i32, c_vp, c_vp]),
     "hisparse_plan_capacity": (c_i32, [c_vp]),
     "hisparse_state_export": (ctypes.c_int, [c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
@@ -173,6 +191,22 @@ def hisparse_sparse_mla_decode(st, layer_id, batch, num_heads, n_locs, q, locs, 
     return lib().hisparse_sparse_mla_decode(st, layer_id, batch, num_heads, n_locs, q, locs,
                                             page_table, softmax_scale, out, lse, workspace,
                                             workspace_bytes, stream)
+
+
+def hisparse_topk_plan_ints(batch, max_len) -> int:
+    return lib().hisparse_topk_plan_ints(batch, max_len)
+
+
+def hisparse_topk_plan(batch, max_len, seq_lens, plan, plan_ints, stream) -> int:
+    return lib().hisparse_topk_plan(batch, max_len, seq_lens, plan, plan_ints, stream)
+
+
+def hisparse_topk_workspace_bytes(batch, max_len, k) -> int:
+    return lib().hisparse_topk_workspace_bytes(batch, max_len, k)
+
+
+def hisparse_topk_index_build(call: HisparseTopkCall, stream) -> int:
+    return lib().hisparse_topk_index_build(ctypes.byref(call), stream)
 
 
 def hisparse_request_reset(st, n, req_pool_indices, stream) -> int:
@@ -407,3 +441,56 @@ class HiSparseState:
 
     def profile_read(self) -> dict:
         return hisparse_profile_read(self.handle)
+
+
+class TopkIndexBuilder:
+    """Top-k selection + index-table build for `batch` rows of up to
+    `max_len` scores (torch tensors on one device).  Holds the plan of the
+    current sequence lengths, the candidate workspace and an error word;
+    :meth:`plan` once per step, :meth:`build` once per layer."""
+
+    def __init__(self, batch: int, max_len: int, k: int, device="cuda"):
+        self.batch, self.max_len, self.k = batch, max_len, k
+        ints = hisparse_topk_plan_ints(batch, max_len)
+        if ints == 0:
+            raise HiSparseError(HISPARSE_E_UNSUPPORTED, "hisparse_topk_plan_ints")
+        self.plan_buf = torch.zeros(ints, dtype=torch.int32, device=device)
+        ws = hisparse_topk_workspace_bytes(batch, max_len, k)
+        self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
+        self.workspace_bytes = ws
+        self.err = torch.zeros(1, dtype=torch.int32, device=device)
+
+    def plan(self, seq_lens: torch.Tensor, stream=None):
+        assert seq_lens.dtype == torch.int32 and seq_lens.numel() == self.batch
+        _check(hisparse_topk_plan(self.batch, self.max_len, _ptr(seq_lens), _ptr(self.plan_buf),
+                                  self.plan_buf.numel(), _stream(stream)), "hisparse_topk_plan")
+
+    def build(self, logits: torch.Tensor, seq_lens: torch.Tensor, indices: torch.Tensor,
+              locs: torch.Tensor | None = None, mode: str = "none", page_table=None,
+              page_size: int = 1, row_offsets=None, stream=None):
+        assert logits.dtype == torch.float32 and logits.is_contiguous()
+        assert tuple(logits.shape) == (self.batch, self.max_len)
+        assert tuple(indices.shape) == (self.batch, self.k) and indices.dtype == torch.int32
+        c = HisparseTopkCall()
+        c.batch, c.max_len, c.k = self.batch, self.max_len, self.k
+        c.logits = logits.data_ptr()
+        c.seq_lens = _ptr(seq_lens)
+        c.plan = _ptr(self.plan_buf)
+        c.plan_ints = self.plan_buf.numel()
+        c.mode = INDEX_MODE[mode]
+        c.page_table = _ptr(page_table)
+        c.pt_stride = 0 if page_table is None else page_table.shape[1]
+        c.page_size = page_size
+        c.row_offsets = _ptr(row_offsets)
+        c.indices = _ptr(indices)
+        c.locs = _ptr(locs)
+        c.workspace = self.workspace.data_ptr() if self.workspace_bytes else None
+        c.workspace_bytes = self.workspace_bytes
+        c.error_word = _ptr(self.err)
+        _check(hisparse_topk_index_build(c, _stream(stream)), "hisparse_topk_index_build")
+
+    def error_flags(self, clear: bool = True) -> int:
+        v = int(self.err.item()) & 0xFFFFFFFF
+        if clear:
+            self.err.zero_()
+        return v

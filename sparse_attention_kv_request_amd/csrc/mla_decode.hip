@@ -316,7 +316,6 @@ void mla_decode(MlaArgs a) {
     const int next = replay ? 0 : it + 1;
     const uint32_t valid = valid_next;  // bit t: row t of this tile is present
     if (next < ntiles) valid_next = issue(next, cur ^ 1);
-    const int t0 = it * kTile;
     const uint16_t* tile;
     if constexpr (fp8) {
       dequant_tile(stage + kTileBytes + cur * kRawBytes, reinterpret_cast<uint16_t*>(stage));

@@ -376,3 +376,18 @@ def mla_kv_rows(rng: np.random.Generator, n: int, item_bytes: int) -> np.ndarray
 def mla_queries(rng: np.random.Generator, batch: int, heads: int) -> np.ndarray:
     """bfloat16 bits [batch, heads, 576] of N(0,1) queries."""
     return _to_bf16_bits(rng.standard_normal((batch, heads, MLA_LATENT + MLA_ROPE)))
+
+
+def indexer_logits(rng: np.random.Generator, batch: int, n: int) -> np.ndarray:
+    """float32 [batch, n] stand-ins for indexer scores with the structure the
+    index recipes above encode: N(0, 1) noise, the newest 128 positions
+    raised by 4, and 8 Gaussian bumps (height 2.5, width 300 positions) at
+    random centres, so that a top-2048 mixes recency, clusters and noise."""
+    out = rng.standard_normal((batch, n)).astype(np.float32)
+    pos = np.arange(n, dtype=np.float32)
+    for b in range(batch):
+        out[b, max(0, n - 128):] += np.float32(4.0)
+        for c in rng.integers(0, n, size=8):
+            lo, hi = max(0, c - 900), min(n, c + 900)
+            out[b, lo:hi] += (2.5 * np.exp(-0.5 * ((pos[lo:hi] - c) / 300.0) ** 2)).astype(np.float32)
+    return out

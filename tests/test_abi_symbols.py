@@ -72,3 +72,25 @@ def test_page_mode_and_clock_limits():
     assert binding.hisparse_device_rows_per_request(cfg) == 4096 + 4 * 2048 - 4096
     cfg.max_steps = 1
     assert binding.hisparse_device_rows_per_request(cfg) == -1
+
+
+def test_topk_sizes_and_host_validation():
+    """Host-side sizes and argument checks of the top-k entry points (no
+    kernel is launched: every call below is rejected before any HIP call)."""
+    import math
+    for B, N in [(1, 1), (64, 32768), (128, 131072), (3, 32769), (7, 1 << 20)]:
+        chunks = max(1, math.ceil(N / 32768))
+        assert binding.hisparse_topk_plan_ints(B, N) == 2 + 3 * B + 4 * B * chunks
+        ws = binding.hisparse_topk_workspace_bytes(B, N, 2048)
+        assert ws == (0 if chunks == 1 else 8 * B * chunks * 2048 + 4 * B * chunks)
+    assert binding.hisparse_topk_plan_ints(0, 10) == 0
+    assert binding.hisparse_topk_plan_ints(4, (1 << 20) + 1) == 0
+    assert binding.hisparse_topk_plan(4, 100, None, None, 100, None) == binding.HISPARSE_E_INVAL
+    c = binding.HisparseTopkCall(batch=2, max_len=100, k=0)
+    assert binding.hisparse_topk_index_build(c, None) == binding.HISPARSE_E_INVAL
+    c.k = 40000
+    assert binding.hisparse_topk_index_build(c, None) == binding.HISPARSE_E_UNSUPPORTED
+    c.k, c.max_len = 8192, 5 * 32768               # 5 chunks x 8192 candidates > 32768
+    assert binding.hisparse_topk_index_build(c, None) == binding.HISPARSE_E_UNSUPPORTED
+    c.k, c.max_len = 16, 100
+    assert binding.hisparse_topk_index_build(c, None) == binding.HISPARSE_E_INVAL  # NULL pointers

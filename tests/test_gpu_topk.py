@@ -1,0 +1,137 @@
+"""Top-k selection + index-table build (HIP, through the C ABI) against the
+CPU oracle: indices, index tables, plan and error bits must match exactly."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import topk_oracle as tk
+from sparse_attention_kv_request_amd import binding
+from tests.gpu_harness import DEV, log
+
+pytestmark = pytest.mark.gpu
+
+
+def logits_with_specials(rng, B, N, ties=False):
+    x = rng.standard_normal((B, N)).astype(np.float32)
+    if ties:
+        x = np.round(x * 2).astype(np.float32)          # few distinct values
+    flat = x.reshape(-1)
+    for v in (np.nan, -np.inf, np.inf, -0.0, 0.0):
+        flat[rng.choice(flat.size, max(1, flat.size // 500), replace=False)] = v
+    return x
+
+
+def run(logits, seq_lens, k, mode="none", page_table=None, page_size=1, row_offsets=None,
+        layers=1, check_plan=True):
+    B, N = logits.shape
+    b = binding.TopkIndexBuilder(B, N, k, device=DEV)
+    sl = torch.from_numpy(np.asarray(seq_lens, np.int32)).to(DEV)
+    b.plan(sl)
+    if check_plan:
+        info, items = tk.plan(np.asarray(seq_lens), N)
+        plan = b.plan_buf.cpu().numpy()
+        n_items = len(items)
+        assert plan[0] == n_items and plan[1] == N
+        assert np.array_equal(plan[2:2 + 2 * B].reshape(B, 2), info)
+        assert np.array_equal(plan[2 + 2 * B:2 + 2 * B + 4 * n_items].reshape(-1, 4), items)
+    t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(DEV)
+    pt, ro = t(page_table), t(row_offsets)
+    for layer in range(layers):
+        lg = logits if layer == 0 else np.roll(logits, layer * 7, axis=1)
+        idx = torch.full((B, k), 12345, dtype=torch.int32, device=DEV)
+        locs = None if mode == "none" else torch.full((B, k), 12345, dtype=torch.int32, device=DEV)
+        b.build(torch.from_numpy(lg).to(DEV), sl, idx, locs, mode=mode, page_table=pt,
+                page_size=page_size, row_offsets=ro)
+        torch.cuda.synchronize()
+        ref_idx, ref_locs, ref_err = tk.topk_index_build(lg, np.asarray(seq_lens), k, mode=mode,
+                                                          page_table=page_table,
+                                                          page_size=page_size,
+                                                          row_offsets=row_offsets)
+        got = idx.cpu().numpy()
+        bad = np.nonzero(np.any(got != ref_idx, axis=1))[0]
+        assert bad.size == 0, f"layer {layer}: rows {bad[:5]} differ, e.g. {got[bad[0]][:8]} vs {ref_idx[bad[0]][:8]}"
+        if mode != "none":
+            assert np.array_equal(locs.cpu().numpy(), ref_locs)
+        assert b.error_flags() == ref_err
+    # the tickets are back at 0 after every call
+    info = b.plan_buf.cpu().numpy()
+    assert np.all(info[-B:] == 0)
+    return b
+
+
+def test_small_rows_edge_lengths():
+    rng = np.random.default_rng(1)
+    lg = logits_with_specials(rng, 6, 1000)
+    run(lg, [0, 1, 63, 64, 1000, 999], 64)
+    run(lg, [0, 1, 63, 64, 1000, 999], 1)
+    run(lg, [1000, 5, 700, 64, 2, 999], 1000)
+
+
+def test_ties_and_specials():
+    rng = np.random.default_rng(2)
+    lg = logits_with_specials(rng, 4, 5000, ties=True)
+    run(lg, [5000, 4096, 1234, 4999], 777)
+    const = np.full((2, 3000), 1.5, np.float32)
+    run(const, [3000, 2000], 100)
+    nan = np.full((1, 2048), np.nan, np.float32)
+    nan[0, 100] = -np.inf
+    run(nan, [2048], 10)
+
+
+def test_split_rows_and_ragged_table():
+    rng = np.random.default_rng(3)
+    N = 32768 + 5000
+    lg = logits_with_specials(rng, 5, N, ties=True)
+    lens = [N, 32768, 32769, 40000 - 3000, 17]
+    offs = np.cumsum([0] + lens[:-1]).astype(np.int32)
+    run(lg, lens, 512, mode="ragged", row_offsets=offs, layers=3)
+
+
+def test_long_rows_paged_table_with_holes():
+    rng = np.random.default_rng(4)
+    B, N, P = 3, 131072, 64
+    lg = logits_with_specials(rng, B, N)
+    pt = rng.permutation(B * (N // P)).astype(np.int32).reshape(B, N // P)
+    pt[0, rng.choice(N // P, 50, replace=False)] = -1     # unmapped pages -> error bit
+    run(lg, [131072, 100000, 70001], 2048, mode="paged", page_table=pt, page_size=P, layers=2)
+
+
+def test_equal_scores_across_chunks():
+    """All scores equal: the lowest positions win, across chunk boundaries."""
+    lg = np.zeros((2, 4 * 32768), np.float32)
+    run(lg, [4 * 32768, 3 * 32768 + 1], 2048)
+    lg[1, -5:] = 1.0
+    run(lg, [4 * 32768, 4 * 32768], 8)
+
+
+def test_rejected_rows_and_unaligned_stride():
+    rng = np.random.default_rng(5)
+    lg = logits_with_specials(rng, 4, 4099)                 # row stride not a multiple of 4
+    run(lg, [4099, -1, 4100, 300], 50, mode="ragged", row_offsets=[0, 1, 2, 3])
+
+
+@pytest.mark.parametrize("B,N", [(64, 32768), (128, 131072)])
+def test_full_size(B, N):
+    """The two deployment shapes: 64 rows of 32768 and 128 rows of 131072
+    scores, k = 2048, the recency-and-cluster score recipe of the bench."""
+    from sparse_attention_kv_request_amd import workloads
+    rng = np.random.default_rng(B)
+    lg = workloads.indexer_logits(rng, B, N)
+    lens = np.full(B, N, np.int32)
+    lens[::3] = rng.integers(2048, N, size=len(lens[::3]))
+    run(lg, lens, 2048)
+    log(f"topk B={B} N={N}: exact")
+
+
+def test_rejects_bad_arguments():
+    with pytest.raises(binding.HiSparseError) as e:
+        binding.TopkIndexBuilder(4, 1 << 21, 16, device=DEV)
+    assert e.value.code == binding.HISPARSE_E_UNSUPPORTED
+    b = binding.TopkIndexBuilder(2, 70000, 4096, device=DEV)   # 3 chunks x 4096 <= 32768: ok
+    idx = torch.empty((2, 4096), dtype=torch.int32, device=DEV)
+    lg = torch.zeros((2, 70000), dtype=torch.float32, device=DEV)
+    sl = torch.full((2,), 70000, dtype=torch.int32, device=DEV)
+    b.plan(sl)
+    with pytest.raises(binding.HiSparseError) as e:
+        b.build(lg, sl, idx, None, mode="paged")               # paged without a table
+    assert e.value.code == binding.HISPARSE_E_INVAL
