@@ -311,19 +311,19 @@ int hisparse_sparse_mla_decode(hisparse_state_t st, int32_t layer_id, int32_t ba
 #define HISPARSE_INDEX_NONE 0
 #define HISPARSE_INDEX_PAGED 1
 #define HISPARSE_INDEX_RAGGED 2
-#define HISPARSE_TOPK_CHUNK 32768     /* positions per workgroup; longer rows are split */
-#define HISPARSE_TOPK_MAX_CHUNKS 32   /* max_len <= 32 * 32768 */
+#define HISPARSE_TOPK_CHUNK 32768            /* positions per workgroup; longer rows are split */
+#define HISPARSE_TOPK_MAX_CANDIDATES 32768   /* chunks x k merged per split row */
+#define HISPARSE_TOPK_MAX_CHUNKS 64
 
 typedef struct hisparse_topk_call {
   int32_t batch;               /* rows, >= 1 */
-  int32_t max_len;             /* logits row length (stride), 1 .. 2^20 */
-  int32_t k;                   /* >= 1; ceil(max_len / 32768) * k <= 32768 */
+  int32_t max_len;             /* logits row length (stride) >= 1 */
+  int32_t k;                   /* 1 .. 32768; if max_len > 32768: ceil(max_len / 32768)
+                                  <= 64 and ceil(max_len / 32768) * k <= 32768 */
   const float* logits;         /* device fp32 [batch][max_len], caller-owned */
   const int32_t* seq_lens;     /* device int32 [batch] */
-  int32_t* plan;               /* device plan from hisparse_topk_plan for the same
-                                  batch, max_len and seq_lens; its per-row ticket
-                                  words are used and left at 0, so calls sharing a
-                                  plan must be ordered on one stream */
+  const int32_t* plan;         /* device plan from hisparse_topk_plan for the same
+                                  batch, max_len and seq_lens (read only) */
   size_t plan_ints;            /* size of `plan` in int32 */
   int32_t mode;                /* HISPARSE_INDEX_* */
   const int32_t* page_table;   /* PAGED: device int32 [batch][pt_stride] */
@@ -340,15 +340,15 @@ typedef struct hisparse_topk_call {
 
 /*
  * Plan of the work split: int32 words needed for `batch` rows of length up
- * to max_len, and the plan itself (device seq_lens in, device plan out:
- * n_items, max_len, per row (first item, n_chunks), per item (row, chunk,
- * start, length), per row a ticket word set to 0).  A row of s positions is
+ * to max_len (0 if the sizes are invalid), and the plan itself (device
+ * seq_lens in, device plan out: n_items, max_len, per row (first item,
+ * n_chunks), per item (row, chunk, start, length)).  A row of s positions is
  * split into n = max(1, ceil(s / 32768)) chunks of 1024 * ceil(ceil(s / n) /
  * 1024) positions (the last shorter); rows outside [0, max_len] get one empty
  * chunk.  The plan depends on seq_lens only: one plan serves every layer of a
  * decode step.  Enqueued on `stream`; allocates nothing.
  * Errors: HISPARSE_E_INVAL (bad sizes, NULL pointers, plan_ints too small),
- * HISPARSE_E_UNSUPPORTED (max_len above 2^20), HISPARSE_E_HIP.
+ * HISPARSE_E_HIP.
  */
 size_t hisparse_topk_plan_ints(int32_t batch, int32_t max_len);
 int hisparse_topk_plan(int32_t batch, int32_t max_len, const int32_t* seq_lens, int32_t* plan,
@@ -356,12 +356,13 @@ int hisparse_topk_plan(int32_t batch, int32_t max_len, const int32_t* seq_lens, 
 /*
  * Scratch bytes for hisparse_topk_index_build: 0 when no row can be split
  * (max_len <= 32768), else 8 * k + 4 bytes per plan item for the chunks'
- * candidates.
+ * candidates.  0 as well for unsupported (max_len, k).
  */
 size_t hisparse_topk_workspace_bytes(int32_t batch, int32_t max_len, int32_t k);
 /*
- * One layer's selection and index table (see above) in one kernel launch on
- * `stream`; reads each logit once.  Allocates nothing.
+ * One layer's selection and index table (see above) on `stream`: one kernel
+ * launch, plus a second one that merges the chunks of rows longer than 32768
+ * positions; reads each logit once.  Allocates nothing.
  * Errors: HISPARSE_E_INVAL (NULL pointers, bad sizes or mode, plan or
  * workspace too small), HISPARSE_E_UNSUPPORTED (k or max_len beyond the
  * limits above), HISPARSE_E_HIP.

@@ -24,13 +24,13 @@ T3  Output order: the selected positions in ascending order, then -1 up to k
 T4  Index table: PAGED  loc = page_table[b][p // P] * P + p % P, -1 stays -1;
     a position whose page entry is negative or beyond the table gives -1 and
     the bad-index error bit.  RAGGED  loc = row_offset[b] + p.
-T5  The plan splits row b into n_b = max(1, ceil(seq_len_b / C)) chunks
-    (C = 32768 positions, the threshold above which a row is shared by
-    several workgroups) of length L_b = 1024 * ceil(ceil(seq_len_b / n_b) /
-    1024) (the last one shorter); a row outside [0, N] (N = the logits row
-    length) gets one empty chunk.  It lists, per row, its first work item and
-    n_b, and per work item (row, chunk, start, length).  The plan depends on
-    the sequence lengths only, so one plan serves every layer of a step.
+T5  The plan splits row b into n_b = max(1, ceil(seq_len_b / 32768))
+    chunks (32768 positions is the threshold above which a row is shared by
+    several workgroups) of length L_b = 1024 * ceil(ceil(seq_len_b / n_b) / 1024) (the
+    last one shorter); a row outside [0, N] (N = the logits row length) gets
+    one empty chunk.  It lists, per row, its first work item and n_b, and per
+    work item (row, chunk, start, length).  The plan depends on the sequence
+    lengths only, so one plan serves every layer of a step.
 
 Every function is pinned by tests/test_topk_oracle.py (brute force over all
 tiny inputs against a characterisation of T2, torch.topk on distinct scores,
@@ -42,7 +42,7 @@ import numpy as np
 
 ERR_BAD_INDEX = 1
 ERR_BAD_ROW = 8
-CHUNK = 32768          # T5: positions per workgroup above which a row is split
+SPLIT = 32768          # T5: positions above which a row is split
 CHUNK_ALIGN = 1024
 
 
@@ -119,7 +119,7 @@ def plan(seq_lens: np.ndarray, max_len: int):
     items = []
     for b, s in enumerate(int(x) for x in seq_lens):
         s = s if 0 <= s <= max_len else 0
-        n = max(1, -(-s // CHUNK))
+        n = max(1, -(-s // SPLIT))
         length = CHUNK_ALIGN * (-(-(-(-s // n)) // CHUNK_ALIGN))
         row_info[b] = (len(items), n)
         for c in range(n):

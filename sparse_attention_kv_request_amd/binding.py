@@ -453,7 +453,11 @@ class TopkIndexBuilder:
         self.batch, self.max_len, self.k = batch, max_len, k
         ints = hisparse_topk_plan_ints(batch, max_len)
         if ints == 0:
-            raise HiSparseError(HISPARSE_E_UNSUPPORTED, "hisparse_topk_plan_ints")
+            raise HiSparseError(HISPARSE_E_INVAL, "hisparse_topk_plan_ints")
+        c = HisparseTopkCall(batch=batch, max_len=max_len, k=k)
+        code = hisparse_topk_index_build(c, 0)      # shape check only: rejected before launch
+        if code == HISPARSE_E_UNSUPPORTED:
+            raise HiSparseError(code, "hisparse_topk_index_build")
         self.plan_buf = torch.zeros(ints, dtype=torch.int32, device=device)
         ws = hisparse_topk_workspace_bytes(batch, max_len, k)
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)

@@ -492,15 +492,12 @@ int hisparse_sparse_mla_decode(hisparse_state_t st, int32_t layer_id, int32_t ba
 
 namespace {
 bool topk_sizes_ok(int32_t batch, int32_t max_len) {
-  return batch >= 1 && batch <= (1 << 20) && max_len >= 1;
-}
-bool topk_len_supported(int32_t max_len) {
-  return max_len <= hisparse::kTopkMaxChunks * hisparse::kTopkChunk;
+  return batch >= 1 && batch <= (1 << 20) && max_len >= 1 && max_len <= (1 << 28);
 }
 }  // namespace
 
 size_t hisparse_topk_plan_ints(int32_t batch, int32_t max_len) {
-  if (!topk_sizes_ok(batch, max_len) || !topk_len_supported(max_len)) return 0;
+  if (!topk_sizes_ok(batch, max_len)) return 0;
   return static_cast<size_t>(
       hisparse::topk_plan_layout(batch, hisparse::topk_max_items(batch, max_len)).ints);
 }
@@ -509,22 +506,19 @@ int hisparse_topk_plan(int32_t batch, int32_t max_len, const int32_t* seq_lens, 
                        size_t plan_ints, void* stream) {
   if (!topk_sizes_ok(batch, max_len) || seq_lens == nullptr || plan == nullptr)
     return HISPARSE_E_INVAL;
-  if (!topk_len_supported(max_len)) return HISPARSE_E_UNSUPPORTED;
   if (plan_ints < hisparse_topk_plan_ints(batch, max_len)) return HISPARSE_E_INVAL;
   return status_of(
       hisparse::launch_topk_plan(seq_lens, plan, batch, max_len, static_cast<hipStream_t>(stream)));
 }
 
 size_t hisparse_topk_workspace_bytes(int32_t batch, int32_t max_len, int32_t k) {
-  if (!topk_sizes_ok(batch, max_len) || !topk_len_supported(max_len) || k < 1) return 0;
+  if (!topk_sizes_ok(batch, max_len) || !hisparse::topk_shape_supported(max_len, k)) return 0;
   return hisparse::topk_workspace_layout(batch, max_len, k).bytes;
 }
 
 int hisparse_topk_index_build(const hisparse_topk_call_t* c, void* stream) {
   if (c == nullptr || !topk_sizes_ok(c->batch, c->max_len) || c->k < 1) return HISPARSE_E_INVAL;
-  if (!topk_len_supported(c->max_len) || c->k > hisparse::kTopkChunk ||
-      static_cast<int64_t>(hisparse::topk_chunks_max(c->max_len)) * c->k > hisparse::kTopkChunk)
-    return HISPARSE_E_UNSUPPORTED;
+  if (!hisparse::topk_shape_supported(c->max_len, c->k)) return HISPARSE_E_UNSUPPORTED;
   if (!c->logits || !c->seq_lens || !c->plan || !c->indices || !c->error_word)
     return HISPARSE_E_INVAL;
   if (c->plan_ints < hisparse_topk_plan_ints(c->batch, c->max_len)) return HISPARSE_E_INVAL;

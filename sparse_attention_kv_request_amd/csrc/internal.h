@@ -36,25 +36,26 @@ static_assert((HISPARSE_MAX_HOT + 31) / 32 <= kPlanThreads,
 
 // Top-k selection + index-table build (topk.hip).
 constexpr int kTopkThreads = 1024;
-constexpr int kTopkChunk = HISPARSE_TOPK_CHUNK;
-constexpr int kTopkAlign = 1024;
+constexpr int kTopkChunk = HISPARSE_TOPK_CHUNK;          // rows above this are split
+constexpr int kTopkMaxCandidates = HISPARSE_TOPK_MAX_CANDIDATES;
 constexpr int kTopkMaxChunks = HISPARSE_TOPK_MAX_CHUNKS;
-static_assert(kTopkChunk % kTopkThreads == 0 && kTopkChunk % kTopkAlign == 0, "chunk shape");
+constexpr int kTopkAlign = 1024;
+static_assert(kTopkChunk % kTopkThreads == 0 && kTopkMaxCandidates <= kTopkChunk, "chunk shape");
 
 // Word offsets inside a plan: [0] n_items, [1] max_len, row_info [batch][2],
-// items [max_items][4], tickets [batch].
+// items [max_items][4].
 struct TopkPlan {
-  int row_info, items, tickets, ints;
+  int row_info, items, ints;
 };
-__host__ __device__ inline int topk_chunks_max(int max_len) {
-  const int n = (max_len + kTopkChunk - 1) / kTopkChunk;
+__host__ __device__ inline int topk_chunks(int len) {
+  const int n = (len + kTopkChunk - 1) / kTopkChunk;
   return n < 1 ? 1 : n;
 }
 __host__ __device__ inline int topk_max_items(int batch, int max_len) {
-  return batch * topk_chunks_max(max_len);
+  return batch * topk_chunks(max_len);
 }
 __host__ __device__ inline TopkPlan topk_plan_layout(int batch, int max_items) {
-  return TopkPlan{2, 2 + 2 * batch, 2 + 2 * batch + 4 * max_items, 2 + 3 * batch + 4 * max_items};
+  return TopkPlan{2, 2 + 2 * batch, 2 + 2 * batch + 4 * max_items};
 }
 // Byte offsets of the candidate arrays in the workspace (none when no row
 // can be split).
@@ -62,10 +63,17 @@ struct TopkWorkspace {
   size_t key, pos, cnt, bytes;
 };
 inline TopkWorkspace topk_workspace_layout(int batch, int max_len, int k) {
-  if (topk_chunks_max(max_len) == 1) return TopkWorkspace{0, 0, 0, 0};
+  if (topk_chunks(max_len) == 1) return TopkWorkspace{0, 0, 0, 0};
   const size_t items = static_cast<size_t>(topk_max_items(batch, max_len));
   const size_t words = items * static_cast<size_t>(k);
   return TopkWorkspace{0, 4 * words, 8 * words, 8 * words + 4 * items};
+}
+// A split row merges chunks x k candidates: at most 32768, from at most 64
+// chunks.
+inline bool topk_shape_supported(int max_len, int k) {
+  const int n = topk_chunks(max_len);
+  if (k < 1 || k > kTopkChunk) return false;
+  return n == 1 || (n <= kTopkMaxChunks && static_cast<int64_t>(n) * k <= kTopkMaxCandidates);
 }
 hipError_t launch_topk_plan(const int32_t* seq_lens, int32_t* plan, int32_t batch, int32_t max_len,
                             hipStream_t st);

@@ -8,33 +8,46 @@
 // largest scores, ties to the lower position, NaN below every number; output
 // in ascending position order, -1 padded.  Scores map to order-preserving
 // 32-bit keys (+0/-0 merged, NaN lowest, 0 reserved for "absent"), so the
-// selection is: find the exact threshold key T by radix select (four 8-bit
-// digits, LDS histograms), then keep keys > T and the first `need` keys == T
-// in position order.
+// selection is: find the exact threshold key T by radix select, then keep
+// keys > T and the first `need` keys == T in position order.  The radix
+// select takes a 12-bit digit over all keys (a 4096-bin LDS histogram; sign,
+// exponent and 3 mantissa bits, so a binade of scores spreads over 8 bins),
+// then gathers the keys of the threshold bin into an LDS list (typically a
+// few percent) and finishes with 12- and 8-bit digits over that list.
 //
-// Work split (the plan): a row of up to 32768 positions is one workgroup of
-// 1024 threads holding 32 consecutive scores per thread in registers; a
-// longer row is split into equal chunks of at most 32768.  Each chunk
-// selects its own top-k (exact: the row's top-k is the top-k of the union of
-// its chunks' top-k), writes it as candidates, and the last chunk of the row
-// to finish (a device-scope ticket) selects the final top-k from the
-// candidates.  The logits are read from HBM exactly once.
+// Work split (the plan): a workgroup of 1024 threads takes one chunk of up
+// to 32768 positions, 32 scores per thread in registers (8 coalesced
+// 16-byte loads); longer rows are split into equal chunks.  A row of one chunk
+// is selected and its index table written by that workgroup alone.  The
+// chunks of a longer row each select their own top-k (exact: the row's
+// top-k is the top-k of the union of its chunks' top-k) and write them as
+// candidates; a second kernel on the same stream (its launch is the only
+// synchronisation needed) selects each such row's top-k from its
+// candidates and writes its index table.  The logits are read from HBM once.
+//
+// Position order is kept in LDS bitmaps (one bit per position of the
+// chunk): the kept positions and the ties at the threshold are marked, and
+// one workgroup scan over the bitmap words gives every kept position its
+// output index.  Prefix sums use wave64 DPP scans (row shifts and row
+// broadcasts, VALU only) and one LDS exchange per workgroup scan.
 #include "internal.h"
 
 namespace hisparse {
 
 namespace {
 
-constexpr int kThreads = kTopkThreads;       // 1024
-constexpr int kPer = kTopkChunk / kThreads;  // 32 scores per thread
-constexpr int kWaves = kThreads / kWave;     // 16
+constexpr int kThreads = kTopkThreads;             // 1024
+constexpr int kPer = kTopkChunk / kThreads;        // 32 keys per thread
+constexpr int kWaves = kThreads / kWave;           // 16
+constexpr int kBins = 4096;                        // 12-bit digits
+constexpr int kListCap = 4096;                     // keys of the threshold bin kept in LDS
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct TopkArgs {
   const float* logits;       // [batch][max_len]
   const int32_t* seq_lens;   // [batch]
-  int32_t* plan;             // TopkPlan layout (its ticket counters are updated)
+  const int32_t* plan;       // TopkPlan layout
   int32_t batch, max_len, k, max_items;
   int32_t mode;
   const int32_t* page_table;  // [batch][pt_stride]
@@ -58,74 +71,169 @@ __device__ __forceinline__ uint32_t score_key(float x) {
   return k + 1u;  // -inf -> 0x00800000; +inf -> 0xFF800001
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: row shifts 1, 2, 4, 8
+// within each 16-lane row, then the last lane of row 0 broadcast into rows 1
+// and 3 and the last lane of row 1 into rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false); // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false); // row_bcast:31
+  return x;
+}
+
+// Exclusive prefix sum over the workgroup; *total gets the sum.  Two
+// barriers; `xch` holds kWaves words.  Every thread must call it.
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* xch, uint32_t* total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const uint32_t incl = wave_incl_scan(v);
+  if (lane == kWave - 1) xch[wid] = incl;
+  __syncthreads();
+  const uint32_t w = lane < kWaves ? xch[lane] : 0u;
+  const uint32_t wi = wave_incl_scan(w);
+  const uint32_t before = wid > 0 ? __builtin_amdgcn_readlane(wi, wid - 1) : 0u;
+  *total = __builtin_amdgcn_readlane(wi, kWaves - 1);
+  __syncthreads();
+  return before + incl - v;
+}
+
 struct Lds {
-  uint32_t hist[kWaves][256];
-  int scan[kWaves + 1];
+  uint32_t hist[kBins];
+  uint32_t list[kListCap];
+  uint32_t gt_bits[kTopkChunk / 32];  // slot bitmaps: key > T, key == T
+  uint32_t eq_bits[kTopkChunk / 32];
+  uint32_t xch[kWaves];
   int pick[2];
+  int list_count;
   int offs[kTopkMaxChunks + 1];
-  int last;
 };
 
-// Exact threshold of the kk largest keys (kk >= 1, at most the number of
-// present keys): T and the number `need` of keys equal to T to keep.
+// Slot of element e (= 4v + j) of thread t: slots are positions in the
+// chunk (or candidate order in a merge); each thread owns 8 groups of 4
+// consecutive slots 4096 apart, so every load of a wave is one coalesced
+// 1 KiB block.
+__device__ __forceinline__ int slot_of(int e) { return ((e >> 2) * kThreads + threadIdx.x) * 4 + (e & 3); }
+
+// Digit of a key for pass 1 (bits 19..8) and 2 (7..0); pass 0 is bits 31..20.
+__device__ __forceinline__ uint32_t digit(uint32_t x, int pass) {
+  return pass == 1 ? (x >> 8) & 4095u : x & 255u;
+}
+
+// From this pass's histogram in s.hist: the bin holding the
+// `remaining`-th largest key and the number of keys in higher bins.  Thread
+// j scans bins / 1024 bins (at least one), highest first.  Block-wide.
+__device__ __forceinline__ void pick_bin(Lds& s, int bins, int remaining, uint32_t& bin,
+                                         int& above_out) {
+  const int tid = threadIdx.x;
+  const int per = bins >= kThreads ? bins / kThreads : 1;
+  const int top = bins - 1 - tid * per;
+  uint32_t c = 0u;
+  if (top >= 0)
+    for (int i = 0; i < per; ++i) c += s.hist[top - i];
+  uint32_t total;
+  int above = static_cast<int>(block_scan(c, s.xch, &total));
+  if (top >= 0 && c > 0u && above < remaining && remaining <= above + static_cast<int>(c)) {
+    for (int i = 0; i < per; ++i) {
+      const int h = static_cast<int>(s.hist[top - i]);
+      if (remaining <= above + h) {
+        s.pick[0] = top - i;
+        s.pick[1] = above;
+        break;
+      }
+      above += h;
+    }
+  }
+  __syncthreads();
+  bin = static_cast<uint32_t>(s.pick[0]);
+  above_out = s.pick[1];
+}
+
+// Exact threshold of the kk largest keys of the workgroup (key 0 = absent;
+// kk >= 1, at most the number of present keys): T and the number `need` of
+// keys equal to T to keep.  The first-digit histogram is built by the
+// caller (hist0) while the keys are loaded.
 __device__ __forceinline__ void radix_threshold(const uint32_t (&key)[kPer], int kk, Lds& s,
                                                 uint32_t& T, int& need) {
-  const int tid = threadIdx.x, wave = tid / kWave;
-  uint32_t prefix = 0u, mask = 0u;
-  int remaining = kk;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  uint32_t b0;
+  int above;
+  pick_bin(s, kBins, kk, b0, above);
+  int remaining = kk - above;
+  uint32_t prefix = b0 << 20;
+
+  // keys of bin b0 -> LDS list (any order; typically a few percent of keys)
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const bool in = key[e] != 0u && (key[e] >> 20) == b0;
+    const uint64_t mask = __ballot(in);
+    if (mask != 0u) {
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&s.list_count, __popcll(mask));
+      base = __builtin_amdgcn_readfirstlane(base);
+      const int at = base + __popcll(mask & ((uint64_t{1} << lane) - 1u));
+      if (in && at < kListCap) s.list[at] = key[e];
+    }
+  }
+  __syncthreads();
+  const int m = s.list_count;
+  const bool listed = m <= kListCap;
 #pragma unroll 1
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < kWaves * 256; i += kThreads) (&s.hist[0][0])[i] = 0u;
+  for (int pass = 1; pass < 3; ++pass) {
+    const int bins = pass == 1 ? kBins : 256;
+    const uint32_t pm = pass == 1 ? 0xFFF00000u : 0xFFFFFF00u;  // bits fixed so far
+    for (int i = tid; i < bins; i += kThreads) s.hist[i] = 0u;
     __syncthreads();
+    if (listed) {  // the list holds exactly the keys of bin b0
+      for (int i = tid; i < m; i += kThreads) {
+        const uint32_t x = s.list[i];
+        if ((x & pm) == prefix) atomicAdd(&s.hist[digit(x, pass)], 1u);
+      }
+    } else {
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const uint32_t x = key[e];
-      if (x != 0u && (x & mask) == prefix) atomicAdd(&s.hist[wave][(x >> shift) & 255u], 1u);
+      for (int e = 0; e < kPer; ++e)
+        if (key[e] != 0u && (key[e] & pm) == prefix) atomicAdd(&s.hist[digit(key[e], pass)], 1u);
     }
     __syncthreads();
-    // thread j < 256 looks at bin 255 - j, so the exclusive scan gives the
-    // number of keys in higher bins
-    int c = 0;
-    if (tid < 256) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) c += static_cast<int>(s.hist[w][255 - tid]);
-    }
-    int total;
-    const int above = block_exclusive_scan<kThreads>(c, s.scan, &total);
-    if (tid < 256 && c > 0 && above < remaining && remaining <= above + c) {
-      s.pick[0] = 255 - tid;
-      s.pick[1] = above;
-    }
-    __syncthreads();
-    const uint32_t digit = static_cast<uint32_t>(s.pick[0]);
-    remaining -= s.pick[1];
-    prefix |= digit << shift;
-    mask |= 255u << shift;
-    __syncthreads();
+    uint32_t b;
+    pick_bin(s, bins, remaining, b, above);
+    remaining -= above;
+    prefix |= pass == 1 ? (b << 8) : b;
   }
   T = prefix;
   need = remaining;
 }
 
-// Keeps keys > T and the first `need` keys == T (position order = thread
-// order, then element order) and returns, per thread, the selection mask and
-// the output offset of its first kept element.
-__device__ __forceinline__ uint32_t select_mask(const uint32_t (&key)[kPer], uint32_t T, int need,
+// Marks keys > T and keys == T in the slot bitmaps, then thread w takes
+// bitmap word w (slots 32w .. 32w + 31): one workgroup scan of the packed
+// (count > T, count == T) per word gives, in slot order, the output offset of
+// the word's first kept slot; ties are kept while their rank is below
+// `need`.  Returns the word's kept bits and its output offset.
+__device__ __forceinline__ uint32_t select_word(const uint32_t (&key)[kPer], uint32_t T, int need,
                                                 Lds& s, int& offset) {
-  int ties = 0;
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) ties += key[e] == T;
-  int total;
-  int rank = block_exclusive_scan<kThreads>(ties, s.scan, &total);
-  uint32_t m = 0u;
+  const int tid = threadIdx.x;
+  s.gt_bits[tid] = 0u;
+  s.eq_bits[tid] = 0u;
+  __syncthreads();
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
-    bool keep = key[e] > T;
-    if (key[e] == T) keep = rank++ < need;
-    m |= static_cast<uint32_t>(keep) << e;
+    if (key[e] >= T) {
+      const int i = slot_of(e);
+      atomicOr(key[e] > T ? &s.gt_bits[i >> 5] : &s.eq_bits[i >> 5], 1u << (i & 31));
+    }
   }
-  offset = block_exclusive_scan<kThreads>(__popc(m), s.scan, &total);
-  return m;
+  __syncthreads();
+  const uint32_t g = s.gt_bits[tid], q = s.eq_bits[tid];
+  uint32_t total;
+  const uint32_t pre = block_scan((static_cast<uint32_t>(__popc(g)) << 16) | __popc(q), s.xch, &total);
+  const int q_pre = static_cast<int>(pre & 0xFFFFu), g_pre = static_cast<int>(pre >> 16);
+  int keep_ties = need - q_pre;
+  uint32_t qk = 0u;
+  for (uint32_t r = q; r != 0u && keep_ties > 0; r &= r - 1u, --keep_ties) qk |= r & (~r + 1u);
+  offset = g_pre + min(q_pre, need);
+  return g | qk;
 }
 
 __device__ __forceinline__ int32_t table_loc(const TopkArgs& a, int row, int32_t p) {
@@ -139,15 +247,15 @@ __device__ __forceinline__ int32_t table_loc(const TopkArgs& a, int row, int32_t
   return page * a.page_size + (p - j * a.page_size);
 }
 
-// Final outputs of a row from the kept elements (position of element e:
-// pos_of(e)) and -1 padding from kk on.
+// Final outputs of a row: the kept slots of this thread's bitmap word at
+// `offset` on (position of slot i: pos_of(i)), then -1 padding from kk on.
 template <class PosOf>
-__device__ __forceinline__ void emit_final(const TopkArgs& a, int row, PosOf pos_of, uint32_t m,
+__device__ __forceinline__ void emit_final(const TopkArgs& a, int row, PosOf pos_of, uint32_t w,
                                            int offset, int kk) {
   int32_t* idx = a.indices + static_cast<size_t>(row) * a.k;
   int32_t* loc = a.locs ? a.locs + static_cast<size_t>(row) * a.k : nullptr;
-  for (uint32_t r = m; r != 0u; r &= r - 1u) {
-    const int32_t p = pos_of(__builtin_ctz(r));
+  for (uint32_t r = w; r != 0u; r &= r - 1u) {
+    const int32_t p = pos_of(32 * static_cast<int>(threadIdx.x) + __builtin_ctz(r));
     idx[offset] = p;
     if (loc) loc[offset] = table_loc(a, row, p);
     ++offset;
@@ -158,10 +266,15 @@ __device__ __forceinline__ void emit_final(const TopkArgs& a, int row, PosOf pos
   }
 }
 
+__device__ __forceinline__ bool row_rejected(const TopkArgs& a, int row) {
+  const int seq = a.seq_lens[row];
+  return seq < 0 || seq > a.max_len;
+}
+
 __global__ __launch_bounds__(kThreads) void topk_plan_kernel(const int32_t* seq_lens, int32_t* plan,
                                                              int32_t batch, int32_t max_len,
                                                              int32_t max_items) {
-  __shared__ int scan[kWaves + 1];
+  __shared__ uint32_t xch[kWaves];
   const TopkPlan p = topk_plan_layout(batch, max_items);
   int carry = 0;
   for (int b0 = 0; b0 < batch; b0 += kThreads) {
@@ -172,12 +285,11 @@ __global__ __launch_bounds__(kThreads) void topk_plan_kernel(const int32_t* seq_
       if (s < 0 || s > max_len) s = 0;
       n = max(1, (s + kTopkChunk - 1) / kTopkChunk);
     }
-    int total;
-    const int first = carry + block_exclusive_scan<kThreads>(n, scan, &total);
+    uint32_t total;
+    const int first = carry + static_cast<int>(block_scan(static_cast<uint32_t>(n), xch, &total));
     if (b < batch) {
       plan[p.row_info + 2 * b] = first;
       plan[p.row_info + 2 * b + 1] = n;
-      plan[p.tickets + b] = 0;
       const int per = (s + n - 1) / n;
       const int len = (per + kTopkAlign - 1) / kTopkAlign * kTopkAlign;
       for (int c = 0; c < n; ++c) {
@@ -188,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void topk_plan_kernel(const int32_t* seq_
         it[3] = max(0, min(len, s - c * len));
       }
     }
-    carry += total;
+    carry += static_cast<int>(total);
   }
   if (threadIdx.x == 0) {
     plan[0] = carry;
@@ -196,7 +308,8 @@ __global__ __launch_bounds__(kThreads) void topk_plan_kernel(const int32_t* seq_
   }
 }
 
-__global__ __launch_bounds__(kThreads) void topk_index_build_kernel(TopkArgs a) {
+// One workgroup per plan item (chunk).
+__global__ __launch_bounds__(kThreads) void topk_chunk_kernel(TopkArgs a) {
   __shared__ Lds s;
   const TopkPlan p = topk_plan_layout(a.batch, a.max_items);
   const int w = blockIdx.x;
@@ -205,8 +318,7 @@ __global__ __launch_bounds__(kThreads) void topk_index_build_kernel(TopkArgs a) 
   const int32_t* item = a.plan + p.items + 4 * w;
   const int row = item[0], start = item[2], len = item[3];
   const int n_chunks = a.plan[p.row_info + 2 * row + 1];
-  const int seq = a.seq_lens[row];
-  if (seq < 0 || seq > a.max_len) {  // rejected row: one empty chunk
+  if (row_rejected(a, row)) {  // one empty chunk
     if (tid == 0) raise_error(a.err, HISPARSE_ERR_BAD_ROW);
     for (int i = tid; i < a.k; i += kThreads) {
       a.indices[static_cast<size_t>(row) * a.k + i] = -1;
@@ -215,59 +327,68 @@ __global__ __launch_bounds__(kThreads) void topk_index_build_kernel(TopkArgs a) 
     return;
   }
 
-  // this thread's scores: positions start + 32 tid + e
+  // keys of this thread's slots (positions start + slot), first-digit
+  // histogram as they arrive
+  for (int i = tid; i < kBins; i += kThreads) s.hist[i] = 0u;
+  if (tid == 0) s.list_count = 0;
+  __syncthreads();
   uint32_t key[kPer];
-  const int base = kPer * tid;
   {
-    const float* src = a.logits + static_cast<size_t>(row) * a.max_len + start + base;
-    if (base + kPer <= len && ((reinterpret_cast<uintptr_t>(src) & 15u) == 0u)) {
+    const float* src = a.logits + static_cast<size_t>(row) * a.max_len + start;
+    const bool vec = (reinterpret_cast<uintptr_t>(src) & 15u) == 0u;
 #pragma unroll
-      for (int v = 0; v < kPer / 4; ++v) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(src + 4 * v);
+    for (int v = 0; v < kPer / 4; ++v) {
+      const int i0 = slot_of(4 * v);
+      if (vec && i0 + 3 < len) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(src + i0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) key[4 * v + j] = score_key(x[j]);
-      }
-    } else {
+      } else {
 #pragma unroll
-      for (int e = 0; e < kPer; ++e) key[e] = base + e < len ? score_key(src[e]) : 0u;
+        for (int j = 0; j < 4; ++j) key[4 * v + j] = i0 + j < len ? score_key(src[i0 + j]) : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (key[4 * v + j] != 0u) atomicAdd(&s.hist[key[4 * v + j] >> 20], 1u);
     }
   }
+  __syncthreads();
   const int kk = min(a.k, len);
-  uint32_t T = 0u;
-  int need = 0;
-  if (kk > 0) radix_threshold(key, kk, s, T, need);
-  int offset;
-  const uint32_t m = kk > 0 ? select_mask(key, T, need, s, offset) : (offset = 0, 0u);
+  uint32_t T = 0u, kept = 0u;
+  int need = 0, offset = 0;
+  if (kk > 0) {
+    radix_threshold(key, kk, s, T, need);
+    kept = select_word(key, T, need, s, offset);
+  }
   if (n_chunks == 1) {
-    emit_final(a, row, [&](int e) { return start + base + e; }, m, offset, kk);
+    emit_final(a, row, [&](int i) { return start + i; }, kept, offset, kk);
     return;
   }
-
-  // several chunks: publish this chunk's candidates, take a ticket
-  {
-    uint32_t* ck = a.cand_key + static_cast<size_t>(w) * a.k;
-    int32_t* cp = a.cand_pos + static_cast<size_t>(w) * a.k;
-    for (uint32_t r = m; r != 0u; r &= r - 1u) {
-      const int e = __builtin_ctz(r);
-      ck[offset] = key[e];
-      cp[offset] = start + base + e;
-      ++offset;
-    }
-    if (tid == 0) a.cand_cnt[w] = kk;
+  // a chunk of a split row: its candidates (key, position) in slot order,
+  // for topk_merge_kernel; the keys of the kept slots are read again (L2)
+  uint32_t* ck = a.cand_key + static_cast<size_t>(blockIdx.x) * a.k;
+  int32_t* cp = a.cand_pos + static_cast<size_t>(blockIdx.x) * a.k;
+  const float* src = a.logits + static_cast<size_t>(row) * a.max_len + start;
+  for (uint32_t r = kept; r != 0u; r &= r - 1u) {
+    const int i = 32 * tid + __builtin_ctz(r);
+    ck[offset] = score_key(src[i]);
+    cp[offset] = start + i;
+    ++offset;
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int old = atomicAdd(a.plan + p.tickets + row, 1);
-    s.last = old == n_chunks - 1;
-  }
-  __syncthreads();
-  if (!s.last) return;
-  __threadfence();
+  if (tid == 0) a.cand_cnt[blockIdx.x] = kk;
+}
 
-  // the last chunk of the row: final selection over all candidates, which
-  // are in position order (chunk order, ascending within a chunk)
+// One workgroup per row: rows of several chunks select their top-k from the
+// chunks' candidates, which are in position order (chunk order, ascending
+// within a chunk).
+__global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
+  __shared__ Lds s;
+  const TopkPlan p = topk_plan_layout(a.batch, a.max_items);
+  const int row = blockIdx.x;
+  const int n_chunks = a.plan[p.row_info + 2 * row + 1];
+  if (n_chunks == 1 || row_rejected(a, row)) return;
   const int first = a.plan[p.row_info + 2 * row];
+  const int tid = threadIdx.x;
   if (tid == 0) {
     int acc = 0;
     for (int c = 0; c < n_chunks; ++c) {
@@ -275,25 +396,34 @@ __global__ __launch_bounds__(kThreads) void topk_index_build_kernel(TopkArgs a) 
       acc += a.cand_cnt[first + c];
     }
     s.offs[n_chunks] = acc;
-    a.plan[p.tickets + row] = 0;  // ready for the next call
   }
   __syncthreads();
   const int M = s.offs[n_chunks];
-  // candidate i of the row sits in chunk c with offs[c] <= i < offs[c + 1]
+  // candidate i sits in chunk c with offs[c] <= i < offs[c + 1]
   auto cand_at = [&](int i) {
     int c = 0;
     while (c + 1 < n_chunks && s.offs[c + 1] <= i) ++c;
     return static_cast<size_t>(first + c) * a.k + (i - s.offs[c]);
   };
+  for (int i = tid; i < kBins; i += kThreads) s.hist[i] = 0u;
+  if (tid == 0) s.list_count = 0;
+  __syncthreads();
+  uint32_t key[kPer];
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
-    const int i = base + e;
+    const int i = slot_of(e);
     key[e] = i < M ? a.cand_key[cand_at(i)] : 0u;
+    if (key[e] != 0u) atomicAdd(&s.hist[key[e] >> 20], 1u);
   }
+  __syncthreads();
   const int kf = min(a.k, M);
-  if (kf > 0) radix_threshold(key, kf, s, T, need);
-  const uint32_t mf = kf > 0 ? select_mask(key, T, need, s, offset) : (offset = 0, 0u);
-  emit_final(a, row, [&](int e) { return a.cand_pos[cand_at(base + e)]; }, mf, offset, kf);
+  uint32_t T = 0u, w = 0u;
+  int need = 0, offset = 0;
+  if (kf > 0) {
+    radix_threshold(key, kf, s, T, need);
+    w = select_word(key, T, need, s, offset);
+  }
+  emit_final(a, row, [&](int i) { return a.cand_pos[cand_at(i)]; }, w, offset, kf);
 }
 
 }  // namespace
@@ -327,7 +457,10 @@ hipError_t launch_topk_index_build(const hisparse_topk_call_t& c, hipStream_t st
   a.cand_pos = ws.bytes ? reinterpret_cast<int32_t*>(base + ws.pos) : nullptr;
   a.cand_cnt = ws.bytes ? reinterpret_cast<int32_t*>(base + ws.cnt) : nullptr;
   a.err = c.error_word;
-  hipLaunchKernelGGL(topk_index_build_kernel, dim3(a.max_items), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL(topk_chunk_kernel, dim3(a.max_items), dim3(kThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.max_items == a.batch) return e;  // no row can be split
+  hipLaunchKernelGGL(topk_merge_kernel, dim3(a.batch), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

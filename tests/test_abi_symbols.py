@@ -78,13 +78,15 @@ def test_topk_sizes_and_host_validation():
     """Host-side sizes and argument checks of the top-k entry points (no
     kernel is launched: every call below is rejected before any HIP call)."""
     import math
-    for B, N in [(1, 1), (64, 32768), (128, 131072), (3, 32769), (7, 1 << 20)]:
+    for B, N, k in [(1, 1, 1), (64, 32768, 2048), (128, 131072, 2048), (3, 32769, 2048),
+                    (7, 64 * 32768, 512), (5, 30000, 30000)]:
         chunks = max(1, math.ceil(N / 32768))
-        assert binding.hisparse_topk_plan_ints(B, N) == 2 + 3 * B + 4 * B * chunks
-        ws = binding.hisparse_topk_workspace_bytes(B, N, 2048)
-        assert ws == (0 if chunks == 1 else 8 * B * chunks * 2048 + 4 * B * chunks)
+        assert binding.hisparse_topk_plan_ints(B, N) == 2 + 2 * B + 4 * B * chunks
+        ws = binding.hisparse_topk_workspace_bytes(B, N, k)
+        assert ws == (0 if chunks == 1 else 8 * B * chunks * k + 4 * B * chunks)
     assert binding.hisparse_topk_plan_ints(0, 10) == 0
-    assert binding.hisparse_topk_plan_ints(4, (1 << 20) + 1) == 0
+    assert binding.hisparse_topk_workspace_bytes(4, 17 * 32768, 2048) == 0   # 17 x 2048 > 32768
+    assert binding.hisparse_topk_workspace_bytes(4, 65 * 32768, 16) == 0     # 65 chunks
     assert binding.hisparse_topk_plan(4, 100, None, None, 100, None) == binding.HISPARSE_E_INVAL
     c = binding.HisparseTopkCall(batch=2, max_len=100, k=0)
     assert binding.hisparse_topk_index_build(c, None) == binding.HISPARSE_E_INVAL

@@ -53,9 +53,6 @@ def run(logits, seq_lens, k, mode="none", page_table=None, page_size=1, row_offs
         if mode != "none":
             assert np.array_equal(locs.cpu().numpy(), ref_locs)
         assert b.error_flags() == ref_err
-    # the tickets are back at 0 after every call
-    info = b.plan_buf.cpu().numpy()
-    assert np.all(info[-B:] == 0)
     return b
 
 
@@ -125,7 +122,7 @@ def test_full_size(B, N):
 
 def test_rejects_bad_arguments():
     with pytest.raises(binding.HiSparseError) as e:
-        binding.TopkIndexBuilder(4, 1 << 21, 16, device=DEV)
+        binding.TopkIndexBuilder(4, 17 * 32768, 2048, device=DEV)  # 17 chunks x 2048 > 32768
     assert e.value.code == binding.HISPARSE_E_UNSUPPORTED
     b = binding.TopkIndexBuilder(2, 70000, 4096, device=DEV)   # 3 chunks x 4096 <= 32768: ok
     idx = torch.empty((2, 4096), dtype=torch.int32, device=DEV)

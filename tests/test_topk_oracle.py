@@ -126,7 +126,7 @@ def test_plan_closed_forms_and_tiling():
         # chunks tile [0, s) in order, each at most the threshold, none empty when s > 0
         assert rows[0, 2] == 0 and int(rows[:, 3].sum()) == s
         assert np.all(rows[1:, 2] == rows[:-1, 2] + rows[:-1, 3])
-        assert np.all(rows[:, 3] <= tk.CHUNK)
+        assert np.all(rows[:, 3] <= tk.SPLIT)
         if s > 0:
             assert np.all(rows[:, 3] > 0)
     assert len(items) == int(info[:, 1].sum())
