@@ -261,7 +261,8 @@ int hisparse_copy_planned(hisparse_state_t st, int32_t layer_id, int32_t batch,
  * decoded from the KV row of location i in layer `layer_id`'s hot buffer.
  * Row formats by item_size_bytes: 1152 = 576 bf16; 656 = 512 fp8 e4m3fn
  * latent, 4 fp32 scales (one per 128 latent dims), 64 bf16 rope.  Other
- * item sizes: HISPARSE_E_UNSUPPORTED.
+ * item sizes, and a layer's hot buffer of 2 GiB or more (rows are addressed
+ * by 32-bit offsets): HISPARSE_E_UNSUPPORTED.
  *
  *   q           bf16 [batch][num_heads][576] (device).
  *   locs        int32 [batch][n_locs]: token mode, device rows as returned in

@@ -464,7 +464,7 @@ int hisparse_sparse_mla_decode(hisparse_state_t st, int32_t layer_id, int32_t ba
   if (page != (page_table != nullptr)) return HISPARSE_E_INVAL;
   if (n_locs > mla_max_locations()) return HISPARSE_E_UNSUPPORTED;
   const int64_t kv_rows = static_cast<int64_t>(st->cfg.max_requests) * st->rows * st->cfg.page_size;
-  if (kv_rows >= (int64_t{1} << 31)) return HISPARSE_E_UNSUPPORTED;
+  if (kv_rows * I >= (int64_t{1} << 31)) return HISPARSE_E_UNSUPPORTED;  // 32-bit buffer offsets
   if (workspace_bytes < mla_workspace_bytes(batch, num_heads, n_locs, st->num_cus) ||
       (workspace_bytes > 0 && workspace == nullptr))
     return HISPARSE_E_INVAL;

@@ -24,6 +24,8 @@
 // With heads as the N dimension every lane's accumulators belong to one head,
 // so the online-softmax rescale is a per-lane scalar, and the C layout of S^T
 // is directly the B operand of the P.V product.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace hisparse {
@@ -74,11 +76,6 @@ constexpr int kRawBytes = kRawInstr * kWave * 16;                      // 21504
 constexpr int kStageBytes = (2 * kTileBytes > kTileBytes + 2 * kRawBytes)
                                 ? 2 * kTileBytes : kTileBytes + 2 * kRawBytes;
 
-// Source of the loads of rows that are absent (padding, skipped locations,
-// the tail of the last tile): zeros, so that their zero weights meet zero
-// values rather than whatever the hot buffer holds.
-__device__ __attribute__((aligned(256))) uint8_t g_zero_row[2 * kDim];
-
 struct MlaArgs {
   const uint16_t* q;          // bf16 bits [B][Hq][576]
   const int32_t* locs;        // [B][n_locs]
@@ -124,45 +121,53 @@ __device__ __forceinline__ int64_t token_row(const MlaArgs& a, int b, int32_t lo
   return row < a.kv_rows ? row : -1;
 }
 
-// Issues this wave's share of the global->LDS loads of tile rows
-// [t0, t0 + 32): instruction i fills slots 64i .. 64i + 63 of the buffer, lane
-// l slot 64i + l.  All row numbers are read from LDS before the first load is
-// issued (one wait, not one per instruction).  Returns the tile's valid-row
-// mask (bit t: row t0 + t exists and is present).
+// This wave's share of the loads of tile rows [t0, t0 + 32) straight into
+// LDS (buffer loads with the LDS bit, 16 bytes per lane): instruction i
+// fills slots 64i .. 64i + 63 of the buffer, lane l slot 64i + l.  `rowoff`
+// holds each location's byte offset in the hot buffer, or kAbsent (padding,
+// skipped locations, and the table's tail past the last location); the
+// bf16 pitch pad adds kAbsent too.  Offsets of 2^31 and above fail the
+// buffer range check and read zeros, so absent rows meet their zero weights
+// with zero values.  (A pad slot of an absent row wraps to a small offset
+// and loads harmless bytes that nothing reads.)  All loads of the next tile
+// are issued right after the phase barrier: interleaved with the QK LDS
+// reads they would make the compiler wait for them before each read.
+constexpr uint32_t kAbsent = 0x80000000u;  // beyond every hot buffer (< 2 GiB)
+
 template <int kSlots, int kInstr>
-__device__ __forceinline__ uint32_t load_tile(const MlaArgs& a, const int32_t* rows, int nrows,
-                                              int t0, uint8_t* buf, int wave, int lane) {
-  constexpr int row_bytes = kSlots == kFp8Slots ? kFp8Row : 2 * kDim;
-  constexpr int kPerWave = (kInstr + kWaves - 1) / kWaves;
-  // Opaque copy of the lane index: keeps the (tile-invariant) per-slot
-  // address math here instead of letting it be hoisted out of the tile loop
-  // into dozens of live registers.
-  int ln = lane;
-  asm volatile("" : "+v"(ln));
-  int row[kPerWave];
+struct TileLoader {
+  static constexpr int kRowBytes = kSlots == kFp8Slots ? kFp8Row : 2 * kDim;
+  static constexpr int kPerWave = (kInstr + kWaves - 1) / kWaves;
+  uint32_t off[kPerWave];
+  uint8_t* buf;
+
+  // Offsets of this wave's loads of tile rows [t0, t0 + 32) into `dst`
+  // (rowoff reads only); returns the tile's valid-row mask.
+  __device__ __forceinline__ uint32_t prepare(const uint32_t* rowoff, int t0, uint8_t* dst,
+                                              int wave, int lane) {
+    buf = dst;
 #pragma unroll
-  for (int k = 0; k < kPerWave; ++k) {
-    const int r = (kWave * (wave + kWaves * k) + ln) / kSlots;
-    row[k] = (r < kTile && t0 + r < nrows) ? rows[t0 + r] : -1;
-  }
-  const int own = t0 + (ln & (kTile - 1));
-  const bool present = ln < kTile && own < nrows && rows[min(own, nrows - 1)] >= 0;
-#pragma unroll
-  for (int k = 0; k < kPerWave; ++k) {
-    const int i = wave + kWaves * k;
-    if (i < kInstr) {
-      const int s = kWave * i + ln;
-      const int c = s - (s / kSlots) * kSlots;
-      // slots past a row's bytes (the bf16 pitch pad) read zeros
-      const int cc = min(c, row_bytes / 16 - 1);
-      const uint8_t* src = (row[k] >= 0 && 16 * c < row_bytes)
-                               ? a.kv + static_cast<int64_t>(row[k]) * row_bytes + 16 * c
-                               : g_zero_row + 16 * cc;
-      __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(buf + i * kWave * 16), 16, 0, 0);
+    for (int k = 0; k < kPerWave; ++k) {
+      const int s = kWave * (wave + kWaves * k) + lane;
+      const int r = s / kSlots;
+      const int c = s - r * kSlots;
+      off[k] = rowoff[t0 + r] + (16 * c < kRowBytes ? 16u * c : kAbsent);
     }
+    const bool present = lane < kTile && rowoff[t0 + (lane & (kTile - 1))] != kAbsent;
+    return static_cast<uint32_t>(__ballot(present));
   }
-  return static_cast<uint32_t>(__ballot(present));
-}
+  // Load k of this wave.
+  __device__ __forceinline__ void fire(__amdgpu_buffer_rsrc_t kv, int k, int wave) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kv, (LDS_AS void*)(buf + (wave + kWaves * k) * kWave * 16),
+                                             16, off[k], 0, 0, 0);
+  }
+  // The loads from k0 on that this wave has.
+  __device__ __forceinline__ void fire_rest(__amdgpu_buffer_rsrc_t kv, int k0, int wave) {
+#pragma unroll
+    for (int k = 0; k < kPerWave; ++k)
+      if (k >= k0 && wave + kWaves * k < kInstr) fire(kv, k, wave);
+  }
+};
 
 // fp8 rows: the raw tile (codes, 4 scales, bf16 rope per row) -> bf16 tile.
 // Job j = 8 latent codes of one row (2048 jobs) or one 16-byte rope chunk
@@ -226,7 +231,7 @@ template <bool fp8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode(MlaArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t stage[kStageBytes];
-  __shared__ int32_t rows[kMaxPerSplit];
+  __shared__ uint32_t rowoff[kMaxPerSplit + kTile + 1];  // byte offset of each location's row
   __shared__ int32_t restart_at[2];
 
   // XCD-aware mapping: the head groups of one (row, split) unit run on the
@@ -245,16 +250,22 @@ void mla_decode(MlaArgs a) {
   const int tid = threadIdx.x;
   if (tid < 2) restart_at[tid] = -2;
 
-  // rows of this split's locations (-1 = skipped)
-  for (int t = tid; t < nrows; t += kThreads) {
-    const int32_t loc = a.locs[static_cast<size_t>(b) * a.n_locs + t_begin + t];
-    const int64_t row = token_row(a, b, loc);
-    if (row < 0 && loc >= 0) raise_error(a.err, HISPARSE_ERR_BAD_INDEX);
-    rows[t] = static_cast<int32_t>(row);
+  // byte offsets of this split's rows (kAbsent = skipped), padded with
+  // kAbsent up to one tile past the last one
+  const int padded = (nrows + kTile - 1) / kTile * kTile + kTile + 1;
+  for (int t = tid; t < padded; t += kThreads) {
+    uint32_t off = kAbsent;
+    if (t < nrows) {
+      const int32_t loc = a.locs[static_cast<size_t>(b) * a.n_locs + t_begin + t];
+      const int64_t row = token_row(a, b, loc);
+      if (row < 0 && loc >= 0) raise_error(a.err, HISPARSE_ERR_BAD_INDEX);
+      if (row >= 0) off = static_cast<uint32_t>(row) * static_cast<uint32_t>(a.item_bytes);
+    }
+    rowoff[t] = off;
   }
 
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: scalar branches
   const int g = lane >> 4;       // lane group
   const int n = lane & 15;       // head within a block / row within a 16-row tile
 
@@ -285,17 +296,20 @@ void mla_decode(MlaArgs a) {
 
   // buffers: bf16 rows -> tiles at stage + {0, kTileBytes};
   //          fp8 rows  -> tile at stage, raw tiles at stage + kTileBytes + {0, kRawBytes}
-  auto issue = [&](int it, int buf) -> uint32_t {
-    const int t0 = it * kTile;
-    if constexpr (fp8)
-      return load_tile<kFp8Slots, kRawInstr>(a, rows, nrows, t0,
-                                             stage + kTileBytes + buf * kRawBytes, wave, lane);
-    else
-      return load_tile<kRowSlots, kTileInstr>(a, rows, nrows, t0, stage + buf * kTileBytes, wave,
-                                              lane);
+  const __amdgpu_buffer_rsrc_t kv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.kv), 0, static_cast<int>(a.kv_rows * a.item_bytes), 0x00020000);
+  using Loader = std::conditional_t<fp8, TileLoader<kFp8Slots, kRawInstr>,
+                                    TileLoader<kRowSlots, kTileInstr>>;
+  Loader ld;
+  auto dst = [&](int buf) {
+    return fp8 ? stage + kTileBytes + buf * kRawBytes : stage + buf * kTileBytes;
   };
   const int ntiles = (nrows + kTile - 1) / kTile;
-  uint32_t valid_next = ntiles > 0 ? issue(0, 0) : 0u;  // valid rows of the tile in flight
+  uint32_t valid_next = 0u;  // valid rows of the tile in flight
+  if (ntiles > 0) {
+    valid_next = ld.prepare(rowoff, 0, dst(0), wave, lane);
+    ld.fire_rest(kv, 0, wave);
+  }
   // The weights are exp2(s - m_ref) with m_ref fixed per head at the first
   // tile's maximum, so the accumulators are never rescaled (they sit in
   // AGPRs, where a read-modify-write would cost more than the whole tile).
@@ -315,7 +329,10 @@ void mla_decode(MlaArgs a) {
     const bool replay = restart_at[cur ^ 1] == phase - 1;
     const int next = replay ? 0 : it + 1;
     const uint32_t valid = valid_next;  // bit t: row t of this tile is present
-    if (next < ntiles) valid_next = issue(next, cur ^ 1);
+    // loads of the next tile (past the last tile: all absent, harmless zeros
+    // into the idle buffer)
+    valid_next = ld.prepare(rowoff, next * kTile, dst(cur ^ 1), wave, lane);
+    ld.fire_rest(kv, 0, wave);
     const uint16_t* tile;
     if constexpr (fp8) {
       dequant_tile(stage + kTileBytes + cur * kRawBytes, reinterpret_cast<uint16_t*>(stage));
@@ -364,6 +381,7 @@ void mla_decode(MlaArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
 
+
     // weights per head block; lane holds tokens 4g+i and 16+4g+i
     bf16x8 pop[2];
     bool restart = false;
@@ -389,7 +407,7 @@ void mla_decode(MlaArgs a) {
       u16x8 pbits;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float p = exp2f(sc[i] - mr);
+        const float p = __builtin_amdgcn_exp2f(sc[i] - mr);  // v_exp_f32; tiny -> 0
         const uint16_t pb = bf16_bits(p);
         pbits[i] = pb;
         psum += __builtin_bit_cast(float, static_cast<uint32_t>(pb) << 16);
