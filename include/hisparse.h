@@ -275,6 +275,7 @@ int hisparse_copy_planned(hisparse_state_t st, int32_t layer_id, int32_t batch,
  *   workspace   device scratch of at least
  *               hisparse_sparse_mla_workspace_bytes(st, batch, num_heads,
  *               n_locs) bytes (split partials), NULL when that is 0.
+ * softmax_scale must be positive and finite (else HISPARSE_E_INVAL).
  * Computes in bf16 MFMA with fp32 accumulation; the softmax weights are
  * rounded to bf16 before the weighted sum.  Enqueued on `stream`; allocates
  * nothing.  Errors: HISPARSE_E_INVAL, HISPARSE_E_UNSUPPORTED, HISPARSE_E_HIP.

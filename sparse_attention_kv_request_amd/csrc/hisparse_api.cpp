@@ -5,6 +5,7 @@
 // the host; this keeps the pages' stream-ordering lesson (PR #20343 summary,
 // "Review highlights": an overlap race fixed by a stream wait) structural --
 // there is no side stream to wait for.
+#include <cmath>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -456,6 +457,7 @@ int hisparse_sparse_mla_decode(hisparse_state_t st, int32_t layer_id, int32_t ba
                                size_t workspace_bytes, void* stream) {
   if (st == nullptr || layer_id < 0 || layer_id >= st->cfg.num_layers) return HISPARSE_E_INVAL;
   if (batch < 0 || num_heads < 1 || num_heads > 1024 || n_locs < 1) return HISPARSE_E_INVAL;
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return HISPARSE_E_INVAL;
   if (batch == 0) return HISPARSE_OK;
   if (q == nullptr || locs == nullptr || out == nullptr) return HISPARSE_E_INVAL;
   const int I = st->cfg.item_size_bytes;

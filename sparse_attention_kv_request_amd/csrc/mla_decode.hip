@@ -382,32 +382,41 @@ void mla_decode(MlaArgs a) {
     }
 
 
-    // weights per head block; lane holds tokens 4g+i and 16+4g+i
+    // weights per head block; lane holds tokens 4g+i and 16+4g+i.  The
+    // maximum is taken over the unscaled scores (the scale is positive) and
+    // the scale folds into one FMA in front of the exponential; a tile whose
+    // rows are all present skips the per-score masking.
+    const bool full = valid == 0xFFFFFFFFu;
     bf16x8 pop[2];
     bool restart = false;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      float sc[8];
-      float tmax = -INFINITY;
+      float raw[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int tok = (i < 4 ? 0 : 16) + 4 * g + (i & 3);
-        const float v = (valid >> tok) & 1u ? s[hb][i >> 2][i & 3] * a.scale_log2 : -INFINITY;
-        sc[i] = v;
-        tmax = fmaxf(tmax, v);
+      for (int i = 0; i < 8; ++i) raw[i] = s[hb][i >> 2][i & 3];
+      if (!full) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int tok = (i < 4 ? 0 : 16) + 4 * g + (i & 3);
+          if (!((valid >> tok) & 1u)) raw[i] = -INFINITY;
+        }
       }
-      tmax = fmaxf(tmax, xor16(tmax));
-      tmax = fmaxf(tmax, xor32(tmax));
+      float rmax = fmaxf(fmaxf(fmaxf(raw[0], raw[1]), fmaxf(raw[2], raw[3])),
+                         fmaxf(fmaxf(raw[4], raw[5]), fmaxf(raw[6], raw[7])));
+      rmax = fmaxf(rmax, xor16(rmax));
+      rmax = fmaxf(rmax, xor32(rmax));
+      const float tmax = rmax * a.scale_log2;
       const bool beyond = tmax > m_ref[hb] + kRefSlack;
       restart |= beyond && m_ref[hb] != -INFINITY;
       if (beyond) m_ref[hb] = tmax;
-      // no reference yet means no valid row yet: every sc is -inf, every p 0
+      // no reference yet means no valid row yet: every score is -inf, every p 0
       const float mr = m_ref[hb] == -INFINITY ? 0.f : m_ref[hb];
       float psum = 0.f;
       u16x8 pbits;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float p = __builtin_amdgcn_exp2f(sc[i] - mr);  // v_exp_f32; tiny -> 0
+        // v_exp_f32: results below the smallest normal flush to 0
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(raw[i], a.scale_log2, -mr));
         const uint16_t pb = bf16_bits(p);
         pbits[i] = pb;
         psum += __builtin_bit_cast(float, static_cast<uint32_t>(pb) << 16);

@@ -166,6 +166,11 @@ def test_mla_rejects_bad_arguments():
         with pytest.raises(binding.HiSparseError) as e:
             st.sparse_mla_decode(0, q, locs, out)              # 48-byte rows: no MLA layout
         assert e.value.code == binding.HISPARSE_E_UNSUPPORTED
+        for bad_scale in (0.0, -0.5, float("inf"), float("nan")):
+            rc = binding.hisparse_sparse_mla_decode(st.handle, 0, 1, 16, 8, q.data_ptr(),
+                                                    locs.data_ptr(), None, bad_scale,
+                                                    out.data_ptr(), None, None, 0, None)
+            assert rc == binding.HISPARSE_E_INVAL
     finally:
         st.close()
         host.free()
