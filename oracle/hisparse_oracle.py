@@ -39,6 +39,10 @@ R6  CLOCK: ref <- 1 on hit and on insert; the hand starts at 0, walks slots in
 R7  multi-step overflow (more misses than unpinned slots): admit the misses
     with the largest last step, ties by first occurrence; the rest go to
     per-request scratch rows H, H+1, ... and are not inserted in the map.
+    Two variants of the priority, for comparing admission policies (the
+    pages call admission under overflow approximate and name no rule):
+    "frequent" = the number of steps naming the key, "first" = none (first
+    occurrence alone).  R7 proper is "recent", the default.
 R8  duplicates inside a call resolve to one row and count as one miss.
 R9  -1 is padding (output -1, no error); any other index outside
     [0, seq_len) outputs -1 and raises the bad-index error bit.
@@ -158,15 +162,31 @@ def clock_sweep(inst: CacheInstance, count: int, pinned: set):
     return victims
 
 
-def clock_admit(inst: CacheInstance, working_set, last_step):
+ADMISSION = ("recent", "frequent", "first")
+
+
+def admission_priority(steps: set, admission: str) -> int:
+    """R7 and its variants: the priority of a missing key under overflow
+    (higher is admitted first; ties by first occurrence)."""
+    if admission == "recent":
+        return max(steps)
+    if admission == "frequent":
+        return len(steps)
+    if admission == "first":
+        return 0
+    raise ValueError(admission)
+
+
+def clock_admit(inst: CacheInstance, working_set, steps_of, admission="recent"):
     """Resolve one multi-step call's working set under CLOCK.
 
     PR #32162 report, "Implementation breakdown" item 1 and "Risks and impact".
     ``working_set``: distinct keys in first-occurrence order over the
-    step-major flattened ``[steps, top_k]`` rows; ``last_step[key]``: the last
-    step the key appears in.  Returns ``(placed, overflow)`` where ``placed``
-    lists ``(key, slot, evicted)`` in admission order and ``overflow`` lists
-    the keys sent to scratch rows (R7), in first-occurrence order.
+    step-major flattened ``[steps, top_k]`` rows; ``steps_of[key]``: the set
+    of steps the key appears in.  Returns ``(placed, overflow)`` where
+    ``placed`` lists ``(key, slot, evicted)`` in admission order and
+    ``overflow`` lists the keys sent to scratch rows (R7), in first-occurrence
+    order.
     """
     hot = inst.hot
     hits = [k for k in working_set if k in inst.key_slot]
@@ -178,7 +198,8 @@ def clock_admit(inst: CacheInstance, working_set, last_step):
     if len(misses) <= capacity:
         admitted, overflow = misses, []
     else:                                             # R7
-        rank = sorted(range(len(misses)), key=lambda j: (-last_step[misses[j]], j))
+        rank = sorted(range(len(misses)),
+                      key=lambda j: (-admission_priority(steps_of[misses[j]], admission), j))
         keep = set(rank[:capacity])
         admitted = [k for j, k in enumerate(misses) if j in keep]
         overflow = [k for j, k in enumerate(misses) if j not in keep]
@@ -205,9 +226,13 @@ class OracleState:
     """
 
     def __init__(self, *, max_requests, num_layers, hot, top_k, item_bytes,
-                 max_seq_len, max_steps=1, page_size=1, policy="lru", host_kv=None):
+                 max_seq_len, max_steps=1, page_size=1, policy="lru", host_kv=None,
+                 admission="recent"):
         if policy not in ("lru", "clock"):
             raise ValueError(policy)
+        if admission not in ADMISSION:
+            raise ValueError(admission)
+        self.admission = admission
         if page_size > 1 and max_seq_len % page_size:
             raise ValueError("page mode needs max_seq_len % page_size == 0 (R15)")
         self.R, self.L, self.H, self.K = max_requests, num_layers, hot, top_k
@@ -356,11 +381,11 @@ class OracleState:
             flat = topk[b].reshape(-1)                # step-major (s, i)
             entries = self._valid_entries(flat, int(seq_lens[b]))
             ws = distinct_in_first_occurrence(t for _, t in entries)
-            last_step = {}
+            steps_of = {}
             for pos, t in entries:
-                last_step[t] = pos // K                   # increasing pos: last wins
+                steps_of.setdefault(t, set()).add(pos // K)
             inst = self.instance(r, layer)
-            placed, overflow = clock_admit(inst, ws, last_step)
+            placed, overflow = clock_admit(inst, ws, steps_of, self.admission)
             for key, slot, ev in placed:
                 self._copy(layer, r, key, slot)
                 plan[b].append((r * self.N + key, r * self.rows + slot, ev))

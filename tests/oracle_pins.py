@@ -119,15 +119,16 @@ class TwoLapClock:
         self.ref = [0] * hot
         self.hand = 0
 
-    def call(self, ws, last_step):
+    def call(self, ws, priority):
+        """`priority[key]`: higher is admitted first under overflow (stable)."""
         hot = self.hot
         pinned = {self.where[k] for k in ws if k in self.where}
         for p in pinned:
             self.ref[p] = 1
         misses = [k for k in ws if k not in self.where]
         room = hot - len(pinned)
-        by_recency = sorted(misses, key=lambda k: -last_step[k])   # stable
-        admit_set = set(by_recency[:room])
+        by_priority = sorted(misses, key=lambda k: -priority[k])   # stable
+        admit_set = set(by_priority[:room])
         admitted = [k for k in misses if k in admit_set]
         overflow = [k for k in misses if k not in admit_set]
         circ = [(self.hand + d) % hot for d in range(hot)]
@@ -165,13 +166,14 @@ class TwoLapClock:
 # Helpers
 # --------------------------------------------------------------------------
 
-def make_state(ora, *, R=1, L=1, H, K, N, S=1, P=1, I=16, policy="lru", seed=0):
+def make_state(ora, *, R=1, L=1, H, K, N, S=1, P=1, I=16, policy="lru", seed=0,
+               admission="recent"):
     """Oracle state with a shadow device buffer and random host bytes."""
     rng = np.random.default_rng(seed)
     host = [rng.integers(0, 256, (R, N, I), dtype=np.uint8) for _ in range(L)]
     return ora.OracleState(max_requests=R, num_layers=L, hot=H, top_k=K, item_bytes=I,
                            max_seq_len=N, max_steps=S, page_size=P, policy=policy,
-                           host_kv=host)
+                           host_kv=host, admission=admission)
 
 
 def resident(st, req, layer):
@@ -339,8 +341,8 @@ def pin_lru_random(ora, seed=5, trials=60):
         _lru_compare_trace(ora, H, N, [[int(x) for x in row] for row in trace])
 
 
-def _clock_compare_trace(ora, H, N, S, K, trace, import_state=None):
-    st = make_state(ora, H=H, K=K, N=N, S=S, policy="clock")
+def _clock_compare_trace(ora, H, N, S, K, trace, import_state=None, admission="recent"):
+    st = make_state(ora, H=H, K=K, N=N, S=S, policy="clock", admission=admission)
     ref = TwoLapClock(H)
     if import_state is not None:
         slot_key, refbits, hand = import_state
@@ -352,15 +354,18 @@ def _clock_compare_trace(ora, H, N, S, K, trace, import_state=None):
     for call in trace:
         topk = np.asarray(call).reshape(1, S, K)
         res = checked_call(ora, st, 0, [0], [N], topk, multi=True)
-        ws, last = [], {}
+        ws, last, count = [], {}, {}
         for pos, t in enumerate(topk.reshape(-1)):
             t = int(t)
             if t < 0:
                 continue
             if t not in ws:
                 ws.append(t)
+            if last.get(t) != pos // K:        # a step counts once however often it names t
+                count[t] = count.get(t, 0) + 1
             last[t] = pos // K
-        placed, overflow = ref.call(ws, last)
+        priority = {"recent": last, "frequent": count, "first": {t: 0 for t in ws}}[admission]
+        placed, overflow = ref.call(ws, priority)
         rows = st.rows
         exp_plan = [(k, s, v) for k, s, v in placed] + \
                    [(k, H + j, EMPTY) for j, k in enumerate(overflow)]
@@ -420,6 +425,33 @@ def pin_overflow_closed_form(ora):
     assert res["plan"][0][:4] == [(8, 0, EMPTY), (9, 1, EMPTY), (10, 2, EMPTY), (11, 3, EMPTY)]
     assert res["plan"][0][4:] == [(t, 4 + t, EMPTY) for t in range(8)]
     assert res["out_locs"][0].reshape(-1).tolist() == [4, 5, 6, 7, 8, 9, 10, 11, 0, 1, 2, 3]
+
+
+def pin_admission_variants(ora, seed=11, trials=40):
+    """The admission priorities under overflow (R7 and two variants), by a
+    closed form: H = 4 empty slots; steps {0,1,2,3}, {4,5,2,3}, {6,7,4,2};
+    key 2 is named by three steps, 3 and 4 by two, 4 and 6, 7 last by step 2.
+    Then random overflowing traces against the two-lap CLOCK with the same
+    priority computed independently."""
+    H, S, K, N = 4, 3, 4, 40
+    topk = np.array([[0, 1, 2, 3], [4, 5, 2, 3], [6, 7, 4, 2]]).reshape(1, S, K)
+    expected = {"recent": ([2, 4, 6, 7], [0, 1, 3, 5]),
+                "frequent": ([0, 2, 3, 4], [1, 5, 6, 7]),
+                "first": ([0, 1, 2, 3], [4, 5, 6, 7])}
+    for admission, (admitted, overflow) in expected.items():
+        st = make_state(ora, H=H, K=K, N=N, S=S, policy="clock", admission=admission)
+        res = checked_call(ora, st, 0, [0], [N], topk, multi=True)
+        assert res["plan"][0] == [(k, j, EMPTY) for j, k in enumerate(admitted)] + \
+                                 [(k, H + j, EMPTY) for j, k in enumerate(overflow)]
+    rng = np.random.default_rng(seed)
+    for trial in range(trials):
+        H = int(rng.integers(1, 6))
+        S = int(rng.integers(2, 5))
+        K = int(rng.integers(2, 5))
+        N = int(rng.integers(H + 2, 20))
+        trace = [rng.integers(-1, N, S * K).tolist() for _ in range(8)]
+        for admission in ("frequent", "first"):
+            _clock_compare_trace(ora, H, N, S, K, trace, admission=admission)
 
 
 def pin_page_mode(ora, seed=7):
@@ -535,7 +567,8 @@ def pin_multi_request_clock(ora, seed=10):
                     assert x // st.rows == req[b]
 
 
-ALL_PINS = [pin_first_call_closed_form, pin_overflow_closed_form, pin_row_semantics,
+ALL_PINS = [pin_first_call_closed_form, pin_overflow_closed_form, pin_admission_variants,
+            pin_row_semantics,
             pin_lru_textbook_k1, pin_clock_textbook_k1, pin_repeat_and_large_cache,
             pin_page_mode, pin_layers_independent, pin_multi_request_clock,
             pin_lru_random, pin_clock_random,

@@ -50,11 +50,17 @@ MUTANTS = {
         "        inst.ref[slot] = 1                            # R6: ref set on insert",
         "        inst.ref[slot] = 0"),
     "overflow_prefers_old_steps": (
-        "key=lambda j: (-last_step[misses[j]], j)",
-        "key=lambda j: (last_step[misses[j]], j)"),
+        "key=lambda j: (-admission_priority(steps_of[misses[j]], admission), j)",
+        "key=lambda j: (admission_priority(steps_of[misses[j]], admission), j)"),
     "last_step_from_offset": (
-        "                last_step[t] = pos // K",
-        "                last_step[t] = pos % K"),
+        "                steps_of.setdefault(t, set()).add(pos // K)",
+        "                steps_of.setdefault(t, set()).add(pos % K)"),
+    "frequent_is_recent": (
+        "    if admission == \"frequent\":\n        return len(steps)",
+        "    if admission == \"frequent\":\n        return max(steps)"),
+    "first_by_last_step": (
+        "    if admission == \"first\":\n        return 0",
+        "    if admission == \"first\":\n        return -max(steps)"),
     "scratch_rows_off_by_one": (
         "self.scratch = max(0, max_steps * top_k - hot) if max_steps > 1 else 0",
         "self.scratch = max(0, max_steps * top_k - hot + 1) if max_steps > 1 else 0"),
