@@ -46,6 +46,12 @@ R7  multi-step overflow (more misses than unpinned slots): admit the misses
 R8  duplicates inside a call resolve to one row and count as one miss.
 R9  -1 is padding (output -1, no error); any other index outside
     [0, seq_len) outputs -1 and raises the bad-index error bit.
+R10 extra-page lookup (PR #32162 report, item 1: done before the hash
+    lookup; its meaning is not given): each request keeps its newest E
+    tokens on the device in a ring of E rows after its hot and scratch rows
+    (row H + X + t mod E, written by the decode, not by these calls).  An
+    entry t with seq_len - E <= t < seq_len resolves to its ring row: no
+    probe, no miss, no copy, no change to the cache state.  Token mode only.
 R11 each (request, layer) pair is an independent cache instance.
 R14 page mode with more distinct pages than hot pages: error bit, the row
     outputs -1 and the instance is left untouched.
@@ -227,19 +233,23 @@ class OracleState:
 
     def __init__(self, *, max_requests, num_layers, hot, top_k, item_bytes,
                  max_seq_len, max_steps=1, page_size=1, policy="lru", host_kv=None,
-                 admission="recent"):
+                 admission="recent", extra_rows=0):
         if policy not in ("lru", "clock"):
             raise ValueError(policy)
         if admission not in ADMISSION:
             raise ValueError(admission)
         self.admission = admission
+        if extra_rows and page_size > 1:
+            raise ValueError("the extra-row ring is token mode only (R10)")
+        self.E = extra_rows
         if page_size > 1 and max_seq_len % page_size:
             raise ValueError("page mode needs max_seq_len % page_size == 0 (R15)")
         self.R, self.L, self.H, self.K = max_requests, num_layers, hot, top_k
         self.I, self.N, self.S, self.P = item_bytes, max_seq_len, max_steps, page_size
         self.policy = policy
         self.scratch = max(0, max_steps * top_k - hot) if max_steps > 1 else 0
-        self.rows = hot + self.scratch               # device rows per request
+        self.ring = hot + self.scratch               # first extra-ring row (R10)
+        self.rows = hot + self.scratch + extra_rows  # device rows per request
         self.inst: dict[tuple[int, int], CacheInstance] = {}
         self.error_flags = 0
         self.host_kv = host_kv
@@ -269,6 +279,13 @@ class OracleState:
         if int(np.count_nonzero(np.asarray(req) == r)) > 1:
             return ERR_DUP_REQUEST
         return 0
+
+    def _split_extra(self, entries, seq_len):
+        """R10: (cached entries, extra entries) of a row's valid entries."""
+        lo = seq_len - self.E
+        if self.E == 0:
+            return entries, []
+        return [e for e in entries if e[1] < lo], [e for e in entries if e[1] >= lo]
 
     def _valid_entries(self, keys, seq_len):
         """(position, token) of the valid entries of a row (R9)."""
@@ -321,6 +338,9 @@ class OracleState:
                 continue
             r = int(req_pool_indices[b])
             entries = self._valid_entries(topk[b], int(seq_lens[b]))
+            entries, extra = self._split_extra(entries, int(seq_lens[b]))
+            for i, t in extra:
+                out[b, i] = r * self.rows + self.ring + t % self.E
             inst = self.instance(r, layer)
             if self.P == 1:
                 ws = distinct_in_first_occurrence(t for _, t in entries)
@@ -380,6 +400,9 @@ class OracleState:
             r = int(req_pool_indices[b])
             flat = topk[b].reshape(-1)                # step-major (s, i)
             entries = self._valid_entries(flat, int(seq_lens[b]))
+            entries, extra = self._split_extra(entries, int(seq_lens[b]))
+            for pos, t in extra:
+                out[b, pos // K, pos % K] = r * self.rows + self.ring + t % self.E
             ws = distinct_in_first_occurrence(t for _, t in entries)
             steps_of = {}
             for pos, t in entries:
@@ -467,8 +490,12 @@ def check_call(state: OracleState, layer, req_pool_indices, seq_lens, topk, res,
         keys = topk[b].reshape(-1)
         outs = np.asarray(res["out_locs"][b]).reshape(-1)
         sl = int(seq_lens[b])
-        valid = [(i, int(t)) for i, t in enumerate(keys) if 0 <= t < sl]
+        lo = sl - state.E if state.E else sl
+        valid = [(i, int(t)) for i, t in enumerate(keys) if 0 <= t < lo]
         assert all(outs[i] == -1 for i, t in enumerate(keys) if not (0 <= t < sl))
+        for i, t in enumerate(keys):                  # R10: the extra ring
+            if lo <= t < sl:
+                assert outs[i] == r * state.rows + state.ring + int(t) % state.E
         if state.P == 1:
             row_of = {}
             for i, t in valid:

@@ -167,13 +167,13 @@ class TwoLapClock:
 # --------------------------------------------------------------------------
 
 def make_state(ora, *, R=1, L=1, H, K, N, S=1, P=1, I=16, policy="lru", seed=0,
-               admission="recent"):
+               admission="recent", E=0):
     """Oracle state with a shadow device buffer and random host bytes."""
     rng = np.random.default_rng(seed)
     host = [rng.integers(0, 256, (R, N, I), dtype=np.uint8) for _ in range(L)]
     return ora.OracleState(max_requests=R, num_layers=L, hot=H, top_k=K, item_bytes=I,
                            max_seq_len=N, max_steps=S, page_size=P, policy=policy,
-                           host_kv=host, admission=admission)
+                           host_kv=host, admission=admission, extra_rows=E)
 
 
 def resident(st, req, layer):
@@ -454,6 +454,51 @@ def pin_admission_variants(ora, seed=11, trials=40):
             _clock_compare_trace(ora, H, N, S, K, trace, admission=admission)
 
 
+def pin_extra_ring(ora, seed=12, trials=30):
+    """Reading R10 closed form: E = 4 newest tokens in the ring after the hot
+    slots (rows 5..8 for H = 5).  With seq_len 20, tokens 16..19 are ring rows
+    5 + t % 4; the others go through the LRU as if the ring tokens were not
+    there.  Then random traces: a state with the ring and a state without,
+    fed the same rows minus their ring entries, end every call in the same
+    cache state with the same misses."""
+    H, K, N, E = 5, 6, 40, 4
+    st = make_state(ora, H=H, K=K, N=N, E=E)
+    res = checked_call(ora, st, 0, [0], [20], np.array([[0, 16, 17, 19, 3, 16]]))
+    assert res["out_locs"][0].tolist() == [0, 5, 6, 8, 1, 5]
+    assert res["miss_count"][0] == 2 and [p[:2] for p in res["plan"][0]] == [(0, 0), (3, 1)]
+    res = checked_call(ora, st, 0, [0], [24], np.array([[16, 17, 0, 21, -1, 23]]))
+    assert res["out_locs"][0].tolist() == [2, 3, 0, 6, -1, 8]
+    assert res["miss_count"][0] == 2
+    rng = np.random.default_rng(seed)
+    for trial in range(trials):
+        clock = trial % 2 == 1
+        H = int(rng.integers(2, 7))
+        S = int(rng.integers(2, 4)) if clock else 1
+        K = int(rng.integers(1, H + 1)) if not clock else int(rng.integers(1, 4))
+        N = int(rng.integers(H + 4, 30))
+        E = int(rng.integers(1, 5))
+        pol = "clock" if clock else "lru"
+        with_ring = make_state(ora, H=H, K=K, N=N, S=S, E=E, policy=pol)
+        plain = make_state(ora, H=H, K=K, N=N, S=S, policy=pol)
+        for call in range(8):
+            seq = int(rng.integers(E + 1, N + 1))
+            shape = (1, S, K) if clock else (1, K)
+            topk = rng.integers(-1, seq, shape)
+            res = checked_call(ora, with_ring, 0, [0], [seq], topk, multi=clock)
+            stripped = np.where(topk >= seq - E, -1, topk)
+            ref = checked_call(ora, plain, 0, [0], [seq], stripped, multi=clock)
+            assert res["miss_count"].tolist() == ref["miss_count"].tolist()
+            a, b = with_ring.instance(0, 0), plain.instance(0, 0)
+            assert a.slot_key == b.slot_key and a.key_slot == b.key_slot
+            ring = (topk >= seq - E) & (topk >= 0)
+            base = H + (max(0, S * K - H) if clock else 0)     # after hot and scratch rows
+            assert np.all(res["out_locs"][ring] == base + topk[ring] % E)
+            assert np.all(res["out_locs"][~ring] == np.where(
+                ref["out_locs"][~ring] >= 0,
+                ref["out_locs"][~ring] // plain.rows * with_ring.rows + ref["out_locs"][~ring] % plain.rows,
+                -1))
+
+
 def pin_page_mode(ora, seed=7):
     """Page translation: pages are the distinct t div P in ascending order,
     ``page_table`` lists their rows, ``out_locs`` = page index * P + t mod P;
@@ -568,6 +613,7 @@ def pin_multi_request_clock(ora, seed=10):
 
 
 ALL_PINS = [pin_first_call_closed_form, pin_overflow_closed_form, pin_admission_variants,
+            pin_extra_ring,
             pin_row_semantics,
             pin_lru_textbook_k1, pin_clock_textbook_k1, pin_repeat_and_large_cache,
             pin_page_mode, pin_layers_independent, pin_multi_request_clock,

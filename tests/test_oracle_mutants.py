@@ -55,6 +55,12 @@ MUTANTS = {
     "last_step_from_offset": (
         "                steps_of.setdefault(t, set()).add(pos // K)",
         "                steps_of.setdefault(t, set()).add(pos % K)"),
+    "extra_window_short": (
+        "        lo = seq_len - self.E\n",
+        "        lo = seq_len - self.E + 1\n"),
+    "extra_ring_ignores_scratch": (
+        "        self.ring = hot + self.scratch ",
+        "        self.ring = hot "),
     "frequent_is_recent": (
         "    if admission == \"frequent\":\n        return len(steps)",
         "    if admission == \"frequent\":\n        return max(steps)"),
