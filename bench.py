@@ -55,6 +55,15 @@ def parse():
     ap.add_argument("--topk", action="store_true",
                     help="time the fused top-k selection + paged index table on the "
                          "batch/sequence shape of --workload (2: 64 x 32768, 4: 128 x 131072)")
+    ap.add_argument("--hot", type=int, default=0,
+                    help="hot buffer size override (slots, or pages in page mode)")
+    ap.add_argument("--admission", default="recent", choices=["recent", "frequent", "first"],
+                    help="CLOCK admission priority under multi-step overflow")
+    ap.add_argument("--compare-admission", action="store_true",
+                    help="workload 3: also run the other two admission priorities on the "
+                         "same trace and report their misses per step")
+    ap.add_argument("--extra-rows", type=int, default=0,
+                    help="extra-row ring of the newest tokens (token mode)")
     ap.add_argument("--item", type=int, default=0,
                     help="KV row bytes for --attention (1152 bf16 or 656 fp8; default: workload's)")
     return ap.parse_args()
@@ -197,12 +206,12 @@ def traffic_from_profiles(workload):
 
 
 WORKLOAD_TEXT = {
-    1: "single-step LRU swap-in: 1 request, top_k 2048, hot 4096, 8192 host tokens x 1152 B (bf16)",
-    2: ("single-step LRU swap-in: 64 requests x 8 layers, top_k 2048, hot buffer 4096 slots, "
+    1: "single-step LRU swap-in: 1 request, top_k 2048, hot {H}, 8192 host tokens x 1152 B (bf16)",
+    2: ("single-step LRU swap-in: 64 requests x 8 layers, top_k 2048, hot buffer {H} slots, "
         "32768 host tokens x 656 B (fp8 MLA), 70% reuse + Zipf(1.1) recency"),
-    3: ("multi-step CLOCK swap-in: 64 requests, {S} MTP steps x top_k 2048, hot 4096, "
+    3: ("multi-step CLOCK swap-in: 64 requests, {S} MTP steps x top_k 2048, hot {H}, "
         "32768 host tokens x 656 B, 80% intra-call share, 60% call-to-call reuse"),
-    4: "single-step LRU swap-in: 128 requests, top_k 2048, hot 8192, 131072 host tokens x 656 B, 30% reuse",
+    4: "single-step LRU swap-in: 128 requests, top_k 2048, hot {H}, 131072 host tokens x 656 B, 30% reuse",
     5: ("page-mode LRU swap-in: 32 requests, 256-token pages, 512 clustered tokens, "
         "64 hot pages, 65536 host tokens x 656 B"),
 }
@@ -211,23 +220,29 @@ WORKLOAD_TEXT = {
 class Runner:
     """One workload on the GPU: host tier, traces, state, per-step calls."""
 
-    def __init__(self, torch, binding, workloads, w, policy=None):
+    def __init__(self, torch, binding, workloads, w, policy=None, admission="recent",
+                 extra_rows=0, share=None):
         import numpy as np
 
         self.torch, self.w = torch, w
         self.np = np
         self.dev = torch.device("cuda", 0)
         self.policy = policy or w.policy
-        t0 = time.perf_counter()
-        self.host = [binding.HostKV(w.requests, w.seq_len, w.item_bytes) for _ in range(w.layers)]
-        workloads.fill_host_kv(w, [h.array for h in self.host], threads=16)
-        log(f"host KV {w.layers} x {self.host[0].nbytes / 2**30:.2f} GiB in "
-            f"{time.perf_counter() - t0:.1f} s")
-        t0 = time.perf_counter()
-        self.trace = workloads.batch_trace(w, threads=16)     # [L, steps, B, S, K]
-        log(f"trace {self.trace.shape} in {time.perf_counter() - t0:.1f} s")
-        self.topk = torch.from_numpy(np.ascontiguousarray(
-            self.trace.transpose(1, 0, 2, 3, 4))).to(self.dev)  # [steps, L, B, S, K]
+        self.owns_host = share is None
+        if share is not None:       # same host tier and trace as another runner
+            self.host, self.trace, self.topk = share.host, share.trace, share.topk
+        else:
+            t0 = time.perf_counter()
+            self.host = [binding.HostKV(w.requests, w.seq_len, w.item_bytes)
+                         for _ in range(w.layers)]
+            workloads.fill_host_kv(w, [h.array for h in self.host], threads=16)
+            log(f"host KV {w.layers} x {self.host[0].nbytes / 2**30:.2f} GiB in "
+                f"{time.perf_counter() - t0:.1f} s")
+            t0 = time.perf_counter()
+            self.trace = workloads.batch_trace(w, threads=16)     # [L, steps, B, S, K]
+            log(f"trace {self.trace.shape} in {time.perf_counter() - t0:.1f} s")
+            self.topk = torch.from_numpy(np.ascontiguousarray(
+                self.trace.transpose(1, 0, 2, 3, 4))).to(self.dev)  # [steps, L, B, S, K]
         # per-MTP-step rows for the sequential comparator: [steps, L, S, B, K]
         self.topk_seq = (self.topk.permute(0, 1, 3, 2, 4).contiguous()
                          if self.policy != "clock" and w.num_steps > 1 else None)
@@ -239,7 +254,7 @@ class Runner:
             max_requests=w.requests, num_layers=w.layers, hot_buffer_size=w.hot,
             top_k=w.top_k, item_size_bytes=w.item_bytes, max_seq_len=w.seq_len,
             max_steps=w.num_steps if multi else 1, page_size=w.page_size, policy=self.policy,
-            host_kv=self.host)
+            host_kv=self.host, admission=admission, extra_rows=extra_rows)
         S = w.num_steps
         self.outs = [torch.empty((B, S, w.top_k) if multi else (B, w.top_k), dtype=torch.int32,
                                  device=self.dev) for _ in range(w.layers)]
@@ -290,8 +305,9 @@ class Runner:
 
     def close(self):
         self.st.close()
-        for h in self.host:
-            h.free()
+        if self.owns_host:
+            for h in self.host:
+                h.free()
 
 
 BF16_MFMA_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
@@ -453,8 +469,11 @@ def main():
     over = {"steps": W + K}
     if args.workload == 3:
         over["num_steps"] = args.num_steps
+    if args.hot:
+        over["hot"] = args.hot
     w = workloads.config(args.workload, **over)
-    run = Runner(torch, binding, workloads, w)
+    run = Runner(torch, binding, workloads, w, admission=args.admission,
+                 extra_rows=args.extra_rows)
     link = {} if args.no_link_probe else link_probes(torch, run.st, w, run.st.rows)
     if link:
         log(f"link probes {link}")
@@ -472,10 +491,14 @@ def main():
                                       dist.reshape(-1)))
     plan_kernel = {"lru": "lru_page_plan" if w.page_size > 1 else "lru_token_plan",
                    "clock": "clock_plan"}[w.policy]
-    cfg = {"workload": WORKLOAD_TEXT[args.workload].format(S=w.num_steps),
+    cfg = {"workload": WORKLOAD_TEXT[args.workload].format(S=w.num_steps, H=w.hot),
            "batch": w.batch, "layers": w.layers, "num_steps": w.num_steps, "top_k": w.top_k,
            "hot_buffer_size": w.hot, "seq_len": w.seq_len, "item_size_bytes": w.item_bytes,
            "page_size": w.page_size, "policy": w.policy}
+    if w.policy == "clock":
+        cfg["admission"] = args.admission
+    if args.extra_rows:
+        cfg["extra_rows"] = args.extra_rows
     res = {
         "metric": METRIC,
         "value": round(entries / elapsed, 1),
@@ -513,13 +536,26 @@ def main():
     }
     if args.workload == 3:
         # the per-step path the multi-step call replaces: S single-step LRU calls
-        seq_run = Runner(torch, binding, workloads, w, policy="lru")
+        seq_run = Runner(torch, binding, workloads, w, policy="lru", share=run)
         seq_elapsed, _, _ = seq_run.timed(W, K)
         seq_run.close()
         res["sequential_lru"] = {
             "ms_per_call_multistep": round(elapsed * 1e3 / (K * w.layers), 4),
             "ms_per_call_sequential": round(seq_elapsed * 1e3 / (K * w.layers), 4),
             "latency_reduction": round(1 - elapsed / seq_elapsed, 4)}
+    if args.compare_admission and w.policy == "clock":
+        cmp = {args.admission: {"misses_per_step": int(m.sum()) // K,
+                                "ms_per_step": round(elapsed * 1e3 / K, 4)}}
+        for adm in ("recent", "frequent", "first"):
+            if adm in cmp:
+                continue
+            other = Runner(torch, binding, workloads, w, admission=adm,
+                           extra_rows=args.extra_rows, share=run)
+            o_el, _, o_m = other.timed(W, K)
+            other.close()
+            cmp[adm] = {"misses_per_step": int(o_m.sum()) // K,
+                        "ms_per_step": round(o_el * 1e3 / K, 4)}
+        res["admission_compare"] = cmp
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
         res["cpu_baseline"] = cpu_baseline(w, run.host, run.trace, args.cpu_seconds)

@@ -68,6 +68,13 @@ extern "C" {
 #define HISPARSE_POLICY_LRU 0   /* single-step calls (PR #20343 summary) */
 #define HISPARSE_POLICY_CLOCK 1 /* multi-step calls (PR #32162 report, item 1) */
 
+/* Which misses a multi-step call admits when they outnumber the unpinned
+ * slots (PR #32162 report, "Risks and impact": admission is approximate under
+ * overflow; the pages name no rule).  Ties go to the first occurrence. */
+#define HISPARSE_ADMIT_RECENT 0   /* latest step naming the key first (default) */
+#define HISPARSE_ADMIT_FREQUENT 1 /* most steps naming the key first */
+#define HISPARSE_ADMIT_FIRST 2    /* first occurrence alone */
+
 /* Limits of this build. */
 #define HISPARSE_MAX_HOT 32768        /* hot_buffer_size bound (PR #32162, "Risks and impact") */
 #define HISPARSE_MIN_STEPS 2          /* multi-step range (PR #32162, item 2) */
@@ -104,10 +111,22 @@ typedef struct hisparse_state* hisparse_state_t;
  *                    buffer).  Owned by the caller; must outlive the state and
  *                    every enqueued call.
  *   dev_kv           host array of L device pointers; layer l's hot KV
- *                    buffer: token mode [R][H + X][I] bytes with
+ *                    buffer: token mode [R][H + X + E][I] bytes with
  *                    X = max(0, max_steps*K - H) scratch rows for CLOCK states
- *                    (0 for LRU); page mode [R][H][P][I] bytes.  Owned by the
- *                    caller (for example torch tensors).
+ *                    (0 for LRU) and E extra rows; page mode [R][H][P][I]
+ *                    bytes.  Owned by the caller (for example torch tensors).
+ *   admission        HISPARSE_ADMIT_*: which misses of a multi-step call
+ *                    take hot slots when they outnumber the unpinned slots
+ *                    (CLOCK states; ignored for LRU).  Zero-initialised
+ *                    configs get HISPARSE_ADMIT_RECENT.
+ *   extra_rows       E >= 0, token mode only: the extra-page lookup (PR
+ *                    #32162 report, item 1, before the hash lookup).  Each
+ *                    request keeps its newest E tokens on the device in a ring
+ *                    of E rows after its hot and scratch rows: token t lives
+ *                    in row H + X + t % E, written by the caller's decode, never
+ *                    by this library.  A top-k entry t with seq_len - E <= t <
+ *                    seq_len resolves to its ring row: no probe, no miss, no
+ *                    copy, no change to the cache state.
  */
 typedef struct hisparse_config {
   int32_t max_requests;
@@ -122,6 +141,8 @@ typedef struct hisparse_config {
   int32_t max_batch;
   const void* const* host_kv;
   void* const* dev_kv;
+  int32_t admission;
+  int32_t extra_rows;
 } hisparse_config_t;
 
 /*
@@ -130,7 +151,7 @@ typedef struct hisparse_config {
  * prefetch replay path).  Arrays are device int32 [batch][capacity]; row b's
  * first miss_count[b] entries are written, the rest are left untouched.
  *   miss_src  host row copied: r*N + t (token mode) or host page r*(N/P) + p.
- *   miss_dst  device row written: r*(H+X) + slot, or r*H + page slot.
+ *   miss_dst  device row written: r*(H+X+E) + slot, or r*H + page slot.
  *   victim    key (token or page) evicted from that slot, or -1.
  * capacity must be >= hisparse_plan_capacity(state).
  */
@@ -149,9 +170,11 @@ typedef struct hisparse_profile {
 } hisparse_profile_t;
 
 /*
- * Device rows per request of a layer's hot KV buffer for `cfg`: H + X in
+ * Device rows per request of a layer's hot KV buffer for `cfg`: H + X + E in
  * token mode, H in page mode (each row then holds P*I bytes).  Returns a
- * negative HISPARSE_E_* code when `cfg` is invalid.
+ * negative HISPARSE_E_* code when `cfg` is invalid (E_INVAL for an admission
+ * outside HISPARSE_ADMIT_* or extra_rows outside [0, N]; E_UNSUPPORTED for
+ * extra_rows > 0 in page mode).
  */
 int64_t hisparse_device_rows_per_request(const hisparse_config_t* cfg);
 
@@ -180,7 +203,9 @@ void hisparse_state_destroy(hisparse_state_t st);
  *   seq_lens          int32 [batch]: valid token range [0, seq_len) per row.
  *   topk_indices      int32 [batch][K]: token indices; -1 is padding.
  *   out_locs          int32 [batch][K], written:
- *                       token mode: device row r*(H+X) + slot of the token;
+ *                       token mode: device row r*(H+X+E) + slot of the token,
+ *                       or r*(H+X+E) + H + X + t % E for a token t among the
+ *                       newest E (extra_rows);
  *                       page mode: j*P + (t mod P), j = index of the token's
  *                       page among the row's distinct pages (ascending);
  *                       -1 for padding, invalid entries and rejected rows.
@@ -215,7 +240,8 @@ int hisparse_swap_in_selected(hisparse_state_t st, int32_t layer_id, int32_t bat
  *   num_steps     S, 2..max_steps.
  *   topk_indices  int32 [batch][S][K]; -1 is padding.
  *   out_locs      int32 [batch][S][K], written: device row of each token, a
- *                 hot slot or, on overflow, a scratch row r*(H+X) + H + j.
+ *                 hot slot, on overflow a scratch row r*(H+X+E) + H + j, or
+ *                 a ring row r*(H+X+E) + H + X + t % E for the newest E tokens.
  *   miss_count    int32 [batch]: distinct missing tokens over all S steps.
  *   plan          NULL or a miss plan; admitted misses first, then scratch.
  *
@@ -223,8 +249,9 @@ int hisparse_swap_in_selected(hisparse_state_t st, int32_t layer_id, int32_t bat
  * resolve to one row and one copy.  Resident keys of the call are pinned;
  * victims come from a CLOCK sweep (reference bit set on hit and insert, hand
  * persists per instance, stops after the last victim).  When the misses
- * exceed the unpinned slots, the misses seen in the latest steps are admitted
- * and the rest are copied to scratch rows without entering the cache (the
+ * exceed the unpinned slots, the misses ranked first by the state's admission
+ * priority (default: seen in the latest steps) are admitted and the rest are
+ * copied to scratch rows without entering the cache (the
  * pages call this admission approximate; the data of the call stays exact).
  * Row rejection rules and errors as for hisparse_swap_in_selected.
  */

@@ -47,7 +47,7 @@ class HisparseConfig(ctypes.Structure):
         ("top_k", c_i32), ("max_steps", c_i32), ("page_size", c_i32),
         ("item_size_bytes", c_i32), ("max_seq_len", c_i32), ("policy", c_i32),
         ("max_batch", c_i32), ("host_kv", ctypes.POINTER(c_vp)),
-        ("dev_kv", ctypes.POINTER(c_vp)),
+        ("dev_kv", ctypes.POINTER(c_vp)), ("admission", c_i32), ("extra_rows", c_i32),
     ]
 
 
@@ -66,6 +66,7 @@ class HisparseTopkCall(ctypes.Structure):
 
 
 INDEX_MODE = {"none": 0, "paged": 1, "ragged": 2}
+ADMISSION = {"recent": 0, "frequent": 1, "first": 2}
 TOPK_CHUNK = 32768
 
 
@@ -306,17 +307,20 @@ class HiSparseState:
 
     def __init__(self, *, max_requests, num_layers, hot_buffer_size, top_k, item_size_bytes,
                  max_seq_len, host_kv, max_steps=1, page_size=1, policy="lru",
-                 max_batch=None, dev_kv=None, stream=None):
+                 max_batch=None, dev_kv=None, stream=None, admission="recent", extra_rows=0):
         self.cfg = HisparseConfig(
             max_requests=max_requests, num_layers=num_layers, hot_buffer_size=hot_buffer_size,
             top_k=top_k, max_steps=max_steps, page_size=page_size,
             item_size_bytes=item_size_bytes, max_seq_len=max_seq_len, policy=POLICY[policy],
-            max_batch=max_batch or max_requests)
+            max_batch=max_batch or max_requests, admission=ADMISSION[admission],
+            extra_rows=extra_rows)
         rows = hisparse_device_rows_per_request(self.cfg)
         if rows < 0:
             raise HiSparseError(rows, "hisparse_device_rows_per_request")
         self.rows = rows
         self.policy = policy
+        self.admission = admission
+        self.extra_rows = extra_rows
         self.page_size = page_size
         self.host_kv = host_kv
         unit = item_size_bytes * page_size

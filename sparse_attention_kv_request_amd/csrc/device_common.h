@@ -28,6 +28,8 @@ struct PlanArgs {
   int32_t* ctrl;        // [L*R][2]      {LRU call counter, CLOCK hand}
   uint32_t* err;        // sticky error word
   int32_t R, H, Hw, K, S, N, P, nkeys, rows, layer;
+  int32_t ext, ext_base;  // extra-row ring: E rows from row ext_base of each request
+  int32_t admission;      // HISPARSE_ADMIT_* (multi-step overflow)
   // the call
   int32_t batch;
   const int32_t* req;

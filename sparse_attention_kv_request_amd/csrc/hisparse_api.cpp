@@ -57,6 +57,10 @@ int derive(const hisparse_config_t* c, Derived* d) {
   if (c->max_seq_len < 1) return HISPARSE_E_INVAL;
   if (c->max_seq_len > HISPARSE_MAX_SEQ_LEN) return HISPARSE_E_UNSUPPORTED;
   if (c->max_batch < 1 || c->max_batch > c->max_requests) return HISPARSE_E_INVAL;
+  if (c->admission < HISPARSE_ADMIT_RECENT || c->admission > HISPARSE_ADMIT_FIRST)
+    return HISPARSE_E_INVAL;
+  if (c->extra_rows < 0 || c->extra_rows > c->max_seq_len) return HISPARSE_E_INVAL;
+  if (c->extra_rows > 0 && c->page_size > 1) return HISPARSE_E_UNSUPPORTED;
   const int64_t H = c->hot_buffer_size, K = c->top_k, P = c->page_size;
   if (lru) {
     if (c->max_steps != 1) return HISPARSE_E_INVAL;
@@ -75,7 +79,8 @@ int derive(const hisparse_config_t* c, Derived* d) {
     if (c->max_steps * K > HISPARSE_MAX_WORKING_SET) return HISPARSE_E_UNSUPPORTED;
   }
   d->scratch = clock ? static_cast<int32_t>(std::max<int64_t>(0, c->max_steps * K - H)) : 0;
-  d->rows = P > 1 ? static_cast<int32_t>(H) : static_cast<int32_t>(H + d->scratch);
+  d->rows = P > 1 ? static_cast<int32_t>(H)
+                  : static_cast<int32_t>(H + d->scratch + c->extra_rows);
   d->nkeys = P > 1 ? c->max_seq_len / c->page_size : c->max_seq_len;
   d->hw = static_cast<int32_t>((H + 31) / 32);
   d->cap = P > 1 ? static_cast<int32_t>(H) : static_cast<int32_t>(c->max_steps * K);
@@ -115,6 +120,9 @@ PlanArgs plan_args(const hisparse_state* st, int32_t layer, int32_t batch, int32
   a.P = st->cfg.page_size;
   a.nkeys = st->nkeys;
   a.rows = st->rows;
+  a.ext = st->cfg.extra_rows;
+  a.ext_base = st->rows - st->cfg.extra_rows;
+  a.admission = st->cfg.admission;
   a.layer = layer;
   a.batch = batch;
   a.req = req;

@@ -97,16 +97,21 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
   if (tid < HISPARSE_MAX_STEPS) s_cnt[tid] = 0;
   __syncthreads();
 
-  // 1. flatten [S][K] step-major; insert with the step bit
+  // 1. flatten [S][K] step-major; insert with the step bit.  Entries among
+  // the newest ext tokens resolve to their ring row (the extra-page lookup)
+  // and stay out of the working set.
   int32_t tok[EPT];
   int hpos[EPT];
+  int ring[EPT];
   bool bad_index = false;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
     const int32_t t = raw[e];
     const bool valid = t >= 0 && t < sl;
     bad_index |= (!valid && t != -1);
-    tok[e] = valid ? t : -1;
+    const bool extra = valid && t >= sl - a.ext;
+    ring[e] = extra ? a.ext_base + t % a.ext : -1;
+    tok[e] = valid && !extra ? t : -1;
     hpos[e] = 0;
   }
 #pragma unroll
@@ -140,7 +145,11 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
       hval[hpos[e]] = slot[e];
       packed += 1 << 16;
     } else {
-      last[e] = 31 - __clz(hkey[hpos[e]] >> kKeyBits);
+      // admission priority under overflow: latest step, number of steps, or none
+      const uint32_t steps = hkey[hpos[e]] >> kKeyBits;
+      last[e] = a.admission == HISPARSE_ADMIT_RECENT     ? 31 - __clz(steps)
+                : a.admission == HISPARSE_ADMIT_FREQUENT ? __popc(steps) - 1
+                                                         : 0;
       atomicAdd(&s_cnt[last[e]], 1);
       if (sw) bit_set_atomic(mbits, tok[e]);
       packed += 1;
@@ -152,7 +161,7 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
   const int nhits = tot >> 16;
   const int room = a.H - nhits;
 
-  // admitted misses: all, or (overflow) the latest last steps first
+  // admitted misses: all, or (overflow) the highest priorities first
   int ma = m;
   int sstar = -1, take_eq = 0;
   if (m > room) {
@@ -329,7 +338,7 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
   for (int e = 0; e < EPT; ++e) {
     const int i = tid * EPT + e;
     if (i >= E) continue;
-    out[i] = tok[e] >= 0 ? r * a.rows + hval[hpos[e]] : -1;
+    out[i] = tok[e] >= 0 ? r * a.rows + hval[hpos[e]] : (ring[e] >= 0 ? r * a.rows + ring[e] : -1);
   }
   if (tid == 0) {
     a.miss_count[b] = m;

@@ -181,16 +181,21 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
   for (int i = tid; i < sw; i += NT) mbits[i] = 0u;
   __syncthreads();
 
-  // 1. validate and insert every entry; the first occurrence keeps its position
+  // 1. validate and insert every entry; the first occurrence keeps its position.
+  // Entries among the newest ext tokens resolve to their ring row instead
+  // (the extra-page lookup, before the hash lookup) and stay out of the cache.
   int32_t tok[EPT];
   int hpos[EPT];
+  int ring[EPT];
   bool bad_index = false;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
     const int32_t t = raw[e];
     const bool valid = t >= 0 && t < sl;
     bad_index |= (!valid && t != -1);
-    tok[e] = valid ? t : -1;
+    const bool extra = valid && t >= sl - a.ext;
+    ring[e] = extra ? a.ext_base + t % a.ext : -1;
+    tok[e] = valid && !extra ? t : -1;
     hpos[e] = 0;
   }
 #pragma unroll
@@ -250,7 +255,7 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
   for (int e = 0; e < EPT; ++e) {
     const int i = tid * EPT + e;
     if (i >= a.K) continue;
-    int loc = -1;
+    int loc = ring[e] >= 0 ? r * a.rows + ring[e] : -1;
     if (tok[e] >= 0) {
       const int v = hval[hpos[e]];
       loc = r * a.rows + (v >= 0 ? v : vslot[-v - 1]);

@@ -36,7 +36,7 @@ def t32(x):
 
 class Pair:
     def __init__(self, *, R, L, H, K, N, I, S=1, P=1, policy="lru", seed=0, max_batch=None,
-                 shadow=True, host_fill=None):
+                 shadow=True, host_fill=None, admission="recent", extra_rows=0):
         self.R, self.L, self.H, self.K, self.N, self.I, self.S, self.P = R, L, H, K, N, I, S, P
         self.policy = policy
         rng = np.random.default_rng(seed)
@@ -49,12 +49,14 @@ class Pair:
         self.gpu = binding.HiSparseState(
             max_requests=R, num_layers=L, hot_buffer_size=H, top_k=K, item_size_bytes=I,
             max_seq_len=N, max_steps=S, page_size=P, policy=policy,
-            max_batch=max_batch or R, host_kv=self.host)
+            max_batch=max_batch or R, host_kv=self.host, admission=admission,
+            extra_rows=extra_rows)
         self.shadow = shadow
         self.cpu = ora.OracleState(
             max_requests=R, num_layers=L, hot=H, top_k=K, item_bytes=I, max_seq_len=N,
             max_steps=S, page_size=P, policy=policy,
-            host_kv=[h.array for h in self.host] if shadow else None)
+            host_kv=[h.array for h in self.host] if shadow else None,
+            admission=admission, extra_rows=extra_rows)
         self.rows = self.cpu.rows
         assert self.gpu.rows == self.rows
 

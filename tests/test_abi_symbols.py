@@ -46,6 +46,8 @@ def test_strerror_and_rows_are_host_only():
     ("hot_buffer_size", 0, -1), ("hot_buffer_size", 32769, -1), ("top_k", 101, -1),
     ("item_size_bytes", 24, -1), ("max_steps", 2, -1), ("max_batch", 5, -1),
     ("policy", 7, -1), ("top_k", 8193, -4), ("max_seq_len", 1 << 28, -4),
+    ("admission", 3, -1), ("admission", -1, -1), ("extra_rows", -1, -1),
+    ("extra_rows", 501, -1),
 ])
 def test_config_validation(field, value, code):
     cfg = binding.HisparseConfig(max_requests=4, num_layers=1, hot_buffer_size=100, top_k=60,
@@ -96,3 +98,18 @@ def test_topk_sizes_and_host_validation():
     assert binding.hisparse_topk_index_build(c, None) == binding.HISPARSE_E_UNSUPPORTED
     c.k, c.max_len = 16, 100
     assert binding.hisparse_topk_index_build(c, None) == binding.HISPARSE_E_INVAL  # NULL pointers
+
+
+def test_extra_rows_extend_the_token_rows():
+    """The extra-row ring adds E rows after the hot (and scratch) rows of a
+    token-mode request; page mode has no ring."""
+    cfg = binding.HisparseConfig(max_requests=4, num_layers=1, hot_buffer_size=100, top_k=60,
+                                 max_steps=3, page_size=1, item_size_bytes=32, max_seq_len=500,
+                                 policy=1, max_batch=4, admission=2, extra_rows=500)
+    assert binding.hisparse_device_rows_per_request(cfg) == 100 + 3 * 60 - 100 + 500
+    cfg.policy, cfg.max_steps, cfg.extra_rows = 0, 1, 7
+    assert binding.hisparse_device_rows_per_request(cfg) == 107
+    cfg = binding.HisparseConfig(max_requests=2, num_layers=1, hot_buffer_size=64, top_k=512,
+                                 max_steps=1, page_size=256, item_size_bytes=656,
+                                 max_seq_len=65536, policy=0, max_batch=2, extra_rows=1)
+    assert binding.hisparse_device_rows_per_request(cfg) == binding.HISPARSE_E_UNSUPPORTED
