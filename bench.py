@@ -181,12 +181,12 @@ def cpu_baseline(w, host, trace, budget_s):
                        f"into a shadow device buffer), {dt:.1f} s on one core")}
 
 
-COPY_SOURCES = ("copy.hip", "plan_lru.hip", "internal.h")
+COPY_SOURCES = ("copy.hip", "copy.h", "device_common.h")
 
 
 def copy_kernel_hash():
-    """Hash of the sources that decide the copy kernel's launches (the kernel,
-    its launch shape and the copy list the plan kernel writes)."""
+    """Hash of the sources the copy kernel is built from (the kernel, its
+    arguments and launch shape, and the device helpers it uses)."""
     m = hashlib.sha256()
     for name in COPY_SOURCES:
         m.update((ROOT / "sparse_attention_kv_request_amd" / "csrc" / name).read_bytes())

@@ -1,0 +1,46 @@
+// Miss copy (copy.hip): its arguments and launch shape.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace hisparse {
+
+// Launch shape of the miss copy; the macros let a build sweep other shapes.
+#ifndef HISPARSE_COPY_THREADS
+#define HISPARSE_COPY_THREADS 256
+#endif
+#ifndef HISPARSE_COPY_UNROLL
+#define HISPARSE_COPY_UNROLL 4
+#endif
+#ifndef HISPARSE_COPY_BLOCKS
+#define HISPARSE_COPY_BLOCKS 1024
+#endif
+#ifndef HISPARSE_COPY_NT_LOAD
+#define HISPARSE_COPY_NT_LOAD 0
+#endif
+
+constexpr int kCopyThreads = HISPARSE_COPY_THREADS;
+constexpr int kCopyUnroll = HISPARSE_COPY_UNROLL;  // 16-byte loads in flight per lane
+constexpr int kCopyBlocks = HISPARSE_COPY_BLOCKS;  // 4 workgroups per CU on 256 CUs
+
+// Rows of `unit_bytes` from the host tier to the hot buffer.
+struct CopyArgs {
+  const int32_t* miss_count;  // [batch]
+  const int32_t* src;         // [batch][cap] host row
+  const int32_t* dst;         // [batch][cap] device row
+  int32_t batch;
+  int32_t cap;
+  const uint8_t* host;        // device-visible address of the host tier
+  uint8_t* dev;
+  int32_t unit16;             // 16-byte chunks per row
+  int64_t unit_bytes;
+  int64_t src_rows;           // valid host rows [0, src_rows)
+  int64_t dst_rows;           // valid device rows [0, dst_rows)
+  uint32_t* err;
+};
+
+hipError_t launch_miss_copy(const CopyArgs& a, hipStream_t s);
+
+}  // namespace hisparse

@@ -12,7 +12,8 @@
 // link needs many outstanding reads), and rows land in HBM with non-temporal
 // stores.  The row of a chunk is found by a search over the per-row prefix
 // of miss counts held in LDS.
-#include "internal.h"
+#include "copy.h"
+#include "device_common.h"
 
 namespace hisparse {
 
@@ -89,40 +90,12 @@ __global__ __launch_bounds__(NT) void miss_copy(CopyArgs a) {
   }
 }
 
-__global__ __launch_bounds__(256) void reset_instances(ResetArgs a) {
-  const int r = a.reqs ? a.reqs[blockIdx.x] : static_cast<int>(blockIdx.x);
-  const int layer = blockIdx.y;
-  if (r < 0 || r >= a.R) {
-    if (threadIdx.x == 0 && layer == 0) raise_error(a.err, HISPARSE_ERR_BAD_ROW);
-    return;
-  }
-  const size_t q = static_cast<size_t>(layer) * a.R + r;
-  int16_t* ks = a.key_slot + q * a.nkeys;
-  for (int i = threadIdx.x; i < a.nkeys; i += blockDim.x) ks[i] = static_cast<int16_t>(kEmpty);
-  for (int s = threadIdx.x; s < a.H; s += blockDim.x) {
-    a.slot_key[q * a.H + s] = kEmpty;
-    if (a.ts) a.ts[q * a.H + s] = -1;
-    if (a.order) a.order[q * a.H + s] = static_cast<int16_t>(s);
-  }
-  if (a.refbits)
-    for (int w = threadIdx.x; w < a.Hw; w += blockDim.x) a.refbits[q * a.Hw + w] = 0u;
-  if (threadIdx.x == 0) {
-    a.ctrl[2 * q] = 0;
-    a.ctrl[2 * q + 1] = 0;
-  }
-}
-
 }  // namespace
 
 hipError_t launch_miss_copy(const CopyArgs& a, hipStream_t s) {
   const size_t lds = (static_cast<size_t>(a.batch) + 1) * sizeof(int);
   hipLaunchKernelGGL((miss_copy<kCopyThreads, kCopyUnroll>), dim3(kCopyBlocks),
                      dim3(kCopyThreads), lds, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_reset(const ResetArgs& a, int n, int layers, hipStream_t s) {
-  hipLaunchKernelGGL(reset_instances, dim3(n, layers), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -7,29 +7,13 @@
 #include <cstdint>
 #include <vector>
 
+#include "copy.h"
 #include "device_common.h"
 #include "hisparse.h"
 
 namespace hisparse {
 
-// Launch shape of the miss copy; the macros let a build sweep other shapes.
-#ifndef HISPARSE_COPY_THREADS
-#define HISPARSE_COPY_THREADS 256
-#endif
-#ifndef HISPARSE_COPY_UNROLL
-#define HISPARSE_COPY_UNROLL 4
-#endif
-#ifndef HISPARSE_COPY_BLOCKS
-#define HISPARSE_COPY_BLOCKS 1024
-#endif
-#ifndef HISPARSE_COPY_NT_LOAD
-#define HISPARSE_COPY_NT_LOAD 0
-#endif
-
 constexpr int kPlanThreads = 1024;  // one workgroup (16 waves) per batch row
-constexpr int kCopyThreads = HISPARSE_COPY_THREADS;
-constexpr int kCopyUnroll = HISPARSE_COPY_UNROLL;  // 16-byte loads in flight per lane
-constexpr int kCopyBlocks = HISPARSE_COPY_BLOCKS;  // 4 workgroups per CU on 256 CUs
 constexpr int kMaxPageModeHot = 4096;
 static_assert((HISPARSE_MAX_HOT + 31) / 32 <= kPlanThreads,
               "one thread per word of an H-bit mask in the plan kernels");
@@ -79,22 +63,6 @@ hipError_t launch_topk_plan(const int32_t* seq_lens, int32_t* plan, int32_t batc
                             hipStream_t st);
 hipError_t launch_topk_index_build(const hisparse_topk_call_t& c, hipStream_t st);
 
-// Miss copy: rows of `unit_bytes` from the host tier to the hot buffer.
-struct CopyArgs {
-  const int32_t* miss_count;  // [batch]
-  const int32_t* src;         // [batch][cap] host row
-  const int32_t* dst;         // [batch][cap] device row
-  int32_t batch;
-  int32_t cap;
-  const uint8_t* host;        // device-visible address of the host tier
-  uint8_t* dev;
-  int32_t unit16;             // 16-byte chunks per row
-  int64_t unit_bytes;
-  int64_t src_rows;           // valid host rows [0, src_rows)
-  int64_t dst_rows;           // valid device rows [0, dst_rows)
-  uint32_t* err;
-};
-
 struct ResetArgs {
   const int32_t* reqs;  // NULL = requests 0..n-1
   int16_t* key_slot;
@@ -136,7 +104,6 @@ size_t clock_lds_bytes(const PlanArgs& a);
 hipError_t launch_lru_token_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_lru_page_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_clock_plan(const PlanArgs& a, hipStream_t s);
-hipError_t launch_miss_copy(const CopyArgs& a, hipStream_t s);
 hipError_t launch_reset(const ResetArgs& a, int n, int layers, hipStream_t s);
 
 }  // namespace hisparse
