@@ -52,38 +52,65 @@ struct PlanArgs {
   int32_t sort_words;   // words of the LDS miss bitmap; 0 = no copy list
 };
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: four row
+// shifts inside each 16-lane row, then row 0's total broadcast into row 1
+// (and row 2's into row 3), then the low half's total into the high half.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false); // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false); // row_bcast:31
+  return x;
+}
+
 // Exclusive prefix sum over the NT threads of a workgroup.  `scratch` holds
-// NT/64 + 1 ints of LDS.  Returns the exclusive prefix; *total receives the
-// sum.  Contains barriers: every thread of the block must call it.
+// NT/64 ints of LDS.  Returns the exclusive prefix; *total receives the sum.
+// Two barriers (the second keeps `scratch` intact until every wave has read
+// it): every thread of the block must call it.
 template <int NT>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
   static_assert(NT % kWave == 0 && NT / kWave <= kWave, "block shape");
+  constexpr int kWaves = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wid = threadIdx.x / kWave;
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    int y = __shfl_up(x, d, kWave);
-    if (lane >= d) x += y;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int incl = static_cast<int>(wave_incl_scan(static_cast<uint32_t>(v)));
+  if (lane == kWave - 1) scratch[wid] = incl;
+  __syncthreads();
+  const int w = lane < kWaves ? scratch[lane] : 0;
+  const int wi = static_cast<int>(wave_incl_scan(static_cast<uint32_t>(w)));
+  const int before = wid > 0 ? __builtin_amdgcn_readlane(wi, wid - 1) : 0;
+  *total = __builtin_amdgcn_readlane(wi, kWaves - 1);
+  __syncthreads();
+  return before + incl - v;
+}
+
+// Two independent exclusive prefix sums over the workgroup in one pass (each
+// word may pack narrower fields whose sums cannot carry into each other).
+// `scratch` holds 2*NT/64 ints of LDS.  Two barriers; every thread must call it.
+template <int NT>
+__device__ __forceinline__ void block_exclusive_scan2(uint32_t x, uint32_t y, int* scratch,
+                                                      uint32_t* x_pre, uint32_t* y_pre,
+                                                      uint32_t* x_tot, uint32_t* y_tot) {
+  constexpr int kWaves = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const uint32_t xi = wave_incl_scan(x);
+  const uint32_t yi = wave_incl_scan(y);
+  uint32_t* sc = reinterpret_cast<uint32_t*>(scratch);
+  if (lane == kWave - 1) {
+    sc[wid] = xi;
+    sc[kWaves + wid] = yi;
   }
-  if (lane == kWave - 1) scratch[wid] = x;
   __syncthreads();
-  if (wid == 0) {
-    int w = lane < NT / kWave ? scratch[lane] : 0;
-    int s = w;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      int y = __shfl_up(s, d, kWave);
-      if (lane >= d) s += y;
-    }
-    if (lane < NT / kWave) scratch[lane] = s - w;
-    if (lane == NT / kWave - 1) scratch[NT / kWave] = s;
-  }
+  const uint32_t wx = wave_incl_scan(lane < kWaves ? sc[lane] : 0u);
+  const uint32_t wy = wave_incl_scan(lane < kWaves ? sc[kWaves + lane] : 0u);
+  *x_pre = (wid > 0 ? __builtin_amdgcn_readlane(wx, wid - 1) : 0u) + xi - x;
+  *y_pre = (wid > 0 ? __builtin_amdgcn_readlane(wy, wid - 1) : 0u) + yi - y;
+  *x_tot = __builtin_amdgcn_readlane(wx, kWaves - 1);
+  *y_tot = __builtin_amdgcn_readlane(wy, kWaves - 1);
   __syncthreads();
-  const int excl = scratch[wid] + x - v;
-  *total = scratch[NT / kWave];
-  __syncthreads();
-  return excl;
 }
 
 __device__ __forceinline__ bool bit_test(const uint32_t* bm, int i) {
@@ -104,8 +131,9 @@ __device__ __forceinline__ int hash_bucket(int32_t t, int size) {
 }
 
 // Inserts token t (0 <= t < 2^28 - 1) into the open-addressing LDS table
-// `keys` (0 = empty) and returns its bucket.  The table is sized above the
-// number of distinct keys, so the probe terminates.
+// `keys` (0 = empty, key + 1 in the low 28 bits) and returns its bucket.  The
+// table is sized above the number of distinct keys, so the probe terminates.
+// (One entry at a time: issuing a thread's probes together measured slower.)
 __device__ __forceinline__ int hash_insert(uint32_t* keys, int size, int32_t t) {
   const uint32_t want = static_cast<uint32_t>(t) + 1u;
   int h = hash_bucket(t, size);

@@ -112,10 +112,10 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
     const bool extra = valid && t >= sl - a.ext;
     ring[e] = extra ? a.ext_base + t % a.ext : -1;
     tok[e] = valid && !extra ? t : -1;
-    hpos[e] = 0;
   }
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
+    hpos[e] = 0;
     if (tok[e] >= 0) {
       const int i = tid * EPT + e;
       hpos[e] = hash_insert(hkey, T, tok[e]);

@@ -46,32 +46,33 @@ __device__ void reject_row(const PlanArgs& a, int b, int entries, uint32_t code,
   }
 }
 
-// Victim selection over the LRU order, commit of the m misses and rewrite of
-// the order.  `o` holds order positions tid*EPH .. tid*EPH+EPH-1.  `used` has
-// the bits of the slots hit by this call; victims are added to it.  Miss j
-// (key miss_key[j]) goes to vslot[j].
-template <int NT, int EPH>
-__device__ void lru_select_commit(const PlanArgs& a, int b, int r, int now, int m,
-                                  const int (&o)[EPH], uint32_t* used, const int32_t* miss_key,
-                                  int32_t* vslot, int* scan, int16_t* ks, int32_t* sk,
-                                  int32_t* tsq, int16_t* ord, const uint32_t* mbits,
-                                  const int32_t* mwpre, const int (&oldk)[EPH]) {
-  const int tid = threadIdx.x;
-  bool avail[EPH];
+// Order positions tid*EPH .. tid*EPH+EPH-1 (slots o[e]) that this call did
+// not use (`used` holds the hit slots), and their ranks among all such
+// positions in order.  Returns the count of this thread's available positions.
+template <int EPH>
+__device__ __forceinline__ int lru_available(const int (&o)[EPH], const uint32_t* used,
+                                             bool (&avail)[EPH]) {
   int navail = 0;
 #pragma unroll
   for (int e = 0; e < EPH; ++e) {
     avail[e] = o[e] >= 0 && !bit_test(used, o[e]);
     navail += avail[e];
   }
-  int total_avail;
-  int rk = block_exclusive_scan<NT>(navail, scan, &total_avail);
-  int rank[EPH];
-#pragma unroll
-  for (int e = 0; e < EPH; ++e) {
-    rank[e] = rk;
-    rk += avail[e];
-  }
+  return navail;
+}
+
+// Commit of the m misses into the first m available order positions and
+// rewrite of the order.  `o` holds order positions tid*EPH .. tid*EPH+EPH-1;
+// avail/rank come from lru_available and a scan over it.  `used` has the
+// bits of the slots hit by this call; victims are added to it.  Miss j (key
+// miss_key[j]) goes to vslot[j].
+template <int NT, int EPH>
+__device__ void lru_commit(const PlanArgs& a, int b, int r, int now, int m,
+                           const int (&o)[EPH], const bool (&avail)[EPH], const int (&rank)[EPH],
+                           uint32_t* used, const int32_t* miss_key, int32_t* vslot, int* scan,
+                           int16_t* ks, int32_t* sk, int32_t* tsq, int16_t* ord,
+                           const uint32_t* mbits, const int32_t* mwpre, const int (&oldk)[EPH]) {
+  const int tid = threadIdx.x;
   // commit: the owner of a victim slot replaces its key
   int32_t* msrc = a.miss_src + static_cast<size_t>(b) * a.cap;
   int32_t* mdst = a.miss_dst + static_cast<size_t>(b) * a.cap;
@@ -134,9 +135,9 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
   uint32_t* used = reinterpret_cast<uint32_t*>(hval + T);          // [Hw]
   int32_t* miss_key = reinterpret_cast<int32_t*>(used + a.Hw);     // [K]
   int32_t* vslot = miss_key + a.K;                                 // [K]
-  int* scan = vslot + a.K;                                         // [NT/64+1]
+  int* scan = vslot + a.K;                                         // [2*NT/64]
   const int sw = a.sort_words;
-  uint32_t* mbits = reinterpret_cast<uint32_t*>(scan + NT / kWave + 1);  // [sw] miss keys
+  uint32_t* mbits = reinterpret_cast<uint32_t*>(scan + 2 * NT / kWave);  // [sw] miss keys
   int32_t* mwpre = reinterpret_cast<int32_t*>(mbits + sw);              // [sw]
 
   const int b = blockIdx.x;
@@ -196,10 +197,10 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
     const bool extra = valid && t >= sl - a.ext;
     ring[e] = extra ? a.ext_base + t % a.ext : -1;
     tok[e] = valid && !extra ? t : -1;
-    hpos[e] = 0;
   }
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
+    hpos[e] = 0;
     if (tok[e] >= 0) {
       hpos[e] = hash_insert(hkey, T, tok[e]);
       atomicMin(&hval[hpos[e]], tid * EPT + e);
@@ -225,31 +226,53 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
       hval[hpos[e]] = slot[e];
     } else {
       ++nmiss;
+      if (sw) bit_set_atomic(mbits, tok[e]);
     }
   }
-  int m;
-  int j = block_exclusive_scan<NT>(nmiss, scan, &m);
+  __syncthreads();
+
+  // 3. one scan ranks the misses (position order), the available order
+  // positions (order) and the miss keys' bitmap words (key order): misses
+  // and available positions share one word (at most 8192 and 32768).
+  bool avail[EPH];
+  const int navail = lru_available<EPH>(o, used, avail);
+  const int wpt = (sw + NT - 1) / NT;
+  const int w0 = tid * wpt;
+  int nbits = 0;
+  for (int w = w0; w < w0 + wpt && w < sw; ++w) nbits += __popc(mbits[w]);
+  uint32_t x_pre, y_pre, x_tot, y_tot;
+  block_exclusive_scan2<NT>(static_cast<uint32_t>(nmiss) | (static_cast<uint32_t>(navail) << 16),
+                            static_cast<uint32_t>(nbits), scan, &x_pre, &y_pre, &x_tot, &y_tot);
+  const int m = static_cast<int>(x_tot & 0xffffu);
+  int j = static_cast<int>(x_pre & 0xffffu);
+  int rank[EPH];
+  int rk = static_cast<int>(x_pre >> 16);
+#pragma unroll
+  for (int e = 0; e < EPH; ++e) {
+    rank[e] = rk;
+    rk += avail[e];
+  }
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
     if (rep[e] && slot[e] < 0) {
       hval[hpos[e]] = -(j + 1);
       miss_key[j] = tok[e];
-      if (sw) bit_set_atomic(mbits, tok[e]);
       ++j;
     }
   }
-  __syncthreads();
-  if (sw) {
-    bitmap_word_prefix<NT>(mbits, mwpre, sw, scan);
-    __syncthreads();
+  int wp = static_cast<int>(y_pre);
+  for (int w = w0; w < w0 + wpt && w < sw; ++w) {
+    mwpre[w] = wp;
+    wp += __popc(mbits[w]);
   }
-
-  // 3. victims, commit, new order
-  lru_select_commit<NT, EPH>(a, b, r, now, m, o, used, miss_key, vslot, scan, ks, sk, tsq, ord,
-                             sw ? mbits : nullptr, mwpre, oldk);
   __syncthreads();
 
-  // 4. outputs
+  // 4. victims, commit, new order
+  lru_commit<NT, EPH>(a, b, r, now, m, o, avail, rank, used, miss_key, vslot, scan, ks, sk, tsq,
+                      ord, sw ? mbits : nullptr, mwpre, oldk);
+  __syncthreads();
+
+  // 5. outputs
   int32_t* out = a.out_locs + static_cast<size_t>(b) * a.K;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
@@ -382,8 +405,18 @@ __global__ __launch_bounds__(NT) void lru_page_plan(PlanArgs a) {
   __syncthreads();
 
   // 4. victims, commit, new order (pages are already in ascending order)
-  lru_select_commit<NT, EPH>(a, b, r, now, m, o, used, miss_key, vslot, scan, ks, sk, tsq, ord,
-                             nullptr, nullptr, oldk);
+  bool avail[EPH];
+  const int navail = lru_available<EPH>(o, used, avail);
+  int total_avail;
+  int rk = block_exclusive_scan<NT>(navail, scan, &total_avail);
+  int rank[EPH];
+#pragma unroll
+  for (int e = 0; e < EPH; ++e) {
+    rank[e] = rk;
+    rk += avail[e];
+  }
+  lru_commit<NT, EPH>(a, b, r, now, m, o, avail, rank, used, miss_key, vslot, scan, ks, sk, tsq,
+                      ord, nullptr, nullptr, oldk);
   __syncthreads();
 
   // 5. outputs: page table, page count, token locations (page index, offset)
@@ -439,7 +472,7 @@ int hash_size_for(int entries) {
 
 size_t lru_token_lds_bytes(const PlanArgs& a) {
   return (2 * static_cast<size_t>(a.hash_size) + a.Hw + 2 * static_cast<size_t>(a.K) +
-          kPlanThreads / kWave + 1 + 2 * static_cast<size_t>(a.sort_words)) * 4;
+          2 * kPlanThreads / kWave + 2 * static_cast<size_t>(a.sort_words)) * 4;
 }
 
 size_t lru_page_lds_bytes(const PlanArgs& a) {

@@ -71,20 +71,7 @@ __device__ __forceinline__ uint32_t score_key(float x) {
   return k + 1u;  // -inf -> 0x00800000; +inf -> 0xFF800001
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave: row shifts 1, 2, 4, 8
-// within each 16-lane row, then the last lane of row 0 broadcast into rows 1
-// and 3 and the last lane of row 1 into rows 2 and 3.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
-  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, true);  // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, true);  // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, true);  // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, true);  // row_shr:8
-  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false); // row_bcast:15
-  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false); // row_bcast:31
-  return x;
-}
-
-// Exclusive prefix sum over the workgroup; *total gets the sum.  Two
+// Exclusive prefix sum over the workgroup (wave_incl_scan per wave); *total gets the sum.  Two
 // barriers; `xch` holds kWaves words.  Every thread must call it.
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* xch, uint32_t* total) {
   const int lane = threadIdx.x & (kWave - 1);
