@@ -36,6 +36,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -89,7 +90,7 @@ struct MlaArgs {
   float scale_log2;           // softmax scale * log2(e)
   float* out;                 // [B][Hq][512]
   float* lse;                 // [B][Hq] or null
-  float* part_out;            // [B][splits][Hq][512]
+  _Float16* part_out;         // [B][splits][Hq][512] normalised split outputs (fp16)
   float* part_ml;             // [B][splits][Hq][2]: running max (log2 units), sum
   uint32_t* err;
 };
@@ -471,24 +472,29 @@ void mla_decode(MlaArgs a) {
     const int head = hg * kHeadsPerGroup + wave * kHeadsPerWave + hb * 16 + n;
     if (head >= a.heads) continue;
     const float inv = l_run[hb] > 0.f ? 1.f / l_run[hb] : 0.f;
-    float* dst;
+    // dim block db, C row 4g + i  <->  dim 16db + 4g + i
     if (a.splits == 1) {
-      dst = a.out + (static_cast<size_t>(b) * a.heads + head) * kLatent;
+      float* dst = a.out + (static_cast<size_t>(b) * a.heads + head) * kLatent;
       if (a.lse != nullptr && g == 0)
         a.lse[static_cast<size_t>(b) * a.heads + head] =
             l_run[hb] > 0.f ? (m_ref[hb] + log2f(l_run[hb])) * kLn2 : -INFINITY;
+#pragma unroll
+      for (int db = 0; db < kDimBlocks; ++db)
+        *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * g) = acc[hb][db] * inv;
     } else {
+      // a split's output is a convex combination of its values, so fp16
+      // (relative 2^-11) holds it; the split's max and sum stay fp32
       const size_t ps = (static_cast<size_t>(b) * a.splits + split) * a.heads + head;
-      dst = a.part_out + ps * kLatent;
+      _Float16* dst = a.part_out + ps * kLatent;
       if (g == 0) {
         a.part_ml[2 * ps] = m_ref[hb];
         a.part_ml[2 * ps + 1] = l_run[hb];
       }
-    }
-    // dim block db, C row 4g + i  <->  dim 16db + 4g + i
 #pragma unroll
-    for (int db = 0; db < kDimBlocks; ++db)
-      *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * g) = acc[hb][db] * inv;
+      for (int db = 0; db < kDimBlocks; ++db)
+        *reinterpret_cast<f16x4*>(dst + 16 * db + 4 * g) =
+            __builtin_convertvector(acc[hb][db] * inv, f16x4);
+    }
   }
 }
 
@@ -510,7 +516,8 @@ __global__ __launch_bounds__(128) void mla_combine(MlaArgs a) {
     if (!(l > 0.f)) continue;
     const float w = exp2f(a.part_ml[2 * ps] + log2f(l) - big);
     wsum += w;
-    const f32x4 p = *reinterpret_cast<const f32x4*>(a.part_out + ps * kLatent + 4 * threadIdx.x);
+    const f32x4 p = __builtin_convertvector(
+        *reinterpret_cast<const f16x4*>(a.part_out + ps * kLatent + 4 * threadIdx.x), f32x4);
     o += w * p;
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
@@ -538,7 +545,8 @@ int mla_max_locations() { return 64 * kMaxPerSplit; }
 size_t mla_workspace_bytes(int batch, int heads, int n_locs, int num_cus) {
   const int splits = mla_splits(batch, heads, n_locs, num_cus);
   if (splits == 1) return 0;
-  return static_cast<size_t>(batch) * splits * heads * (kLatent + 2) * sizeof(float);
+  return static_cast<size_t>(batch) * splits * heads *
+         (kLatent * sizeof(_Float16) + 2 * sizeof(float));
 }
 
 hipError_t launch_mla_decode(const MlaDecodeCall& c, hipStream_t s) {
@@ -563,8 +571,9 @@ hipError_t launch_mla_decode(const MlaDecodeCall& c, hipStream_t s) {
   a.lse = c.lse;
   a.err = c.err;
   if (a.splits > 1) {
-    a.part_out = static_cast<float*>(c.workspace);
-    a.part_ml = a.part_out + static_cast<size_t>(c.batch) * a.splits * c.heads * kLatent;
+    a.part_out = static_cast<_Float16*>(c.workspace);
+    a.part_ml = reinterpret_cast<float*>(a.part_out + static_cast<size_t>(c.batch) * a.splits *
+                                                          c.heads * kLatent);
   }
   const int padded_units = (a.units + 7) / 8 * 8;
   if (c.item_bytes == 2 * kDim)

@@ -8,8 +8,12 @@ Tolerance, per (row, head), from the arithmetic of the kernel:
 * each softmax weight is rounded to bf16 (relative 2^-9) and moves by at most
   exp(2d) - 1 through the scores, so every normalised weight moves by a
   relative e = 2 * (exp(2d) - 1 + 2^-9);
-* values are the same bf16 latents (fp8: rounded, relative 2^-9).
-Hence |out^ - out| <= max_i |c_i| * (e + 2^-9 [fp8]) and |lse^ - lse| <= d + 2^-8.
+* values are the same bf16 latents (fp8: rounded, relative 2^-9);
+* with the locations split over workgroups, each split's normalised output
+  (a convex combination of values, so at most max_i |c_i|) is stored in fp16
+  before the log-sum-exp merge: at most 2^-11 max_i |c_i| more.
+Hence |out^ - out| <= max_i |c_i| * (e + 2^-9 [fp8] + 2^-11) and
+|lse^ - lse| <= d + 2^-8.
 """
 import numpy as np
 import pytest
@@ -36,7 +40,7 @@ def tolerances(q_bits, locs_host, host_rows, scale, fp8):
         d = scale * ((2.0 ** -9 if fp8 else 0.0) + 2.0 ** -20) * (q @ k.T).max(axis=1)
         e = 2 * (np.expm1(2 * d) + 2.0 ** -9)
         vmax = np.abs(lat).max()
-        tol_out[b] = vmax * (e + (2.0 ** -9 if fp8 else 0.0)) + 1e-6
+        tol_out[b] = vmax * (e + (2.0 ** -9 if fp8 else 0.0) + 2.0 ** -11) + 1e-6
         tol_lse[b] = d + 2.0 ** -8 + 1e-6
     return tol_out, tol_lse
 
