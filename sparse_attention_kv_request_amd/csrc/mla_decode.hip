@@ -235,34 +235,35 @@ void mla_decode(MlaArgs a) {
   __shared__ uint32_t rowoff[kMaxPerSplit + kTile + 1];  // byte offset of each location's row
   __shared__ int32_t restart_at[2];
 
-  // XCD-aware mapping: the head groups of one (row, split) unit run on the
-  // same XCD (workgroups are dealt to the 8 XCDs round robin) and share its
-  // rows through that XCD's L2.
+  // XCD-aware mapping (workgroups are dealt to the 8 XCDs round robin):
+  // every split and head group of batch row b runs on XCD b mod 8, so the
+  // row's queries are fetched from HBM once and shared through that XCD's
+  // L2.
   const int id = blockIdx.x;
   const int xcd = id & 7;
   const int kx = id >> 3;
   const int hg = kx % a.groups;
-  const int unit = (kx / a.groups) * 8 + xcd;
-  if (unit >= a.units) return;
-  const int b = unit / a.splits;
-  const int split = unit - b * a.splits;
+  const int su = kx / a.groups;
+  const int split = su % a.splits;
+  const int b = (su / a.splits) * 8 + xcd;
+  if (b >= a.batch) return;
   const int t_begin = split * a.per_split;
   const int nrows = max(0, min(a.n_locs, t_begin + a.per_split) - t_begin);
   const int tid = threadIdx.x;
   if (tid < 2) restart_at[tid] = -2;
 
   // byte offsets of this split's rows (kAbsent = skipped), padded with
-  // kAbsent up to one tile past the last one
+  // kAbsent up to one tile past the last one.  Every location load goes out
+  // before the first is used (one round trip, not one per pass), and so do
+  // the page-table loads of page mode.
+  constexpr int kRowIters = (kMaxPerSplit + kTile + 1 + kThreads - 1) / kThreads;
   const int padded = (nrows + kTile - 1) / kTile * kTile + kTile + 1;
-  for (int t = tid; t < padded; t += kThreads) {
-    uint32_t off = kAbsent;
-    if (t < nrows) {
-      const int32_t loc = a.locs[static_cast<size_t>(b) * a.n_locs + t_begin + t];
-      const int64_t row = token_row(a, b, loc);
-      if (row < 0 && loc >= 0) raise_error(a.err, HISPARSE_ERR_BAD_INDEX);
-      if (row >= 0) off = static_cast<uint32_t>(row) * static_cast<uint32_t>(a.item_bytes);
-    }
-    rowoff[t] = off;
+  const int32_t* lrow = a.locs + static_cast<size_t>(b) * a.n_locs + t_begin;
+  int32_t locv[kRowIters];
+#pragma unroll
+  for (int k = 0; k < kRowIters; ++k) {
+    const int t = tid + k * kThreads;
+    locv[k] = t < nrows ? lrow[t] : -1;
   }
 
   const int lane = tid & (kWave - 1);
@@ -271,20 +272,38 @@ void mla_decode(MlaArgs a) {
   const int n = lane & 15;       // head within a block / row within a 16-row tile
 
   // Q^T operands: lane holds q[head][32*ks + 8*g .. +8] of its head in each
-  // of the wave's two 16-head blocks
+  // of the wave's two 16-head blocks (issued behind the location loads, so
+  // the row table waits for the locations only and the queries land behind
+  // the first tile's gather; nothing uses them before the first tile).  A
+  // lane past the last head loads head 0: its results are never stored, and
+  // its scores equal head 0's, so it cannot ask for a restart head 0 would
+  // not ask for.
   bf16x8 qreg[2][kKSteps];
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
     const int head = hg * kHeadsPerGroup + wave * kHeadsPerWave + hb * 16 + n;
-    const bool ok = head < a.heads;
-    const uint16_t* qh = a.q + (static_cast<size_t>(b) * a.heads + (ok ? head : 0)) * kDim;
+    const uint16_t* qh =
+        a.q + (static_cast<size_t>(b) * a.heads + (head < a.heads ? head : 0)) * kDim;
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(qh + 32 * ks + 8 * g);
-      if (!ok) v = u32x4{0u, 0u, 0u, 0u};
-      qreg[hb][ks] = as_bf16x8(v);
-    }
+    for (int ks = 0; ks < kKSteps; ++ks)
+      qreg[hb][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qh + 32 * ks + 8 * g));
   }
+
+  int64_t rowv[kRowIters];
+#pragma unroll
+  for (int k = 0; k < kRowIters; ++k) rowv[k] = token_row(a, b, locv[k]);
+  bool bad = false;
+#pragma unroll
+  for (int k = 0; k < kRowIters; ++k) {
+    const int t = tid + k * kThreads;
+    bad |= rowv[k] < 0 && locv[k] >= 0;
+    if (t < padded)
+      rowoff[t] = rowv[k] >= 0
+                      ? static_cast<uint32_t>(rowv[k]) * static_cast<uint32_t>(a.item_bytes)
+                      : kAbsent;
+  }
+  if (bad) raise_error(a.err, HISPARSE_ERR_BAD_INDEX);
+
   __syncthreads();  // rows[] complete
 
   f32x4 acc[2][kDimBlocks];
@@ -575,11 +594,11 @@ hipError_t launch_mla_decode(const MlaDecodeCall& c, hipStream_t s) {
     a.part_ml = reinterpret_cast<float*>(a.part_out + static_cast<size_t>(c.batch) * a.splits *
                                                           c.heads * kLatent);
   }
-  const int padded_units = (a.units + 7) / 8 * 8;
+  const int grid = (c.batch + 7) / 8 * 8 * a.splits * a.groups;
   if (c.item_bytes == 2 * kDim)
-    hipLaunchKernelGGL(mla_decode<false>, dim3(padded_units * a.groups), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(mla_decode<false>, dim3(grid), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(mla_decode<true>, dim3(padded_units * a.groups), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(mla_decode<true>, dim3(grid), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   hipLaunchKernelGGL(mla_combine, dim3(c.batch * c.heads), dim3(128), 0, s, a);
