@@ -517,32 +517,41 @@ void mla_decode(MlaArgs a) {
   }
 }
 
-// Merges the splits of every (row, head) by their log-sum-exp.
-__global__ __launch_bounds__(128) void mla_combine(MlaArgs a) {
-  const int bh = blockIdx.x;  // b * heads + h
+// Merges the splits of every (row, head) by their log-sum-exp: 64 lanes per
+// head, 8 dims (one 16-byte fp16 load per split) per lane, 4 heads per
+// workgroup.
+constexpr int kCombineHeads = 4;
+__global__ __launch_bounds__(kCombineHeads * kWave) void mla_combine(MlaArgs a) {
+  const int bh = blockIdx.x * kCombineHeads + static_cast<int>(threadIdx.x / kWave);
+  if (bh >= a.batch * a.heads) return;
+  const int lane = threadIdx.x & (kWave - 1);
   const int b = bh / a.heads, h = bh - b * a.heads;
+  const size_t ps0 = static_cast<size_t>(b) * a.splits * a.heads + h;  // split s: ps0 + s*heads
   float big = -INFINITY;
   for (int s = 0; s < a.splits; ++s) {
-    const size_t ps = (static_cast<size_t>(b) * a.splits + s) * a.heads + h;
-    const float l = a.part_ml[2 * ps + 1];
-    if (l > 0.f) big = fmaxf(big, a.part_ml[2 * ps] + log2f(l));
+    const size_t ps = ps0 + static_cast<size_t>(s) * a.heads;
+    const f32x2 ml = *reinterpret_cast<const f32x2*>(a.part_ml + 2 * ps);
+    if (ml[1] > 0.f) big = fmaxf(big, ml[0] + log2f(ml[1]));
   }
   float wsum = 0.f;
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < a.splits; ++s) {
-    const size_t ps = (static_cast<size_t>(b) * a.splits + s) * a.heads + h;
-    const float l = a.part_ml[2 * ps + 1];
-    if (!(l > 0.f)) continue;
-    const float w = exp2f(a.part_ml[2 * ps] + log2f(l) - big);
+    const size_t ps = ps0 + static_cast<size_t>(s) * a.heads;
+    const f32x2 ml = *reinterpret_cast<const f32x2*>(a.part_ml + 2 * ps);
+    if (!(ml[1] > 0.f)) continue;
+    const float w = exp2f(ml[0] + log2f(ml[1]) - big);
     wsum += w;
-    const f32x4 p = __builtin_convertvector(
-        *reinterpret_cast<const f16x4*>(a.part_out + ps * kLatent + 4 * threadIdx.x), f32x4);
-    o += w * p;
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(a.part_out + ps * kLatent + 8 * lane);
+    const f16x4 lo = __builtin_bit_cast(f16x4, u32x2{raw[0], raw[1]});
+    const f16x4 hi = __builtin_bit_cast(f16x4, u32x2{raw[2], raw[3]});
+    o0 += w * __builtin_convertvector(lo, f32x4);
+    o1 += w * __builtin_convertvector(hi, f32x4);
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  *reinterpret_cast<f32x4*>(a.out + static_cast<size_t>(bh) * kLatent + 4 * threadIdx.x) = o * inv;
-  if (a.lse != nullptr && threadIdx.x == 0)
-    a.lse[bh] = wsum > 0.f ? (big + log2f(wsum)) * kLn2 : -INFINITY;
+  float* dst = a.out + static_cast<size_t>(bh) * kLatent + 8 * lane;
+  *reinterpret_cast<f32x4*>(dst) = o0 * inv;
+  *reinterpret_cast<f32x4*>(dst + 4) = o1 * inv;
+  if (a.lse != nullptr && lane == 0) a.lse[bh] = wsum > 0.f ? (big + log2f(wsum)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
@@ -601,7 +610,8 @@ hipError_t launch_mla_decode(const MlaDecodeCall& c, hipStream_t s) {
     hipLaunchKernelGGL(mla_decode<true>, dim3(grid), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
-  hipLaunchKernelGGL(mla_combine, dim3(c.batch * c.heads), dim3(128), 0, s, a);
+  hipLaunchKernelGGL(mla_combine, dim3((c.batch * c.heads + kCombineHeads - 1) / kCombineHeads),
+                     dim3(kCombineHeads * kWave), 0, s, a);
   return hipGetLastError();
 }
 
