@@ -253,6 +253,67 @@ __device__ __forceinline__ void emit_final(const TopkArgs& a, int row, PosOf pos
   }
 }
 
+// Largest output count staged through LDS (the list and histogram arrays,
+// free once the threshold is known); above it the outputs go word by word.
+constexpr int kStageCap = kListCap < kBins ? kListCap : kBins;
+
+// Puts the kept slots in output order into LDS: s.list[o] = slot and
+// s.hist[o] = key of the o-th output.  Word w's kept bits and output offset
+// (thread w's select_word result) go through the bitmap arrays; each slot's
+// owner, which holds its key, places it.  kk <= kStageCap.
+__device__ __forceinline__ void stage_kept(const uint32_t (&key)[kPer], uint32_t kept, int offset,
+                                           Lds& s) {
+  const int tid = threadIdx.x;
+  s.gt_bits[tid] = kept;
+  s.eq_bits[tid] = static_cast<uint32_t>(offset);
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int i = slot_of(e);
+    const uint32_t wv = s.gt_bits[i >> 5];
+    const uint32_t bit = 1u << (i & 31);
+    if (wv & bit) {
+      const int o = static_cast<int>(s.eq_bits[i >> 5]) + __popc(wv & (bit - 1u));
+      s.list[o] = static_cast<uint32_t>(i);
+      s.hist[o] = key[e];
+    }
+  }
+  __syncthreads();
+}
+
+// Final outputs from the staged slots: thread t writes outputs t, t + 1024,
+// ... (contiguous stores; the position and page-table loads of a thread's
+// outputs go out together), then -1 padding from kk on.
+template <class PosOf>
+__device__ __forceinline__ void emit_staged(const TopkArgs& a, int row, PosOf pos_of, const Lds& s,
+                                            int kk) {
+  constexpr int kBatch = 2;
+  int32_t* idx = a.indices + static_cast<size_t>(row) * a.k;
+  int32_t* loc = a.locs ? a.locs + static_cast<size_t>(row) * a.k : nullptr;
+  for (int o0 = threadIdx.x; o0 < kk; o0 += kBatch * kThreads) {
+    int32_t pos[kBatch], lv[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int o = o0 + j * kThreads;
+      pos[j] = o < kk ? pos_of(static_cast<int>(s.list[o])) : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) lv[j] = loc && pos[j] >= 0 ? table_loc(a, row, pos[j]) : -1;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int o = o0 + j * kThreads;
+      if (o < kk) {
+        idx[o] = pos[j];
+        if (loc) loc[o] = lv[j];
+      }
+    }
+  }
+  for (int i = kk + threadIdx.x; i < a.k; i += kThreads) {
+    idx[i] = -1;
+    if (loc) loc[i] = -1;
+  }
+}
+
 __device__ __forceinline__ bool row_rejected(const TopkArgs& a, int row) {
   const int seq = a.seq_lens[row];
   return seq < 0 || seq > a.max_len;
@@ -296,7 +357,10 @@ __global__ __launch_bounds__(kThreads) void topk_plan_kernel(const int32_t* seq_
 }
 
 // One workgroup per plan item (chunk).
-__global__ __launch_bounds__(kThreads) void topk_chunk_kernel(TopkArgs a) {
+// At most 64 VGPRs (8 waves per SIMD): two 1024-thread workgroups share a CU,
+// so a 512-chunk call runs in one round instead of two.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void topk_chunk_kernel(TopkArgs a) {
   __shared__ Lds s;
   const TopkPlan p = topk_plan_layout(a.batch, a.max_items);
   const int w = blockIdx.x;
@@ -347,20 +411,32 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(TopkArgs a) {
     radix_threshold(key, kk, s, T, need);
     kept = select_word(key, T, need, s, offset);
   }
+  const bool staged = kk <= kStageCap;
+  if (staged) stage_kept(key, kept, offset, s);
   if (n_chunks == 1) {
-    emit_final(a, row, [&](int i) { return start + i; }, kept, offset, kk);
+    if (staged)
+      emit_staged(a, row, [&](int i) { return start + i; }, s, kk);
+    else
+      emit_final(a, row, [&](int i) { return start + i; }, kept, offset, kk);
     return;
   }
   // a chunk of a split row: its candidates (key, position) in slot order,
-  // for topk_merge_kernel; the keys of the kept slots are read again (L2)
+  // for topk_merge_kernel
   uint32_t* ck = a.cand_key + static_cast<size_t>(blockIdx.x) * a.k;
   int32_t* cp = a.cand_pos + static_cast<size_t>(blockIdx.x) * a.k;
-  const float* src = a.logits + static_cast<size_t>(row) * a.max_len + start;
-  for (uint32_t r = kept; r != 0u; r &= r - 1u) {
-    const int i = 32 * tid + __builtin_ctz(r);
-    ck[offset] = score_key(src[i]);
-    cp[offset] = start + i;
-    ++offset;
+  if (staged) {
+    for (int o = tid; o < kk; o += kThreads) {
+      ck[o] = s.hist[o];
+      cp[o] = start + static_cast<int>(s.list[o]);
+    }
+  } else {  // the keys of the kept slots are read again (L2)
+    const float* src = a.logits + static_cast<size_t>(row) * a.max_len + start;
+    for (uint32_t r = kept; r != 0u; r &= r - 1u) {
+      const int i = 32 * tid + __builtin_ctz(r);
+      ck[offset] = score_key(src[i]);
+      cp[offset] = start + i;
+      ++offset;
+    }
   }
   if (tid == 0) a.cand_cnt[blockIdx.x] = kk;
 }
@@ -410,7 +486,12 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
     radix_threshold(key, kf, s, T, need);
     w = select_word(key, T, need, s, offset);
   }
-  emit_final(a, row, [&](int i) { return a.cand_pos[cand_at(i)]; }, w, offset, kf);
+  if (kf <= kStageCap) {
+    if (kf > 0) stage_kept(key, w, offset, s);
+    emit_staged(a, row, [&](int i) { return a.cand_pos[cand_at(i)]; }, s, kf);
+  } else {
+    emit_final(a, row, [&](int i) { return a.cand_pos[cand_at(i)]; }, w, offset, kf);
+  }
 }
 
 }  // namespace
