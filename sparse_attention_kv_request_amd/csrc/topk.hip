@@ -43,6 +43,7 @@ constexpr int kBins = 4096;                        // 12-bit digits
 constexpr int kListCap = 4096;                     // keys of the threshold bin kept in LDS
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct TopkArgs {
   const float* logits;       // [batch][max_len]
@@ -151,17 +152,24 @@ __device__ __forceinline__ void radix_threshold(const uint32_t (&key)[kPer], int
   int remaining = kk - above;
   uint32_t prefix = b0 << 20;
 
-  // keys of bin b0 -> LDS list (any order; typically a few percent of keys)
+  // keys of bin b0 -> LDS list (any order; typically a few percent of keys):
+  // a wave scan of the lanes' counts places them, one LDS atomic per wave
+  // reserves the wave's room
+  uint32_t cnt = 0u;
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const bool in = key[e] != 0u && (key[e] >> 20) == b0;
-    const uint64_t mask = __ballot(in);
-    if (mask != 0u) {
-      int base = 0;
-      if (lane == 0) base = atomicAdd(&s.list_count, __popcll(mask));
-      base = __builtin_amdgcn_readfirstlane(base);
-      const int at = base + __popcll(mask & ((uint64_t{1} << lane) - 1u));
-      if (in && at < kListCap) s.list[at] = key[e];
+  for (int e = 0; e < kPer; ++e) cnt += key[e] != 0u && (key[e] >> 20) == b0;
+  const uint32_t incl = wave_incl_scan(cnt);
+  const uint32_t wave_total = __builtin_amdgcn_readlane(incl, kWave - 1);
+  if (wave_total > 0u) {
+    uint32_t base = 0u;
+    if (lane == kWave - 1) base = atomicAdd(reinterpret_cast<uint32_t*>(&s.list_count), wave_total);
+    int at = static_cast<int>(__builtin_amdgcn_readlane(base, kWave - 1) + incl - cnt);
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      if (key[e] != 0u && (key[e] >> 20) == b0) {
+        if (at < kListCap) s.list[at] = key[e];
+        ++at;
+      }
     }
   }
   __syncthreads();
@@ -268,14 +276,20 @@ __device__ __forceinline__ void stage_kept(const uint32_t (&key)[kPer], uint32_t
   s.eq_bits[tid] = static_cast<uint32_t>(offset);
   __syncthreads();
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const int i = slot_of(e);
-    const uint32_t wv = s.gt_bits[i >> 5];
-    const uint32_t bit = 1u << (i & 31);
-    if (wv & bit) {
-      const int o = static_cast<int>(s.eq_bits[i >> 5]) + __popc(wv & (bit - 1u));
-      s.list[o] = static_cast<uint32_t>(i);
-      s.hist[o] = key[e];
+  for (int v = 0; v < kPer / 4; ++v) {  // slots i0 .. i0 + 3 share a bitmap word
+    const int i0 = slot_of(4 * v);
+    const uint32_t wv = s.gt_bits[i0 >> 5];
+    const uint32_t sh = static_cast<uint32_t>(i0 & 31);
+    if ((wv >> sh) & 15u) {
+      int o = static_cast<int>(s.eq_bits[i0 >> 5]) + __popc(wv & ((1u << sh) - 1u));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if ((wv >> (sh + j)) & 1u) {
+          s.list[o] = static_cast<uint32_t>(i0 + j);
+          s.hist[o] = key[4 * v + j];
+          ++o;
+        }
+      }
     }
   }
   __syncthreads();
@@ -471,12 +485,31 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
   for (int i = tid; i < kBins; i += kThreads) s.hist[i] = 0u;
   if (tid == 0) s.list_count = 0;
   __syncthreads();
+  // slots i0 .. i0 + 3 usually sit in one chunk (chunk candidate counts are
+  // k or a chunk's length, multiples of 4 except at a row's end): one 16-byte
+  // load then, else one load per slot
   uint32_t key[kPer];
+  const bool vec4 = (a.k & 3) == 0 && (reinterpret_cast<uintptr_t>(a.cand_key) & 15u) == 0u;
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const int i = slot_of(e);
-    key[e] = i < M ? a.cand_key[cand_at(i)] : 0u;
-    if (key[e] != 0u) atomicAdd(&s.hist[key[e] >> 20], 1u);
+  for (int v = 0; v < kPer / 4; ++v) {
+    const int i0 = slot_of(4 * v);
+    if (i0 >= M) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) key[4 * v + j] = 0u;
+      continue;
+    }
+    const size_t c0 = cand_at(i0);
+    if (vec4 && i0 + 3 < M && cand_at(i0 + 3) == c0 + 3 && (c0 & 3) == 0) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(a.cand_key + c0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) key[4 * v + j] = x[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) key[4 * v + j] = i0 + j < M ? a.cand_key[cand_at(i0 + j)] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (key[4 * v + j] != 0u) atomicAdd(&s.hist[key[4 * v + j] >> 20], 1u);
   }
   __syncthreads();
   const int kf = min(a.k, M);
