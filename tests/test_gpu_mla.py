@@ -59,7 +59,10 @@ def boost_rows(host, item, req_row, tokens, factor):
             sc *= np.float32(factor)
 
 
-def run_case(*, R, B, H, K, N, item, heads, P=1, seed=0, pad_row=None, calls=2, boost=None):
+def run_case(*, R, B, H, K, N, item, heads, P=1, seed=0, pad_row=None, calls=2, boost=None,
+             check_rows=None):
+    """One state, `calls` swap + decode calls; every batch row (or the
+    `check_rows` sample) is compared with the oracle."""
     rng = np.random.default_rng(seed)
     host = binding.HostKV(R, N, item)
     for r in range(R):
@@ -99,10 +102,13 @@ def run_case(*, R, B, H, K, N, item, heads, P=1, seed=0, pad_row=None, calls=2, 
             # the oracle reads the host tier by token: row r*N + t
             locs_host = np.where(topk >= 0, req[:, None].astype(np.int64) * N + topk, -1)
             host_rows = host.array.reshape(R * N, item)
-            ref_out, ref_lse = mla.sparse_mla_decode(q_bits, locs_host, host_rows, scale)
-            tol_out, tol_lse = tolerances(q_bits, locs_host, host_rows, scale, item == 656)
             got_out = out.cpu().numpy().astype(np.float64)
             got_lse = lse.cpu().numpy().astype(np.float64)
+            if check_rows is not None:
+                q_bits, locs_host = q_bits[check_rows], locs_host[check_rows]
+                got_out, got_lse = got_out[check_rows], got_lse[check_rows]
+            ref_out, ref_lse = mla.sparse_mla_decode(q_bits, locs_host, host_rows, scale)
+            tol_out, tol_lse = tolerances(q_bits, locs_host, host_rows, scale, item == 656)
             err = np.abs(got_out - ref_out).max(axis=2)
             assert np.all(err <= tol_out), f"out error {err.max()} > {tol_out[err > tol_out].min()}"
             both_inf = np.isneginf(got_lse) & np.isneginf(ref_lse)
@@ -157,6 +163,14 @@ def test_mla_replay_after_large_score_jump(item):
     later tiles of a split: the split restarts with a raised reference."""
     run_case(R=64, B=64, H=400, K=300, N=1200, item=item, heads=128, seed=item + 3, calls=1,
              boost=[(0, 50, 2000.0), (0, 80, 5000.0), (7, 230, 3000.0)])
+
+
+@pytest.mark.parametrize("item", [1152, 656])
+def test_mla_bench_shape(item):
+    """The bench's launch shape: 64 rows x 128 heads x 2048 locations (four
+    splits of 512 per row), rows placed by a swap call; every row against the
+    oracle."""
+    run_case(R=64, B=64, H=4096, K=2048, N=8192, item=item, heads=128, seed=item + 9, calls=1)
 
 
 def test_mla_rejects_bad_arguments():
