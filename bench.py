@@ -64,6 +64,12 @@ def parse():
                          "same trace and report their misses per step")
     ap.add_argument("--extra-rows", type=int, default=0,
                     help="extra-row ring of the newest tokens (token mode)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip timing the same steps replayed from HIP graphs (one captured "
+                         "graph per step, reported beside the eager steps)")
+    ap.add_argument("--batched-state", action="store_true",
+                    help="state traffic of the plan kernel with config 2's 512 (request, layer) "
+                         "instances in one launch, hit-only steady state")
     ap.add_argument("--item", type=int, default=0,
                     help="KV row bytes for --attention (1152 bf16 or 656 fp8; default: workload's)")
     return ap.parse_args()
@@ -303,6 +309,34 @@ class Runner:
         m = self.miss[W:W + K].cpu().numpy().astype(self.np.int64)
         return elapsed, prof, m
 
+    def timed_graphs(self, W, K):
+        """The timed steps of timed() replayed from HIP graphs: each step's
+        layer calls are captured once (on a side stream, outside the timed
+        region) and replayed in order.  Runs on a fresh state after W eager
+        warm-up steps, like timed()."""
+        torch = self.torch
+        for s in range(W):
+            self.step(s)
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        graphs = []
+        for s in range(W, W + K):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                self.step(s)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for g in graphs:
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        flags = self.st.error_flags()
+        if flags:
+            raise SystemExit(f"device error flags {flags} during the graph replays")
+        return e0.elapsed_time(e1) * 1e-3
+
     def close(self):
         self.st.close()
         if self.owns_host:
@@ -311,6 +345,61 @@ class Runner:
 
 
 BF16_MFMA_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+
+
+def batched_state_bench(args, torch, binding, workloads):
+    """Plan-kernel state traffic with many instances per launch: config 2's
+    64 requests x 8 layers as 512 requests of one layer, all resolved by one
+    swap call.  After the first (cold) call every later call repeats the same
+    top-k rows, so every entry hits: the step is the plan kernel alone
+    (lookup, hit touch, LRU order rewrite, outputs) plus an empty copy
+    launch.  Host KV bytes are left zero (no miss reads them after call 0)."""
+    import numpy as np
+
+    W, K = args.warmup, args.steps
+    w = workloads.config(2, steps=2)
+    R = w.batch * w.layers
+    host = [binding.HostKV(R, w.seq_len, w.item_bytes)]
+    st = binding.HiSparseState(max_requests=R, num_layers=1, hot_buffer_size=w.hot,
+                               top_k=w.top_k, item_size_bytes=w.item_bytes,
+                               max_seq_len=w.seq_len, host_kv=host)
+    trace = workloads.batch_trace(w, threads=16)             # [L, steps, B, 1, K]
+    rows = np.ascontiguousarray(trace[:, 0, :, 0].reshape(R, w.top_k))
+    dev = torch.device("cuda", 0)
+    topk = torch.from_numpy(rows).to(dev)
+    req = torch.arange(R, dtype=torch.int32, device=dev)
+    seq = torch.full((R,), w.seq_len, dtype=torch.int32, device=dev)
+    out = torch.empty((R, w.top_k), dtype=torch.int32, device=dev)
+    mc = torch.empty(R, dtype=torch.int32, device=dev)
+    for _ in range(1 + W):
+        st.swap_in_selected(0, req, seq, topk, out, mc)
+    torch.cuda.synchronize()
+    st.profile(True)
+    st.profile_read()
+    for _ in range(K):
+        st.swap_in_selected(0, req, seq, topk, out, mc)
+    torch.cuda.synchronize()
+    prof = st.profile_read()
+    st.profile(False)
+    if int(mc.sum().item()) != 0 or st.error_flags():
+        raise SystemExit("the batched-state steady state must be hit-only and error-free")
+    distinct = np.array([np.unique(r[r >= 0]).size for r in rows])
+    per_launch = sum(state_bytes_per_row(w, 0, int(d)) for d in distinct)
+    plan_s = prof["plan_ms"] * 1e-3 / prof["calls"]
+    st.close()
+    host[0].free()
+    gbps = per_launch / plan_s / 1e9
+    return {"metric": "plan-kernel state GB/s, 512 instances per launch, hit-only",
+            "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+            "ms_per_step": round(plan_s * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+            "config": {"workload": "config 2 instances (64 requests x 8 layers) as 512 rows of "
+                                   "one launch, top_k 2048, hot 4096, step-0 rows repeated",
+                       "batch": R, "top_k": w.top_k, "hot_buffer_size": w.hot},
+            "roofline": {"bound": "hbm", "kernel": "lru_token_plan", "achieved": round(gbps, 2),
+                         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                         "avg_launch_us": round(plan_s * 1e6, 2), "bytes_per_launch": per_launch}}
 
 
 def attention_bench(args, torch, binding, workloads):
@@ -465,6 +554,9 @@ def main():
     if args.topk:
         print(json.dumps(topk_bench(args, torch, binding, workloads)), flush=True)
         return
+    if args.batched_state:
+        print(json.dumps(batched_state_bench(args, torch, binding, workloads)), flush=True)
+        return
     W, K = args.warmup, args.steps
     over = {"steps": W + K}
     if args.workload == 3:
@@ -556,6 +648,15 @@ def main():
             cmp[adm] = {"misses_per_step": int(o_m.sum()) // K,
                         "ms_per_step": round(o_el * 1e3 / K, 4)}
         res["admission_compare"] = cmp
+    if not args.no_graph:
+        log("timing the same steps replayed from HIP graphs")
+        g_run = Runner(torch, binding, workloads, w, admission=args.admission,
+                       extra_rows=args.extra_rows, share=run)
+        g_elapsed = g_run.timed_graphs(W, K)
+        g_run.close()
+        res["graph"] = {"ms_per_step_eager": round(elapsed * 1e3 / K, 4),
+                        "ms_per_step_graph": round(g_elapsed * 1e3 / K, 4),
+                        "entries_per_s_graph": round(entries / g_elapsed, 1)}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
         res["cpu_baseline"] = cpu_baseline(w, run.host, run.trace, args.cpu_seconds)
