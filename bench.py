@@ -309,6 +309,43 @@ class Runner:
         m = self.miss[W:W + K].cpu().numpy().astype(self.np.int64)
         return elapsed, prof, m
 
+    def replay_rate(self, s_rec, reps):
+        """The plan/copy split: step s_rec's layer calls record their miss
+        plans (this state has made steps 0 .. s_rec - 1), then the recorded
+        plans are replayed `reps` times by the copy alone
+        (hisparse_copy_planned), timed with HIP events.  Returns (miss bytes
+        per replay of the 8 layers, seconds per replay)."""
+        torch, w, st = self.torch, self.w, self.st
+        for s in range(s_rec):
+            self.step(s)
+        cap = st.capacity
+        B = w.batch
+        plans, counts = [], []
+        for l in range(w.layers):
+            plan = tuple(torch.empty((B, cap), dtype=torch.int32, device=self.dev)
+                         for _ in range(3))
+            mc = torch.empty(B, dtype=torch.int32, device=self.dev)
+            if self.policy == "clock":
+                st.swap_in_spec_multistep(l, self.req, self.seq, self.topk[s_rec, l], self.outs[l],
+                                          mc, plan=plan)
+            else:
+                st.swap_in_selected(l, self.req, self.seq, self.topk[s_rec, l, :, 0], self.outs[l],
+                                    mc, page_table=self.pt, num_pages=self.npg, plan=plan)
+            plans.append(plan)
+            counts.append(mc)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            for l in range(w.layers):
+                st.copy_planned(l, counts[l], plans[l])
+        e1.record()
+        torch.cuda.synchronize()
+        if st.error_flags():
+            raise SystemExit("device error flags during the plan replays")
+        misses = sum(int(c.sum().item()) for c in counts)
+        return misses * w.item_bytes * w.page_size, e0.elapsed_time(e1) * 1e-3 / reps
+
     def timed_graphs(self, W, K):
         """The timed steps of timed() replayed from HIP graphs: each step's
         layer calls are captured once (on a side stream, outside the timed
@@ -648,6 +685,16 @@ def main():
             cmp[adm] = {"misses_per_step": int(o_m.sum()) // K,
                         "ms_per_step": round(o_el * 1e3 / K, 4)}
         res["admission_compare"] = cmp
+    log("timing the replay of recorded miss plans (copy only)")
+    r_run = Runner(torch, binding, workloads, w, admission=args.admission,
+                   extra_rows=args.extra_rows, share=run)
+    r_bytes, r_sec = r_run.replay_rate(W + K - 1, 10)
+    r_run.close()
+    res["plan_replay"] = {"kernel": "miss_copy", "bytes_per_replay": r_bytes,
+                          "ms_per_replay": round(r_sec * 1e3, 4),
+                          "GBps": round(r_bytes / r_sec / 1e9, 2),
+                          "frac_of_measured_link": (round(r_bytes / r_sec / 1e9 / measured_link, 4)
+                                                    if measured_link else None)}
     if not args.no_graph:
         log("timing the same steps replayed from HIP graphs")
         g_run = Runner(torch, binding, workloads, w, admission=args.admission,
