@@ -44,8 +44,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--num-steps", type=int, default=4, help="MTP steps of workload 3")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="wall-clock budget of the CPU-oracle baseline sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="oracle seconds per worker of the CPU baseline (one worker alone, "
+                         "then one per core)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-link-probe", action="store_true")
     ap.add_argument("--attention", action="store_true",
@@ -153,38 +154,38 @@ def link_probes(torch, st, w, rows):
     return res
 
 
-def cpu_baseline(w, host, trace, budget_s):
-    """The oracle as it stands, timed on one host core over whole instances
-    (request r, layer l, every step of the trace) until the budget is spent."""
-    from oracle import hisparse_oracle as ora
+def cpu_baseline(w, overrides, budget_s):
+    """The oracle as it stands on the host's cores: one worker process alone,
+    then `cores` workers at once (up to 16, the CPU share of one GPU), each
+    over its own instances (instances are independent).  Runs before this
+    process touches the GPU; the workers are spawned interpreters."""
+    import multiprocessing as mp
 
-    st = ora.OracleState(max_requests=w.requests, num_layers=w.layers, hot=w.hot,
-                         top_k=w.top_k, item_bytes=w.item_bytes, max_seq_len=w.seq_len,
-                         max_steps=w.num_steps, page_size=w.page_size, policy=w.policy,
-                         host_kv=[h.array for h in host])
-    entries = insts = 0
-    t0 = time.perf_counter()
-    done = False
-    for l in range(w.layers):
-        for r in range(w.batch):
-            for s in range(trace.shape[1]):
-                rows = trace[l, s, r:r + 1]
-                if w.policy == "clock":
-                    st.swap_in_spec_multistep(l, [r], [w.seq_len], rows)
-                else:
-                    st.swap_in_selected(l, [r], [w.seq_len], rows[:, 0])
-                entries += w.num_steps * w.top_k
-            insts += 1
-            if time.perf_counter() - t0 >= budget_s:
-                done = True
-                break
-        if done:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": round(entries / dt, 1), "unit": "entries/s", "cores": 1, "kind": "oracle",
-            "sample": (f"{insts} of {w.batch * w.layers} (request, layer) instances, all "
-                       f"{trace.shape[1]} steps each ({entries} entries, with byte copies "
-                       f"into a shadow device buffer), {dt:.1f} s on one core")}
+    from oracle.baseline_worker import run_instances
+
+    cores = max(1, min(16, os.cpu_count() or 1))
+    jobs = [(r, l) for l in range(w.layers) for r in range(w.batch)]
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(1) as pool:
+        e1, i1, s1 = pool.map(run_instances, [(w.cfg_id, overrides, jobs, budget_s)])[0]
+    with ctx.Pool(cores) as pool:
+        outs = pool.map(run_instances, [(w.cfg_id, overrides, jobs[c::cores], budget_s)
+                                         for c in range(cores)])
+    rate = sum(e / s for e, _, s in outs if s > 0)
+    insts = sum(i for _, i, _ in outs)
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next(line.split(":", 1)[1].strip() for line in f if line.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    return {"value": round(rate, 1), "unit": "entries/s", "cores": cores, "kind": "oracle",
+            "single_core_value": round(e1 / s1, 1) if s1 > 0 else None,
+            "sample": (f"{cores} worker processes x about {budget_s:.0f} s of oracle time each, "
+                       f"{insts} whole (request, layer) instances of {w.batch * w.layers} over "
+                       f"all {w.steps} steps (byte copies into a shadow device buffer); "
+                       f"alone, one worker did {i1} instances at the single-core rate; "
+                       f"host: {model}")}
 
 
 COPY_SOURCES = ("copy.hip", "copy.h", "device_common.h")
@@ -580,9 +581,23 @@ def main():
               "the path would shard). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    from sparse_attention_kv_request_amd import workloads
+
+    swap_mode = not (args.attention or args.topk or args.batched_state)
+    over = {"steps": args.warmup + args.steps}
+    if args.workload == 3:
+        over["num_steps"] = args.num_steps
+    if args.hot:
+        over["hot"] = args.hot
+    cpu_res = None
+    if swap_mode and not args.no_cpu_baseline:
+        # before this process touches the GPU: the workers are spawned
+        log("timing the CPU oracle baseline")
+        cpu_res = cpu_baseline(workloads.config(args.workload, **over), over, args.cpu_seconds)
+
     import torch
 
-    from sparse_attention_kv_request_amd import binding, workloads
+    from sparse_attention_kv_request_amd import binding
 
     torch.cuda.set_device(0)
     if args.attention:
@@ -595,11 +610,6 @@ def main():
         print(json.dumps(batched_state_bench(args, torch, binding, workloads)), flush=True)
         return
     W, K = args.warmup, args.steps
-    over = {"steps": W + K}
-    if args.workload == 3:
-        over["num_steps"] = args.num_steps
-    if args.hot:
-        over["hot"] = args.hot
     w = workloads.config(args.workload, **over)
     run = Runner(torch, binding, workloads, w, admission=args.admission,
                  extra_rows=args.extra_rows)
@@ -704,9 +714,8 @@ def main():
         res["graph"] = {"ms_per_step_eager": round(elapsed * 1e3 / K, 4),
                         "ms_per_step_graph": round(g_elapsed * 1e3 / K, 4),
                         "entries_per_s_graph": round(entries / g_elapsed, 1)}
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle baseline")
-        res["cpu_baseline"] = cpu_baseline(w, run.host, run.trace, args.cpu_seconds)
+    if cpu_res is not None:
+        res["cpu_baseline"] = cpu_res
     run.close()
     print(json.dumps(res), flush=True)
 
