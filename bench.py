@@ -576,9 +576,9 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(each request/layer cache instance is independent; see DESIGN.md for how "
-              "the path would shard). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: there is no multi-GPU path (every "
+              "(request, layer) cache instance is independent, so requests would shard "
+              "across GPUs with no exchange step). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     from sparse_attention_kv_request_amd import workloads

@@ -55,7 +55,7 @@ extern "C" {
 #define HISPARSE_E_INVAL (-1)       /* an argument is out of range or NULL */
 #define HISPARSE_E_NOMEM (-2)       /* a device or pinned host allocation failed */
 #define HISPARSE_E_HIP (-3)         /* a HIP runtime call failed */
-#define HISPARSE_E_UNSUPPORTED (-4) /* valid request outside what this build supports */
+#define HISPARSE_E_UNSUPPORTED (-4) /* valid request outside what this library supports */
 
 /* Device-side error bits (sticky; see hisparse_get_error_flags). */
 #define HISPARSE_ERR_BAD_INDEX 1u     /* top-k entry outside [0, seq_len), not -1 */
@@ -75,7 +75,7 @@ extern "C" {
 #define HISPARSE_ADMIT_FREQUENT 1 /* most steps naming the key first */
 #define HISPARSE_ADMIT_FIRST 2    /* first occurrence alone */
 
-/* Limits of this build. */
+/* Limits of this library. */
 #define HISPARSE_MAX_HOT 32768        /* hot_buffer_size bound (PR #32162, "Risks and impact") */
 #define HISPARSE_MIN_STEPS 2          /* multi-step range (PR #32162, item 2) */
 #define HISPARSE_MAX_STEPS 4

@@ -674,7 +674,7 @@ const char* hisparse_strerror(int code) {
     case HISPARSE_E_INVAL: return "invalid argument";
     case HISPARSE_E_NOMEM: return "out of memory";
     case HISPARSE_E_HIP: return "HIP runtime error";
-    case HISPARSE_E_UNSUPPORTED: return "outside the limits of this build";
+    case HISPARSE_E_UNSUPPORTED: return "outside the limits of this library";
     default: return "unknown status";
   }
 }
