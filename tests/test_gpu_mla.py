@@ -166,6 +166,13 @@ def test_mla_replay_after_large_score_jump(item):
 
 
 @pytest.mark.parametrize("item", [1152, 656])
+def test_mla_unsplit_rows(item):
+    """256 rows: one workgroup per row and head group already fills the
+    chip, so the locations are not split (outputs written directly)."""
+    run_case(R=256, B=256, H=300, K=200, N=600, item=item, heads=16, seed=item + 11, calls=1)
+
+
+@pytest.mark.parametrize("item", [1152, 656])
 def test_mla_bench_shape(item):
     """The bench's launch shape: 64 rows x 128 heads x 2048 locations (four
     splits of 512 per row), rows placed by a swap call; every row against the

@@ -120,6 +120,17 @@ def test_full_size(B, N):
     log(f"topk B={B} N={N}: exact")
 
 
+def test_k_above_the_staging_limit():
+    """k = 5000 (more outputs than the 4096 the kernels stage in LDS): the
+    word-by-word output of single-chunk rows and of the merge of split rows."""
+    rng = np.random.default_rng(6)
+    lg = logits_with_specials(rng, 3, 32768, ties=True)
+    run(lg, [32768, 20000, 4999], 5000, mode="paged",
+        page_table=rng.permutation(3 * 512).astype(np.int32).reshape(3, 512), page_size=64)
+    lg = logits_with_specials(rng, 2, 4 * 32768)
+    run(lg, [4 * 32768, 3 * 32768 + 7], 5000, mode="ragged", row_offsets=[0, 4 * 32768])
+
+
 def test_rejects_bad_arguments():
     with pytest.raises(binding.HiSparseError) as e:
         binding.TopkIndexBuilder(4, 17 * 32768, 2048, device=DEV)  # 17 chunks x 2048 > 32768
