@@ -14,16 +14,18 @@
 // the hot buffer straight into LDS with 16-byte global->LDS loads (no VGPR
 // staging), double buffered so the next tile streams in while the current
 // one is computed; fp8 rows land in a raw buffer and are dequantised to bf16
-// by the whole workgroup.  Each wave owns 32 heads (two 16-head blocks) and
-// computes with MFMA 16x16x32 bf16:
-//   S^T (tokens x heads) = K (tokens x 576) . Q^T    -- Q^T held in VGPRs
-//   O^T (dims x heads)  += V^T (dims x tokens) . P^T -- O^T in AGPRs
-// One K operand read from LDS feeds both head blocks.  V^T operands come from
-// the same token-major tile through the transposing LDS read: a 16-lane group
-// that reads a 4-token x 16-dim block hands every lane the 4 tokens of one dim.
-// With heads as the N dimension every lane's accumulators belong to one head,
-// so the online-softmax rescale is a per-lane scalar, and the C layout of S^T
-// is directly the B operand of the P.V product.
+// by the whole workgroup.  Each wave owns 32 heads and computes with MFMA
+// 32x32x16 bf16 (one wave per SIMD issues it at 82-86 % of the matrix peak,
+// MFMA 16x16x32 at 54 %):
+//   S^T (32 tokens x 32 heads) = K (tokens x 576) . Q^T  -- Q^T held in VGPRs
+//   O^T (dims x heads)        += V^T (dims x tokens) . P^T -- O^T in AGPRs
+// V^T operands come from the same token-major tile through the transposing
+// LDS read: a 16-lane group that reads a 4-token x 16-dim block hands every
+// lane the 4 tokens of one dim.  With heads as the N dimension every lane's
+// accumulators belong to one head (lane l: head l%32), so the softmax
+// reductions are in-lane plus one exchange with lane l ^ 32, and the C layout
+// of S^T is directly the B operand of the P.V product (the P.V contraction
+// takes the tokens in the order the lanes hold them).
 #include <type_traits>
 
 #include "internal.h"
@@ -35,6 +37,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
@@ -50,8 +53,8 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;  // 256
 constexpr int kHeadsPerWave = 32;
 constexpr int kHeadsPerGroup = kHeadsPerWave * kWaves;
-constexpr int kKSteps = kDim / 32;        // 18
-constexpr int kDimBlocks = kLatent / 16;  // 32
+constexpr int kKSteps = kDim / 16;        // 36 k-steps of MFMA 32x32x16
+constexpr int kDimBlocks = kLatent / 32;  // 16 blocks of 32 output dims
 constexpr int kMaxPerSplit = 2048;        // locations one workgroup handles
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kQkAhead = 2;               // k-steps of K operands read ahead
@@ -214,16 +217,28 @@ __device__ __forceinline__ float xor16(float x) {
   return __builtin_bit_cast(float, (threadIdx.x & 16) ? r[0] : r[1]);
 }
 
-// K operand of k-step ks for tokens 16 st + [0, 16): base = tile row n, dim 8g.
-__device__ __forceinline__ bf16x8 k_operand(const uint16_t* base, int ks, int st) {
-  return as_bf16x8(*reinterpret_cast<const u32x4*>(base + st * 16 * kPitch + 32 * ks));
+// K operand (A of MFMA 32x32x16) of k-step ks: base = tile row lane%32, dim
+// 8(lane/32).
+__device__ __forceinline__ bf16x8 k_operand(const uint16_t* base, int ks) {
+  return as_bf16x8(*reinterpret_cast<const u32x4*>(base + 16 * ks));
 }
 
-// V^T operand of dim block [d0, d0 + 16): two transposing reads at p (rows
-// 4g + n/4) and p + 16 rows, giving k-slots 0..3 and 4..7.
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// V^T operand (A of MFMA 32x32x16) of a 32-dim block and 16 tokens: two
+// transposing reads at p and p + 8 rows, giving k-slots 0..3 and 4..7.
 __device__ __forceinline__ bf16x8 v_operand(const uint16_t* p) {
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(p));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(p + 16 * kPitch));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(p + 8 * kPitch));
   const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
   return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
 }
@@ -268,25 +283,24 @@ void mla_decode(MlaArgs a) {
 
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: scalar branches
-  const int g = lane >> 4;       // lane group
-  const int n = lane & 15;       // head within a block / row within a 16-row tile
+  const int hl = lane & 31;      // head of the wave's 32 / tile row of the K operand
+  const int h2 = lane >> 5;      // k-slot half
 
-  // Q^T operands: lane holds q[head][32*ks + 8*g .. +8] of its head in each
-  // of the wave's two 16-head blocks (issued behind the location loads, so
-  // the row table waits for the locations only and the queries land behind
-  // the first tile's gather; nothing uses them before the first tile).  A
-  // lane past the last head loads head 0: its results are never stored, and
-  // its scores equal head 0's, so it cannot ask for a restart head 0 would
-  // not ask for.
-  bf16x8 qreg[2][kKSteps];
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const int head = hg * kHeadsPerGroup + wave * kHeadsPerWave + hb * 16 + n;
+  // Q^T operands (B of S^T = K . Q^T): lane holds q[head][16 ks + 8 (lane/32)
+  // .. +8] of head lane%32 of the wave's 32 (issued behind the location
+  // loads, so the row table waits for the locations only and the queries
+  // land behind the first tile's gather; nothing uses them before the first
+  // tile).  A lane past the last head loads head 0: its results are never
+  // stored, and its scores equal head 0's, so it cannot ask for a restart
+  // head 0 would not ask for.
+  bf16x8 qreg[kKSteps];
+  {
+    const int head = hg * kHeadsPerGroup + wave * kHeadsPerWave + hl;
     const uint16_t* qh =
-        a.q + (static_cast<size_t>(b) * a.heads + (head < a.heads ? head : 0)) * kDim;
+        a.q + (static_cast<size_t>(b) * a.heads + (head < a.heads ? head : 0)) * kDim + 8 * h2;
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks)
-      qreg[hb][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qh + 32 * ks + 8 * g));
+      qreg[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qh + 16 * ks));
   }
 
   int64_t rowv[kRowIters];
@@ -306,13 +320,13 @@ void mla_decode(MlaArgs a) {
 
   __syncthreads();  // rows[] complete
 
-  f32x4 acc[2][kDimBlocks];
+  // O^T of the wave's 32 heads: block db holds dims 32 db + [0, 32); its
+  // register j at lane l is dim 32 db + 8 (j/4) + 4 (l/32) + j%4 of head l%32
+  f32x16 acc[kDimBlocks];
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-    for (int i = 0; i < kDimBlocks; ++i) acc[hb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref[2] = {-INFINITY, -INFINITY};  // reference of the weights, log2 units
-  float l_run[2] = {0.f, 0.f};              // sum of the (bf16-rounded) weights
+  for (int i = 0; i < kDimBlocks; ++i) acc[i] = zero16();
+  float m_ref = -INFINITY;  // reference of the weights of head lane%32, log2 units
+  float l_run = 0.f;        // sum of its (bf16-rounded) weights
 
   // buffers: bf16 rows -> tiles at stage + {0, kTileBytes};
   //          fp8 rows  -> tile at stage, raw tiles at stage + kTileBytes + {0, kRawBytes}
@@ -361,124 +375,109 @@ void mla_decode(MlaArgs a) {
     } else {
       tile = reinterpret_cast<const uint16_t*>(stage + cur * kTileBytes);
     }
-    // S^T for tokens [0,16) and [16,32) of the tile, both head blocks
+    // S^T (32 tokens x the wave's 32 heads) = K . Q^T: 36 k-steps of MFMA
+    // 32x32x16 in one accumulation chain, K operands read
+    // kQkAhead steps ahead (one wave per SIMD: nothing else hides the LDS
+    // latency), the interleave pinned by scheduling-group barriers.
     __builtin_amdgcn_sched_barrier(0);
-    f32x4 s[2][2];
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) s[hb][st] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // Software pipeline: the K operands of k-step ks + kQkAhead are read
-    // while the MFMAs of k-step ks run (one wave per SIMD: nothing else hides
-    // the LDS latency), the interleave pinned by scheduling-group barriers.
+    f32x16 s0 = zero16();
     {
-      const uint16_t* kbase = tile + n * kPitch + 8 * g;
-      bf16x8 kf[kQkAhead + 1][2];
+      const uint16_t* kbase = tile + hl * kPitch + 8 * h2;
+      bf16x8 kf[kQkAhead + 1];
 #pragma unroll
-      for (int j = 0; j < kQkAhead; ++j)
-#pragma unroll
-        for (int st = 0; st < 2; ++st) kf[j][st] = k_operand(kbase, j, st);
+      for (int j = 0; j < kQkAhead; ++j) kf[j] = k_operand(kbase, j);
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
-        if (ks + kQkAhead < kKSteps) {
-#pragma unroll
-          for (int st = 0; st < 2; ++st)
-            kf[(ks + kQkAhead) % (kQkAhead + 1)][st] = k_operand(kbase, ks + kQkAhead, st);
-        }
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb)
-            s[hb][st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks % (kQkAhead + 1)][st],
-                                                                qreg[hb][ks], s[hb][st], 0, 0, 0);
+        if (ks + kQkAhead < kKSteps) kf[(ks + kQkAhead) % (kQkAhead + 1)] = k_operand(kbase, ks + kQkAhead);
+        s0 = mfma32(kf[ks % (kQkAhead + 1)], qreg[ks], s0);
       }
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kQkAhead, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kQkAhead, 0);
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
-        if (ks + kQkAhead < kKSteps) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
+        if (ks + kQkAhead < kKSteps) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
 
-
-    // weights per head block; lane holds tokens 4g+i and 16+4g+i.  The
-    // maximum is taken over the unscaled scores (the scale is positive) and
-    // the scale folds into one FMA in front of the exponential; a tile whose
-    // rows are all present skips the per-score masking.
+    // Weights of head lane%32: register j holds token 8 (j/4) + 4 (lane/32) +
+    // j%4, lane ^ 32 the other 16 tokens.  The maximum is taken over the
+    // unscaled scores (the scale is positive) and the scale folds into one
+    // FMA in front of the exponential; a tile whose rows are all present
+    // skips the per-score masking.
     const bool full = valid == 0xFFFFFFFFu;
-    bf16x8 pop[2];
-    bool restart = false;
+    float raw[16];
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      float raw[8];
+    for (int j = 0; j < 16; ++j) raw[j] = s0[j];
+    if (!full) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) raw[i] = s[hb][i >> 2][i & 3];
-      if (!full) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int tok = (i < 4 ? 0 : 16) + 4 * g + (i & 3);
-          if (!((valid >> tok) & 1u)) raw[i] = -INFINITY;
-        }
+      for (int j = 0; j < 16; ++j) {
+        const int tok = 8 * (j >> 2) + 4 * h2 + (j & 3);
+        if (!((valid >> tok) & 1u)) raw[j] = -INFINITY;
       }
-      float rmax = fmaxf(fmaxf(fmaxf(raw[0], raw[1]), fmaxf(raw[2], raw[3])),
-                         fmaxf(fmaxf(raw[4], raw[5]), fmaxf(raw[6], raw[7])));
-      rmax = fmaxf(rmax, xor16(rmax));
-      rmax = fmaxf(rmax, xor32(rmax));
-      const float tmax = rmax * a.scale_log2;
-      const bool beyond = tmax > m_ref[hb] + kRefSlack;
-      restart |= beyond && m_ref[hb] != -INFINITY;
-      if (beyond) m_ref[hb] = tmax;
-      // no reference yet means no valid row yet: every score is -inf, every p 0
-      const float mr = m_ref[hb] == -INFINITY ? 0.f : m_ref[hb];
-      float psum = 0.f;
-      u16x8 pbits;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        // v_exp_f32: results below the smallest normal flush to 0
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(raw[i], a.scale_log2, -mr));
-        const uint16_t pb = bf16_bits(p);
-        pbits[i] = pb;
-        psum += __builtin_bit_cast(float, static_cast<uint32_t>(pb) << 16);
-      }
-      psum += xor16(psum);
-      psum += xor32(psum);
-      l_run[hb] = fresh ? psum : l_run[hb] + psum;
-      pop[hb] = __builtin_bit_cast(bf16x8, pbits);
     }
+    float m8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m8[j] = fmaxf(raw[j], raw[j + 8]);
+    float rmax = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
+                       fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
+    rmax = fmaxf(rmax, xor32(rmax));
+    const float tmax = rmax * a.scale_log2;
+    const bool beyond = tmax > m_ref + kRefSlack;
+    const bool restart = beyond && m_ref != -INFINITY;
+    if (beyond) m_ref = tmax;
+    // no reference yet means no valid row yet: every score is -inf, every p 0
+    const float mr = m_ref == -INFINITY ? 0.f : m_ref;
+    float psum = 0.f;
+    u16x8 pbits[2];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      // v_exp_f32: results below the smallest normal flush to 0
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(raw[j], a.scale_log2, -mr));
+      const uint16_t pb = bf16_bits(p);
+      pbits[j >> 3][j & 7] = pb;
+      psum += __builtin_bit_cast(float, static_cast<uint32_t>(pb) << 16);
+    }
+    psum += xor32(psum);
+    l_run = fresh ? psum : l_run + psum;
+    const bf16x8 pop[2] = {__builtin_bit_cast(bf16x8, pbits[0]), __builtin_bit_cast(bf16x8, pbits[1])};
     if (__any(restart) && lane == 0) restart_at[cur] = phase;
 
-    // O^T += V^T . P^T.  Dim block db covers dims 16db + [0,16).  Its A
-    // operand (lane: dim 16db + n, k-slots = tokens 4g..4g+3 and
-    // 16+4g..16+4g+3, the token order of P^T) is two transposing reads: lane
-    // n of group g points at row 4g + n/4 (then 16 + 4g + n/4), dims
-    // 16db + 4(n%4) .. +3.
-    const uint16_t* vbase = tile + (4 * g + (n >> 2)) * kPitch + 4 * (n & 3);
+    // O^T += V^T . P^T, MFMA 32x32x16: for token half u, k-slot 8 (lane/32)
+    // + i is token 16u + 4 (lane/32) + i (i < 4) or 16u + 8 + 4 (lane/32) +
+    // i - 4, the tokens of the lane's S^T registers 8u .. 8u + 7, so P^T
+    // comes straight from the softmax.  The V^T operand of (block db, half
+    // u) is two transposing reads: lane j of 16-lane group q points at row
+    // 16u + 4 (q/2) + j/4 (then 8 rows below), dims 32 db + 16 (q%2) +
+    // 4 (j%4) .. +3, and receives dim 32 db + lane%32 of those 4 rows.
+    // Operands run half-major, so consecutive MFMAs feed different blocks.
+    const int q16 = lane >> 4, j16 = lane & 15;
+    const uint16_t* vbase =
+        tile + (4 * (q16 >> 1) + (j16 >> 2)) * kPitch + 16 * (q16 & 1) + 4 * (j16 & 3);
     __builtin_amdgcn_sched_barrier(0);
     if (fresh) {  // replay: the sums start over
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-        for (int db = 0; db < kDimBlocks; ++db) acc[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int db = 0; db < kDimBlocks; ++db) acc[db] = zero16();
     }
     {
+      constexpr int kOps = 2 * kDimBlocks;  // operand o: half o / 16, block o % 16
+      auto vop = [&](int o) {
+        return v_operand(vbase + 16 * (o / kDimBlocks) * kPitch + 32 * (o % kDimBlocks));
+      };
       bf16x8 vf[kPvAhead + 1];
 #pragma unroll
-      for (int j = 0; j < kPvAhead; ++j) vf[j] = v_operand(vbase + 16 * j);
+      for (int j = 0; j < kPvAhead; ++j) vf[j] = vop(j);
 #pragma unroll
-      for (int db = 0; db < kDimBlocks; ++db) {
-        if (db + kPvAhead < kDimBlocks)
-          vf[(db + kPvAhead) % (kPvAhead + 1)] = v_operand(vbase + 16 * (db + kPvAhead));
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-          acc[hb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db % (kPvAhead + 1)], pop[hb],
-                                                                acc[hb][db], 0, 0, 0);
+      for (int o = 0; o < kOps; ++o) {
+        if (o + kPvAhead < kOps) vf[(o + kPvAhead) % (kPvAhead + 1)] = vop(o + kPvAhead);
+        acc[o % kDimBlocks] =
+            mfma32(vf[o % (kPvAhead + 1)], pop[o / kDimBlocks], acc[o % kDimBlocks]);
       }
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPvAhead, 0);
 #pragma unroll
-      for (int db = 0; db < kDimBlocks; ++db) {
-        if (db + kPvAhead < kDimBlocks) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+      for (int o = 0; o < kOps; ++o) {
+        if (o + kPvAhead < kOps) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -486,33 +485,54 @@ void mla_decode(MlaArgs a) {
     it = next;
   }
 
+  const int head = hg * kHeadsPerGroup + wave * kHeadsPerWave + hl;
+  if (head >= a.heads) return;
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  // block db, register 4 jj + i  <->  dim 32 db + 8 jj + 4 (lane/32) + i
+  if (a.splits == 1) {
+    float* dst = a.out + (static_cast<size_t>(b) * a.heads + head) * kLatent + 4 * h2;
+    if (a.lse != nullptr && h2 == 0)
+      a.lse[static_cast<size_t>(b) * a.heads + head] =
+          l_run > 0.f ? (m_ref + log2f(l_run)) * kLn2 : -INFINITY;
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const int head = hg * kHeadsPerGroup + wave * kHeadsPerWave + hb * 16 + n;
-    if (head >= a.heads) continue;
-    const float inv = l_run[hb] > 0.f ? 1.f / l_run[hb] : 0.f;
-    // dim block db, C row 4g + i  <->  dim 16db + 4g + i
-    if (a.splits == 1) {
-      float* dst = a.out + (static_cast<size_t>(b) * a.heads + head) * kLatent;
-      if (a.lse != nullptr && g == 0)
-        a.lse[static_cast<size_t>(b) * a.heads + head] =
-            l_run[hb] > 0.f ? (m_ref[hb] + log2f(l_run[hb])) * kLn2 : -INFINITY;
+    for (int db = 0; db < kDimBlocks; ++db)
 #pragma unroll
-      for (int db = 0; db < kDimBlocks; ++db)
-        *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * g) = acc[hb][db] * inv;
-    } else {
-      // a split's output is a convex combination of its values, so fp16
-      // (relative 2^-11) holds it; the split's max and sum stay fp32
-      const size_t ps = (static_cast<size_t>(b) * a.splits + split) * a.heads + head;
-      _Float16* dst = a.part_out + ps * kLatent;
-      if (g == 0) {
-        a.part_ml[2 * ps] = m_ref[hb];
-        a.part_ml[2 * ps + 1] = l_run[hb];
+      for (int jj = 0; jj < 4; ++jj)
+        *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * jj) =
+            f32x4{acc[db][4 * jj], acc[db][4 * jj + 1], acc[db][4 * jj + 2], acc[db][4 * jj + 3]} * inv;
+  } else {
+    // a split's output is a convex combination of its values, so fp16
+    // (relative 2^-11) holds it; the split's max and sum stay fp32
+    const size_t ps = (static_cast<size_t>(b) * a.splits + split) * a.heads + head;
+    if (h2 == 0) {
+      a.part_ml[2 * ps] = m_ref;
+      a.part_ml[2 * ps + 1] = l_run;
+    }
+    // Lanes l and l ^ 32 hold alternating 4-dim groups of one head: one swap
+    // of the group each lacks (the fp16 bits of 4 dims, two dwords) gives
+    // lane l dims 32 db + 16 p + 8 (l/32) .. +7, one 16-byte store.
+    _Float16* dst8 = a.part_out + ps * kLatent + 8 * h2;
+#pragma unroll
+    for (int db = 0; db < kDimBlocks; ++db) {
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        const f32x4 g0 = f32x4{acc[db][8 * pr], acc[db][8 * pr + 1], acc[db][8 * pr + 2],
+                               acc[db][8 * pr + 3]} * inv;
+        const f32x4 g1 = f32x4{acc[db][8 * pr + 4], acc[db][8 * pr + 5], acc[db][8 * pr + 6],
+                               acc[db][8 * pr + 7]} * inv;
+        const u32x2 b0 = __builtin_bit_cast(u32x2, __builtin_convertvector(g0, f16x4));
+        const u32x2 b1 = __builtin_bit_cast(u32x2, __builtin_convertvector(g1, f16x4));
+        const u32x2 send = h2 == 0 ? b1 : b0;
+        u32x2 recv;
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const auto r = __builtin_amdgcn_permlane32_swap(send[w], send[w], false, false);
+          recv[w] = h2 ? r[0] : r[1];
+        }
+        const u32x4 out = h2 == 0 ? u32x4{b0[0], b0[1], recv[0], recv[1]}
+                                  : u32x4{recv[0], recv[1], b1[0], b1[1]};
+        *reinterpret_cast<u32x4*>(dst8 + 32 * db + 16 * pr) = out;
       }
-#pragma unroll
-      for (int db = 0; db < kDimBlocks; ++db)
-        *reinterpret_cast<f16x4*>(dst + 16 * db + 4 * g) =
-            __builtin_convertvector(acc[hb][db] * inv, f16x4);
     }
   }
 }
