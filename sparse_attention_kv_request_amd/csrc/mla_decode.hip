@@ -160,10 +160,16 @@ struct TileLoader {
     const bool present = lane < kTile && rowoff[t0 + (lane & (kTile - 1))] != kAbsent;
     return static_cast<uint32_t>(__ballot(present));
   }
-  // Load k of this wave.
+  // Load k of this wave.  Issued as inline assembly so that the compiler
+  // does not track these LDS writes: it cannot tell the two tile buffers
+  // apart and would make the transposing LDS reads of the current tile wait
+  // for the next tile's gather.  Completion is awaited explicitly (vmcnt 0)
+  // before the barrier that publishes a tile.
   __device__ __forceinline__ void fire(__amdgpu_buffer_rsrc_t kv, int k, int wave) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(kv, (LDS_AS void*)(buf + (wave + kWaves * k) * kWave * 16),
-                                             16, off[k], 0, 0, 0);
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (LDS_AS uint8_t*)(buf + (wave + kWaves * k) * kWave * 16))));
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off[k]), "s"(kv), "{m0}"(lds)
+                 : "memory");
   }
   // The loads from k0 on that this wave has.
   __device__ __forceinline__ void fire_rest(__amdgpu_buffer_rsrc_t kv, int k0, int wave) {
@@ -353,7 +359,16 @@ void mla_decode(MlaArgs a) {
   // wave reads the request, fetches the first tile again instead of the next
   // one and, one phase later, replays the range from the start with zeroed
   // sums and accumulators (a write-only reset; the tile computed in between
-  // is discarded with the rest).
+  // is discarded with the rest).  A request posted by the last tile is read
+  // after one more barrier at the end of the range, which then starts over
+  // (a replay that a later phase requests again is harmless: it restarts
+  // the sums once more).
+  //
+  // The query loads and the first tile are awaited by the compiler's own
+  // wait instruction here, so that it knows the query registers are loaded
+  // and puts no waits for them inside the loop (where they would also wait
+  // for the gather).
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   int it = 0;          // tile in buffer `cur`
   bool fresh = false;  // this phase starts the sums over
   for (int phase = 0; it < ntiles; ++phase) {
@@ -410,11 +425,10 @@ void mla_decode(MlaArgs a) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) raw[j] = s0[j];
     if (!full) {
+      const uint32_t lv = valid >> (4 * h2);  // bit 8 (j/4) + j%4: register j's row
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int tok = 8 * (j >> 2) + 4 * h2 + (j & 3);
-        if (!((valid >> tok) & 1u)) raw[j] = -INFINITY;
-      }
+      for (int j = 0; j < 16; ++j)
+        if (!((lv >> (8 * (j >> 2) + (j & 3))) & 1u)) raw[j] = -INFINITY;
     }
     float m8[8];
 #pragma unroll
@@ -483,6 +497,18 @@ void mla_decode(MlaArgs a) {
     }
     fresh = replay;
     it = next;
+    if (it >= ntiles) {
+      // end of the range: the gather of the all-absent tile past it lands,
+      // and a request posted by the last tile sends the range round again
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (restart_at[cur] == phase) {
+        valid_next = ld.prepare(rowoff, 0, dst(cur ^ 1), wave, lane);
+        ld.fire_rest(kv, 0, wave);
+        it = 0;
+        fresh = true;
+      }
+    }
   }
 
   const int head = hg * kHeadsPerGroup + wave * kHeadsPerWave + hl;

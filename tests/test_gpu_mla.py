@@ -166,6 +166,17 @@ def test_mla_replay_after_large_score_jump(item):
 
 
 @pytest.mark.parametrize("item", [1152, 656])
+def test_mla_replay_requested_by_the_last_tile(item):
+    """The only large score of a split sits in its last tile (a full tile,
+    and a partial one): the request is read after the range ends and the
+    split still replays."""
+    run_case(R=64, B=64, H=400, K=300, N=1200, item=item, heads=128, seed=item + 5, calls=1,
+             boost=[(0, 80, 5000.0)])
+    run_case(R=64, B=64, H=400, K=280, N=1200, item=item, heads=128, seed=item + 6, calls=1,
+             boost=[(3, 270, 5000.0)])
+
+
+@pytest.mark.parametrize("item", [1152, 656])
 def test_mla_unsplit_rows(item):
     """256 rows: one workgroup per row and head group already fills the
     chip, so the locations are not split (outputs written directly)."""
