@@ -40,7 +40,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
@@ -63,22 +62,34 @@ constexpr int kSchedMfma = 0x008;         // scheduling-group masks: MFMA
 constexpr int kSchedDsRead = 0x100;       // LDS read
 constexpr float kRefSlack = 64.f;         // log2 headroom of the weights over their reference
 
-// bf16 tile: row pitch 584 elements = 1168 B = 73 16-byte slots (292 dwords:
-// 16 consecutive rows start in distinct 4-bank groups).  A global->LDS load
-// instruction fills 64 consecutive slots, so a tile takes 37 of them and its
-// buffer is rounded up to 37 KiB.
-constexpr int kPitch = kDim + 8;
-constexpr int kRowSlots = kPitch / 8;                                  // 73
-constexpr int kTileInstr = (kTile * kRowSlots + kWave - 1) / kWave;    // 37
-constexpr int kTileBytes = kTileInstr * kWave * 16;                    // 37888
+// bf16 tile: row pitch 608 elements = 1216 B = 76 16-byte slots, and the
+// 16-byte chunk c of row r sits in slot c ^ ((r >> 2) & 3) of its row.  With
+// 64 banks of 4 bytes a slot covers one of 16 four-bank groups, slot p of row
+// r group (12 r + p) mod 16.  That makes both operand reads conflict-free:
+// the K reads (16 lanes: 16 consecutive rows, one chunk) hit 16 groups since
+// 12 r takes every multiple of 4 once per 4 rows and the XOR separates the
+// four rows that share one; the transposing V reads (32 lanes: 4 consecutive
+// rows x 4 aligned chunks) keep each row's chunks inside one aligned 4-group
+// and put the 4 rows 12 apart.  (A 73-slot pitch without the XOR gave the V
+// reads a two-way conflict.)  A global->LDS load instruction fills 64
+// consecutive slots, so a tile takes 38 of them; the swizzle lives in the
+// global offsets each lane loads.
+constexpr int kPitch = kDim + 32;
+constexpr int kRowSlots = kPitch / 8;                                  // 76
+constexpr int kTileInstr = (kTile * kRowSlots + kWave - 1) / kWave;    // 38
+constexpr int kTileBytes = kTileInstr * kWave * 16;                    // 38912
+
+// Slot of 16-byte chunk c of tile row r (c < 72; aligned 4-chunk groups map
+// to themselves).
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 2) & 3); }
 // raw fp8 tile: rows of 656 B = 41 slots back to back
 constexpr int kFp8Row = kLatent + 16 + 2 * kRope;                      // 656
 constexpr int kFp8Slots = kFp8Row / 16;                                // 41
 constexpr int kRawInstr = (kTile * kFp8Slots + kWave - 1) / kWave;     // 21
 constexpr int kRawBytes = kRawInstr * kWave * 16;                      // 21504
-// LDS: bf16 rows use two tile buffers; fp8 rows two raw buffers + one tile
-constexpr int kStageBytes = (2 * kTileBytes > kTileBytes + 2 * kRawBytes)
-                                ? 2 * kTileBytes : kTileBytes + 2 * kRawBytes;
+// LDS: bf16 rows use two tile buffers; fp8 rows two tiles + two raw buffers
+template <bool fp8>
+constexpr int kStageBytes = fp8 ? 2 * kTileBytes + 2 * kRawBytes : 2 * kTileBytes;
 
 struct MlaArgs {
   const uint16_t* q;          // bf16 bits [B][Hq][576]
@@ -100,13 +111,12 @@ struct MlaArgs {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-__device__ __forceinline__ uint16_t bf16_bits(float x) {
-  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
-}
-
-// Two floats rounded to bf16 (nearest even), low one in the low half.
+// Two floats rounded to bf16 (nearest even), low one in the low half: one
+// pair conversion (v_cvt_pk_bf16_f32) rather than two conversions, a shift
+// and an OR.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return static_cast<uint32_t>(bf16_bits(lo)) | (static_cast<uint32_t>(bf16_bits(hi)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 // Token row of location `loc` of batch row b, or -1.
@@ -155,7 +165,10 @@ struct TileLoader {
       const int s = kWave * (wave + kWaves * k) + lane;
       const int r = s / kSlots;
       const int c = s - r * kSlots;
-      off[k] = rowoff[t0 + r] + (16 * c < kRowBytes ? 16u * c : kAbsent);
+      // bf16 rows: slot c holds chunk swz(r, c) (an involution; pad slots
+      // 72..75 stay past the row)
+      const int lc = kSlots == kFp8Slots ? c : swz(r, c);
+      off[k] = rowoff[t0 + r] + (16 * lc < kRowBytes ? 16u * lc : kAbsent);
     }
     const bool present = lane < kTile && rowoff[t0 + (lane & (kTile - 1))] != kAbsent;
     return static_cast<uint32_t>(__ballot(present));
@@ -179,13 +192,16 @@ struct TileLoader {
   }
 };
 
-// fp8 rows: the raw tile (codes, 4 scales, bf16 rope per row) -> bf16 tile.
-// Job j = 8 latent codes of one row (2048 jobs) or one 16-byte rope chunk
-// (256 jobs); consecutive lanes take consecutive chunks of a row.
-__device__ __forceinline__ void dequant_tile(const uint8_t* raw, uint16_t* tile) {
+// fp8 rows: the raw tile (codes, 4 scales, bf16 rope per row) -> bf16 tile,
+// as 9 jobs per thread.  Job k < 8 of thread t: latent chunk j = t + 256 k
+// (8 codes of row j / 64, chunk j % 64; consecutive lanes take consecutive
+// chunks of a row); job 8: rope chunk t % 8 of row t / 8 (16 bytes).
+constexpr int kDequantJobs = kTile * (kLatent / 8) / kThreads + 1;  // 9
+constexpr int kJobStride = 2;  // P.V operands per dequantisation job
+static_assert(kDequantJobs * kJobStride <= 2 * kDimBlocks, "jobs must fit the P.V loop");
+__device__ __forceinline__ void dequant_job(const uint8_t* raw, uint16_t* tile, int k) {
   const int tid = threadIdx.x;
-#pragma unroll 4
-  for (int k = 0; k < kTile * (kLatent / 8) / kThreads; ++k) {
+  if (k < kDequantJobs - 1) {
     const int j = tid + kThreads * k;
     const int r = j >> 6, c = j & 63;
     const uint8_t* src = raw + r * kFp8Row;
@@ -199,11 +215,10 @@ __device__ __forceinline__ void dequant_tile(const uint8_t* raw, uint16_t* tile)
       o[2 * w] = pack_bf16(x0[0] * sc, x0[1] * sc);
       o[2 * w + 1] = pack_bf16(x1[0] * sc, x1[1] * sc);
     }
-    *reinterpret_cast<u32x4*>(tile + r * kPitch + 8 * c) = o;
-  }
-  if (tid < kTile * 8) {
+    *reinterpret_cast<u32x4*>(tile + r * kPitch + 8 * swz(r, c)) = o;
+  } else {
     const int r = tid >> 3, c = tid & 7;
-    *reinterpret_cast<u32x4*>(tile + r * kPitch + kLatent + 8 * c) =
+    *reinterpret_cast<u32x4*>(tile + r * kPitch + 8 * swz(r, kLatent / 8 + c)) =
         *reinterpret_cast<const u32x4*>(raw + r * kFp8Row + kLatent + 16 + 16 * c);
   }
 }
@@ -223,10 +238,11 @@ __device__ __forceinline__ float xor16(float x) {
   return __builtin_bit_cast(float, (threadIdx.x & 16) ? r[0] : r[1]);
 }
 
-// K operand (A of MFMA 32x32x16) of k-step ks: base = tile row lane%32, dim
-// 8(lane/32).
-__device__ __forceinline__ bf16x8 k_operand(const uint16_t* base, int ks) {
-  return as_bf16x8(*reinterpret_cast<const u32x4*>(base + 16 * ks));
+// K operand (A of MFMA 32x32x16) of k-step ks: tile row lane%32, chunk 2 ks +
+// lane/32, whose slot is 4 (ks/2) + ((2 (ks%2) + lane/32) ^ swizzle): kb[p]
+// points at the slot of chunk 2 p + lane/32 of that row.
+__device__ __forceinline__ bf16x8 k_operand(const uint16_t* const kb[2], int ks) {
+  return as_bf16x8(*reinterpret_cast<const u32x4*>(kb[ks & 1] + 32 * (ks >> 1)));
 }
 
 __device__ __forceinline__ f32x16 zero16() {
@@ -241,10 +257,11 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 // V^T operand (A of MFMA 32x32x16) of a 32-dim block and 16 tokens: two
-// transposing reads at p and p + 8 rows, giving k-slots 0..3 and 4..7.
-__device__ __forceinline__ bf16x8 v_operand(const uint16_t* p) {
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(p));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(p + 8 * kPitch));
+// transposing reads, at plo and at phi (8 rows below, with that row's
+// swizzle), giving k-slots 0..3 and 4..7.
+__device__ __forceinline__ bf16x8 v_operand(const uint16_t* plo, const uint16_t* phi) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(plo));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(phi));
   const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
   return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
 }
@@ -252,8 +269,8 @@ __device__ __forceinline__ bf16x8 v_operand(const uint16_t* p) {
 template <bool fp8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode(MlaArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t stage[kStageBytes];
-  __shared__ uint32_t rowoff[kMaxPerSplit + kTile + 1];  // byte offset of each location's row
+  __shared__ __attribute__((aligned(1024))) uint8_t stage[kStageBytes<fp8>];
+  __shared__ uint32_t rowoff[kMaxPerSplit + 2 * kTile + 1];  // byte offset of each location's row
   __shared__ int32_t restart_at[2];
 
   // XCD-aware mapping (workgroups are dealt to the 8 XCDs round robin):
@@ -274,11 +291,12 @@ void mla_decode(MlaArgs a) {
   if (tid < 2) restart_at[tid] = -2;
 
   // byte offsets of this split's rows (kAbsent = skipped), padded with
-  // kAbsent up to one tile past the last one.  Every location load goes out
+  // kAbsent up to two tiles past the last one (plus the one row a raw fp8
+  // gather's last instruction reaches into).  Every location load goes out
   // before the first is used (one round trip, not one per pass), and so do
   // the page-table loads of page mode.
-  constexpr int kRowIters = (kMaxPerSplit + kTile + 1 + kThreads - 1) / kThreads;
-  const int padded = (nrows + kTile - 1) / kTile * kTile + kTile + 1;
+  constexpr int kRowIters = (kMaxPerSplit + 2 * kTile + 1 + kThreads - 1) / kThreads;
+  const int padded = (nrows + kTile - 1) / kTile * kTile + 2 * kTile + 1;
   const int32_t* lrow = a.locs + static_cast<size_t>(b) * a.n_locs + t_begin;
   int32_t locv[kRowIters];
 #pragma unroll
@@ -334,62 +352,29 @@ void mla_decode(MlaArgs a) {
   float m_ref = -INFINITY;  // reference of the weights of head lane%32, log2 units
   float l_run = 0.f;        // sum of its (bf16-rounded) weights
 
-  // buffers: bf16 rows -> tiles at stage + {0, kTileBytes};
-  //          fp8 rows  -> tile at stage, raw tiles at stage + kTileBytes + {0, kRawBytes}
   const __amdgpu_buffer_rsrc_t kv = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(a.kv), 0, static_cast<int>(a.kv_rows * a.item_bytes), 0x00020000);
   using Loader = std::conditional_t<fp8, TileLoader<kFp8Slots, kRawInstr>,
                                     TileLoader<kRowSlots, kTileInstr>>;
   Loader ld;
-  auto dst = [&](int buf) {
-    return fp8 ? stage + kTileBytes + buf * kRawBytes : stage + buf * kTileBytes;
-  };
   const int ntiles = (nrows + kTile - 1) / kTile;
-  uint32_t valid_next = 0u;  // valid rows of the tile in flight
-  if (ntiles > 0) {
-    valid_next = ld.prepare(rowoff, 0, dst(0), wave, lane);
-    ld.fire_rest(kv, 0, wave);
-  }
   // The weights are exp2(s - m_ref) with m_ref fixed per head at the first
   // tile's maximum, so the accumulators are never rescaled (they sit in
   // AGPRs, where a read-modify-write would cost more than the whole tile).
   // Weights may exceed 1 by up to 2^kRefSlack; a tile whose maximum goes
   // beyond that asks for a restart: it raises the wave's reference and
-  // posts the phase in restart_at[phase & 1].  After the next barrier every
-  // wave reads the request, fetches the first tile again instead of the next
-  // one and, one phase later, replays the range from the start with zeroed
-  // sums and accumulators (a write-only reset; the tile computed in between
-  // is discarded with the rest).  A request posted by the last tile is read
-  // after one more barrier at the end of the range, which then starts over
-  // (a replay that a later phase requests again is harmless: it restarts
-  // the sums once more).
+  // posts the phase in restart_at[phase & 1].  Every wave reads the request
+  // after a later barrier and replays the range from the start with zeroed
+  // sums and accumulators (a write-only reset; a replay that a later phase
+  // requests again is harmless: it restarts the sums once more).
   //
-  // The query loads and the first tile are awaited by the compiler's own
-  // wait instruction here, so that it knows the query registers are loaded
-  // and puts no waits for them inside the loop (where they would also wait
-  // for the gather).
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  int it = 0;          // tile in buffer `cur`
-  bool fresh = false;  // this phase starts the sums over
-  for (int phase = 0; it < ntiles; ++phase) {
-    const int cur = phase & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // this phase's tile is in LDS; every wave is done with the last one
-    const bool replay = restart_at[cur ^ 1] == phase - 1;
-    const int next = replay ? 0 : it + 1;
-    const uint32_t valid = valid_next;  // bit t: row t of this tile is present
-    // loads of the next tile (past the last tile: all absent, harmless zeros
-    // into the idle buffer)
-    valid_next = ld.prepare(rowoff, next * kTile, dst(cur ^ 1), wave, lane);
-    ld.fire_rest(kv, 0, wave);
-    const uint16_t* tile;
-    if constexpr (fp8) {
-      dequant_tile(stage + kTileBytes + cur * kRawBytes, reinterpret_cast<uint16_t*>(stage));
-      __syncthreads();
-      tile = reinterpret_cast<const uint16_t*>(stage);
-    } else {
-      tile = reinterpret_cast<const uint16_t*>(stage + cur * kTileBytes);
-    }
+  // One tile (bf16, in LDS): S^T, softmax and O^T += V^T P^T; job(o) runs
+  // beside the P.V MFMA of operand o.
+  // bf16: operand reads and MFMAs pinned in turn; fp8: left to the
+  // scheduler between the fenced dequantisation jobs
+  constexpr bool kPinPv = !fp8;
+  auto tile_step = [&](const uint16_t* tile, uint32_t valid, bool fresh, int phase,
+                       auto&& job) {
     // S^T (32 tokens x the wave's 32 heads) = K . Q^T: 36 k-steps of MFMA
     // 32x32x16 in one accumulation chain, K operands read
     // kQkAhead steps ahead (one wave per SIMD: nothing else hides the LDS
@@ -397,7 +382,9 @@ void mla_decode(MlaArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     f32x16 s0 = zero16();
     {
-      const uint16_t* kbase = tile + hl * kPitch + 8 * h2;
+      const int ksw = (hl >> 2) & 3;
+      const uint16_t* const kbase[2] = {tile + hl * kPitch + 8 * (h2 ^ ksw),
+                                        tile + hl * kPitch + 8 * ((2 + h2) ^ ksw)};
       bf16x8 kf[kQkAhead + 1];
 #pragma unroll
       for (int j = 0; j < kQkAhead; ++j) kf[j] = k_operand(kbase, j);
@@ -443,19 +430,21 @@ void mla_decode(MlaArgs a) {
     // no reference yet means no valid row yet: every score is -inf, every p 0
     const float mr = m_ref == -INFINITY ? 0.f : m_ref;
     float psum = 0.f;
-    u16x8 pbits[2];
+    u32x4 pbits[2];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < 16; j += 2) {
       // v_exp_f32: results below the smallest normal flush to 0
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(raw[j], a.scale_log2, -mr));
-      const uint16_t pb = bf16_bits(p);
-      pbits[j >> 3][j & 7] = pb;
-      psum += __builtin_bit_cast(float, static_cast<uint32_t>(pb) << 16);
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(raw[j], a.scale_log2, -mr));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(raw[j + 1], a.scale_log2, -mr));
+      const uint32_t pw = pack_bf16(p0, p1);
+      pbits[j >> 3][(j & 7) >> 1] = pw;
+      psum += __builtin_bit_cast(float, pw << 16);
+      psum += __builtin_bit_cast(float, pw & 0xFFFF0000u);
     }
     psum += xor32(psum);
     l_run = fresh ? psum : l_run + psum;
     const bf16x8 pop[2] = {__builtin_bit_cast(bf16x8, pbits[0]), __builtin_bit_cast(bf16x8, pbits[1])};
-    if (__any(restart) && lane == 0) restart_at[cur] = phase;
+    if (__any(restart) && lane == 0) restart_at[phase & 1] = phase;
 
     // O^T += V^T . P^T, MFMA 32x32x16: for token half u, k-slot 8 (lane/32)
     // + i is token 16u + 4 (lane/32) + i (i < 4) or 16u + 8 + 4 (lane/32) +
@@ -464,10 +453,16 @@ void mla_decode(MlaArgs a) {
     // u) is two transposing reads: lane j of 16-lane group q points at row
     // 16u + 4 (q/2) + j/4 (then 8 rows below), dims 32 db + 16 (q%2) +
     // 4 (j%4) .. +3, and receives dim 32 db + lane%32 of those 4 rows.
+    // Those dims are half j%2 of chunk 4 db + 2 (q%2) + (j%4)/2, whose slot
+    // differs from it only in the low two bits (the row's swizzle, (q/2) for
+    // the first read and (q/2 + 2) mod 4 for the second, whatever u and db).
     // Operands run half-major, so consecutive MFMAs feed different blocks.
     const int q16 = lane >> 4, j16 = lane & 15;
-    const uint16_t* vbase =
-        tile + (4 * (q16 >> 1) + (j16 >> 2)) * kPitch + 16 * (q16 & 1) + 4 * (j16 & 3);
+    const int vc = 2 * (q16 & 1) + ((j16 & 3) >> 1);
+    const uint16_t* vlo = tile + (4 * (q16 >> 1) + (j16 >> 2)) * kPitch +
+                          8 * (vc ^ ((q16 >> 1) & 3)) + 4 * (j16 & 1);
+    const uint16_t* vhi = tile + (4 * (q16 >> 1) + (j16 >> 2) + 8) * kPitch +
+                          8 * (vc ^ (((q16 >> 1) + 2) & 3)) + 4 * (j16 & 1);
     __builtin_amdgcn_sched_barrier(0);
     if (fresh) {  // replay: the sums start over
 #pragma unroll
@@ -476,7 +471,8 @@ void mla_decode(MlaArgs a) {
     {
       constexpr int kOps = 2 * kDimBlocks;  // operand o: half o / 16, block o % 16
       auto vop = [&](int o) {
-        return v_operand(vbase + 16 * (o / kDimBlocks) * kPitch + 32 * (o % kDimBlocks));
+        const int d = 16 * (o / kDimBlocks) * kPitch + 32 * (o % kDimBlocks);
+        return v_operand(vlo + d, vhi + d);
       };
       bf16x8 vf[kPvAhead + 1];
 #pragma unroll
@@ -486,27 +482,125 @@ void mla_decode(MlaArgs a) {
         if (o + kPvAhead < kOps) vf[(o + kPvAhead) % (kPvAhead + 1)] = vop(o + kPvAhead);
         acc[o % kDimBlocks] =
             mfma32(vf[o % (kPvAhead + 1)], pop[o / kDimBlocks], acc[o % kDimBlocks]);
+        job(o);
       }
+      if constexpr (kPinPv) {
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPvAhead, 0);
 #pragma unroll
       for (int o = 0; o < kOps; ++o) {
         if (o + kPvAhead < kOps) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
       }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
-    fresh = replay;
-    it = next;
-    if (it >= ntiles) {
-      // end of the range: the gather of the all-absent tile past it lands,
-      // and a request posted by the last tile sends the range round again
+  };
+
+  if constexpr (!fp8) {
+    // bf16 rows are gathered straight into the two tile buffers (stage + {0,
+    // kTileBytes}), one tile ahead.  A restart request read after a phase's
+    // barrier fetches the first tile again instead of the next one and, one
+    // phase later, replays from it; a request posted by the last tile is
+    // read after one more barrier at the end of the range.
+    auto dst = [&](int buf) { return stage + buf * kTileBytes; };
+    uint32_t valid_next = 0u;  // valid rows of the tile in flight
+    if (ntiles > 0) {
+      valid_next = ld.prepare(rowoff, 0, dst(0), wave, lane);
+      ld.fire_rest(kv, 0, wave);
+    }
+    // The query loads and the first tile are awaited by the compiler's own
+    // wait instruction here, so that it knows the query registers are loaded
+    // and puts no waits for them inside the loop (where they would also wait
+    // for the gather).
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    int it = 0;          // tile in buffer `cur`
+    bool fresh = false;  // this phase starts the sums over
+    for (int phase = 0; it < ntiles; ++phase) {
+      const int cur = phase & 1;
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (restart_at[cur] == phase) {
-        valid_next = ld.prepare(rowoff, 0, dst(cur ^ 1), wave, lane);
-        ld.fire_rest(kv, 0, wave);
-        it = 0;
-        fresh = true;
+      __syncthreads();  // this phase's tile is in LDS; every wave is done with the last one
+      const bool replay = restart_at[cur ^ 1] == phase - 1;
+      const int next = replay ? 0 : it + 1;
+      const uint32_t valid = valid_next;  // bit t: row t of this tile is present
+      // loads of the next tile (past the last tile: all absent, harmless
+      // zeros into the idle buffer)
+      valid_next = ld.prepare(rowoff, next * kTile, dst(cur ^ 1), wave, lane);
+      ld.fire_rest(kv, 0, wave);
+      tile_step(reinterpret_cast<const uint16_t*>(dst(cur)), valid, fresh, phase, [](int) {});
+      fresh = replay;
+      it = next;
+      if (it >= ntiles) {
+        // end of the range: the gather of the all-absent tile past it lands,
+        // and a request posted by the last tile sends the range round again
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (restart_at[cur] == phase) {
+          valid_next = ld.prepare(rowoff, 0, dst(cur ^ 1), wave, lane);
+          ld.fire_rest(kv, 0, wave);
+          it = 0;
+          fresh = true;
+        }
+      }
+    }
+  } else {
+    // fp8 rows: raw tiles are gathered two tiles ahead into R(0..1), and the
+    // next tile is dequantised into the idle bf16 tile T(pb ^ 1) by every
+    // thread in the gaps of the current tile's P.V MFMAs (9 jobs per
+    // thread: 8 latent jobs of 8 codes, one 16-byte rope chunk).  A phase
+    // computes tile ci from T(pb), dequantises raw tile di = ci + 1 from
+    // R(pb ^ 1) and gathers raw tile gi = ci + 2 into R(pb), which the
+    // previous phase's dequantisation read before its closing barrier.
+    // A restart request read after that barrier sends the next gather to
+    // tile 0: the two phases already in flight compute tiles whose sums are
+    // dropped, since every phase that computes tile 0 starts the sums over.
+    auto T = [&](int i) { return stage + i * kTileBytes; };
+    auto R = [&](int i) { return stage + 2 * kTileBytes + i * kRawBytes; };
+    uint32_t valid_c = 0u, valid_d = 0u;  // valid rows of tiles ci and di
+    if (ntiles > 0) {
+      valid_c = ld.prepare(rowoff, 0, R(0), wave, lane);
+      ld.fire_rest(kv, 0, wave);
+      valid_d = ld.prepare(rowoff, kTile, R(1), wave, lane);
+      ld.fire_rest(kv, 0, wave);
+    }
+    // the compiler's own wait (see the bf16 path): the queries are loaded
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (ntiles > 0) {
+      for (int k = 0; k < kDequantJobs; ++k)
+        dequant_job(R(0), reinterpret_cast<uint16_t*>(T(0)), k);
+    }
+    __syncthreads();  // tile 0 dequantised
+    int ci = 0, di = 1, gi = 2, pb = 0;
+    int pending = 0;  // discarded phases left before tile 0 comes round again
+    // at the top of a phase: T(pb) complete, R(pb ^ 1) landed, T(pb ^ 1) and
+    // R(pb) idle
+    for (int phase = 0; ci < ntiles || pending > 0; ++phase) {
+      const uint32_t valid_g = ld.prepare(rowoff, gi * kTile, R(pb), wave, lane);
+      ld.fire_rest(kv, 0, wave);
+      const uint8_t* raw = R(pb ^ 1);
+      uint16_t* nt = reinterpret_cast<uint16_t*>(T(pb ^ 1));
+      // job k runs after P.V operand kJobStride k + 1, fenced: hoisting every
+      // job's LDS loads ahead would spill (and loading them a job or two
+      // early measured slower)
+      tile_step(reinterpret_cast<const uint16_t*>(T(pb)), valid_c, ci == 0, phase, [&](int o) {
+        if (o % kJobStride == kJobStride - 1 && o / kJobStride < kDequantJobs) {
+          __builtin_amdgcn_sched_barrier(0);
+          dequant_job(raw, nt, o / kJobStride);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      });
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();  // raw tile gi landed, tile di dequantised, the request posted
+      ci = di;
+      di = gi;
+      gi = gi + 1;
+      pb ^= 1;
+      valid_c = valid_d;
+      valid_d = valid_g;
+      if (pending > 0) --pending;
+      if (restart_at[phase & 1] == phase) {
+        gi = 0;
+        pending = 2;
       }
     }
   }
