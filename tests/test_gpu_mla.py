@@ -177,6 +177,15 @@ def test_mla_replay_requested_by_the_last_tile(item):
 
 
 @pytest.mark.parametrize("item", [1152, 656])
+def test_mla_replay_in_two_tile_splits(item):
+    """Splits of two tiles (64 rows x 256 locations: four splits of 64) with
+    the large score in the second and last tile of three of them: the
+    replay starts while the tiles past the range are still in flight."""
+    run_case(R=64, B=64, H=400, K=256, N=1200, item=item, heads=128, seed=item + 13, calls=1,
+             boost=[(0, 40, 5000.0), (0, 97, 3000.0), (0, 255, 4000.0)])
+
+
+@pytest.mark.parametrize("item", [1152, 656])
 def test_mla_unsplit_rows(item):
     """256 rows: one workgroup per row and head group already fills the
     chip, so the locations are not split (outputs written directly)."""
