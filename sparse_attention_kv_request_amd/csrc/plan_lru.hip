@@ -170,21 +170,9 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
     reject_row<NT>(a, b, a.K, code, false);
     return;
   }
-  // slot->key of every order position, for the victims' commit
-  int oldk[EPH];
-#pragma unroll
-  for (int e = 0; e < EPH; ++e) oldk[e] = o[e] >= 0 ? sk[o[e]] : kEmpty;
-  for (int i = tid; i < T; i += NT) {
-    hkey[i] = 0u;
-    hval[i] = 0x7fffffff;
-  }
-  for (int i = tid; i < a.Hw; i += NT) used[i] = 0u;
-  for (int i = tid; i < sw; i += NT) mbits[i] = 0u;
-  __syncthreads();
-
-  // 1. validate and insert every entry; the first occurrence keeps its position.
-  // Entries among the newest ext tokens resolve to their ring row instead
-  // (the extra-page lookup, before the hash lookup) and stay out of the cache.
+  // 1. validate every entry.  Entries among the newest ext tokens resolve to
+  // their ring row instead (the extra-page lookup, before the hash lookup)
+  // and stay out of the cache.
   int32_t tok[EPT];
   int hpos[EPT];
   int ring[EPT];
@@ -198,6 +186,27 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
     ring[e] = extra ? a.ext_base + t % a.ext : -1;
     tok[e] = valid && !extra ? t : -1;
   }
+  // One round trip for the slot->key of every order position (the victims'
+  // commit) and the key->slot probe of every entry: the probe needs only the
+  // token, and nothing writes this instance's key->slot entries before the
+  // commit, so it goes out now and lands during the dedup below (duplicates
+  // probe too and read the same word; only representatives use it).
+  int oldk[EPH];
+#pragma unroll
+  for (int e = 0; e < EPH; ++e) oldk[e] = o[e] >= 0 ? sk[o[e]] : kEmpty;
+  int probe[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) probe[e] = tok[e] >= 0 ? static_cast<int>(ks[tok[e]]) : -1;
+  for (int i = tid; i < T; i += NT) {
+    hkey[i] = 0u;
+    hval[i] = 0x7fffffff;
+  }
+  for (int i = tid; i < a.Hw; i += NT) used[i] = 0u;
+  for (int i = tid; i < sw; i += NT) mbits[i] = 0u;
+  __syncthreads();
+
+  // insert every entry into the LDS hash; the first occurrence keeps its
+  // position
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
     hpos[e] = 0;
@@ -208,14 +217,14 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
   }
   __syncthreads();
 
-  // 2. representatives look their key up
+  // 2. representatives take their key's probe
   bool rep[EPT];
 #pragma unroll
   for (int e = 0; e < EPT; ++e) rep[e] = tok[e] >= 0 && hval[hpos[e]] == tid * EPT + e;
   __syncthreads();
   int slot[EPT];
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) slot[e] = rep[e] ? static_cast<int>(ks[tok[e]]) : -1;
+  for (int e = 0; e < EPT; ++e) slot[e] = rep[e] ? probe[e] : -1;
   int nmiss = 0;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
