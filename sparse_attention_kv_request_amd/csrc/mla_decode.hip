@@ -13,8 +13,9 @@
 // rows of the range are resolved once.  Tiles of 32 rows are gathered from
 // the hot buffer straight into LDS with 16-byte global->LDS loads (no VGPR
 // staging), double buffered so the next tile streams in while the current
-// one is computed; fp8 rows land in a raw buffer and are dequantised to bf16
-// by the whole workgroup.  Each wave owns 32 heads and computes with MFMA
+// one is computed; fp8 rows land two tiles ahead in raw buffers, and every
+// thread dequantises the next tile to bf16 between the current tile's P.V
+// MFMAs.  Each wave owns 32 heads and computes with MFMA
 // 32x32x16 bf16 (one wave per SIMD issues it at 82-86 % of the matrix peak,
 // MFMA 16x16x32 at 54 %):
 //   S^T (32 tokens x 32 heads) = K (tokens x 576) . Q^T  -- Q^T held in VGPRs
