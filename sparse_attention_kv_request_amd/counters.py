@@ -31,9 +31,10 @@ def calib():
     print(f"copied {CALIB_BYTES} bytes x 3", flush=True)
 
 
-def read_counter(path, kernel_substr, skip=0):
+def read_counter(path, kernel_substr, skip=0, limit=0):
     """Per-dispatch values of one counter for kernels whose name contains
-    `kernel_substr`, in dispatch order, the first `skip` dropped."""
+    `kernel_substr`, in dispatch order, the first `skip` dropped and at most
+    `limit` kept (0: all)."""
     vals = {}
     with open(path) as f:
         for row in csv.DictReader(f):
@@ -42,13 +43,13 @@ def read_counter(path, kernel_substr, skip=0):
                 continue
             disp = int(row.get("Dispatch_Id", row.get("Correlation_Id", "0")))
             vals[disp] = vals.get(disp, 0.0) + float(row["Counter_Value"])
-    seq = [vals[k] for k in sorted(vals)]
-    return seq[skip:]
+    seq = [vals[k] for k in sorted(vals)][skip:]
+    return seq[:limit] if limit else seq
 
 
 def summarize(args):
-    fetch = read_counter(args.fetch, args.kernel, args.skip)
-    write = read_counter(args.write, args.kernel, args.skip)
+    fetch = read_counter(args.fetch, args.kernel, args.skip, args.limit)
+    write = read_counter(args.write, args.kernel, args.skip, args.limit)
     cf = read_counter(args.calib_fetch, args.calib_kernel)
     cw = read_counter(args.calib_write, args.calib_kernel)
     kib = CALIB_BYTES / 1024
@@ -82,6 +83,8 @@ def main():
     s.add_argument("--kernel", default="miss_copy")
     s.add_argument("--calib-kernel", default="elementwise")
     s.add_argument("--skip", type=int, default=0)
+    s.add_argument("--limit", type=int, default=0,
+                   help="use at most this many dispatches after the skipped ones")
     a = ap.parse_args()
     if a.cmd == "calib":
         calib()
