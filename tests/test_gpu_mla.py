@@ -185,6 +185,38 @@ def test_mla_replay_in_two_tile_splits(item):
              boost=[(0, 40, 5000.0), (0, 97, 3000.0), (0, 255, 4000.0)])
 
 
+def _random_case(case):
+    """Case `case` of a seeded sweep over batch, heads, location count, hot
+    size and boosted rows (which force replays at varied tiles), alternating
+    bf16 and fp8 rows."""
+    rng = np.random.default_rng([20261203, case])
+    item = [1152, 656][case % 2]
+    B = int(rng.choice([1, 2, 3, 8, 17, 64]))
+    heads = int(rng.choice([16, 48, 128]))
+    K = int(rng.integers(3, 700))
+    N = int(K + rng.integers(0, 800))
+    H = int(K + rng.integers(0, 200))
+    R = B + int(rng.integers(0, 3))
+    boost = []
+    if K > 40 and rng.random() < 0.6:
+        for _ in range(int(rng.integers(1, 3))):
+            pos = int(rng.integers(3, K))
+            while pos % 7 == 0:                               # padding positions
+                pos += 1
+            if pos < K:
+                boost.append((int(rng.integers(0, B)), pos, float(rng.choice([3000.0, 6000.0]))))
+    return dict(R=R, B=B, H=H, K=K, N=N, item=item, heads=heads, seed=2000 + case, calls=1,
+                boost=boost or None)
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_mla_random_shapes(case):
+    """Seeded random shapes, split counts and replays, against the oracle."""
+    kw = _random_case(case)
+    log(f"mla random case {case}: {kw}")
+    run_case(**kw)
+
+
 @pytest.mark.parametrize("item", [1152, 656])
 def test_mla_unsplit_rows(item):
     """256 rows: one workgroup per row and head group already fills the
