@@ -68,6 +68,43 @@ def test_lru_token_parity(H, K, N, I):
         p.close()
 
 
+def _random_lru_case(case):
+    """Case `case` of a seeded sweep of the single-step LRU token path: top-k
+    size (1 to 4096, ragged against the thread tiles), hot size, host length,
+    item size, batch, layers, and the rows' reuse, in-row duplicate, padding
+    and out-of-range rates."""
+    rng = np.random.default_rng([20261204, case])
+    K = int(rng.choice([1, 2, 31, 64, 257, 1000, 2048, 2049, 3000, 4096]))
+    H = min(int(K + rng.integers(0, 3000)), 32768)
+    N = int(max(K + 1, H // 2) + rng.integers(0, 6000))
+    I = int(rng.choice([16, 32, 48, 656]))
+    R = int(rng.integers(1, 7))
+    B = int(rng.integers(1, R + 1))
+    L = int(rng.integers(1, 3))
+    return dict(K=K, H=H, N=N, I=I, R=R, B=B, L=L, reuse=float(rng.choice([0.0, 0.5, 0.9])),
+                dup=float(rng.choice([0.0, 0.03, 0.3])), pad=float(rng.choice([0.0, 0.02, 0.2])),
+                bad=float(rng.choice([0.0, 0.0, 0.01])))
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_lru_token_random_shapes(case):
+    c = _random_lru_case(case)
+    log(f"lru token random case {case}: {c}")
+    rng = np.random.default_rng([7, case])
+    p = Pair(R=c["R"], L=c["L"], H=c["H"], K=c["K"], N=c["N"], I=c["I"], seed=case)
+    prev = {}
+    try:
+        for call in range(6):
+            layer = call % c["L"]
+            req = rng.permutation(c["R"])[:c["B"]]
+            rows = make_rows(rng, c["B"], c["K"], c["N"], prev=prev.get(layer), reuse=c["reuse"],
+                             pad=c["pad"], dup=c["dup"], bad=c["bad"])
+            prev[layer] = np.where(rows < c["N"], rows, -1)   # reuse only valid tokens
+            p.call(layer, req, np.full(c["B"], c["N"]), rows)
+    finally:
+        p.close()
+
+
 PAGE_SHAPES = [
     # (P, pages per request, H pages, K tokens, I)
     (16, 150, 64, 300, 32),
