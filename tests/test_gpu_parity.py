@@ -171,6 +171,83 @@ def test_clock_multistep_parity(H, K, N, I, S):
         p.close()
 
 
+def _random_clock_case(case):
+    """Case `case` of a seeded sweep of the multi-step CLOCK path: steps,
+    top-k size, hot size from half of K (overflow on every call) to 4K, host
+    length, item size, requests, layers, reuse between calls and between
+    steps, duplicate and padding rates, admission priority and the
+    extra-row ring."""
+    rng = np.random.default_rng([20261205, case])
+    S = int(rng.integers(2, 5))
+    K = int(rng.choice([1, 7, 64, 300, 1024, 2048]))
+    H = max(1, min(int(rng.choice([max(1, K // 2), K, K + 500, 4 * K + 7])), 32768))
+    N = int(K + 1 + rng.integers(0, 8000))
+    return dict(S=S, K=K, H=H, N=N, I=int(rng.choice([16, 48, 656])), R=int(rng.integers(1, 5)),
+                L=int(rng.integers(1, 3)), reuse=float(rng.choice([0.0, 0.5, 0.9])),
+                share=float(rng.choice([0.5, 0.8, 1.0])), dup=float(rng.choice([0.0, 0.03])),
+                pad=float(rng.choice([0.0, 0.05])),
+                admission=str(rng.choice(["recent", "frequent", "first"])),
+                extra=int(rng.choice([0, 0, 16])))
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_clock_random_shapes(case):
+    c = _random_clock_case(case)
+    log(f"clock random case {case}: {c}")
+    rng = np.random.default_rng([8, case])
+    B = int(rng.integers(1, c["R"] + 1))
+    p = Pair(R=c["R"], L=c["L"], H=c["H"], K=c["K"], N=c["N"], I=c["I"], S=c["S"], policy="clock",
+             seed=case, admission=c["admission"], extra_rows=c["extra"])
+    prev = {}
+    try:
+        for call in range(6):
+            layer = call % c["L"]
+            req = rng.permutation(c["R"])[:B]
+            base = make_rows(rng, B, c["K"], c["N"], prev=prev.get(layer), reuse=c["reuse"],
+                             dup=c["dup"], pad=c["pad"])
+            prev[layer] = base
+            steps = [base] + [make_rows(rng, B, c["K"], c["N"], prev=np.where(base >= 0, base, -1),
+                                        reuse=c["share"], dup=c["dup"], pad=c["pad"])
+                              for _ in range(1, c["S"])]
+            p.call(layer, req, np.full(B, c["N"]), np.stack(steps, axis=1))
+    finally:
+        p.close()
+
+
+def _random_page_case(case):
+    """Case `case` of a seeded sweep of page mode: page size, pages per
+    request, hot pages (some calls name more pages than fit: rejected rows),
+    token count, item size, requests."""
+    rng = np.random.default_rng([20261206, case])
+    P = int(rng.choice([4, 16, 64, 256]))
+    NP = int(rng.integers(8, 400))
+    return dict(P=P, NP=NP, H=int(rng.integers(4, 200)), K=int(rng.integers(1, 1024)),
+                I=int(rng.choice([16, 32])), R=int(rng.integers(1, 5)))
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_lru_page_random_shapes(case):
+    c = _random_page_case(case)
+    log(f"page random case {case}: {c}")
+    rng = np.random.default_rng([9, case])
+    N = c["P"] * c["NP"]
+    B = int(rng.integers(1, c["R"] + 1))
+    p = Pair(R=c["R"], L=1, H=c["H"], K=c["K"], N=N, I=c["I"], P=c["P"], seed=case)
+    try:
+        for call in range(6):
+            req = rng.permutation(c["R"])[:B]
+            rows = np.empty((B, c["K"]), np.int64)
+            for b in range(B):   # clustered tokens: four page windows
+                centres = rng.integers(0, N, 4)
+                width = max(c["P"] * 3, 8)
+                rows[b] = np.clip(centres[rng.integers(0, 4, c["K"])]
+                                  + rng.integers(-width, width, c["K"]), 0, N - 1)
+            rows[:, ::13] = -1
+            p.call(0, req, np.full(B, N), rows.astype(np.int32))
+    finally:
+        p.close()
+
+
 def test_clock_with_fewer_steps_than_max():
     rng = np.random.default_rng(5)
     p = Pair(R=3, L=1, H=200, K=64, N=1000, I=16, S=4, policy="clock", seed=5)
