@@ -131,6 +131,45 @@ def test_k_above_the_staging_limit():
     run(lg, [4 * 32768, 3 * 32768 + 7], 5000, mode="ragged", row_offsets=[0, 4 * 32768])
 
 
+def _random_topk_case(case):
+    """Case `case` of a seeded sweep: rows, row length (1 to 131072, so
+    single-chunk and split rows), k within the candidate limit, table mode,
+    page size, ties, a rejected row, an unmapped page, one or two layers."""
+    rng = np.random.default_rng([20261207, case])
+    B = int(rng.integers(1, 41))
+    N = int(rng.choice([1, 7, 100, 1000, 4096, 32767, 32768, 32769, 70000, 131072]))
+    chunks = -(-N // 32768)
+    k = int(rng.integers(1, min(4096, 32768 // chunks) + 1))
+    mode = str(rng.choice(["none", "paged", "ragged"]))
+    return dict(B=B, N=N, k=k, mode=mode, P=int(rng.choice([16, 64])), ties=bool(rng.random() < 0.3),
+                reject=bool(rng.random() < 0.2), holes=bool(rng.random() < 0.3),
+                layers=int(rng.integers(1, 3)))
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_shapes(case):
+    c = _random_topk_case(case)
+    log(f"topk random case {case}: {c}")
+    rng = np.random.default_rng([10, case])
+    B, N, k = c["B"], c["N"], c["k"]
+    lg = logits_with_specials(rng, B, N, ties=c["ties"])
+    lens = rng.integers(0, N + 1, B)
+    lens[rng.random(B) < 0.4] = N
+    if c["reject"] and B > 1:
+        lens[0] = -1 if rng.random() < 0.5 else N + 1
+    kw = {}
+    if c["mode"] == "paged":
+        npg = -(-N // c["P"])
+        pt = rng.permutation(B * npg).astype(np.int32).reshape(B, npg)
+        if c["holes"]:
+            pt[rng.integers(0, B), rng.integers(0, npg)] = -1
+        kw = dict(mode="paged", page_table=pt, page_size=c["P"])
+    elif c["mode"] == "ragged":
+        kw = dict(mode="ragged",
+                  row_offsets=np.cumsum(np.r_[0, np.maximum(lens[:-1], 0)]).astype(np.int32))
+    run(lg, lens, k, layers=c["layers"], **kw)
+
+
 def test_rejects_bad_arguments():
     with pytest.raises(binding.HiSparseError) as e:
         binding.TopkIndexBuilder(4, 17 * 32768, 2048, device=DEV)  # 17 chunks x 2048 > 32768
