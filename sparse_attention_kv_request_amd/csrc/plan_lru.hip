@@ -105,20 +105,31 @@ __device__ void lru_commit(const PlanArgs& a, int b, int r, int now, int m,
 #pragma unroll
   for (int e = 0; e < EPH; ++e)
     if (avail[e] && rank[e] >= m) ord[rank[e] - m] = static_cast<int16_t>(o[e]);
-  // slots used by this call (timestamp = now) go to the back in slot order
-  const int wpt = (a.Hw + NT - 1) / NT;
-  const int w0 = tid * wpt;
-  int cnt = 0;
-  for (int w = w0; w < w0 + wpt && w < a.Hw; ++w) cnt += __popc(used[w]);
-  int ntouched;
-  int pos = block_exclusive_scan<NT>(cnt, scan, &ntouched);
-  pos += a.H - ntouched;
-  for (int w = w0; w < w0 + wpt && w < a.Hw; ++w) {
-    uint32_t bits = used[w];
-    while (bits) {
-      const int bit = __ffs(bits) - 1;
-      bits &= bits - 1u;
-      ord[pos++] = static_cast<int16_t>(w * 32 + bit);
+  // slots used by this call (timestamp = now) go to the back in slot order.
+  // Thread w owns bitmap word w (Hw <= NT); each wave that owns words takes
+  // its prefix from wave scans over all the words (Hw / 64 of them), so no
+  // block barrier is needed here.
+  static_assert(HISPARSE_MAX_HOT / 32 <= NT, "one bitmap word per thread");
+  (void)scan;
+  const int lane = tid & (kWave - 1);
+  const int wbase = tid - lane;  // first word of this wave
+  if (wbase < a.Hw) {            // uniform over the wave
+    int before = 0, ntouched = 0;
+    for (int c0 = 0; c0 < a.Hw; c0 += kWave) {
+      const int w = c0 + lane;
+      const uint32_t n = w < a.Hw ? static_cast<uint32_t>(__popc(used[w])) : 0u;
+      const uint32_t incl = wave_incl_scan(n);
+      if (c0 == wbase) before = ntouched + static_cast<int>(incl - n);
+      ntouched += static_cast<int>(__builtin_amdgcn_readlane(incl, kWave - 1));
+    }
+    if (tid < a.Hw) {
+      int pos = a.H - ntouched + before;
+      uint32_t bits = used[tid];
+      while (bits) {
+        const int bit = __ffs(bits) - 1;
+        bits &= bits - 1u;
+        ord[pos++] = static_cast<int16_t>(tid * 32 + bit);
+      }
     }
   }
 }
