@@ -228,11 +228,14 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
   }
   __syncthreads();
 
-  // 2. representatives take their key's probe
+  // 2. representatives take their key's probe.  From here on a bucket's
+  // key word (no longer read: inserts are done) holds its key's result, the
+  // slot of a hit or -(miss rank + 1), so the representative checks above
+  // (reads of hval) need no barrier before these writes.
   bool rep[EPT];
 #pragma unroll
   for (int e = 0; e < EPT; ++e) rep[e] = tok[e] >= 0 && hval[hpos[e]] == tid * EPT + e;
-  __syncthreads();
+  int32_t* hres = reinterpret_cast<int32_t*>(hkey);
   int slot[EPT];
 #pragma unroll
   for (int e = 0; e < EPT; ++e) slot[e] = rep[e] ? probe[e] : -1;
@@ -243,7 +246,7 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
     if (slot[e] >= 0) {
       bit_set_atomic(used, slot[e]);
       tsq[slot[e]] = now;
-      hval[hpos[e]] = slot[e];
+      hres[hpos[e]] = slot[e];
     } else {
       ++nmiss;
       if (sw) bit_set_atomic(mbits, tok[e]);
@@ -275,7 +278,7 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
     if (rep[e] && slot[e] < 0) {
-      hval[hpos[e]] = -(j + 1);
+      hres[hpos[e]] = -(j + 1);
       miss_key[j] = tok[e];
       ++j;
     }
@@ -300,7 +303,7 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
     if (i >= a.K) continue;
     int loc = ring[e] >= 0 ? r * a.rows + ring[e] : -1;
     if (tok[e] >= 0) {
-      const int v = hval[hpos[e]];
+      const int v = hres[hpos[e]];
       loc = r * a.rows + (v >= 0 ? v : vslot[-v - 1]);
     }
     out[i] = loc;
