@@ -176,6 +176,14 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
     const int i = tid * EPT + e;
     raw[e] = i < a.K ? row[i] : -1;
   }
+  // The LDS hash and bitmaps are cleared before the row checks, whose
+  // barrier then publishes the cleared state (a rejected row just returns).
+  for (int i = tid; i < T; i += NT) {
+    hkey[i] = 0u;
+    hval[i] = 0x7fffffff;
+  }
+  for (int i = tid; i < a.Hw; i += NT) used[i] = 0u;
+  for (int i = tid; i < sw; i += NT) mbits[i] = 0u;
   const uint32_t code = row_check<NT>(a, b, r, sl);
   if (code) {
     reject_row<NT>(a, b, a.K, code, false);
@@ -208,13 +216,6 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
   int probe[EPT];
 #pragma unroll
   for (int e = 0; e < EPT; ++e) probe[e] = tok[e] >= 0 ? static_cast<int>(ks[tok[e]]) : -1;
-  for (int i = tid; i < T; i += NT) {
-    hkey[i] = 0u;
-    hval[i] = 0x7fffffff;
-  }
-  for (int i = tid; i < a.Hw; i += NT) used[i] = 0u;
-  for (int i = tid; i < sw; i += NT) mbits[i] = 0u;
-  __syncthreads();
 
   // insert every entry into the LDS hash; the first occurrence keeps its
   // position
