@@ -89,7 +89,9 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* xch, uint32
 }
 
 struct Lds {
-  uint32_t hist[kBins];
+  uint32_t hist[kBins];               // first digit (and output staging later)
+  uint32_t hist1[kBins];              // second digit, over the threshold bin
+  uint32_t hist2[256];                // last digit
   uint32_t list[kListCap];
   uint32_t gt_bits[kTopkChunk / 32];  // slot bitmaps: key > T, key == T
   uint32_t eq_bits[kTopkChunk / 32];
@@ -110,22 +112,22 @@ __device__ __forceinline__ uint32_t digit(uint32_t x, int pass) {
   return pass == 1 ? (x >> 8) & 4095u : x & 255u;
 }
 
-// From this pass's histogram in s.hist: the bin holding the
-// `remaining`-th largest key and the number of keys in higher bins.  Thread
-// j scans bins / 1024 bins (at least one), highest first.  Block-wide.
-__device__ __forceinline__ void pick_bin(Lds& s, int bins, int remaining, uint32_t& bin,
-                                         int& above_out) {
+// From a pass's histogram `hist`: the bin holding the `remaining`-th
+// largest key and the number of keys in higher bins.  Thread j scans
+// bins / 1024 bins (at least one), highest first.  Block-wide.
+__device__ __forceinline__ void pick_bin(Lds& s, const uint32_t* hist, int bins, int remaining,
+                                         uint32_t& bin, int& above_out) {
   const int tid = threadIdx.x;
   const int per = bins >= kThreads ? bins / kThreads : 1;
   const int top = bins - 1 - tid * per;
   uint32_t c = 0u;
   if (top >= 0)
-    for (int i = 0; i < per; ++i) c += s.hist[top - i];
+    for (int i = 0; i < per; ++i) c += hist[top - i];
   uint32_t total;
   int above = static_cast<int>(block_scan(c, s.xch, &total));
   if (top >= 0 && c > 0u && above < remaining && remaining <= above + static_cast<int>(c)) {
     for (int i = 0; i < per; ++i) {
-      const int h = static_cast<int>(s.hist[top - i]);
+      const int h = static_cast<int>(hist[top - i]);
       if (remaining <= above + h) {
         s.pick[0] = top - i;
         s.pick[1] = above;
@@ -148,7 +150,7 @@ __device__ __forceinline__ void radix_threshold(const uint32_t (&key)[kPer], int
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   uint32_t b0;
   int above;
-  pick_bin(s, kBins, kk, b0, above);
+  pick_bin(s, s.hist, kBins, kk, b0, above);
   int remaining = kk - above;
   uint32_t prefix = b0 << 20;
 
@@ -179,21 +181,21 @@ __device__ __forceinline__ void radix_threshold(const uint32_t (&key)[kPer], int
   for (int pass = 1; pass < 3; ++pass) {
     const int bins = pass == 1 ? kBins : 256;
     const uint32_t pm = pass == 1 ? 0xFFF00000u : 0xFFFFFF00u;  // bits fixed so far
-    for (int i = tid; i < bins; i += kThreads) s.hist[i] = 0u;
-    __syncthreads();
+    // each pass has its own histogram, cleared at kernel start
+    uint32_t* hist = pass == 1 ? s.hist1 : s.hist2;
     if (listed) {  // the list holds exactly the keys of bin b0
       for (int i = tid; i < m; i += kThreads) {
         const uint32_t x = s.list[i];
-        if ((x & pm) == prefix) atomicAdd(&s.hist[digit(x, pass)], 1u);
+        if ((x & pm) == prefix) atomicAdd(&hist[digit(x, pass)], 1u);
       }
     } else {
 #pragma unroll
       for (int e = 0; e < kPer; ++e)
-        if (key[e] != 0u && (key[e] & pm) == prefix) atomicAdd(&s.hist[digit(key[e], pass)], 1u);
+        if (key[e] != 0u && (key[e] & pm) == prefix) atomicAdd(&hist[digit(key[e], pass)], 1u);
     }
     __syncthreads();
     uint32_t b;
-    pick_bin(s, bins, remaining, b, above);
+    pick_bin(s, hist, bins, remaining, b, above);
     remaining -= above;
     prefix |= pass == 1 ? (b << 8) : b;
   }
@@ -394,7 +396,11 @@ void topk_chunk_kernel(TopkArgs a) {
 
   // keys of this thread's slots (positions start + slot), first-digit
   // histogram as they arrive
-  for (int i = tid; i < kBins; i += kThreads) s.hist[i] = 0u;
+  for (int i = tid; i < kBins; i += kThreads) {
+    s.hist[i] = 0u;
+    s.hist1[i] = 0u;
+  }
+  if (tid < 256) s.hist2[tid] = 0u;
   if (tid == 0) s.list_count = 0;
   __syncthreads();
   uint32_t key[kPer];
@@ -482,7 +488,11 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
     while (c + 1 < n_chunks && s.offs[c + 1] <= i) ++c;
     return static_cast<size_t>(first + c) * a.k + (i - s.offs[c]);
   };
-  for (int i = tid; i < kBins; i += kThreads) s.hist[i] = 0u;
+  for (int i = tid; i < kBins; i += kThreads) {
+    s.hist[i] = 0u;
+    s.hist1[i] = 0u;
+  }
+  if (tid < 256) s.hist2[tid] = 0u;
   if (tid == 0) s.list_count = 0;
   __syncthreads();
   // slots i0 .. i0 + 3 usually sit in one chunk (chunk candidate counts are
