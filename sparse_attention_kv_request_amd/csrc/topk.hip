@@ -211,9 +211,7 @@ __device__ __forceinline__ void radix_threshold(const uint32_t (&key)[kPer], int
 __device__ __forceinline__ uint32_t select_word(const uint32_t (&key)[kPer], uint32_t T, int need,
                                                 Lds& s, int& offset) {
   const int tid = threadIdx.x;
-  s.gt_bits[tid] = 0u;
-  s.eq_bits[tid] = 0u;
-  __syncthreads();
+  // (the bitmaps were cleared at kernel start)
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
     if (key[e] >= T) {
@@ -401,6 +399,8 @@ void topk_chunk_kernel(TopkArgs a) {
     s.hist1[i] = 0u;
   }
   if (tid < 256) s.hist2[tid] = 0u;
+  s.gt_bits[tid] = 0u;  // one word per thread
+  s.eq_bits[tid] = 0u;
   if (tid == 0) s.list_count = 0;
   __syncthreads();
   uint32_t key[kPer];
@@ -493,6 +493,8 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
     s.hist1[i] = 0u;
   }
   if (tid < 256) s.hist2[tid] = 0u;
+  s.gt_bits[tid] = 0u;  // one word per thread
+  s.eq_bits[tid] = 0u;
   if (tid == 0) s.list_count = 0;
   __syncthreads();
   // slots i0 .. i0 + 3 usually sit in one chunk (chunk candidate counts are
