@@ -472,6 +472,8 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
   if (n_chunks == 1 || row_rejected(a, row)) return;
   const int first = a.plan[p.row_info + 2 * row];
   const int tid = threadIdx.x;
+  // one barrier publishes the chunk offsets and the cleared histograms and
+  // bitmaps
   if (tid == 0) {
     int acc = 0;
     for (int c = 0; c < n_chunks; ++c) {
@@ -480,14 +482,6 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
     }
     s.offs[n_chunks] = acc;
   }
-  __syncthreads();
-  const int M = s.offs[n_chunks];
-  // candidate i sits in chunk c with offs[c] <= i < offs[c + 1]
-  auto cand_at = [&](int i) {
-    int c = 0;
-    while (c + 1 < n_chunks && s.offs[c + 1] <= i) ++c;
-    return static_cast<size_t>(first + c) * a.k + (i - s.offs[c]);
-  };
   for (int i = tid; i < kBins; i += kThreads) {
     s.hist[i] = 0u;
     s.hist1[i] = 0u;
@@ -497,6 +491,13 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
   s.eq_bits[tid] = 0u;
   if (tid == 0) s.list_count = 0;
   __syncthreads();
+  const int M = s.offs[n_chunks];
+  // candidate i sits in chunk c with offs[c] <= i < offs[c + 1]
+  auto cand_at = [&](int i) {
+    int c = 0;
+    while (c + 1 < n_chunks && s.offs[c + 1] <= i) ++c;
+    return static_cast<size_t>(first + c) * a.k + (i - s.offs[c]);
+  };
   // slots i0 .. i0 + 3 usually sit in one chunk (chunk candidate counts are
   // k or a chunk's length, multiples of 4 except at a row's end): one 16-byte
   // load then, else one load per slot
