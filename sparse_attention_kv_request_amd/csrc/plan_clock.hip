@@ -64,6 +64,18 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
     raw[e] = i < E ? row[i] : -1;
   }
   const uint32_t ref_word = tid < a.Hw ? refq[tid] : 0u;  // Hw <= NT
+  // The LDS hash, bitmaps and counters are set up before the row checks,
+  // whose barrier then publishes them (a rejected row just returns).
+  for (int i = tid; i < T; i += NT) {
+    hkey[i] = 0u;
+    hval[i] = 0x7fffffff;
+  }
+  if (tid < a.Hw) {
+    pinned[tid] = 0u;
+    refl[tid] = ref_word;
+  }
+  for (int i = tid; i < sw; i += NT) mbits[i] = 0u;
+  if (tid < HISPARSE_MAX_STEPS) s_cnt[tid] = 0;
   const uint32_t code = multistep_row_check<NT>(a, b, r, sl);
   if (code) {
     int32_t* out = a.out_locs + static_cast<size_t>(b) * E;
@@ -85,17 +97,6 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
     sl_of[e] = k < a.H ? s : -1;
     oldk[e] = k < a.H ? sk[s] : kEmpty;
   }
-  for (int i = tid; i < T; i += NT) {
-    hkey[i] = 0u;
-    hval[i] = 0x7fffffff;
-  }
-  if (tid < a.Hw) {
-    pinned[tid] = 0u;
-    refl[tid] = ref_word;
-  }
-  for (int i = tid; i < sw; i += NT) mbits[i] = 0u;
-  if (tid < HISPARSE_MAX_STEPS) s_cnt[tid] = 0;
-  __syncthreads();
 
   // 1. flatten [S][K] step-major; insert with the step bit.  Entries among
   // the newest ext tokens resolve to their ring row (the extra-page lookup)
