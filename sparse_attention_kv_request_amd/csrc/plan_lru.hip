@@ -354,6 +354,10 @@ __global__ __launch_bounds__(NT) void lru_page_plan(PlanArgs a) {
     const int i = tid * EPT + e;
     raw[e] = i < a.K ? row[i] : -1;
   }
+  // the page bitmap and used set are cleared before the row checks, whose
+  // barrier then publishes them (a rejected row just returns)
+  for (int i = tid; i < npw; i += NT) pbits[i] = 0u;
+  for (int i = tid; i < a.Hw; i += NT) used[i] = 0u;
   const uint32_t code = row_check<NT>(a, b, r, sl);
   if (code) {
     reject_row<NT>(a, b, a.K, code, true);
@@ -362,9 +366,6 @@ __global__ __launch_bounds__(NT) void lru_page_plan(PlanArgs a) {
   int oldk[EPH];
 #pragma unroll
   for (int e = 0; e < EPH; ++e) oldk[e] = o[e] >= 0 ? sk[o[e]] : kEmpty;
-  for (int i = tid; i < npw; i += NT) pbits[i] = 0u;
-  for (int i = tid; i < a.Hw; i += NT) used[i] = 0u;
-  __syncthreads();
 
   // 1. tokens -> pages named by the row
   int32_t tok[EPT];
