@@ -63,8 +63,11 @@ R16 a request named twice in one batch is rejected (both rows output -1,
 Parity pins (tests/test_oracle_*.py): textbook LRU and second-chance CLOCK at
 K = 1, closed forms (first call from empty, repeated calls, H >= N), an
 independently written recency-list LRU and two-lap CLOCK on exhaustive tiny
-traces, the invariants of every call, page translation closed forms, and a
-planted-mistake (mutation) suite.  Multi-step overflow admission follows
+traces, the invariants of every call, page translation closed forms, the
+sequential comparator (a textbook LRU over its one-key steps, closed forms
+for disjoint and identical steps), request reset (the named request empty in
+every layer, every other instance unchanged, then a first call from empty),
+and a planted-mistake (mutation) suite.  Multi-step overflow admission follows
 reading R7 and is pinned by a closed-form case only; the pages call that
 admission approximate, so beyond R7 it is "parity unpinned".
 """

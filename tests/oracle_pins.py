@@ -612,10 +612,90 @@ def pin_multi_request_clock(ora, seed=10):
                     assert x // st.rows == req[b]
 
 
+def pin_sequential_comparator(ora, seed=13):
+    """The per-step path the multi-step call replaces (PR #32162 report,
+    "Features and motivation": one single-step call per speculative step).
+    * K = 1: the S one-key calls of each multi-step row are S accesses of a
+      textbook LRU, in step order;
+    * steps with pairwise disjoint keys and H >= S*K, from empty: step s
+      misses all of its K keys, which fill slots s*K .. s*K + K - 1 in the
+      row's order, no victims, and the cache ends holding every key;
+    * identical steps: step 0 misses its distinct keys, later steps miss
+      nothing and return step 0's rows."""
+    rng = np.random.default_rng(seed)
+    N, H, S = 12, 4, 3
+    st = make_state(ora, H=H, K=1, N=N)
+    tb = TextbookLRU(H)
+    for _ in range(60):
+        keys = rng.integers(0, N, S)
+        res = st.swap_sequential(0, [0], [N], keys.reshape(1, S, 1))
+        assert len(res) == S
+        for s, t in enumerate(keys):
+            hit, ev = tb.access(int(t))
+            assert res[s]["miss_count"][0] == (0 if hit else 1)
+            if not hit:
+                (src, _, victim), = res[s]["plan"][0]
+                assert src == t and victim == (EMPTY if ev is None else ev)
+    K = 5
+    st = make_state(ora, H=S * K + 2, K=K, N=40)
+    keys = rng.permutation(40)[:S * K].reshape(1, S, K)
+    res = st.swap_sequential(0, [0], [40], keys)
+    for s in range(S):
+        assert res[s]["miss_count"][0] == K
+        assert res[s]["plan"][0] == [(int(t), s * K + i, EMPTY) for i, t in enumerate(keys[0, s])]
+        assert res[s]["out_locs"][0].tolist() == list(range(s * K, s * K + K))
+    assert sorted(st.instance(0, 0).key_slot) == sorted(keys.reshape(-1).tolist())
+    st = make_state(ora, H=8, K=K, N=40)
+    row = rng.integers(-1, 40, K)
+    res = st.swap_sequential(0, [0], [40], np.stack([row] * S)[None])
+    distinct = len({int(t) for t in row if t >= 0})
+    assert [r["miss_count"][0] for r in res] == [distinct] + [0] * (S - 1)
+    for r in res[1:]:
+        assert np.array_equal(r["out_locs"], res[0]["out_locs"])
+
+
+def pin_request_reset(ora, seed=14):
+    """A newly admitted request (request reset) empties that request's cache
+    in every layer and leaves every other instance as it was; its next call
+    is a first call from empty (closed form: misses fill slots 0, 1, ... in
+    first-occurrence order, LRU counter back at 0; CLOCK hand back at 0)."""
+    rng = np.random.default_rng(seed)
+    R, L, N, K = 3, 2, 30, 5
+    for policy, S, H in (("lru", 1, 8), ("clock", 2, 12)):
+        st = make_state(ora, R=R, L=L, H=H, K=K, N=N, S=S, policy=policy)
+        for _ in range(6):
+            for layer in range(L):
+                shape = (R, K) if S == 1 else (R, S, K)
+                topk = rng.integers(0, N, shape)
+                if S == 1:
+                    st.swap_in_selected(layer, list(range(R)), [N] * R, topk)
+                else:
+                    st.swap_in_spec_multistep(layer, list(range(R)), [N] * R, topk)
+        before = {(r, l): st.export(r, l) for r in range(R) for l in range(L)}
+        st.request_reset([1])
+        for r in range(R):
+            for l in range(L):
+                got = st.export(r, l)
+                if r == 1:
+                    assert got["slot_key"] == [EMPTY] * H and got["map"] == {}
+                    assert got["ts"] == [-1] * H and got["now"] == 0
+                    assert got["ref"] == [0] * H and got["hand"] == 0
+                else:
+                    assert got == before[(r, l)], f"instance ({r}, {l}) changed"
+        keys = rng.permutation(N)[:K]
+        ws = [int(t) for t in keys]
+        if S == 1:
+            res = st.swap_in_selected(1, [1], [N], keys[None])
+        else:
+            res = st.swap_in_spec_multistep(1, [1], [N], np.stack([keys] * S)[None])
+        assert res["plan"][0] == [(N + t, st.rows + j, EMPTY) for j, t in enumerate(ws)]
+
+
 ALL_PINS = [pin_first_call_closed_form, pin_overflow_closed_form, pin_admission_variants,
             pin_extra_ring,
             pin_row_semantics,
             pin_lru_textbook_k1, pin_clock_textbook_k1, pin_repeat_and_large_cache,
             pin_page_mode, pin_layers_independent, pin_multi_request_clock,
             pin_lru_random, pin_clock_random,
+            pin_sequential_comparator, pin_request_reset,
             pin_clock_bruteforce, pin_lru_bruteforce]

@@ -1,59 +1,80 @@
 """Parity at the full sizes of the five workloads, in the launch configuration
 bench.py times.
 
-The oracle replays sampled (request, layer) instances through every call and
-is compared on their outputs, miss counts, plans and final exported state.
-Every row of every call is also checked on the GPU for properties that hold
-at any size: every returned row holds exactly its token's host bytes (against
-a device mirror of the host tier), rows stay inside their request's range,
-and distinct tokens of a row get distinct rows.
+Every (request, layer) instance of every workload is replayed through the
+CPU oracle in spawned worker processes (they never touch the GPU) while the
+library runs the same calls; afterwards every row of every call is compared
+element by element: ``out_locs``, ``miss_count``, the ordered miss plan,
+(page mode) ``page_table`` and ``num_pages``, and every instance's final
+exported state (slot->key, timestamps or reference bits, call counter or
+hand, key->slot).  Every row of every call is also checked on the GPU for
+what holds at any size: every returned row holds exactly its token's host
+bytes (against a device mirror of the host tier), rows stay inside their
+request's range, and distinct tokens of a row get distinct rows.
 """
+import multiprocessing as mp
+import os
+import time
+
 import numpy as np
 import pytest
 import torch
 
-from oracle import hisparse_oracle as ora
 from sparse_attention_kv_request_amd import binding, workloads
+from tests.full_config_oracle import replay_instance
 from tests.gpu_harness import DEV, log
 
-pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
+
+WORKERS = max(1, min(16, os.cpu_count() or 1))
 
 
 class FullRun:
-    def __init__(self, w: workloads.Workload, sample):
+    def __init__(self, w: workloads.Workload, overrides):
         self.w = w
-        self.sample = sample
         self.S = w.num_steps
         self.multi = w.policy == "clock"
         self.P = w.page_size
-        log(f"cfg {w.cfg_id}: generating inputs")
+        # the oracle replays start first, in processes that never touch the GPU
+        self.pool = mp.get_context("spawn").Pool(WORKERS)
+        jobs = [(w.cfg_id, overrides, r, l) for l in range(w.layers) for r in range(w.batch)]
+        self.t0 = time.perf_counter()
+        self.pending = self.pool.map_async(replay_instance, jobs, chunksize=1)
+        log(f"cfg {w.cfg_id}: {len(jobs)} instances queued on {WORKERS} oracle workers; "
+            f"generating inputs")
         self.host = [binding.HostKV(w.requests, w.seq_len, w.item_bytes) for _ in range(w.layers)]
         workloads.fill_host_kv(w, [h.array for h in self.host], threads=16)
         self.host_dev = [torch.from_numpy(h.array).to(DEV) for h in self.host]
-        self.trace = workloads.batch_trace(w, threads=16)       # [L, steps, B, S, K]
+        self.trace = workloads.batch_trace(w, threads=16)       # [L, calls, B, S, K]
         self.gpu = binding.HiSparseState(
             max_requests=w.requests, num_layers=w.layers, hot_buffer_size=w.hot,
             top_k=w.top_k, item_size_bytes=w.item_bytes, max_seq_len=w.seq_len,
             max_steps=self.S if self.multi else 1, page_size=self.P, policy=w.policy,
             host_kv=self.host)
-        self.cpu = ora.OracleState(
-            max_requests=w.requests, num_layers=w.layers, hot=w.hot, top_k=w.top_k,
-            item_bytes=w.item_bytes, max_seq_len=w.seq_len,
-            max_steps=self.S if self.multi else 1, page_size=self.P, policy=w.policy)
         B = w.batch
         cap = self.gpu.capacity
         self.plan = tuple(torch.empty((B, cap), dtype=torch.int32, device=DEV) for _ in range(3))
         self.req = torch.arange(B, dtype=torch.int32, device=DEV)
         self.seq = torch.full((B,), w.seq_len, dtype=torch.int32, device=DEV)
+        calls, E = w.steps, (self.S if self.multi else 1) * w.top_k
+        self.got_out = np.empty((w.layers, calls, B, E), np.int32)
+        self.got_mc = np.empty((w.layers, calls, B), np.int32)
+        self.got_plan = {}                                     # (layer, call) -> [B] of [m, 3]
+        if self.P > 1:
+            self.got_pt = np.empty((w.layers, calls, B, w.hot), np.int32)
+            self.got_np = np.empty((w.layers, calls, B), np.int32)
         self.total_misses = 0
 
     def close(self):
-        self.gpu.close()
-        for h in self.host:
+        self.pool.terminate()
+        self.pool.join()
+        if hasattr(self, "gpu"):
+            self.gpu.close()
+        for h in getattr(self, "host", []):
             h.free()
 
     def call(self, step, layer):
-        w, B, K = self.w, self.w.batch, self.w.top_k
+        w, B = self.w, self.w.batch
         rows = self.trace[layer, step]                         # [B, S, K]
         topk = torch.from_numpy(np.ascontiguousarray(rows if self.multi else rows[:, 0])).to(DEV)
         out = torch.empty(topk.shape, dtype=torch.int32, device=DEV)
@@ -69,24 +90,16 @@ class FullRun:
                                       num_pages=nump, plan=self.plan)
         torch.cuda.synchronize()
         self.check_properties(layer, topk, out, pt)
-        self.total_misses += int(mc.sum())
-        for (r, l) in self.sample:
-            if l != layer:
-                continue
-            one = rows[r:r + 1] if self.multi else rows[r:r + 1, 0]
-            if self.multi:
-                want = self.cpu.swap_in_spec_multistep(layer, [r], [w.seq_len], one)
-            else:
-                want = self.cpu.swap_in_selected(layer, [r], [w.seq_len], one)
-            got = out[r].cpu().numpy()
-            assert np.array_equal(got, want["out_locs"][0]), f"out_locs ({r},{l}) step {step}"
-            m = int(mc[r])
-            assert m == want["miss_count"][0], f"miss_count ({r},{l}) step {step}"
-            plan = list(zip(*(p[r, :m].cpu().tolist() for p in self.plan)))
-            assert plan == [tuple(x) for x in want["plan"][0]], f"plan ({r},{l}) step {step}"
-            if self.P > 1:
-                assert np.array_equal(pt[r].cpu().numpy(), want["page_table"][0])
-                assert int(nump[r]) == want["num_pages"][0]
+        self.got_out[layer, step] = out.reshape(B, -1).cpu().numpy()
+        m = mc.cpu().numpy()
+        self.got_mc[layer, step] = m
+        self.total_misses += int(m.sum())
+        src, dst, vic = (p.cpu().numpy() for p in self.plan)
+        self.got_plan[(layer, step)] = [np.stack([src[b, :m[b]], dst[b, :m[b]], vic[b, :m[b]]], 1)
+                                        for b in range(B)]
+        if self.P > 1:
+            self.got_pt[layer, step] = pt.cpu().numpy()
+            self.got_np[layer, step] = nump.cpu().numpy()
 
     def check_properties(self, layer, topk, out, pt):
         w = self.w
@@ -111,66 +124,74 @@ class FullRun:
         n_tok = torch.unique(kt).numel()
         assert n_tok == torch.unique(kl).numel() == torch.unique(torch.stack([kt, kl]), dim=1).shape[1]
 
-    def compare_final_state(self):
-        for (r, l) in self.sample:
+    def compare_with_oracle(self):
+        t_wait = time.perf_counter()
+        results = self.pending.get(timeout=600)
+        log(f"cfg {self.w.cfg_id}: oracle replays done {time.perf_counter() - self.t0:.1f} s "
+            f"after queueing (waited {time.perf_counter() - t_wait:.1f} s)")
+        calls = self.w.steps
+        for res in results:
+            r, l = res["r"], res["l"]
+            where = f"instance (request {r}, layer {l})"
+            for c in range(calls):
+                if not np.array_equal(self.got_out[l, c, r], res["out"][c]):
+                    bad = np.flatnonzero(self.got_out[l, c, r] != res["out"][c])[:3]
+                    raise AssertionError(f"out_locs of {where} call {c} differ at {bad.tolist()}")
+                assert self.got_mc[l, c, r] == res["miss_count"][c], f"miss_count of {where} call {c}"
+                assert np.array_equal(self.got_plan[(l, c)][r], res["plan"][c]), \
+                    f"plan of {where} call {c}"
+                if self.P > 1:
+                    assert np.array_equal(self.got_pt[l, c, r], res["page_table"][c])
+                    assert self.got_np[l, c, r] == res["num_pages"][c]
+            assert res["flags"] == 0
             g = self.gpu.export(r, l, with_map=True)
-            c = self.cpu.export(r, l)
-            assert g["slot_key"].tolist() == c["slot_key"]
+            assert np.array_equal(g["slot_key"], res["slot_key"]), f"slot_key of {where}"
             if self.multi:
-                assert g["ref"].tolist() == c["ref"] and int(g["ctrl"][1]) == c["hand"]
+                assert np.array_equal(g["ref"], res["ref"]) and int(g["ctrl"][1]) == res["hand"]
             else:
-                assert g["ts"].tolist() == c["ts"] and int(g["ctrl"][0]) == c["now"]
+                assert np.array_equal(g["ts"], res["ts"]) and int(g["ctrl"][0]) == res["now"]
             ks = g["key_slot"]
-            assert {int(k): int(ks[k]) for k in np.flatnonzero(ks >= 0)} == c["map"]
+            keys = np.flatnonzero(ks >= 0)
+            assert np.array_equal(keys, res["map_keys"]), f"resident keys of {where}"
+            assert np.array_equal(ks[keys], res["map_slots"]), f"key->slot of {where}"
+        return len(results)
 
-    def run(self, calls=None):
-        steps = calls or self.w.steps
+    def run(self):
+        steps = self.w.steps
         for step in range(steps):
             for layer in range(self.w.layers):
                 self.call(step, layer)
-        self.compare_final_state()
         assert self.gpu.error_flags() == 0
-        log(f"cfg {self.w.cfg_id}: {steps} steps x {self.w.layers} layers bit-exact on "
-            f"{len(self.sample)} sampled instances; {self.total_misses} misses checked byte-exact")
+        n = self.compare_with_oracle()
+        log(f"cfg {self.w.cfg_id}: {steps} calls x {self.w.layers} layers x {self.w.batch} rows "
+            f"bit-exact on all {n} instances (outputs, plans, final state); "
+            f"{self.total_misses} misses checked byte-exact")
+
+
+def _run(cfg_id, **overrides):
+    run = FullRun(workloads.config(cfg_id, **overrides), overrides)
+    try:
+        run.run()
+    finally:
+        run.close()
 
 
 def test_config1_full():
-    """Single instance: the oracle covers everything, including the bytes."""
-    run = FullRun(workloads.config(1), sample=[(0, 0)])
-    try:
-        run.run()
-    finally:
-        run.close()
+    _run(1)
 
 
 def test_config2_full():
-    run = FullRun(workloads.config(2), sample=[(0, 0), (17, 3), (40, 5), (63, 7)])
-    try:
-        run.run()
-    finally:
-        run.close()
+    _run(2)
 
 
 @pytest.mark.parametrize("steps", [4, 3, 2])
 def test_config3_full(steps):
-    run = FullRun(workloads.config(3, num_steps=steps), sample=[(0, 0), (31, 0), (63, 0)])
-    try:
-        run.run()
-    finally:
-        run.close()
+    _run(3, num_steps=steps)
 
 
 def test_config4_full():
-    run = FullRun(workloads.config(4), sample=[(0, 0), (77, 0), (127, 0)])
-    try:
-        run.run()
-    finally:
-        run.close()
+    _run(4)
 
 
 def test_config5_full():
-    run = FullRun(workloads.config(5), sample=[(0, 0), (13, 0), (31, 0)])
-    try:
-        run.run()
-    finally:
-        run.close()
+    _run(5)

@@ -473,3 +473,34 @@ def test_graph_capture_replays_match_eager(policy):
     finally:
         graph.close()
         eager.close()
+
+
+PAGE_LARGE_TOPK = [
+    # (P, pages per request, H pages, K tokens, I, windows): top-k above 2048
+    # tokens takes the 8-entries-per-thread page kernel
+    (16, 2000, 600, 2049, 32, 6),
+    (8, 6000, 2000, 4096, 16, 16),
+    (64, 1000, 300, 8192, 16, 3),
+]
+
+
+@pytest.mark.parametrize("P,NP,H,K,I,windows", PAGE_LARGE_TOPK)
+def test_lru_page_large_topk(P, NP, H, K, I, windows):
+    log(f"lru page large top-k P={P} NP={NP} H={H} K={K} I={I}")
+    rng = np.random.default_rng([P, K])
+    R, B = 3, 2
+    N = P * NP
+    p = Pair(R=R, L=1, H=H, K=K, N=N, I=I, P=P, seed=K)
+    try:
+        for call in range(8):
+            req = rng.permutation(R)[:B]
+            rows = np.empty((B, K), np.int64)
+            for b in range(B):   # clustered tokens: `windows` windows of 80 pages
+                centres = rng.integers(0, N, windows)
+                w = 40 * P
+                rows[b] = np.clip(centres[rng.integers(0, windows, K)] + rng.integers(-w, w, K),
+                                  0, N - 1)
+            rows[:, ::11] = -1
+            p.call(0, req, np.full(B, N), rows.astype(np.int32))
+    finally:
+        p.close()

@@ -103,6 +103,15 @@ MUTANTS = {
     "page_plan_src_token_units": (
         "plan[b].append((r * (self.N // self.P) + key, r * self.H + slot, ev))",
         "plan[b].append((r * self.N + key, r * self.H + slot, ev))"),
+    "sequential_reuses_step_0": (
+        "self.swap_in_selected(layer, req_pool_indices, seq_lens, topk[:, s])",
+        "self.swap_in_selected(layer, req_pool_indices, seq_lens, topk[:, 0])"),
+    "reset_only_layer_0": (
+        "            for l in range(self.L):\n                self.inst.pop((int(r), l), None)",
+        "            for l in range(1):\n                self.inst.pop((int(r), l), None)"),
+    "reset_request_and_layer_transposed": (
+        "                self.inst.pop((int(r), l), None)",
+        "                self.inst.pop((l, int(r)), None)"),
 }
 
 
