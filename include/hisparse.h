@@ -82,6 +82,7 @@ extern "C" {
 #define HISPARSE_MAX_WORKING_SET 8192 /* top_k (x num_steps) entries per row */
 #define HISPARSE_MAX_SEQ_LEN ((1 << 28) - 2)
 #define HISPARSE_MAX_PAGES_PER_REQUEST (1 << 18)
+#define HISPARSE_MAX_BATCH 16000        /* rows of one call (the copy's per-row prefix in LDS) */
 
 typedef struct hisparse_state* hisparse_state_t;
 
@@ -104,7 +105,8 @@ typedef struct hisparse_state* hisparse_state_t;
  *                    1152 for a 576-dim bf16 MLA entry, 656 for the fp8 layout).
  *   max_seq_len      N: host tokens per request.
  *   policy           HISPARSE_POLICY_LRU or HISPARSE_POLICY_CLOCK.
- *   max_batch        largest batch of one call, 1..R.
+ *   max_batch        largest batch of one call, 1..min(R, HISPARSE_MAX_BATCH);
+ *                    above HISPARSE_MAX_BATCH: HISPARSE_E_UNSUPPORTED.
  *   host_kv          host array of L pointers; layer l's host KV tier,
  *                    row-major [R][N][I] bytes, in pinned host memory the
  *                    device can read (hisparse_host_alloc or any hipHostMalloc
@@ -150,6 +152,9 @@ typedef struct hisparse_config {
  * "Risks and impact": the miss_src / miss_dst / miss_count protocol of the
  * prefetch replay path).  Arrays are device int32 [batch][capacity]; row b's
  * first miss_count[b] entries are written, the rest are left untouched.
+ * The protocol's miss_count is the swap call's own `miss_count` output (device
+ * int32 [batch]), which hisparse_copy_planned takes beside the plan, so the
+ * struct carries no count array of its own.
  *   miss_src  host row copied: r*N + t (token mode) or host page r*(N/P) + p.
  *   miss_dst  device row written: r*(H+X+E) + slot, or r*H + page slot.
  *   victim    key (token or page) evicted from that slot, or -1.
@@ -271,7 +276,8 @@ int hisparse_swap_in_spec_multistep(hisparse_state_t st, int32_t layer_id, int32
  * The victim array is not read.  Entries outside the layer's host rows
  * ([0, R*N) tokens or [0, R*N/P) pages) or device rows are skipped and raise
  * HISPARSE_ERR_BAD_PLAN.  miss_count: device int32 [batch].  Enqueued on
- * `stream`; errors: HISPARSE_E_INVAL, HISPARSE_E_HIP.
+ * `stream`; errors: HISPARSE_E_INVAL, HISPARSE_E_UNSUPPORTED (batch above
+ * HISPARSE_MAX_BATCH), HISPARSE_E_HIP.
  */
 int hisparse_copy_planned(hisparse_state_t st, int32_t layer_id, int32_t batch,
                           const int32_t* miss_count, const hisparse_miss_plan_t* plan,
@@ -401,9 +407,15 @@ size_t hisparse_topk_workspace_bytes(int32_t batch, int32_t max_len, int32_t k);
 int hisparse_topk_index_build(const hisparse_topk_call_t* call, void* stream);
 
 /*
- * Empties the caches of `n` requests in every layer (a newly admitted
- * request).  req_pool_indices: device int32 [n]; out-of-range entries set
- * ERR_BAD_ROW and are skipped.  Enqueued on `stream`.
+ * Empties the caches of `n` requests in every layer: a request newly admitted
+ * to a pool slot starts from an empty hot cache (sglang PR #20343 summary,
+ * "Risks and impact": admit_request_into_staging is where the coordinator
+ * admits a request; "Review highlights": the race there was fixed by a stream
+ * wait, which is why this call is ordered on the same stream as the swap
+ * calls instead of running on a side stream).  req_pool_indices: device int32
+ * [n]; out-of-range entries set ERR_BAD_ROW and are skipped.  Enqueued on
+ * `stream`; allocates nothing.  Errors: HISPARSE_E_INVAL (NULL state, n < 0,
+ * NULL indices with n > 0), HISPARSE_E_HIP.
  */
 int hisparse_request_reset(hisparse_state_t st, int32_t n, const int32_t* req_pool_indices,
                            void* stream);
@@ -412,7 +424,11 @@ int hisparse_request_reset(hisparse_state_t st, int32_t n, const int32_t* req_po
 int32_t hisparse_plan_capacity(hisparse_state_t st);
 
 /*
- * Copies one instance's state to host memory.  Synchronous.
+ * Copies one instance's state to host memory (the inspection side of the
+ * pages' tests, PR #32162 report, "Key files": the correctness test builds a
+ * cache index and state up front and checks them after the swap).
+ * Synchronous; HISPARSE_E_INVAL for a NULL pointer or (req, layer) out of
+ * range, HISPARSE_E_HIP if a copy fails.
  *   slot_key_h  int32 [H]: key held by each slot, -1 if empty.
  *   policy_h    int32 [H]: LRU timestamp of each slot (-1 if empty), or the
  *               CLOCK reference bit (0/1).
@@ -424,28 +440,37 @@ int hisparse_state_export(hisparse_state_t st, int32_t req, int32_t layer, int32
                           int32_t* policy_h, int32_t* ctrl_h, int32_t* key_slot_h, void* stream);
 
 /*
- * Overwrites one instance's state from host memory (same layouts as export;
- * a resident set built up front, as the pages' tests do).  The caller fills
- * the matching device KV rows.  Synchronous.  HISPARSE_E_INVAL if a key is
- * out of range or resident twice, a timestamp is below -1, or an empty slot
- * carries a timestamp other than -1.
+ * Overwrites one instance's state from host memory (same layouts as export):
+ * a resident set built up front, as the pages' tests do with
+ * _make_cache_index / _make_state (PR #32162 report, "Key files").  The caller
+ * fills the matching device KV rows.  Synchronous.  HISPARSE_E_INVAL, with the
+ * state unchanged, if a key is out of range or resident twice; for LRU, if the
+ * call counter ctrl_h[0] is negative, an occupied slot's timestamp is outside
+ * [0, ctrl_h[0]) or an empty slot's is not -1; for CLOCK, if a reference bit
+ * is not 0 or 1 or the hand ctrl_h[1] is outside [0, H).
  */
 int hisparse_state_import(hisparse_state_t st, int32_t req, int32_t layer,
                           const int32_t* slot_key_h, const int32_t* policy_h,
                           const int32_t* ctrl_h, void* stream);
 
 /* Reads the sticky error word into *flags_h; clears it when `clear` != 0.
- * Synchronous. */
+ * The word carries the HISPARSE_ERR_* conditions the pages' risk sections
+ * name as silent failure modes -- a wrong cache-index mapping (sglang PR
+ * #20343 summary, "Risks and impact") shows up as rejected rows and indices
+ * instead of wrong rows.  Synchronous; HISPARSE_E_INVAL for a NULL pointer,
+ * HISPARSE_E_HIP if the read fails. */
 int hisparse_get_error_flags(hisparse_state_t st, uint32_t* flags_h, int32_t clear, void* stream);
 
 /* Static description of a status code. */
 const char* hisparse_strerror(int code);
 
 /*
- * Pinned, device-readable host memory for the host KV tier (hipHostMalloc,
- * mapped, non-coherent so the GPU may cache what it reads).  *out_h receives
- * the host address, usable directly as a host_kv pointer.  Free with
- * hisparse_host_free.
+ * Pinned, device-readable host memory for the host KV tier, where the idle KV
+ * lives (sglang PR #20343 summary, "Features and motivation"): hipHostMalloc
+ * with hipHostMallocMapped and the runtime's default coherence.  *out_h
+ * receives the host address, usable directly as a host_kv pointer.  Free with
+ * hisparse_host_free.  HISPARSE_E_INVAL for bytes == 0 or a NULL out_h,
+ * HISPARSE_E_NOMEM if the allocation fails.
  */
 int hisparse_host_alloc(size_t bytes, void** out_h);
 int hisparse_host_free(void* p_h);

@@ -93,6 +93,8 @@ __global__ __launch_bounds__(NT) void miss_copy(CopyArgs a) {
 }  // namespace
 
 hipError_t launch_miss_copy(const CopyArgs& a, hipStream_t s) {
+  static_assert((HISPARSE_MAX_BATCH + 1 + kCopyThreads / kWave + 1) * sizeof(int) <= 64 * 1024,
+                "the largest batch's prefix and the scan scratch fit the default LDS");
   const size_t lds = (static_cast<size_t>(a.batch) + 1) * sizeof(int);
   hipLaunchKernelGGL((miss_copy<kCopyThreads, kCopyUnroll>), dim3(kCopyBlocks),
                      dim3(kCopyThreads), lds, s, a);

@@ -36,60 +36,8 @@ struct DeviceGuard {
   }
 };
 
-struct Derived {
-  int32_t rows = 0;
-  int32_t scratch = 0;
-  int32_t nkeys = 0;
-  int32_t hw = 0;
-  int32_t cap = 0;
-};
-
-// Scalar validation of a configuration; pointer arrays are checked by create.
-int derive(const hisparse_config_t* c, Derived* d) {
-  if (c == nullptr) return HISPARSE_E_INVAL;
-  const bool lru = c->policy == HISPARSE_POLICY_LRU;
-  const bool clock = c->policy == HISPARSE_POLICY_CLOCK;
-  if (!lru && !clock) return HISPARSE_E_INVAL;
-  if (c->max_requests < 1 || c->num_layers < 1 || c->top_k < 1 || c->page_size < 1)
-    return HISPARSE_E_INVAL;
-  if (c->hot_buffer_size < 1 || c->hot_buffer_size > HISPARSE_MAX_HOT) return HISPARSE_E_INVAL;
-  if (c->item_size_bytes < 16 || c->item_size_bytes % 16) return HISPARSE_E_INVAL;
-  if (c->max_seq_len < 1) return HISPARSE_E_INVAL;
-  if (c->max_seq_len > HISPARSE_MAX_SEQ_LEN) return HISPARSE_E_UNSUPPORTED;
-  if (c->max_batch < 1 || c->max_batch > c->max_requests) return HISPARSE_E_INVAL;
-  if (c->admission < HISPARSE_ADMIT_RECENT || c->admission > HISPARSE_ADMIT_FIRST)
-    return HISPARSE_E_INVAL;
-  if (c->extra_rows < 0 || c->extra_rows > c->max_seq_len) return HISPARSE_E_INVAL;
-  if (c->extra_rows > 0 && c->page_size > 1) return HISPARSE_E_UNSUPPORTED;
-  const int64_t H = c->hot_buffer_size, K = c->top_k, P = c->page_size;
-  if (lru) {
-    if (c->max_steps != 1) return HISPARSE_E_INVAL;
-    if (K > HISPARSE_MAX_WORKING_SET) return HISPARSE_E_UNSUPPORTED;
-    if (P == 1) {
-      if (K > H) return HISPARSE_E_INVAL;  // a row's distinct tokens must fit
-    } else {
-      if (c->max_seq_len % P) return HISPARSE_E_INVAL;
-      if (c->max_seq_len / P > HISPARSE_MAX_PAGES_PER_REQUEST) return HISPARSE_E_UNSUPPORTED;
-      if (H > kMaxPageModeHot) return HISPARSE_E_UNSUPPORTED;
-    }
-  } else {
-    if (P != 1) return HISPARSE_E_INVAL;
-    if (c->max_steps < HISPARSE_MIN_STEPS || c->max_steps > HISPARSE_MAX_STEPS)
-      return HISPARSE_E_INVAL;
-    if (c->max_steps * K > HISPARSE_MAX_WORKING_SET) return HISPARSE_E_UNSUPPORTED;
-  }
-  d->scratch = clock ? static_cast<int32_t>(std::max<int64_t>(0, c->max_steps * K - H)) : 0;
-  d->rows = P > 1 ? static_cast<int32_t>(H)
-                  : static_cast<int32_t>(H + d->scratch + c->extra_rows);
-  d->nkeys = P > 1 ? c->max_seq_len / c->page_size : c->max_seq_len;
-  d->hw = static_cast<int32_t>((H + 31) / 32);
-  d->cap = P > 1 ? static_cast<int32_t>(H) : static_cast<int32_t>(c->max_steps * K);
-  // host rows, device rows and plan entries are int32
-  const int64_t R = c->max_requests;
-  if (R * d->nkeys >= (int64_t{1} << 31) || R * d->rows >= (int64_t{1} << 31))
-    return HISPARSE_E_UNSUPPORTED;
-  return HISPARSE_OK;
-}
+using host::Derived;
+using host::derive;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t{255}; }
 
@@ -158,8 +106,7 @@ struct ProfileSums {
 
 hipError_t drain_events(hisparse_state* st, ProfileSums* sums) {
   hipError_t err = hipSuccess;
-  for (size_t i = 0; i + 2 < st->ev_pending.size(); i += 3) {
-    hipEvent_t e0 = st->ev_pending[i], e1 = st->ev_pending[i + 1], e2 = st->ev_pending[i + 2];
+  st->events.drain([&](hipEvent_t e0, hipEvent_t e1, hipEvent_t e2) {
     hipError_t e = hipEventSynchronize(e2);
     float t1 = 0, t2 = 0;
     if (e == hipSuccess) e = hipEventElapsedTime(&t1, e0, e1);
@@ -171,22 +118,19 @@ hipError_t drain_events(hisparse_state* st, ProfileSums* sums) {
     } else {
       err = e;
     }
-    st->ev_free.push_back(e0);
-    st->ev_free.push_back(e1);
-    st->ev_free.push_back(e2);
-  }
-  st->ev_pending.clear();
+  });
   return err;
 }
 
 hipEvent_t take_event(hisparse_state* st) {
-  if (st->ev_free.empty()) {
+  auto& fl = st->events.free_list;
+  if (fl.empty()) {
     hipEvent_t e = nullptr;
     if (hipEventCreateWithFlags(&e, hipEventDefault) != hipSuccess) return nullptr;
     return e;
   }
-  hipEvent_t e = st->ev_free.back();
-  st->ev_free.pop_back();
+  hipEvent_t e = fl.back();
+  fl.pop_back();
   return e;
 }
 
@@ -199,10 +143,10 @@ void record(hisparse_state* st, hipStream_t s) {
   hipEvent_t e = take_event(st);
   if (e == nullptr) return;
   if (hipEventRecord(e, s) != hipSuccess) {
-    st->ev_free.push_back(e);
+    st->events.free_list.push_back(e);
     return;
   }
-  st->ev_pending.push_back(e);
+  st->events.push(e);
 }
 
 // Turns on the ascending-host-row copy list when its LDS bitmap fits.
@@ -233,8 +177,9 @@ CopyArgs copy_args(const hisparse_state* st, int layer, int batch, const int32_t
 
 int run_swap(hisparse_state* st, const PlanArgs& a, bool multistep, hipStream_t s) {
   auto* ps = static_cast<ProfiledState*>(st);
-  if (st->profiling && st->ev_pending.size() >= 3 * 4096) (void)drain_events(st, &ps->sums);
-  const size_t mark = st->ev_pending.size();
+  if (st->profiling && st->events.pending.size() >= 3 * 4096) (void)drain_events(st, &ps->sums);
+  // every return path keeps this call's events only as one whole triple
+  host::TripleGuard<hipEvent_t> guard(&st->events, st->profiling);
   record(st, s);
   hipError_t e;
   if (multistep)
@@ -253,13 +198,6 @@ int run_swap(hisparse_state* st, const PlanArgs& a, bool multistep, hipStream_t 
   e = launch_miss_copy(c, s);
   if (e != hipSuccess) return status_of(e);
   record(st, s);
-  if (st->profiling && st->ev_pending.size() - mark != 3) {
-    // an event could not be taken: drop this call's partial triple
-    while (st->ev_pending.size() > mark) {
-      st->ev_free.push_back(st->ev_pending.back());
-      st->ev_pending.pop_back();
-    }
-  }
   return HISPARSE_OK;
 }
 
@@ -381,8 +319,8 @@ int hisparse_state_create(const hisparse_config_t* cfg, void* stream, hisparse_s
 void hisparse_state_destroy(hisparse_state_t st) {
   if (st == nullptr) return;
   DeviceGuard g(st->device);
-  for (hipEvent_t e : st->ev_pending) (void)hipEventDestroy(e);
-  for (hipEvent_t e : st->ev_free) (void)hipEventDestroy(e);
+  for (hipEvent_t e : st->events.pending) (void)hipEventDestroy(e);
+  for (hipEvent_t e : st->events.free_list) (void)hipEventDestroy(e);
   (void)hipFree(st->arena);
   delete static_cast<ProfiledState*>(st);
 }
@@ -445,6 +383,7 @@ int hisparse_copy_planned(hisparse_state_t st, int32_t layer_id, int32_t batch,
   if (st == nullptr || plan == nullptr || miss_count == nullptr) return HISPARSE_E_INVAL;
   if (layer_id < 0 || layer_id >= st->cfg.num_layers || batch < 0) return HISPARSE_E_INVAL;
   if (!plan->miss_src || !plan->miss_dst || plan->capacity < 1) return HISPARSE_E_INVAL;
+  if (batch > host::kMaxBatch) return HISPARSE_E_UNSUPPORTED;
   if (batch == 0) return HISPARSE_OK;
   DeviceGuard g(st->device);
   const CopyArgs c = copy_args(st, layer_id, batch, miss_count, plan->miss_src, plan->miss_dst,
@@ -589,10 +528,8 @@ int hisparse_state_export(hisparse_state_t st, int32_t req, int32_t layer, int32
                        hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return status_of(e);
-  if (!st->ts)
-    for (int i = 0; i < H; ++i) policy_h[i] = (bits[i >> 5] >> (i & 31)) & 1u;
-  if (key_slot_h)
-    for (int i = 0; i < st->nkeys; ++i) key_slot_h[i] = ks[i];
+  if (!st->ts) host::decode_refbits(bits.data(), H, policy_h);
+  if (key_slot_h) host::widen_key_slot(ks.data(), st->nkeys, key_slot_h);
   return HISPARSE_OK;
 }
 
@@ -604,49 +541,24 @@ int hisparse_state_import(hisparse_state_t st, int32_t req, int32_t layer,
     return HISPARSE_E_INVAL;
   const int H = st->cfg.hot_buffer_size;
   const bool lru = st->ts != nullptr;
-  std::vector<int16_t> ks(st->nkeys, static_cast<int16_t>(kEmpty));
-  for (int s = 0; s < H; ++s) {
-    const int32_t k = slot_key_h[s];
-    if (k == kEmpty) {
-      if (lru && policy_h[s] != -1) return HISPARSE_E_INVAL;
-      continue;
-    }
-    if (k < 0 || k >= st->nkeys || ks[k] != kEmpty) return HISPARSE_E_INVAL;
-    ks[k] = static_cast<int16_t>(s);
-    if (lru && (policy_h[s] < 0 || policy_h[s] >= ctrl_h[0])) return HISPARSE_E_INVAL;
-  }
-  std::vector<int16_t> order;
-  std::vector<uint32_t> bits;
-  if (lru) {
-    if (ctrl_h[0] < 0) return HISPARSE_E_INVAL;
-    std::vector<int32_t> idx(H);
-    std::iota(idx.begin(), idx.end(), 0);
-    std::stable_sort(idx.begin(), idx.end(),
-                     [&](int32_t x, int32_t y) { return policy_h[x] < policy_h[y]; });
-    order.assign(idx.begin(), idx.end());
-  } else {
-    if (ctrl_h[1] < 0 || ctrl_h[1] >= H) return HISPARSE_E_INVAL;
-    bits.assign(st->hw, 0u);
-    for (int s = 0; s < H; ++s) {
-      if (policy_h[s] != 0 && policy_h[s] != 1) return HISPARSE_E_INVAL;
-      if (policy_h[s]) bits[s >> 5] |= 1u << (s & 31);
-    }
-  }
+  host::InstanceImage img;
+  const int rc = host::encode_import(H, st->nkeys, lru, slot_key_h, policy_h, ctrl_h, &img);
+  if (rc != HISPARSE_OK) return rc;
   DeviceGuard g(st->device);
   auto s = static_cast<hipStream_t>(stream);
   const size_t q = static_cast<size_t>(layer) * st->cfg.max_requests + req;
   hipError_t e = hipMemcpyAsync(st->slot_key + q * H, slot_key_h, H * sizeof(int32_t),
                                 hipMemcpyHostToDevice, s);
   if (e == hipSuccess)
-    e = hipMemcpyAsync(st->key_slot + q * st->nkeys, ks.data(), st->nkeys * sizeof(int16_t),
-                       hipMemcpyHostToDevice, s);
+    e = hipMemcpyAsync(st->key_slot + q * st->nkeys, img.key_slot.data(),
+                       st->nkeys * sizeof(int16_t), hipMemcpyHostToDevice, s);
   if (e == hipSuccess && lru)
     e = hipMemcpyAsync(st->ts + q * H, policy_h, H * sizeof(int32_t), hipMemcpyHostToDevice, s);
   if (e == hipSuccess && lru)
-    e = hipMemcpyAsync(st->order + q * H, order.data(), H * sizeof(int16_t),
+    e = hipMemcpyAsync(st->order + q * H, img.order.data(), H * sizeof(int16_t),
                        hipMemcpyHostToDevice, s);
   if (e == hipSuccess && !lru)
-    e = hipMemcpyAsync(st->refbits + q * st->hw, bits.data(), st->hw * sizeof(uint32_t),
+    e = hipMemcpyAsync(st->refbits + q * st->hw, img.refbits.data(), st->hw * sizeof(uint32_t),
                        hipMemcpyHostToDevice, s);
   if (e == hipSuccess)
     e = hipMemcpyAsync(st->ctrl + 2 * q, ctrl_h, 2 * sizeof(int32_t), hipMemcpyHostToDevice, s);

@@ -10,11 +10,12 @@
 #include "copy.h"
 #include "device_common.h"
 #include "hisparse.h"
+#include "host_logic.h"
 
 namespace hisparse {
 
 constexpr int kPlanThreads = 1024;  // one workgroup (16 waves) per batch row
-constexpr int kMaxPageModeHot = 4096;
+constexpr int kMaxPageModeHot = host::kMaxPageModeHot;
 static_assert((HISPARSE_MAX_HOT + 31) / 32 <= kPlanThreads,
               "one thread per word of an H-bit mask in the plan kernels");
 
@@ -134,8 +135,7 @@ struct hisparse_state {
   uint32_t* err = nullptr;
   size_t max_lds = 0;         // dynamic LDS a workgroup may use
   int num_cus = 0;
-  // profiling
+  // profiling: triples of events (before plan, after plan, after copy)
   bool profiling = false;
-  std::vector<hipEvent_t> ev_free;
-  std::vector<hipEvent_t> ev_pending;  // triples: before plan, after plan, after copy
+  hisparse::host::EventLedger<hipEvent_t> events;
 };

@@ -113,3 +113,17 @@ def test_extra_rows_extend_the_token_rows():
                                  max_steps=1, page_size=256, item_size_bytes=656,
                                  max_seq_len=65536, policy=0, max_batch=2, extra_rows=1)
     assert binding.hisparse_device_rows_per_request(cfg) == binding.HISPARSE_E_UNSUPPORTED
+
+
+def test_batch_limit_of_the_copy():
+    """The miss copy holds a call's per-row prefix of miss counts in LDS, so a
+    state may not accept batches beyond HISPARSE_MAX_BATCH: a larger batch
+    would commit cache state whose copies could not launch."""
+    cfg = binding.HisparseConfig(max_requests=20000, num_layers=1, hot_buffer_size=100,
+                                 top_k=60, max_steps=1, page_size=1, item_size_bytes=32,
+                                 max_seq_len=500, policy=0, max_batch=16000)
+    assert binding.hisparse_device_rows_per_request(cfg) == 100
+    cfg.max_batch = 16001
+    assert binding.hisparse_device_rows_per_request(cfg) == binding.HISPARSE_E_UNSUPPORTED
+    cfg.max_batch = 20000
+    assert binding.hisparse_device_rows_per_request(cfg) == binding.HISPARSE_E_UNSUPPORTED

@@ -504,3 +504,20 @@ def test_lru_page_large_topk(P, NP, H, K, I, windows):
             p.call(0, req, np.full(B, N), rows.astype(np.int32))
     finally:
         p.close()
+
+
+def test_batch_at_the_limit():
+    """A call of HISPARSE_MAX_BATCH rows (16000): the miss copy's per-row
+    prefix then fills its LDS to the limit, and every row is still copied."""
+    B, H, K, N = 16000, 8, 4, 16
+    rng = np.random.default_rng(17)
+    p = Pair(R=B, L=1, H=H, K=K, N=N, I=16, seed=17)
+    try:
+        for call in range(3):
+            rows = np.stack([rng.choice(N, K, replace=False) for _ in range(B)])
+            _, mc, _ = p.call(0, np.arange(B), np.full(B, N), rows, check_state=False)
+            assert int(mc.sum()) > 0
+        for r in (0, 7777, B - 1):
+            p.compare_state(r, 0)
+    finally:
+        p.close()
