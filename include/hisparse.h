@@ -309,11 +309,15 @@ int hisparse_copy_planned(hisparse_state_t st, int32_t layer_id, int32_t batch,
  *               hisparse_sparse_mla_workspace_bytes(st, batch, num_heads,
  *               n_locs) bytes (split partials), NULL when that is 0.
  * softmax_scale must be positive and finite (else HISPARSE_E_INVAL).
- * Computes in bf16 MFMA with fp32 accumulation; the softmax weights are
- * rounded to bf16 before the weighted sum.  When the locations are split
- * over several workgroups, each split's normalised output is kept in fp16
- * (relative 2^-11) until the splits are merged by their log-sum-exp.  Enqueued on `stream`; allocates
- * nothing.  Errors: HISPARSE_E_INVAL, HISPARSE_E_UNSUPPORTED, HISPARSE_E_HIP.
+ * Computes in bf16 MFMA with fp32 accumulation (fp8 latents are dequantised
+ * by one fp32 product and rounded to bf16); the softmax weights are rounded
+ * to bf16 for the weighted sum, while their normaliser and lse sum the fp32
+ * weights.  When the locations are split over several workgroups, each
+ * split's normalised output is kept in fp16 (relative 2^-11) until the splits
+ * are merged by their log-sum-exp, so |latent| values must stay below 65504
+ * (fp16's largest finite value); a split output beyond it is not detected.
+ * Enqueued on `stream`; allocates nothing.  Errors: HISPARSE_E_INVAL,
+ * HISPARSE_E_UNSUPPORTED, HISPARSE_E_HIP.
  */
 size_t hisparse_sparse_mla_workspace_bytes(hisparse_state_t st, int32_t batch, int32_t num_heads,
                                            int32_t n_locs);

@@ -23,10 +23,14 @@ KV row layouts (the item bytes a swap call copies):
 * 656 B: 512 OCP fp8 e4m3fn latent values, 4 float32 scales (one per
   128-dim tile of the latent), 64 bfloat16 rope values.
 
-These layouts and the 576/512/64 split are readings (the pages name neither);
-"parity unpinned" does not apply: every function below is pinned by
-tests/test_sparse_mla_oracle.py against library decoders, a library attention
-routine and closed forms.
+These layouts and the 576/512/64 split are readings (the pages name neither).
+The kernel computes with bf16 keys and values (reading R23): fp8 rows are
+dequantised by one float32 product per value and rounded to bf16;
+``decode_rows_bf16`` gives those values, and the GPU parity tests attend over
+them so that their tolerance covers only the kernel's accumulation and
+softmax roundings.  "Parity unpinned" does not apply: every function below is
+pinned by tests/test_sparse_mla_oracle.py against library decoders and
+conversions, a library attention routine and closed forms.
 """
 from __future__ import annotations
 
@@ -61,6 +65,38 @@ def e4m3fn_to_f64(codes: np.ndarray) -> np.ndarray:
     return np.where((c & 0x7F) == 0x7F, np.nan, val)
 
 
+def f32_to_bf16_rne(x: np.ndarray) -> np.ndarray:
+    """float32 values -> the nearest bfloat16 value (ties to the even
+    significand), returned as float64.  From the format: bfloat16 is the upper
+    16 bits of a float32, so rounding drops the low 16 bits, adding one unit
+    of the kept part when they exceed half of it, or equal half of it and the
+    kept part is odd.  Overflow rounds to infinity; NaN stays NaN."""
+    u = np.ascontiguousarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    low = u & 0xFFFF
+    keep = u >> 16
+    up = (low > 0x8000) | ((low == 0x8000) & ((keep & 1) == 1))
+    r = ((keep + up.astype(np.uint64)) << 16).astype(np.uint32).view(np.float32)
+    r = np.where(np.isnan(np.asarray(x, np.float32)), np.float32(np.nan), r)
+    return r.astype(np.float64)
+
+
+def decode_rows_bf16(rows: np.ndarray):
+    """The values attention computes with (reading R23): bf16 rows as stored;
+    fp8 rows dequantised as one float32 product (code value x the tile's
+    float32 scale, rounded to nearest even) and then rounded to bfloat16.
+    Returns (latent [n, 512], rope [n, 64]) float64."""
+    n, item = rows.shape
+    if item == BF16_ROW:
+        return decode_rows(rows)
+    if item == FP8_ROW:
+        codes = e4m3fn_to_f64(rows[:, :LATENT]).astype(np.float32)      # exact in float32
+        scales = np.ascontiguousarray(rows[:, LATENT:LATENT + 16]).view(np.float32)
+        prod = codes * np.repeat(scales, FP8_TILE, axis=1)               # float32 product
+        rope = bf16_to_f64(np.ascontiguousarray(rows[:, LATENT + 16:]).view(np.uint16))
+        return f32_to_bf16_rne(prod), rope
+    raise ValueError(f"unsupported KV row of {item} bytes")
+
+
 def decode_rows(rows: np.ndarray):
     """uint8 [n, item] KV rows -> (latent [n, 512], rope [n, 64]) float64."""
     n, item = rows.shape
@@ -90,17 +126,21 @@ def attend(q: np.ndarray, latent: np.ndarray, rope: np.ndarray, scale: float):
     return out, lse
 
 
-def sparse_mla_decode(q_bits: np.ndarray, locs: np.ndarray, kv_rows: np.ndarray, scale: float):
+def sparse_mla_decode(q_bits: np.ndarray, locs: np.ndarray, kv_rows: np.ndarray, scale: float,
+                      bf16_kv: bool = False):
     """q_bits: bfloat16 bits uint16 [B, H, 576]; locs: int [B, n] rows of
     kv_rows (uint8 [rows, item]), -1 skipped.  Returns (out [B, H, 512],
-    lse [B, H]) in float64."""
+    lse [B, H]) in float64.  bf16_kv: attend over the values as reading R23
+    has the kernel read them (decode_rows_bf16) instead of the exact values
+    the bytes encode (identical for bf16 rows)."""
     B, H, _ = q_bits.shape
     out = np.zeros((B, H, LATENT))
     lse = np.full((B, H), -np.inf)
+    dec = decode_rows_bf16 if bf16_kv else decode_rows
     for b in range(B):
         rows = [int(x) for x in locs[b] if x >= 0]
-        lat, rope = decode_rows(kv_rows[rows]) if rows else (np.zeros((0, LATENT)),
-                                                             np.zeros((0, ROPE)))
+        lat, rope = dec(kv_rows[rows]) if rows else (np.zeros((0, LATENT)),
+                                                     np.zeros((0, ROPE)))
         out[b], lse[b] = attend(bf16_to_f64(q_bits[b]), lat, rope, scale)
     return out, lse
 

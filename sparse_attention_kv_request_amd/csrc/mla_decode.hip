@@ -351,7 +351,7 @@ void mla_decode(MlaArgs a) {
 #pragma unroll
   for (int i = 0; i < kDimBlocks; ++i) acc[i] = zero16();
   float m_ref = -INFINITY;  // reference of the weights of head lane%32, log2 units
-  float l_run = 0.f;        // sum of its (bf16-rounded) weights
+  float l_run = 0.f;        // sum of its weights (fp32, before the bf16 rounding)
 
   const __amdgpu_buffer_rsrc_t kv = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(a.kv), 0, static_cast<int>(a.kv_rows * a.item_bytes), 0x00020000);
@@ -439,8 +439,8 @@ void mla_decode(MlaArgs a) {
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(raw[j + 1], a.scale_log2, -mr));
       const uint32_t pw = pack_bf16(p0, p1);
       pbits[j >> 3][(j & 7) >> 1] = pw;
-      psum += __builtin_bit_cast(float, pw << 16);
-      psum += __builtin_bit_cast(float, pw & 0xFFFF0000u);
+      psum += p0;  // the normaliser sums the fp32 weights, before their rounding
+      psum += p1;
     }
     psum += xor32(psum);
     l_run = fresh ? psum : l_run + psum;

@@ -100,3 +100,50 @@ def test_equal_scores_average_the_values():
     out, lse = mla.attend(q, lat, rope, 0.5)
     assert np.allclose(out, np.tile(lat.mean(0), (2, 1)), atol=1e-12)
     assert np.allclose(lse, math.log(6), atol=1e-12)
+
+
+def test_f32_to_bf16_rne_matches_torch():
+    """The oracle's float32 -> bfloat16 rounding against torch's conversion
+    (round to nearest, ties to even) over random values of every magnitude,
+    exact ties (odd and even kept parts), subnormals, the largest finite
+    values, infinities and NaN."""
+    rng = np.random.default_rng(3)
+    bits = rng.integers(0, 2 ** 32, 200000, dtype=np.uint64).astype(np.uint32)
+    hi = rng.integers(0, 2 ** 16, 4000, dtype=np.uint64) << np.uint64(16)
+    ties = (hi | np.uint64(0x8000)).astype(np.uint32)
+    low = rng.choice(np.array([0x7FFF, 0x8001, 0x0001, 0xFFFF], np.uint64), 4000)
+    near = (hi | low).astype(np.uint32)
+    special = np.array([0, 0x80000000, 0x00000001, 0x007FFFFF, 0x7F7FFFFF, 0xFF7FFFFF,
+                        0x7F7F8000, 0x7F800000, 0xFF800000, 0x7FC00000], np.uint32)
+    x = np.concatenate([bits, ties, near, special]).view(np.float32)
+    got = mla.f32_to_bf16_rne(x)
+    want = torch.from_numpy(x.copy()).to(torch.bfloat16).to(torch.float64).numpy()
+    both_nan = np.isnan(got) & np.isnan(want)
+    assert np.array_equal(got[~both_nan], want[~both_nan])
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+
+
+def test_bf16_reading_of_fp8_rows_matches_torch():
+    """Reading R23 of an fp8 row: code value x float32 scale as one float32
+    product, then bfloat16 -- against torch's float8_e4m3fn decoding and
+    conversions, over every code and scales of many magnitudes."""
+    rng = np.random.default_rng(4)
+    n = 64
+    rows = np.empty((n, mla.FP8_ROW), np.uint8)
+    rows[:, :mla.LATENT] = np.tile(np.arange(256, dtype=np.uint8), 2)[None]
+    rows[:, :mla.LATENT] = rng.permuted(rows[:, :mla.LATENT], axis=1)
+    rows[:, :mla.LATENT][rows[:, :mla.LATENT] & 0x7F == 0x7F] = 0   # no NaN codes
+    scales = (rng.random((n, 4)) * np.exp2(rng.integers(-20, 20, (n, 4)))).astype(np.float32)
+    rows[:, mla.LATENT:mla.LATENT + 16] = scales.view(np.uint8).reshape(n, 16)
+    rows[:, mla.LATENT + 16:] = rng.integers(0, 256, (n, 128), dtype=np.uint8)
+    lat, rope = mla.decode_rows_bf16(rows)
+    codes = torch.from_numpy(np.ascontiguousarray(rows[:, :mla.LATENT])).view(torch.float8_e4m3fn)
+    prod = codes.to(torch.float32) * torch.from_numpy(np.repeat(scales, 128, axis=1))
+    want = prod.to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(lat, want)
+    _, rope_exact = mla.decode_rows(rows)
+    assert np.array_equal(rope, rope_exact, equal_nan=True)
+    # bf16 rows are read as stored
+    b16 = rng.integers(0, 256, (8, mla.BF16_ROW), dtype=np.uint8)
+    for u, v in zip(mla.decode_rows_bf16(b16), mla.decode_rows(b16)):
+        assert np.array_equal(u, v, equal_nan=True)
