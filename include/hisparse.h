@@ -411,6 +411,28 @@ size_t hisparse_topk_workspace_bytes(int32_t batch, int32_t max_len, int32_t k);
 int hisparse_topk_index_build(const hisparse_topk_call_t* call, void* stream);
 
 /*
+ * hisparse_topk_index_build for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same selection and index table, with the split rows'
+ * candidates kept in a fixed array the library holds on every device it runs
+ * on (HISPARSE_TOPK_STATIC_SCRATCH_BYTES, 16 MiB, for the life of the
+ * process) instead of call->workspace, which is ignored along with
+ * call->workspace_bytes.  The call allocates nothing; the caller still passes
+ * every input and output.  The first call on a device looks the array's
+ * address up once (no allocation).  Nothing in the array needs clearing:
+ * each call's chunk kernel writes every candidate and count its merge kernel
+ * reads.  Every call on one device shares that device's array, so calls that
+ * may overlap on one device (on different streams, or from different host
+ * threads without stream ordering) race; calls on one stream are ordered.
+ * Errors: those of hisparse_topk_index_build, except that a call needing
+ * more than HISPARSE_TOPK_STATIC_SCRATCH_BYTES of candidates
+ * (hisparse_topk_workspace_bytes) returns HISPARSE_E_UNSUPPORTED before any
+ * launch.
+ */
+#define HISPARSE_TOPK_STATIC_SCRATCH_BYTES (16u << 20)
+int hisparse_topk_index_build_noalloc(const hisparse_topk_call_t* call, void* stream);
+
+/*
  * Empties the caches of `n` requests in every layer: a request newly admitted
  * to a pool slot starts from an empty hot cache (sglang PR #20343 summary,
  * "Risks and impact": admit_request_into_staging is where the coordinator

@@ -97,6 +97,8 @@ _SIGNATURES = {
     "hisparse_topk_plan": (ctypes.c_int, [c_i32, c_i32, c_vp, c_vp, ctypes.c_size_t, c_vp]),
     "hisparse_topk_workspace_bytes": (ctypes.c_size_t, [c_i32, c_i32, c_i32]),
     "hisparse_topk_index_build": (ctypes.c_int, [ctypes.POINTER(HisparseTopkCall), c_vp]),
+    "hisparse_topk_index_build_noalloc": (ctypes.c_int, [ctypes.POINTER(HisparseTopkCall),
+                                                         c_vp]),
     "hisparse_request_reset": (ctypes.c_int, [c_vp, c_i32, c_vp, c_vp]),
     "hisparse_plan_capacity": (c_i32, [c_vp]),
     "hisparse_state_export": (ctypes.c_int, [c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
@@ -208,6 +210,10 @@ def hisparse_topk_workspace_bytes(batch, max_len, k) -> int:
 
 def hisparse_topk_index_build(call: HisparseTopkCall, stream) -> int:
     return lib().hisparse_topk_index_build(ctypes.byref(call), stream)
+
+
+def hisparse_topk_index_build_noalloc(call: HisparseTopkCall, stream) -> int:
+    return lib().hisparse_topk_index_build_noalloc(ctypes.byref(call), stream)
 
 
 def hisparse_request_reset(st, n, req_pool_indices, stream) -> int:
@@ -475,7 +481,9 @@ class TopkIndexBuilder:
 
     def build(self, logits: torch.Tensor, seq_lens: torch.Tensor, indices: torch.Tensor,
               locs: torch.Tensor | None = None, mode: str = "none", page_table=None,
-              page_size: int = 1, row_offsets=None, stream=None):
+              page_size: int = 1, row_offsets=None, stream=None, noalloc: bool = False):
+        """noalloc: call hisparse_topk_index_build_noalloc (the library's fixed
+        scratch instead of this builder's workspace)."""
         assert logits.dtype == torch.float32 and logits.is_contiguous()
         assert tuple(logits.shape) == (self.batch, self.max_len)
         assert tuple(indices.shape) == (self.batch, self.k) and indices.dtype == torch.int32
@@ -492,10 +500,14 @@ class TopkIndexBuilder:
         c.row_offsets = _ptr(row_offsets)
         c.indices = _ptr(indices)
         c.locs = _ptr(locs)
-        c.workspace = self.workspace.data_ptr() if self.workspace_bytes else None
-        c.workspace_bytes = self.workspace_bytes
+        c.workspace = self.workspace.data_ptr() if self.workspace_bytes and not noalloc else None
+        c.workspace_bytes = 0 if noalloc else self.workspace_bytes
         c.error_word = _ptr(self.err)
-        _check(hisparse_topk_index_build(c, _stream(stream)), "hisparse_topk_index_build")
+        if noalloc:
+            _check(hisparse_topk_index_build_noalloc(c, _stream(stream)),
+                   "hisparse_topk_index_build_noalloc")
+        else:
+            _check(hisparse_topk_index_build(c, _stream(stream)), "hisparse_topk_index_build")
 
     def error_flags(self, clear: bool = True) -> int:
         v = int(self.err.item()) & 0xFFFFFFFF

@@ -443,6 +443,31 @@ namespace {
 bool topk_sizes_ok(int32_t batch, int32_t max_len) {
   return batch >= 1 && batch <= (1 << 20) && max_len >= 1 && max_len <= (1 << 28);
 }
+
+// Pointer, plan, mode and (optionally) workspace checks of a top-k call whose
+// sizes passed topk_sizes_ok and topk_shape_supported.
+int topk_call_check(const hisparse_topk_call_t* c, bool with_workspace) {
+  if (!c->logits || !c->seq_lens || !c->plan || !c->indices || !c->error_word)
+    return HISPARSE_E_INVAL;
+  if (c->plan_ints < hisparse_topk_plan_ints(c->batch, c->max_len)) return HISPARSE_E_INVAL;
+  switch (c->mode) {
+    case HISPARSE_INDEX_NONE:
+      break;
+    case HISPARSE_INDEX_PAGED:
+      if (!c->locs || !c->page_table || c->pt_stride < 1 || c->page_size < 1) return HISPARSE_E_INVAL;
+      break;
+    case HISPARSE_INDEX_RAGGED:
+      if (!c->locs || !c->row_offsets) return HISPARSE_E_INVAL;
+      break;
+    default:
+      return HISPARSE_E_INVAL;
+  }
+  if (with_workspace) {
+    const size_t need = hisparse_topk_workspace_bytes(c->batch, c->max_len, c->k);
+    if (c->workspace_bytes < need || (need > 0 && c->workspace == nullptr)) return HISPARSE_E_INVAL;
+  }
+  return HISPARSE_OK;
+}
 }  // namespace
 
 size_t hisparse_topk_plan_ints(int32_t batch, int32_t max_len) {
@@ -468,24 +493,24 @@ size_t hisparse_topk_workspace_bytes(int32_t batch, int32_t max_len, int32_t k) 
 int hisparse_topk_index_build(const hisparse_topk_call_t* c, void* stream) {
   if (c == nullptr || !topk_sizes_ok(c->batch, c->max_len) || c->k < 1) return HISPARSE_E_INVAL;
   if (!hisparse::topk_shape_supported(c->max_len, c->k)) return HISPARSE_E_UNSUPPORTED;
-  if (!c->logits || !c->seq_lens || !c->plan || !c->indices || !c->error_word)
-    return HISPARSE_E_INVAL;
-  if (c->plan_ints < hisparse_topk_plan_ints(c->batch, c->max_len)) return HISPARSE_E_INVAL;
-  switch (c->mode) {
-    case HISPARSE_INDEX_NONE:
-      break;
-    case HISPARSE_INDEX_PAGED:
-      if (!c->locs || !c->page_table || c->pt_stride < 1 || c->page_size < 1) return HISPARSE_E_INVAL;
-      break;
-    case HISPARSE_INDEX_RAGGED:
-      if (!c->locs || !c->row_offsets) return HISPARSE_E_INVAL;
-      break;
-    default:
-      return HISPARSE_E_INVAL;
-  }
-  const size_t need = hisparse_topk_workspace_bytes(c->batch, c->max_len, c->k);
-  if (c->workspace_bytes < need || (need > 0 && c->workspace == nullptr)) return HISPARSE_E_INVAL;
+  const int rc = topk_call_check(c, /*with_workspace=*/true);
+  if (rc != HISPARSE_OK) return rc;
   return status_of(hisparse::launch_topk_index_build(*c, static_cast<hipStream_t>(stream)));
+}
+
+int hisparse_topk_index_build_noalloc(const hisparse_topk_call_t* c, void* stream) {
+  if (c == nullptr || !topk_sizes_ok(c->batch, c->max_len) || c->k < 1) return HISPARSE_E_INVAL;
+  if (!hisparse::topk_shape_supported(c->max_len, c->k)) return HISPARSE_E_UNSUPPORTED;
+  if (hisparse_topk_workspace_bytes(c->batch, c->max_len, c->k) >
+      HISPARSE_TOPK_STATIC_SCRATCH_BYTES)
+    return HISPARSE_E_UNSUPPORTED;
+  hisparse_topk_call_t d = *c;
+  d.workspace = nullptr;  // the fixed array stands in for it
+  d.workspace_bytes = 0;
+  const int rc = topk_call_check(&d, /*with_workspace=*/false);
+  if (rc != HISPARSE_OK) return rc;
+  return status_of(
+      hisparse::launch_topk_index_build_noalloc(d, static_cast<hipStream_t>(stream)));
 }
 
 int hisparse_request_reset(hisparse_state_t st, int32_t n, const int32_t* req_pool_indices,

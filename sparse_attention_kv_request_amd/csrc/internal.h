@@ -63,6 +63,7 @@ inline bool topk_shape_supported(int max_len, int k) {
 hipError_t launch_topk_plan(const int32_t* seq_lens, int32_t* plan, int32_t batch, int32_t max_len,
                             hipStream_t st);
 hipError_t launch_topk_index_build(const hisparse_topk_call_t& c, hipStream_t st);
+hipError_t launch_topk_index_build_noalloc(const hisparse_topk_call_t& c, hipStream_t st);
 
 struct ResetArgs {
   const int32_t* reqs;  // NULL = requests 0..n-1

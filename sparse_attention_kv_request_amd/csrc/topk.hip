@@ -30,6 +30,9 @@
 // one workgroup scan over the bitmap words gives every kept position its
 // output index.  Prefix sums use wave64 DPP scans (row shifts and row
 // broadcasts, VALU only) and one LDS exchange per workgroup scan.
+#include <mutex>
+#include <unordered_map>
+
 #include "internal.h"
 
 namespace hisparse {
@@ -547,6 +550,47 @@ hipError_t launch_topk_plan(const int32_t* seq_lens, int32_t* plan, int32_t batc
   hipLaunchKernelGGL(topk_plan_kernel, dim3(1), dim3(kThreads), 0, st, seq_lens, plan, batch,
                      max_len, topk_max_items(batch, max_len));
   return hipGetLastError();
+}
+
+// Scratch of hisparse_topk_index_build_noalloc: the split rows' candidates
+// live in this fixed array instead of a caller workspace.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in for
+// the symbol); it passes the device address hipGetSymbolAddress returns for
+// the current device, looked up once per device.
+static __device__ __align__(256) uint8_t scratch[HISPARSE_TOPK_STATIC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mutex;
+std::unordered_map<int, void*> g_scratch_ptr;  // device -> address of `scratch` there
+
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  auto it = g_scratch_ptr.find(dev);
+  if (it != g_scratch_ptr.end()) {
+    *out = it->second;
+    return hipSuccess;
+  }
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || ptr == nullptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+  g_scratch_ptr.emplace(dev, ptr);
+  *out = ptr;
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_topk_index_build_noalloc(const hisparse_topk_call_t& c, hipStream_t st) {
+  hisparse_topk_call_t d = c;
+  d.workspace_bytes = topk_workspace_layout(c.batch, c.max_len, c.k).bytes;
+  d.workspace = nullptr;
+  if (d.workspace_bytes > 0) {
+    const hipError_t e = scratch_address(&d.workspace);
+    if (e != hipSuccess) return e;
+  }
+  return launch_topk_index_build(d, st);
 }
 
 hipError_t launch_topk_index_build(const hisparse_topk_call_t& c, hipStream_t st) {
