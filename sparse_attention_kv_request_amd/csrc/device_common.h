@@ -17,10 +17,12 @@ constexpr uint32_t kKeyBits = 28;
 constexpr uint32_t kKeyMask = (1u << kKeyBits) - 1u;
 
 // Everything a plan (lookup / victim / commit) kernel needs.  One workgroup
-// handles one batch row = one (request, layer) cache instance.
+// handles one batch row = one (request, layer) cache instance.  The
+// key -> slot lookup is a join computed per call: the row's keys go into an
+// LDS hash, and every resident key of the instance (slot_key, read in full
+// anyway for the victims) is looked up in it, so no key -> slot table is kept.
 struct PlanArgs {
   // persistent state of the layer's instances, instance q = layer * R + r
-  int16_t* key_slot;    // [L*R][nkeys]  key -> slot, -1 = not resident
   int32_t* slot_key;    // [L*R][H]      slot -> key, -1 = empty
   int32_t* ts;          // [L*R][H]      LRU timestamp (-1 = empty)
   int16_t* order;       // [L*R][H]      LRU order of slots, least recent first
@@ -130,6 +132,15 @@ __device__ __forceinline__ int hash_bucket(int32_t t, int size) {
   return static_cast<int>((static_cast<uint64_t>(h) * static_cast<uint32_t>(size)) >> 32);
 }
 
+// Next bucket of a probe sequence: a table of a power-of-two size walks the
+// triangular offsets 1, 2, 3, ... (bucket h0 + i(i+1)/2, which visits every
+// bucket and breaks up the clusters of linear probing, so the longest probe
+// -- what a wave waits for -- stays short); any other size walks linearly.
+__device__ __forceinline__ int hash_next(int h, int& step, int size) {
+  if ((size & (size - 1)) == 0) return (h + ++step) & (size - 1);
+  return h + 1 == size ? 0 : h + 1;
+}
+
 // Inserts token t (0 <= t < 2^28 - 1) into the open-addressing LDS table
 // `keys` (0 = empty, key + 1 in the low 28 bits) and returns its bucket.  The
 // table is sized above the number of distinct keys, so the probe terminates.
@@ -137,11 +148,60 @@ __device__ __forceinline__ int hash_bucket(int32_t t, int size) {
 __device__ __forceinline__ int hash_insert(uint32_t* keys, int size, int32_t t) {
   const uint32_t want = static_cast<uint32_t>(t) + 1u;
   int h = hash_bucket(t, size);
+  int step = 0;
   while (true) {
     const uint32_t old = atomicCAS(&keys[h], 0u, want);
     if (old == 0u || (old & kKeyMask) == want) return h;
-    h = (h + 1 == size) ? 0 : h + 1;
+    h = hash_next(h, step, size);
   }
+}
+
+// Bucket of token t in the LDS table `keys`, or -1 when t is not in it (key
+// bits only; the step bits above them are ignored).  Follows the probe
+// sequence of hash_insert; terminates: the table always has empty buckets.
+__device__ __forceinline__ int hash_find(const uint32_t* keys, int size, int32_t t) {
+  const uint32_t want = static_cast<uint32_t>(t) + 1u;
+  int h = hash_bucket(t, size);
+  int step = 0;
+  while (true) {
+    const uint32_t k = keys[h] & kKeyMask;
+    if (k == want) return h;
+    if (k == 0u) return -1;
+    h = hash_next(h, step, size);
+  }
+}
+
+// Value words of the LDS hash during the lookup: the low 16 bits take the
+// first position of the key in the row (atomicMin of kNoHit | position), the
+// high 16 bits the slot of a resident key found by the join (atomicAnd), or
+// all ones when the key is not resident.  The two halves are written by
+// different threads without a barrier between them.
+constexpr uint32_t kNoHit = 0xFFFF0000u;
+static_assert(HISPARSE_MAX_WORKING_SET < 0xFFFF && HISPARSE_MAX_HOT < 0xFFFF,
+              "positions and slots fit the halves of a value word");
+__device__ __forceinline__ void mark_hit(uint32_t* vals, int h, int slot) {
+  atomicAnd(&vals[h], (static_cast<uint32_t>(slot) << 16) | 0xFFFFu);
+}
+__device__ __forceinline__ int first_pos(uint32_t v) { return static_cast<int>(v & 0xFFFFu); }
+__device__ __forceinline__ int hit_slot(uint32_t v) {  // -1 when not resident
+  return (v >> 16) == 0xFFFFu ? -1 : static_cast<int>(v >> 16);
+}
+
+// Thread t holds the EPH consecutive slots t*EPH .. t*EPH+EPH-1 and a mask
+// of which of them to mark: the 32/EPH lanes that share a bitmap word OR
+// their masks together (lane shuffles, no LDS atomics) and the first of them
+// stores the word.  Every lane of the wave must call it.  Overwrites words
+// [0, words) that the wave's slots cover.
+template <int EPH>
+__device__ __forceinline__ void store_slot_words(uint32_t* bm, int words, uint32_t mask) {
+  static_assert(EPH >= 1 && EPH <= 32 && 32 % EPH == 0, "slots per thread divide a word");
+  constexpr int kLanes = 32 / EPH;
+  const int lane = threadIdx.x & (kWave - 1);
+  uint32_t v = mask << (EPH * (lane % kLanes) % 32);
+#pragma unroll
+  for (int d = 1; d < kLanes; d <<= 1) v |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), d));
+  const int w = static_cast<int>(threadIdx.x) * EPH / 32;
+  if (lane % kLanes == 0 && w < words) bm[w] = v;
 }
 
 // Exclusive prefix of set bits over a bitmap of `words` words: wpre[w] =

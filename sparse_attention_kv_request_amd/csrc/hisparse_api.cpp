@@ -52,7 +52,6 @@ PlanArgs plan_args(const hisparse_state* st, int32_t layer, int32_t batch, int32
                    int32_t* miss_count, int32_t* page_table, int32_t* num_pages,
                    const hisparse_miss_plan_t* plan) {
   PlanArgs a{};
-  a.key_slot = st->key_slot;
   a.slot_key = st->slot_key;
   a.ts = st->ts;
   a.order = st->order;
@@ -266,7 +265,6 @@ int hisparse_state_create(const hisparse_config_t* cfg, void* stream, hisparse_s
 
   const size_t inst = static_cast<size_t>(L) * R;
   size_t off = 0;
-  const size_t o_key_slot = off; off += align256(inst * d.nkeys * sizeof(int16_t));
   const size_t o_slot_key = off; off += align256(inst * H * sizeof(int32_t));
   const size_t o_ts = off;       off += lru ? align256(inst * H * sizeof(int32_t)) : 0;
   const size_t o_order = off;    off += lru ? align256(inst * H * sizeof(int16_t)) : 0;
@@ -286,7 +284,6 @@ int hisparse_state_create(const hisparse_config_t* cfg, void* stream, hisparse_s
     return status_of(e);
   }
   auto* base = static_cast<uint8_t*>(st->arena);
-  st->key_slot = reinterpret_cast<int16_t*>(base + o_key_slot);
   st->slot_key = reinterpret_cast<int32_t*>(base + o_slot_key);
   st->ts = lru ? reinterpret_cast<int32_t*>(base + o_ts) : nullptr;
   st->order = lru ? reinterpret_cast<int16_t*>(base + o_order) : nullptr;
@@ -302,8 +299,8 @@ int hisparse_state_create(const hisparse_config_t* cfg, void* stream, hisparse_s
   auto s = static_cast<hipStream_t>(stream);
   e = hipMemsetAsync(st->err, 0, sizeof(uint32_t), s);
   if (e == hipSuccess) {
-    ResetArgs ra{nullptr, st->key_slot, st->slot_key, st->ts, st->order, st->refbits,
-                 st->ctrl, st->err, R, H, d.hw, d.nkeys};
+    ResetArgs ra{nullptr, st->slot_key, st->ts, st->order, st->refbits, st->ctrl, st->err,
+                 R, H, d.hw};
     e = launch_reset(ra, R, L, s);
   }
   if (e == hipSuccess) e = hipStreamSynchronize(s);
@@ -346,8 +343,15 @@ int hisparse_swap_in_selected(hisparse_state_t st, int32_t layer_id, int32_t bat
   PlanArgs a = plan_args(st, layer_id, batch, 1, req_pool_indices, seq_lens, topk_indices,
                          out_locs, miss_count, page ? page_table : nullptr,
                          page ? num_pages : nullptr, plan);
-  a.hash_size = page ? 0 : hash_size_for(a.K);
-  if (!page) enable_copy_sort(st, &a, lru_token_lds_bytes);
+  if (!page) {
+    // key bitmaps when they fit (direct ranks, no hash); else an LDS hash
+    a.hash_size = 0;
+    enable_copy_sort(st, &a, lru_token_lds_bytes);
+    if (a.sort_words == 0) {
+      a.hash_size = hash_size_for(a.K, true);
+      if (lru_token_lds_bytes(a) > st->max_lds) a.hash_size = hash_size_for(a.K, false);
+    }
+  }
   if ((page ? lru_page_lds_bytes(a) : lru_token_lds_bytes(a)) > st->max_lds)
     return HISPARSE_E_UNSUPPORTED;
   return run_swap(st, a, false, static_cast<hipStream_t>(stream));
@@ -519,9 +523,8 @@ int hisparse_request_reset(hisparse_state_t st, int32_t n, const int32_t* req_po
   if (n == 0) return HISPARSE_OK;
   if (req_pool_indices == nullptr) return HISPARSE_E_INVAL;
   DeviceGuard g(st->device);
-  ResetArgs ra{req_pool_indices, st->key_slot, st->slot_key, st->ts, st->order, st->refbits,
-               st->ctrl, st->err, st->cfg.max_requests, st->cfg.hot_buffer_size, st->hw,
-               st->nkeys};
+  ResetArgs ra{req_pool_indices, st->slot_key, st->ts, st->order, st->refbits, st->ctrl,
+               st->err, st->cfg.max_requests, st->cfg.hot_buffer_size, st->hw};
   return status_of(launch_reset(ra, n, st->cfg.num_layers, static_cast<hipStream_t>(stream)));
 }
 
@@ -536,7 +539,6 @@ int hisparse_state_export(hisparse_state_t st, int32_t req, int32_t layer, int32
   const size_t q = static_cast<size_t>(layer) * st->cfg.max_requests + req;
   const int H = st->cfg.hot_buffer_size;
   std::vector<uint32_t> bits(st->hw);
-  std::vector<int16_t> ks(key_slot_h ? st->nkeys : 0);
   hipError_t e = hipMemcpyAsync(slot_key_h, st->slot_key + q * H, H * sizeof(int32_t),
                                 hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) {
@@ -548,13 +550,11 @@ int hisparse_state_export(hisparse_state_t st, int32_t req, int32_t layer, int32
   }
   if (e == hipSuccess)
     e = hipMemcpyAsync(ctrl_h, st->ctrl + 2 * q, 2 * sizeof(int32_t), hipMemcpyDeviceToHost, s);
-  if (e == hipSuccess && key_slot_h)
-    e = hipMemcpyAsync(ks.data(), st->key_slot + q * st->nkeys, st->nkeys * sizeof(int16_t),
-                       hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return status_of(e);
   if (!st->ts) host::decode_refbits(bits.data(), H, policy_h);
-  if (key_slot_h) host::widen_key_slot(ks.data(), st->nkeys, key_slot_h);
+  if (key_slot_h && host::invert_slot_key(slot_key_h, H, st->nkeys, key_slot_h) != HISPARSE_OK)
+    return HISPARSE_E_HIP;  // the device state is not a valid map
   return HISPARSE_OK;
 }
 
@@ -574,9 +574,6 @@ int hisparse_state_import(hisparse_state_t st, int32_t req, int32_t layer,
   const size_t q = static_cast<size_t>(layer) * st->cfg.max_requests + req;
   hipError_t e = hipMemcpyAsync(st->slot_key + q * H, slot_key_h, H * sizeof(int32_t),
                                 hipMemcpyHostToDevice, s);
-  if (e == hipSuccess)
-    e = hipMemcpyAsync(st->key_slot + q * st->nkeys, img.key_slot.data(),
-                       st->nkeys * sizeof(int16_t), hipMemcpyHostToDevice, s);
   if (e == hipSuccess && lru)
     e = hipMemcpyAsync(st->ts + q * H, policy_h, H * sizeof(int32_t), hipMemcpyHostToDevice, s);
   if (e == hipSuccess && lru)

@@ -84,10 +84,10 @@ inline int derive(const hisparse_config_t* c, Derived* d) {
 }
 
 // Device images of one instance built from the host layout of
-// hisparse_state_import: the key->slot table, and the LRU order (slots by
-// (timestamp, slot)) or the CLOCK reference bitmap.
+// hisparse_state_import: the LRU order (slots by (timestamp, slot)) or the
+// CLOCK reference bitmap.  (The slot->key array is copied as given; no
+// key->slot table is kept on the device.)
 struct InstanceImage {
-  std::vector<int16_t> key_slot;  // [nkeys]
   std::vector<int16_t> order;     // [H]   LRU
   std::vector<uint32_t> refbits;  // [hw]  CLOCK
 };
@@ -103,18 +103,17 @@ inline int encode_import(int32_t H, int32_t nkeys, bool lru, const int32_t* slot
     return HISPARSE_E_INVAL;
   if (lru && ctrl[0] < 0) return HISPARSE_E_INVAL;
   if (!lru && (ctrl[1] < 0 || ctrl[1] >= H)) return HISPARSE_E_INVAL;
-  std::vector<int16_t> ks(static_cast<size_t>(nkeys), static_cast<int16_t>(kEmptyKey));
+  std::vector<bool> seen(static_cast<size_t>(nkeys), false);
   for (int32_t s = 0; s < H; ++s) {
     const int32_t k = slot_key[s];
     if (k == kEmptyKey) {
       if (lru && policy[s] != -1) return HISPARSE_E_INVAL;
       continue;
     }
-    if (k < 0 || k >= nkeys || ks[k] != kEmptyKey) return HISPARSE_E_INVAL;
-    ks[k] = static_cast<int16_t>(s);
+    if (k < 0 || k >= nkeys || seen[static_cast<size_t>(k)]) return HISPARSE_E_INVAL;
+    seen[static_cast<size_t>(k)] = true;
     if (lru && (policy[s] < 0 || policy[s] >= ctrl[0])) return HISPARSE_E_INVAL;
   }
-  img->key_slot = std::move(ks);
   img->order.clear();
   img->refbits.clear();
   if (lru) {
@@ -139,9 +138,18 @@ inline void decode_refbits(const uint32_t* bits, int32_t H, int32_t* policy) {
   for (int32_t s = 0; s < H; ++s) policy[s] = static_cast<int32_t>((bits[s >> 5] >> (s & 31)) & 1u);
 }
 
-// Export: the int16 key->slot table widened to int32 (-1 stays -1).
-inline void widen_key_slot(const int16_t* ks, int32_t n, int32_t* out) {
-  for (int32_t i = 0; i < n; ++i) out[i] = ks[i];
+// Export: the key->slot map as the inverse of the slot->key array (every key
+// -1 except the resident ones).  HISPARSE_E_INVAL if a key is out of range or
+// held by two slots (the array is then not a valid map).
+inline int invert_slot_key(const int32_t* slot_key, int32_t H, int32_t nkeys, int32_t* key_slot) {
+  std::fill(key_slot, key_slot + nkeys, kEmptyKey);
+  for (int32_t s = 0; s < H; ++s) {
+    const int32_t k = slot_key[s];
+    if (k == kEmptyKey) continue;
+    if (k < 0 || k >= nkeys || key_slot[k] != kEmptyKey) return HISPARSE_E_INVAL;
+    key_slot[k] = s;
+  }
+  return HISPARSE_OK;
 }
 
 // Events of the timed swap calls: every call records a triple (before the

@@ -67,14 +67,13 @@ hipError_t launch_topk_index_build_noalloc(const hisparse_topk_call_t& c, hipStr
 
 struct ResetArgs {
   const int32_t* reqs;  // NULL = requests 0..n-1
-  int16_t* key_slot;
   int32_t* slot_key;
   int32_t* ts;
   int16_t* order;
   uint32_t* refbits;
   int32_t* ctrl;
   uint32_t* err;
-  int32_t R, H, Hw, nkeys;
+  int32_t R, H, Hw;
 };
 
 // One sparse MLA decode-attention call (see hisparse_sparse_mla_decode).
@@ -97,7 +96,7 @@ int mla_max_locations();
 size_t mla_workspace_bytes(int batch, int heads, int n_locs, int num_cus);
 hipError_t launch_mla_decode(const MlaDecodeCall& c, hipStream_t s);
 
-int hash_size_for(int entries);
+int hash_size_for(int entries, bool pow2);
 constexpr int kMaxSortedKeys = 1 << 18;  // keys per request with a sorted copy list
 size_t lru_token_lds_bytes(const PlanArgs& a);
 size_t lru_page_lds_bytes(const PlanArgs& a);
@@ -122,7 +121,6 @@ struct hisparse_state {
   int32_t cap = 0;      // plan capacity per row
   // device memory, one allocation
   void* arena = nullptr;
-  int16_t* key_slot = nullptr;
   int32_t* slot_key = nullptr;
   int32_t* ts = nullptr;
   int16_t* order = nullptr;

@@ -33,8 +33,8 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
   const int T = a.hash_size;
   const int E = a.S * a.K;
   uint32_t* hkey = lds;                                         // [T] key | step bits
-  int32_t* hval = reinterpret_cast<int32_t*>(hkey + T);         // [T] first pos, then row
-  uint32_t* pinned = reinterpret_cast<uint32_t*>(hval + T);     // [Hw]
+  uint32_t* hval = hkey + T;                                    // [T] first pos | hit slot, then row
+  uint32_t* pinned = hval + T;                                  // [Hw]
   uint32_t* refl = pinned + a.Hw;                               // [Hw] reference bits
   int* scan = reinterpret_cast<int*>(refl + a.Hw);              // [NT/64+1]
   const int sw = a.sort_words;
@@ -52,7 +52,6 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
   // Loads that need only the instance go out before the row checks so they
   // share one round trip (a rejected row discards them).
   const size_t q = static_cast<size_t>(a.layer) * a.R + (r >= 0 && r < a.R ? r : 0);
-  int16_t* ks = a.key_slot + q * a.nkeys;
   int32_t* sk = a.slot_key + q * a.H;
   uint32_t* refq = a.refbits + q * a.Hw;
   const int hand = a.ctrl[2 * q + 1];
@@ -68,7 +67,7 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
   // whose barrier then publishes them (a rejected row just returns).
   for (int i = tid; i < T; i += NT) {
     hkey[i] = 0u;
-    hval[i] = 0x7fffffff;
+    hval[i] = 0xFFFFFFFFu;
   }
   if (tid < a.Hw) {
     pinned[tid] = 0u;
@@ -86,7 +85,8 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
     }
     return;
   }
-  // circular sweep positions of this thread and their slot->key words
+  // circular sweep positions of this thread and their slot->key words: the
+  // join's probe side, and the victims' old keys for the plan
   int sl_of[EPH];
   int oldk[EPH];
 #pragma unroll
@@ -120,20 +120,37 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
     if (tok[e] >= 0) {
       const int i = tid * EPT + e;
       hpos[e] = hash_insert(hkey, T, tok[e]);
-      atomicMin(&hval[hpos[e]], i);
+      atomicMin(&hval[hpos[e]], kNoHit | static_cast<uint32_t>(i));
       atomicOr(&hkey[hpos[e]], 1u << (kKeyBits + i / a.K));
+      if (sw) bit_set_atomic(mbits, tok[e]);
     }
   }
   __syncthreads();
 
-  // 2. representatives look up; hits are pinned and referenced
+  // 2. the join: each resident key the working set names is a hit; its slot
+  // goes into the high half of the key's value word and is pinned and
+  // referenced.  Representatives (first occurrences) are read from the low
+  // half, which the join does not change.
   bool rep[EPT];
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) rep[e] = tok[e] >= 0 && hval[hpos[e]] == tid * EPT + e;
+  for (int e = 0; e < EPT; ++e)
+    rep[e] = tok[e] >= 0 && first_pos(hval[hpos[e]]) == tid * EPT + e;
+  // (with the key bitmap, a resident key the working set does not name costs
+  // one LDS read instead of a walk to the end of its probe cluster)
+#pragma unroll
+  for (int e = 0; e < EPH; ++e) {
+    if (oldk[e] < 0 || (sw && !bit_test(mbits, oldk[e]))) continue;
+    const int h = hash_find(hkey, T, oldk[e]);
+    if (h < 0) continue;
+    mark_hit(hval, h, sl_of[e]);
+    bit_set_atomic(pinned, sl_of[e]);
+    bit_set_atomic(refl, sl_of[e]);
+    if (sw) bit_clear_atomic(mbits, oldk[e]);
+  }
   __syncthreads();
   int slot[EPT];
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) slot[e] = rep[e] ? static_cast<int>(ks[tok[e]]) : -1;
+  for (int e = 0; e < EPT; ++e) slot[e] = rep[e] ? hit_slot(hval[hpos[e]]) : -1;
   int packed = 0;  // misses | hits << 16
   int last[EPT];
 #pragma unroll
@@ -141,9 +158,7 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
     last[e] = 0;
     if (!rep[e]) continue;
     if (slot[e] >= 0) {
-      bit_set_atomic(pinned, slot[e]);
-      bit_set_atomic(refl, slot[e]);
-      hval[hpos[e]] = slot[e];
+      hval[hpos[e]] = static_cast<uint32_t>(slot[e]);
       packed += 1 << 16;
     } else {
       // admission priority under overflow: latest step, number of steps, or none
@@ -152,7 +167,6 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
                 : a.admission == HISPARSE_ADMIT_FREQUENT ? __popc(steps) - 1
                                                          : 0;
       atomicAdd(&s_cnt[last[e]], 1);
-      if (sw) bit_set_atomic(mbits, tok[e]);
       packed += 1;
     }
   }
@@ -230,7 +244,7 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
       miss_h[ja[e]] = static_cast<int16_t>(hpos[e]);
     } else {  // scratch row H + jo, outside the cache
       const int jo = jm[e] - ja[e];
-      hval[hpos[e]] = a.H + jo;
+      hval[hpos[e]] = static_cast<uint32_t>(a.H + jo);
       msrc[ma + jo] = r * a.nkeys + tok[e];
       mdst[ma + jo] = r * a.rows + a.H + jo;
       mvic[ma + jo] = -1;
@@ -308,11 +322,9 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
     const int h = miss_h[j];
     const int32_t key = static_cast<int32_t>(hkey[h] & kKeyMask) - 1;
     const int32_t old = oldk[e];  // slot_key[s], fetched at kernel start
-    if (old >= 0) ks[old] = static_cast<int16_t>(kEmpty);
     sk[s] = key;
-    ks[key] = static_cast<int16_t>(s);
     bit_set_atomic(refl, s);
-    hval[h] = s;
+    hval[h] = static_cast<uint32_t>(s);
     msrc[j] = r * a.nkeys + key;
     mdst[j] = r * a.rows + s;
     mvic[j] = old;
@@ -339,7 +351,8 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
   for (int e = 0; e < EPT; ++e) {
     const int i = tid * EPT + e;
     if (i >= E) continue;
-    out[i] = tok[e] >= 0 ? r * a.rows + hval[hpos[e]] : (ring[e] >= 0 ? r * a.rows + ring[e] : -1);
+    out[i] = tok[e] >= 0 ? r * a.rows + static_cast<int>(hval[hpos[e]])
+                         : (ring[e] >= 0 ? r * a.rows + ring[e] : -1);
   }
   if (tid == 0) {
     a.miss_count[b] = m;

@@ -5,9 +5,12 @@
 // hit/miss handling and LRU update; "SGLang HiSparse" blog, section 2.1).
 //
 // Layout choices (gfx950):
-//  * key_slot is a direct-address table over the request's keys (int16 per
-//    token or page).  It plays the role of the pages' token->slot hash with a
-//    perfect hash: one 2-byte read per lookup, no probing, no tombstones.
+//  * The token->slot lookup of the pages is a join computed per call: the
+//    row's distinct keys go into an LDS hash (which also deduplicates them),
+//    and every slot's resident key -- read in full anyway, the victims need
+//    it -- is looked up there.  No key->slot table is kept in HBM, so a call
+//    makes no random probe reads and no scattered key->slot stores; the
+//    slot->key array, read once per call with the order, is the whole map.
 //  * The LRU order is an explicit slot list, least recent first, ties in
 //    slot order.  A call moves every slot it used to the back in slot order,
 //    so the list always equals the (timestamp, slot) order and the victims
@@ -70,7 +73,7 @@ template <int NT, int EPH>
 __device__ void lru_commit(const PlanArgs& a, int b, int r, int now, int m,
                            const int (&o)[EPH], const bool (&avail)[EPH], const int (&rank)[EPH],
                            uint32_t* used, const int32_t* miss_key, int32_t* vslot, int* scan,
-                           int16_t* ks, int32_t* sk, int32_t* tsq, int16_t* ord,
+                           int32_t* sk, int32_t* tsq, int16_t* ord,
                            const uint32_t* mbits, const int32_t* mwpre, const int (&oldk)[EPH]) {
   const int tid = threadIdx.x;
   // commit: the owner of a victim slot replaces its key
@@ -84,9 +87,7 @@ __device__ void lru_commit(const PlanArgs& a, int b, int r, int now, int m,
       const int s = o[e];
       const int32_t key = miss_key[j];
       const int32_t old = oldk[e];  // slot_key[s], fetched at kernel start
-      if (old >= 0) ks[old] = static_cast<int16_t>(kEmpty);
       sk[s] = key;
-      ks[key] = static_cast<int16_t>(s);
       tsq[s] = now;
       vslot[j] = s;
       bit_set_atomic(used, s);
@@ -140,16 +141,24 @@ __device__ void lru_commit(const PlanArgs& a, int b, int r, int now, int m,
 template <int NT, int EPT, int EPH>
 __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
   extern __shared__ uint32_t lds[];
-  const int T = a.hash_size;
-  uint32_t* hkey = lds;                                            // [T]
-  int32_t* hval = reinterpret_cast<int32_t*>(hkey + T);            // [T]
-  uint32_t* used = reinterpret_cast<uint32_t*>(hval + T);          // [Hw]
+  // Every distinct key of the row gets one entry of kmin / kres: with key
+  // bitmaps (sw > 0, the request's keys fit a bitmap in LDS) the entry is the
+  // key's rank among the row's keys -- popcounts over the bitmap, a perfect
+  // hash built per call, no probing; otherwise an LDS hash bucket.
+  const int sw = a.sort_words;
+  const int T = a.hash_size;                                       // hash path only
+  const int D = sw ? a.K : T;                                      // entries
+  uint32_t* used = lds;                                            // [Hw]
   int32_t* miss_key = reinterpret_cast<int32_t*>(used + a.Hw);     // [K]
   int32_t* vslot = miss_key + a.K;                                 // [K]
   int* scan = vslot + a.K;                                         // [2*NT/64]
-  const int sw = a.sort_words;
   uint32_t* mbits = reinterpret_cast<uint32_t*>(scan + 2 * NT / kWave);  // [sw] miss keys
   int32_t* mwpre = reinterpret_cast<int32_t*>(mbits + sw);              // [sw]
+  uint32_t* rbits = reinterpret_cast<uint32_t*>(mwpre + sw);            // [sw] row keys
+  int32_t* rwpre = reinterpret_cast<int32_t*>(rbits + sw);              // [sw]
+  uint32_t* kmin = reinterpret_cast<uint32_t*>(rwpre + sw);  // [D] first position of the key
+  int32_t* kres = reinterpret_cast<int32_t*>(kmin + D);      // [D] hit slot, then -(miss rank+1)
+  uint32_t* hkey = reinterpret_cast<uint32_t*>(kres + D);    // [T] hash path: key + 1
 
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -158,16 +167,17 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
   // Loads that need only the instance go out before the row checks so they
   // share one round trip (a rejected row discards them).
   const size_t q = static_cast<size_t>(a.layer) * a.R + (r >= 0 && r < a.R ? r : 0);
-  int16_t* ks = a.key_slot + q * a.nkeys;
   int32_t* sk = a.slot_key + q * a.H;
   int32_t* tsq = a.ts + q * a.H;
   int16_t* ord = a.order + q * a.H;
   const int now = a.ctrl[2 * q];
   int o[EPH];
+  int rkey[EPH];  // resident keys of slots tid*EPH + e: the join's probe side
 #pragma unroll
   for (int e = 0; e < EPH; ++e) {
     const int k = tid * EPH + e;
     o[e] = k < a.H ? static_cast<int>(ord[k]) : -1;
+    rkey[e] = k < a.H ? sk[k] : kEmpty;
   }
   const int32_t* row = a.topk + static_cast<size_t>(b) * a.K;
   int32_t raw[EPT];
@@ -176,14 +186,20 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
     const int i = tid * EPT + e;
     raw[e] = i < a.K ? row[i] : -1;
   }
-  // The LDS hash and bitmaps are cleared before the row checks, whose
-  // barrier then publishes the cleared state (a rejected row just returns).
-  for (int i = tid; i < T; i += NT) {
-    hkey[i] = 0u;
-    hval[i] = 0x7fffffff;
+  // The LDS tables are cleared before the row checks, whose barrier then
+  // publishes the cleared state (a rejected row just returns).
+  for (int i = tid; i < D; i += NT) {
+    kmin[i] = 0xFFFFFFFFu;
+    kres[i] = -1;
   }
-  for (int i = tid; i < a.Hw; i += NT) used[i] = 0u;
-  for (int i = tid; i < sw; i += NT) mbits[i] = 0u;
+  if (sw) {
+    for (int i = tid; i < sw; i += NT) {
+      mbits[i] = 0u;
+      rbits[i] = 0u;
+    }
+  } else {
+    for (int i = tid; i < T; i += NT) hkey[i] = 0u;
+  }
   const uint32_t code = row_check<NT>(a, b, r, sl);
   if (code) {
     reject_row<NT>(a, b, a.K, code, false);
@@ -193,7 +209,7 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
   // their ring row instead (the extra-page lookup, before the hash lookup)
   // and stay out of the cache.
   int32_t tok[EPT];
-  int hpos[EPT];
+  int idx[EPT];   // the entry's key entry (rank or bucket)
   int ring[EPT];
   bool bad_index = false;
 #pragma unroll
@@ -204,60 +220,82 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
     const bool extra = valid && t >= sl - a.ext;
     ring[e] = extra ? a.ext_base + t % a.ext : -1;
     tok[e] = valid && !extra ? t : -1;
+    idx[e] = 0;
   }
-  // One round trip for the slot->key of every order position (the victims'
-  // commit) and the key->slot probe of every entry: the probe needs only the
-  // token, and nothing writes this instance's key->slot entries before the
-  // commit, so it goes out now and lands during the dedup below (duplicates
-  // probe too and read the same word; only representatives use it).
+  // the resident key of every order position: the victims' old keys for the
+  // plan (a gather in LRU order, only needed at the commit)
   int oldk[EPH];
 #pragma unroll
   for (int e = 0; e < EPH; ++e) oldk[e] = o[e] >= 0 ? sk[o[e]] : kEmpty;
-  int probe[EPT];
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) probe[e] = tok[e] >= 0 ? static_cast<int>(ks[tok[e]]) : -1;
 
-  // insert every entry into the LDS hash; the first occurrence keeps its
-  // position
+  // 2. dedup and the join.  kmin takes each key's first position (atomicMin);
+  // the owner of each resident slot whose key the row names writes the slot
+  // into the key's kres entry and marks the slot used now.
+  uint32_t hitmask = 0u;
+  if (sw) {
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    hpos[e] = 0;
-    if (tok[e] >= 0) {
-      hpos[e] = hash_insert(hkey, T, tok[e]);
-      atomicMin(&hval[hpos[e]], tid * EPT + e);
+    for (int e = 0; e < EPT; ++e)
+      if (tok[e] >= 0) bit_set_atomic(rbits, tok[e]);
+    __syncthreads();
+    bitmap_word_prefix<NT>(rbits, rwpre, sw, scan);
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      if (tok[e] < 0) continue;
+      idx[e] = bitmap_rank(rbits, rwpre, tok[e]);
+      atomicMin(&kmin[idx[e]], static_cast<uint32_t>(tid * EPT + e));
+    }
+#pragma unroll
+    for (int e = 0; e < EPH; ++e) {
+      const int32_t k = rkey[e];
+      if (k < 0 || !bit_test(rbits, k)) continue;
+      const int s = tid * EPH + e;
+      kres[bitmap_rank(rbits, rwpre, k)] = s;
+      hitmask |= 1u << e;
+      tsq[s] = now;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      if (tok[e] < 0) continue;
+      idx[e] = hash_insert(hkey, T, tok[e]);
+      atomicMin(&kmin[idx[e]], static_cast<uint32_t>(tid * EPT + e));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < EPH; ++e) {
+      if (rkey[e] < 0) continue;
+      const int h = hash_find(hkey, T, rkey[e]);
+      if (h < 0) continue;
+      const int s = tid * EPH + e;
+      kres[h] = s;
+      hitmask |= 1u << e;
+      tsq[s] = now;
     }
   }
+  // the used set of the hit slots, per word by lane shuffles (this thread's
+  // slots are consecutive)
+  store_slot_words<EPH>(used, a.Hw, hitmask);
   __syncthreads();
 
-  // 2. representatives take their key's probe.  From here on a bucket's
-  // key word (no longer read: inserts are done) holds its key's result, the
-  // slot of a hit or -(miss rank + 1), so the representative checks above
-  // (reads of hval) need no barrier before these writes.
+  // 3. representatives (first occurrences) take their key's result; misses
+  // go into the miss-key bitmap.  One scan then ranks the misses (position
+  // order), the available order positions (order) and the miss keys' bitmap
+  // words (key order): misses and available positions share one word (at
+  // most 8192 and 32768).
   bool rep[EPT];
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) rep[e] = tok[e] >= 0 && hval[hpos[e]] == tid * EPT + e;
-  int32_t* hres = reinterpret_cast<int32_t*>(hkey);
   int slot[EPT];
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) slot[e] = rep[e] ? probe[e] : -1;
   int nmiss = 0;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
-    if (!rep[e]) continue;
-    if (slot[e] >= 0) {
-      bit_set_atomic(used, slot[e]);
-      tsq[slot[e]] = now;
-      hres[hpos[e]] = slot[e];
-    } else {
+    rep[e] = tok[e] >= 0 && kmin[idx[e]] == static_cast<uint32_t>(tid * EPT + e);
+    slot[e] = rep[e] ? kres[idx[e]] : -1;
+    if (rep[e] && slot[e] < 0) {
       ++nmiss;
       if (sw) bit_set_atomic(mbits, tok[e]);
     }
   }
-  __syncthreads();
-
-  // 3. one scan ranks the misses (position order), the available order
-  // positions (order) and the miss keys' bitmap words (key order): misses
-  // and available positions share one word (at most 8192 and 32768).
+  if (sw) __syncthreads();  // the scan below counts the miss bitmap
   bool avail[EPH];
   const int navail = lru_available<EPH>(o, used, avail);
   const int wpt = (sw + NT - 1) / NT;
@@ -279,7 +317,7 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
     if (rep[e] && slot[e] < 0) {
-      hres[hpos[e]] = -(j + 1);
+      kres[idx[e]] = -(j + 1);
       miss_key[j] = tok[e];
       ++j;
     }
@@ -292,7 +330,7 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
   __syncthreads();
 
   // 4. victims, commit, new order
-  lru_commit<NT, EPH>(a, b, r, now, m, o, avail, rank, used, miss_key, vslot, scan, ks, sk, tsq,
+  lru_commit<NT, EPH>(a, b, r, now, m, o, avail, rank, used, miss_key, vslot, scan, sk, tsq,
                       ord, sw ? mbits : nullptr, mwpre, oldk);
   __syncthreads();
 
@@ -304,7 +342,7 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
     if (i >= a.K) continue;
     int loc = ring[e] >= 0 ? r * a.rows + ring[e] : -1;
     if (tok[e] >= 0) {
-      const int v = hres[hpos[e]];
+      const int v = kres[idx[e]];
       loc = r * a.rows + (v >= 0 ? v : vslot[-v - 1]);
     }
     out[i] = loc;
@@ -336,16 +374,17 @@ __global__ __launch_bounds__(NT) void lru_page_plan(PlanArgs a) {
   const int r = a.req[b];
   const int sl = a.seq[b];
   const size_t q = static_cast<size_t>(a.layer) * a.R + (r >= 0 && r < a.R ? r : 0);
-  int16_t* ks = a.key_slot + q * a.nkeys;
   int32_t* sk = a.slot_key + q * a.H;
   int32_t* tsq = a.ts + q * a.H;
   int16_t* ord = a.order + q * a.H;
   const int now = a.ctrl[2 * q];
   int o[EPH];
+  int rkey[EPH];  // resident pages of slots tid*EPH + e: the join's probe side
 #pragma unroll
   for (int e = 0; e < EPH; ++e) {
     const int k = tid * EPH + e;
     o[e] = k < a.H ? static_cast<int>(ord[k]) : -1;
+    rkey[e] = k < a.H ? sk[k] : kEmpty;
   }
   const int32_t* row = a.topk + static_cast<size_t>(b) * a.K;
   int32_t raw[EPT];
@@ -403,18 +442,28 @@ __global__ __launch_bounds__(NT) void lru_page_plan(PlanArgs a) {
   }
   __syncthreads();
 
-  // 3. look every distinct page up; rank misses in page order
+  // 3. the join: every resident page the row names is a hit; its entry in
+  // the distinct-page list takes the slot (flagged), the slot is used now
+  constexpr int32_t kHit = 1 << 30;  // pages < 2^18, slots < 2^12
+#pragma unroll
+  for (int e = 0; e < EPH; ++e) {
+    const int p = rkey[e];
+    if (p < 0 || !bit_test(pbits, p)) continue;
+    const int s = tid * EPH + e;
+    pslot[bitmap_rank(pbits, wpre, p)] = kHit | s;
+    bit_set_atomic(used, s);
+    tsq[s] = now;
+  }
+  __syncthreads();
+  // rank the misses in page order
   int m = 0;
   for (int base = 0; base < npages; base += NT) {
     const int jp = base + tid;
     const bool active = jp < npages;
-    const int p = active ? pslot[jp] : 0;
-    const int s = active ? static_cast<int>(ks[p]) : -1;
+    const int x = active ? pslot[jp] : 0;
+    const int p = x;
+    const int s = x & kHit ? x & ~kHit : -1;
     const bool miss = active && s < 0;
-    if (active && s >= 0) {
-      bit_set_atomic(used, s);
-      tsq[s] = now;
-    }
     int round_misses;
     int jm = block_exclusive_scan<NT>(miss ? 1 : 0, scan, &round_misses) + m;
     if (active) {
@@ -440,7 +489,7 @@ __global__ __launch_bounds__(NT) void lru_page_plan(PlanArgs a) {
     rank[e] = rk;
     rk += avail[e];
   }
-  lru_commit<NT, EPH>(a, b, r, now, m, o, avail, rank, used, miss_key, vslot, scan, ks, sk, tsq,
+  lru_commit<NT, EPH>(a, b, r, now, m, o, avail, rank, used, miss_key, vslot, scan, sk, tsq,
                       ord, nullptr, nullptr, oldk);
   __syncthreads();
 
@@ -490,14 +539,23 @@ hipError_t launch_plan(K kernel, const PlanArgs& a, size_t lds, hipStream_t s) {
 
 }  // namespace
 
-int hash_size_for(int entries) {
-  // about 2 buckets per entry, rounded to a multiple of 64
-  return ((2 * entries + 63) / 64) * 64;
+int hash_size_for(int entries, bool pow2) {
+  // at least 2 buckets per entry: the next power of two (triangular probing)
+  // or, where LDS is short, a multiple of 64 (linear probing)
+  const int need = 2 * entries < 64 ? 64 : 2 * entries;
+  if (!pow2) return ((need + 63) / 64) * 64;
+  int t = 64;
+  while (t < need) t *= 2;
+  return t;
 }
 
 size_t lru_token_lds_bytes(const PlanArgs& a) {
-  return (2 * static_cast<size_t>(a.hash_size) + a.Hw + 2 * static_cast<size_t>(a.K) +
-          2 * kPlanThreads / kWave + 2 * static_cast<size_t>(a.sort_words)) * 4;
+  // used, miss_key, vslot, scan, four key bitmaps / prefixes, kmin + kres,
+  // and the hash's key words when there are no bitmaps
+  const size_t sw = static_cast<size_t>(a.sort_words);
+  const size_t d = sw ? static_cast<size_t>(a.K) : static_cast<size_t>(a.hash_size);
+  return (a.Hw + 2 * static_cast<size_t>(a.K) + 2 * kPlanThreads / kWave + 4 * sw + 2 * d +
+          (sw ? 0 : static_cast<size_t>(a.hash_size))) * 4;
 }
 
 size_t lru_page_lds_bytes(const PlanArgs& a) {

@@ -15,8 +15,6 @@ __global__ __launch_bounds__(256) void reset_instances(ResetArgs a) {
     return;
   }
   const size_t q = static_cast<size_t>(layer) * a.R + r;
-  int16_t* ks = a.key_slot + q * a.nkeys;
-  for (int i = threadIdx.x; i < a.nkeys; i += blockDim.x) ks[i] = static_cast<int16_t>(kEmpty);
   for (int s = threadIdx.x; s < a.H; s += blockDim.x) {
     a.slot_key[q * a.H + s] = kEmpty;
     if (a.ts) a.ts[q * a.H + s] = -1;

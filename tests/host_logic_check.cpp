@@ -154,9 +154,9 @@ static void check_import_export(std::mt19937_64& rng) {
     const int32_t ctrl[2] = {now, static_cast<int32_t>(rng() % H)};
     InstanceImage img;
     CHECK(encode_import(H, nkeys, lru, slot_key.data(), policy.data(), ctrl, &img) == HISPARSE_OK);
-    CHECK(static_cast<int32_t>(img.key_slot.size()) == nkeys);
-    std::vector<int32_t> wide(static_cast<size_t>(nkeys));
-    widen_key_slot(img.key_slot.data(), nkeys, wide.data());
+    // export's key->slot map: the inverse of the slot->key array
+    std::vector<int32_t> wide(static_cast<size_t>(nkeys), 12345);
+    CHECK(invert_slot_key(slot_key.data(), H, nkeys, wide.data()) == HISPARSE_OK);
     int32_t resident = 0;
     for (int32_t k = 0; k < nkeys; ++k) {
       if (wide[k] < 0) {
@@ -196,6 +196,8 @@ static void check_import_export(std::mt19937_64& rng) {
         if (bad[s] != kEmptyKey) (a < 0 ? a : b) = s;
       bad[b] = bad[a];
       CHECK(encode_import(H, nkeys, lru, bad.data(), policy.data(), ctrl, &img) == HISPARSE_E_INVAL);
+      std::vector<int32_t> inv(static_cast<size_t>(nkeys));
+      CHECK(invert_slot_key(bad.data(), H, nkeys, inv.data()) == HISPARSE_E_INVAL);
     }
     {
       std::vector<int32_t> bad = slot_key;
