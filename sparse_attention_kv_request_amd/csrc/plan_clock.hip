@@ -30,17 +30,28 @@ __device__ __forceinline__ uint32_t multistep_row_check(const PlanArgs& a, int b
 template <int NT, int EPT, int EPH>
 __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
   extern __shared__ uint32_t lds[];
+  // Every distinct key of the working set gets one entry.  With key bitmaps
+  // (sw > 0: the request's keys fit a bitmap in LDS) the entry is the key's
+  // rank among the working set's keys -- popcounts over the bitmap, a perfect
+  // hash built per call -- with kmin (first position, then the key) and kres
+  // (hit slot + 1 | step bits << 16, then the key's row).  Otherwise an LDS
+  // hash: hkey (key + 1 | step bits << 28) and hval (first position | hit
+  // slot << 16, then the row) per bucket.
+  const int sw = a.sort_words;
   const int T = a.hash_size;
   const int E = a.S * a.K;
-  uint32_t* hkey = lds;                                         // [T] key | step bits
-  uint32_t* hval = hkey + T;                                    // [T] first pos | hit slot, then row
-  uint32_t* pinned = hval + T;                                  // [Hw]
-  uint32_t* refl = pinned + a.Hw;                               // [Hw] reference bits
-  int* scan = reinterpret_cast<int*>(refl + a.Hw);              // [NT/64+1]
-  const int sw = a.sort_words;
+  const int D = sw ? E : T;
+  uint32_t* pinned = lds;                                        // [Hw]
+  uint32_t* refl = pinned + a.Hw;                                // [Hw] reference bits
+  int* scan = reinterpret_cast<int*>(refl + a.Hw);               // [NT/64+1]
   uint32_t* mbits = reinterpret_cast<uint32_t*>(scan + NT / kWave + 1);  // [sw] miss keys
   int32_t* mwpre = reinterpret_cast<int32_t*>(mbits + sw);              // [sw]
-  int16_t* miss_h = reinterpret_cast<int16_t*>(mwpre + sw);             // [E]
+  uint32_t* rbits = reinterpret_cast<uint32_t*>(mwpre + sw);            // [sw] working-set keys
+  int32_t* rwpre = reinterpret_cast<int32_t*>(rbits + sw);              // [sw]
+  uint32_t* kmin = reinterpret_cast<uint32_t*>(rwpre + sw);  // [D] direct: first pos, then key
+  uint32_t* val = kmin + D;                                  // [D] kres, or hval
+  uint32_t* hkey = kmin;                                     // [T] hash path: key words
+  int16_t* miss_i = reinterpret_cast<int16_t*>(val + D);     // [E] entry of admitted miss j
   __shared__ int s_cnt[HISPARSE_MAX_STEPS];
   __shared__ int s_klast;
   __shared__ int s_last_slot;
@@ -63,17 +74,20 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
     raw[e] = i < E ? row[i] : -1;
   }
   const uint32_t ref_word = tid < a.Hw ? refq[tid] : 0u;  // Hw <= NT
-  // The LDS hash, bitmaps and counters are set up before the row checks,
+  // The LDS tables, bitmaps and counters are set up before the row checks,
   // whose barrier then publishes them (a rejected row just returns).
-  for (int i = tid; i < T; i += NT) {
-    hkey[i] = 0u;
-    hval[i] = 0xFFFFFFFFu;
+  for (int i = tid; i < D; i += NT) {
+    kmin[i] = sw ? 0xFFFFFFFFu : 0u;
+    val[i] = sw ? 0u : 0xFFFFFFFFu;
   }
   if (tid < a.Hw) {
     pinned[tid] = 0u;
     refl[tid] = ref_word;
   }
-  for (int i = tid; i < sw; i += NT) mbits[i] = 0u;
+  for (int i = tid; i < sw; i += NT) {
+    mbits[i] = 0u;
+    rbits[i] = 0u;
+  }
   if (tid < HISPARSE_MAX_STEPS) s_cnt[tid] = 0;
   const uint32_t code = multistep_row_check<NT>(a, b, r, sl);
   if (code) {
@@ -85,8 +99,9 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
     }
     return;
   }
-  // circular sweep positions of this thread and their slot->key words: the
-  // join's probe side, and the victims' old keys for the plan
+  // circular sweep positions of this thread and their slot->key words (in
+  // slot order from the hand, so coalesced): the join's probe side, and the
+  // victims' old keys for the plan
   int sl_of[EPH];
   int oldk[EPH];
 #pragma unroll
@@ -98,11 +113,11 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
     oldk[e] = k < a.H ? sk[s] : kEmpty;
   }
 
-  // 1. flatten [S][K] step-major; insert with the step bit.  Entries among
-  // the newest ext tokens resolve to their ring row (the extra-page lookup)
-  // and stay out of the working set.
+  // 1. flatten [S][K] step-major.  Entries among the newest ext tokens
+  // resolve to their ring row (the extra-page lookup) and stay out of the
+  // working set.
   int32_t tok[EPT];
-  int hpos[EPT];
+  int idx[EPT];  // the entry's key entry (rank or bucket)
   int ring[EPT];
   bool bad_index = false;
 #pragma unroll
@@ -113,65 +128,107 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
     const bool extra = valid && t >= sl - a.ext;
     ring[e] = extra ? a.ext_base + t % a.ext : -1;
     tok[e] = valid && !extra ? t : -1;
+    idx[e] = 0;
   }
+
+  // 2. dedup with first positions and step bits, and the join: each resident
+  // key the working set names is a hit, pinned and referenced.
+  if (sw) {
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    hpos[e] = 0;
-    if (tok[e] >= 0) {
+    for (int e = 0; e < EPT; ++e)
+      if (tok[e] >= 0) bit_set_atomic(rbits, tok[e]);
+    __syncthreads();
+    bitmap_word_prefix<NT>(rbits, rwpre, sw, scan);
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      if (tok[e] < 0) continue;
       const int i = tid * EPT + e;
-      hpos[e] = hash_insert(hkey, T, tok[e]);
-      atomicMin(&hval[hpos[e]], kNoHit | static_cast<uint32_t>(i));
-      atomicOr(&hkey[hpos[e]], 1u << (kKeyBits + i / a.K));
-      if (sw) bit_set_atomic(mbits, tok[e]);
+      idx[e] = bitmap_rank(rbits, rwpre, tok[e]);
+      atomicMin(&kmin[idx[e]], static_cast<uint32_t>(i));
+      atomicOr(&val[idx[e]], 1u << (16 + i / a.K));
+    }
+#pragma unroll
+    for (int e = 0; e < EPH; ++e) {
+      const int32_t k = oldk[e];
+      if (k < 0 || !bit_test(rbits, k)) continue;
+      atomicOr(&val[bitmap_rank(rbits, rwpre, k)], static_cast<uint32_t>(sl_of[e] + 1));
+      bit_set_atomic(pinned, sl_of[e]);
+      bit_set_atomic(refl, sl_of[e]);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      if (tok[e] < 0) continue;
+      const int i = tid * EPT + e;
+      idx[e] = hash_insert(hkey, T, tok[e]);
+      atomicMin(&val[idx[e]], kNoHit | static_cast<uint32_t>(i));
+      atomicOr(&hkey[idx[e]], 1u << (kKeyBits + i / a.K));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < EPH; ++e) {
+      if (oldk[e] < 0) continue;
+      const int h = hash_find(hkey, T, oldk[e]);
+      if (h < 0) continue;
+      mark_hit(val, h, sl_of[e]);
+      bit_set_atomic(pinned, sl_of[e]);
+      bit_set_atomic(refl, sl_of[e]);
     }
   }
   __syncthreads();
 
-  // 2. the join: each resident key the working set names is a hit; its slot
-  // goes into the high half of the key's value word and is pinned and
-  // referenced.  Representatives (first occurrences) are read from the low
-  // half, which the join does not change.
+  // 3. representatives (first occurrences) take their key's result: a hit's
+  // slot becomes its row; a miss's admission priority under overflow comes
+  // from the steps that name it (latest step, number of steps, or none).
   bool rep[EPT];
-#pragma unroll
-  for (int e = 0; e < EPT; ++e)
-    rep[e] = tok[e] >= 0 && first_pos(hval[hpos[e]]) == tid * EPT + e;
-  // (with the key bitmap, a resident key the working set does not name costs
-  // one LDS read instead of a walk to the end of its probe cluster)
-#pragma unroll
-  for (int e = 0; e < EPH; ++e) {
-    if (oldk[e] < 0 || (sw && !bit_test(mbits, oldk[e]))) continue;
-    const int h = hash_find(hkey, T, oldk[e]);
-    if (h < 0) continue;
-    mark_hit(hval, h, sl_of[e]);
-    bit_set_atomic(pinned, sl_of[e]);
-    bit_set_atomic(refl, sl_of[e]);
-    if (sw) bit_clear_atomic(mbits, oldk[e]);
-  }
-  __syncthreads();
   int slot[EPT];
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) slot[e] = rep[e] ? hit_slot(hval[hpos[e]]) : -1;
   int packed = 0;  // misses | hits << 16
   int last[EPT];
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
+    const uint32_t pos = static_cast<uint32_t>(tid * EPT + e);
     last[e] = 0;
-    if (!rep[e]) continue;
+    slot[e] = -1;
+    rep[e] = false;
+    if (tok[e] < 0) continue;
+    const uint32_t v = val[idx[e]];
+    uint32_t steps;
+    if (sw) {
+      rep[e] = kmin[idx[e]] == pos;
+      slot[e] = static_cast<int>(v & 0xFFFFu) - 1;
+      steps = v >> 16;
+    } else {
+      rep[e] = first_pos(v) == static_cast<int>(pos);
+      slot[e] = hit_slot(v);
+      steps = hkey[idx[e]] >> kKeyBits;
+    }
+    if (!rep[e]) {
+      slot[e] = -1;
+      continue;
+    }
     if (slot[e] >= 0) {
-      hval[hpos[e]] = static_cast<uint32_t>(slot[e]);
       packed += 1 << 16;
     } else {
-      // admission priority under overflow: latest step, number of steps, or none
-      const uint32_t steps = hkey[hpos[e]] >> kKeyBits;
       last[e] = a.admission == HISPARSE_ADMIT_RECENT     ? 31 - __clz(steps)
                 : a.admission == HISPARSE_ADMIT_FREQUENT ? __popc(steps) - 1
                                                          : 0;
       atomicAdd(&s_cnt[last[e]], 1);
+      if (sw) bit_set_atomic(mbits, tok[e]);
       packed += 1;
     }
   }
   int tot;
   const int pre = block_exclusive_scan<NT>(packed, scan, &tot);
+  // the scan's barriers end every read of the dedup words: representatives
+  // now store their hit's row, and (direct path) the key in place of the
+  // first position
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    if (!rep[e]) continue;
+    if (slot[e] >= 0) val[idx[e]] = static_cast<uint32_t>(slot[e]);
+    if (sw) kmin[idx[e]] = static_cast<uint32_t>(tok[e]);
+  }
   const int m = tot & 0xffff;
   const int nhits = tot >> 16;
   const int room = a.H - nhits;
@@ -241,10 +298,10 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
   for (int e = 0; e < EPT; ++e) {
     if (jm[e] < 0) continue;
     if (adm[e]) {
-      miss_h[ja[e]] = static_cast<int16_t>(hpos[e]);
+      miss_i[ja[e]] = static_cast<int16_t>(idx[e]);
     } else {  // scratch row H + jo, outside the cache
       const int jo = jm[e] - ja[e];
-      hval[hpos[e]] = static_cast<uint32_t>(a.H + jo);
+      val[idx[e]] = static_cast<uint32_t>(a.H + jo);
       msrc[ma + jo] = r * a.nkeys + tok[e];
       mdst[ma + jo] = r * a.rows + a.H + jo;
       mvic[ma + jo] = -1;
@@ -319,12 +376,13 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
     if (vrank[e] < 0) continue;
     const int j = vrank[e];
     const int s = sl_of[e];
-    const int h = miss_h[j];
-    const int32_t key = static_cast<int32_t>(hkey[h] & kKeyMask) - 1;
+    const int h = miss_i[j];
+    const int32_t key = sw ? static_cast<int32_t>(kmin[h])
+                           : static_cast<int32_t>(hkey[h] & kKeyMask) - 1;
     const int32_t old = oldk[e];  // slot_key[s], fetched at kernel start
     sk[s] = key;
     bit_set_atomic(refl, s);
-    hval[h] = static_cast<uint32_t>(s);
+    val[h] = static_cast<uint32_t>(s);
     msrc[j] = r * a.nkeys + key;
     mdst[j] = r * a.rows + s;
     mvic[j] = old;
@@ -351,7 +409,7 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
   for (int e = 0; e < EPT; ++e) {
     const int i = tid * EPT + e;
     if (i >= E) continue;
-    out[i] = tok[e] >= 0 ? r * a.rows + static_cast<int>(hval[hpos[e]])
+    out[i] = tok[e] >= 0 ? r * a.rows + static_cast<int>(val[idx[e]])
                          : (ring[e] >= 0 ? r * a.rows + ring[e] : -1);
   }
   if (tid == 0) {
@@ -367,8 +425,12 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
 }  // namespace
 
 size_t clock_lds_bytes(const PlanArgs& a) {
-  return (2 * static_cast<size_t>(a.hash_size) + 2 * a.Hw + kPlanThreads / kWave + 1 +
-          2 * static_cast<size_t>(a.sort_words)) * 4 + static_cast<size_t>(a.S) * a.K * 2;
+  // pinned, refl, scan, four key bitmaps / prefixes, two words per entry
+  // (rank or bucket) and the admitted misses' entries (int16)
+  const size_t sw = static_cast<size_t>(a.sort_words);
+  const size_t E = static_cast<size_t>(a.S) * a.K;
+  const size_t d = sw ? E : static_cast<size_t>(a.hash_size);
+  return (2 * static_cast<size_t>(a.Hw) + kPlanThreads / kWave + 1 + 4 * sw + 2 * d) * 4 + E * 2;
 }
 
 hipError_t launch_clock_plan(const PlanArgs& a, hipStream_t s) {
