@@ -521,3 +521,36 @@ def test_batch_at_the_limit():
             p.compare_state(r, 0)
     finally:
         p.close()
+
+
+KEY_RANGE_SHAPES = [
+    # (policy, N, H, K, S): the plan kernels index a row's keys by their rank
+    # in an LDS bitmap of the request's keys when it fits (N <= 2^18 and the
+    # LDS budget), and by an LDS hash otherwise
+    ("lru", 200000, 4096, 2048, 1),     # a large bitmap (6250 words)
+    ("lru", 300000, 4096, 2048, 1),     # beyond a bitmap: the hash path
+    ("lru", 262144, 5000, 3000, 1),     # 2^18 keys with K = 3000: LDS too small for bitmaps
+    ("clock", 300000, 3000, 1024, 4),   # hash path with overflow into scratch rows
+    ("clock", 200000, 8192, 2048, 3),   # a large bitmap, 32 slots per thread
+]
+
+
+@pytest.mark.parametrize("policy,N,H,K,S", KEY_RANGE_SHAPES)
+def test_key_range_paths(policy, N, H, K, S):
+    log(f"key range policy={policy} N={N} H={H} K={K} S={S}")
+    rng = np.random.default_rng([N, K, S])
+    R, B = 2, 2
+    p = Pair(R=R, L=1, H=H, K=K, N=N, I=16, S=S, policy=policy, seed=N % 1000)
+    prev = None
+    try:
+        for call in range(6):
+            base = make_rows(rng, B, K, N, prev=prev, reuse=0.5)
+            prev = base
+            if S == 1:
+                topk = base
+            else:
+                topk = np.stack([base] + [make_rows(rng, B, K, N, prev=base, reuse=0.3)
+                                          for _ in range(1, S)], axis=1)
+            p.call(0, [0, 1], [N, N], topk)
+    finally:
+        p.close()
