@@ -18,7 +18,6 @@ JSON line.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import pathlib
@@ -76,17 +75,34 @@ def parse():
     return ap.parse_args()
 
 
-def state_bytes_per_row(w, m, distinct):
-    """Algorithmic HBM bytes of the plan kernel for one row with `distinct`
-    keys of which m miss: top-k read and output write (4 + 4 B per entry),
-    key->slot probe (2 B per key), hit policy update (4 B), LRU order read +
-    write (2 + 2 B per slot; CLOCK: reference bits read + write, H/4 B),
-    control word (8 B), and per miss slot->key read + write, key->slot delete
-    + insert, policy word and the three plan words (4+4+2+2+4+12 B) plus the
-    two copy-list words (8 B)."""
+def state_bytes_defined(w, m, distinct):
+    """Algorithmic state bytes of one row of one call by the byte model the
+    scope table fixes for the hit path and state: 16 B per resolved entry
+    (4 B index read, 8 B one-bucket probe, 4 B output write), 4 B per
+    distinct key (timestamp or reference write), 4 B per hot slot (the
+    policy scan of victim selection) and 36 B per miss (8 B hash insert, 8 B
+    hash delete, 4 + 4 B slot->key read and write, 12 B of plan)."""
     entries = w.num_steps * w.top_k
-    policy = 4 * w.hot if w.policy == "lru" else w.hot // 4
-    return 8 * entries + 2 * distinct + 4 * (distinct - m) + policy + 8 + 36 * m
+    return 16 * entries + 4 * distinct + 4 * w.hot + 36 * m
+
+
+def state_bytes_kernel(w, m, distinct):
+    """The same row by what the plan kernels here must move (no key->slot
+    table: the lookup joins the row with the slot->key array): top-k read and
+    output write (4 + 4 B per entry), the slot->key array read (4 B per
+    slot), the policy state -- LRU: order read + write (2 + 2 B per slot) and
+    a timestamp per distinct key (4 B); CLOCK: reference bits read + write
+    (H/8 + H/8 B) -- page mode also the page table (4 B per hot page), and
+    per miss the slot->key write (4 B), three plan words (12 B) and, in token
+    mode, the two words of the host-row-ordered copy list (8 B), plus 16 B of
+    request, length and control words."""
+    entries = w.num_steps * w.top_k
+    H = w.hot
+    if w.policy == "clock":
+        return 8 * entries + 4 * H + H // 4 + 24 * m + 16
+    if w.page_size > 1:
+        return 8 * entries + 4 * H + 4 * H + 4 * H + 4 * distinct + 16 * m + 16
+    return 8 * entries + 4 * H + 4 * H + 4 * distinct + 24 * m + 16
 
 
 def distinct_keys(w, trace):
@@ -188,28 +204,7 @@ def cpu_baseline(w, overrides, budget_s):
                        f"host: {model}")}
 
 
-COPY_SOURCES = ("copy.hip", "copy.h", "device_common.h")
-
-
-def copy_kernel_hash():
-    """Hash of the sources the copy kernel is built from (the kernel, its
-    arguments and launch shape, and the device helpers it uses)."""
-    m = hashlib.sha256()
-    for name in COPY_SOURCES:
-        m.update((ROOT / "sparse_attention_kv_request_amd" / "csrc" / name).read_bytes())
-    return m.hexdigest()[:16]
-
-
-def traffic_from_profiles(workload):
-    """HBM bytes per copy launch from the committed counter summary, if it was
-    taken on the current copy kernel source and this workload."""
-    p = ROOT / "profiles" / "miss_copy_counters.json"
-    if not p.exists():
-        return None
-    d = json.loads(p.read_text())
-    if d.get("copy_kernel_sha256_16") != copy_kernel_hash():
-        return None
-    return d.get("traffic_bytes_per_launch", {}).get(str(workload))
+from sparse_attention_kv_request_amd.counters import traffic_from_profiles  # noqa: E402
 
 
 WORKLOAD_TEXT = {
@@ -287,12 +282,16 @@ class Runner:
                     st.swap_in_selected(l, self.req, self.seq, self.topk_seq[s, l, k],
                                         self.outs[l], self.miss[s, l, k])
 
-    def timed(self, W, K):
+    def timed(self, W, K, profile=True):
+        """W warm-up steps, then K timed steps.  With `profile`, the library
+        also records HIP events around each plan and copy launch (per-launch
+        durations, at the cost of the event records between launches); the
+        step time of such a run is not the headline's."""
         torch = self.torch
         for s in range(W):
             self.step(s)
         torch.cuda.synchronize()
-        self.st.profile(True)
+        self.st.profile(profile)
         self.st.profile_read()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -422,7 +421,8 @@ def batched_state_bench(args, torch, binding, workloads):
     if int(mc.sum().item()) != 0 or st.error_flags():
         raise SystemExit("the batched-state steady state must be hit-only and error-free")
     distinct = np.array([np.unique(r[r >= 0]).size for r in rows])
-    per_launch = sum(state_bytes_per_row(w, 0, int(d)) for d in distinct)
+    per_launch = sum(state_bytes_defined(w, 0, int(d)) for d in distinct)
+    per_launch_kernel = sum(state_bytes_kernel(w, 0, int(d)) for d in distinct)
     plan_s = prof["plan_ms"] * 1e-3 / prof["calls"]
     st.close()
     host[0].free()
@@ -437,7 +437,10 @@ def batched_state_bench(args, torch, binding, workloads):
             "roofline": {"bound": "hbm", "kernel": "lru_token_plan", "achieved": round(gbps, 2),
                          "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                         "avg_launch_us": round(plan_s * 1e6, 2), "bytes_per_launch": per_launch}}
+                         "avg_launch_us": round(plan_s * 1e6, 2), "bytes_per_launch": per_launch,
+                         "kernel_model_bytes_per_launch": per_launch_kernel,
+                         "kernel_model_GBps": round(per_launch_kernel / plan_s / 1e9, 2),
+                         "traffic": traffic_from_profiles("lru_token_plan", "batched 512", W, K)}}
 
 
 def attention_bench(args, torch, binding, workloads):
@@ -506,7 +509,9 @@ def attention_bench(args, torch, binding, workloads):
                      "achieved_GBps": round(gbps, 1), "peak_GBps": HBM_PEAK_GBPS,
                      "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4),
                      "us_per_call": round(per_call * 1e6, 2),
-                     "flops_per_call": flops, "bytes_per_call": byts},
+                     "flops_per_call": flops, "bytes_per_call": byts,
+                     "traffic": traffic_from_profiles("mla_decode", f"{args.workload} attention "
+                                                      f"{item} heads {H}", W, K)},
     }
 
 
@@ -557,7 +562,8 @@ def topk_bench(args, torch, binding, workloads):
         "roofline": {"bound": "hbm", "achieved": round(byts / per_call / 1e9, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(byts / per_call / 1e9 / HBM_PEAK_GBPS, 4),
-                     "us_per_call": round(per_call * 1e6, 2), "bytes_per_call": byts},
+                     "us_per_call": round(per_call * 1e6, 2), "bytes_per_call": byts,
+                     "traffic": traffic_from_profiles("topk", f"{args.workload} topk", W, K)},
     }
     if not args.no_cpu_baseline:
         from oracle import topk_oracle
@@ -616,7 +622,15 @@ def main():
     link = {} if args.no_link_probe else link_probes(torch, run.st, w, run.st.rows)
     if link:
         log(f"link probes {link}")
-    elapsed, prof, m = run.timed(W, K)
+    # per-launch plan and copy durations (HIP events around each launch) ...
+    elapsed_prof, prof, m = run.timed(W, K)
+    # ... and the step time of the same steps without those events
+    u_run = Runner(torch, binding, workloads, w, admission=args.admission,
+                   extra_rows=args.extra_rows, share=run)
+    elapsed, _, m_u = u_run.timed(W, K, profile=False)
+    u_run.close()
+    if not (m_u == m).all():
+        raise SystemExit("the unprofiled run missed different entries than the profiled one")
 
     unit = w.item_bytes * w.page_size
     miss_bytes = int(m.sum()) * unit
@@ -625,9 +639,9 @@ def main():
     copy_gbps = miss_bytes / (prof["copy_ms"] * 1e-3) / 1e9
     measured_link = max(link.values(), default=None)
     dist = distinct_keys(w, run.trace[:, W:W + K])           # [L, K, B]
-    state_bytes = sum(state_bytes_per_row(w, int(x), int(d))
-                      for x, d in zip(m[:, :, 0, :].transpose(1, 0, 2).reshape(-1),
-                                      dist.reshape(-1)))
+    pairs = list(zip(m[:, :, 0, :].transpose(1, 0, 2).reshape(-1), dist.reshape(-1)))
+    state_bytes = sum(state_bytes_defined(w, int(x), int(d)) for x, d in pairs)
+    state_bytes_k = sum(state_bytes_kernel(w, int(x), int(d)) for x, d in pairs)
     plan_kernel = {"lru": "lru_page_plan" if w.page_size > 1 else "lru_token_plan",
                    "clock": "clock_plan"}[w.policy]
     cfg = {"workload": WORKLOAD_TEXT[args.workload].format(S=w.num_steps, H=w.hot),
@@ -652,13 +666,15 @@ def main():
         "dtype": "int32",
         "data": "synthetic",
         "config": cfg,
+        "ms_per_step_profiled": round(elapsed_prof * 1e3 / K, 4),
+        "copy_share_of_step": round(prof["copy_ms"] * 1e-3 / elapsed, 4),
         "miss_copy": {"GBps_per_step": round(miss_bytes / elapsed / 1e9, 2),
                       "bytes_per_step": miss_bytes // K,
                       "misses_per_step": int(m.sum()) // K},
         "roofline": {"bound": "pcie", "kernel": "miss_copy",
                      "achieved": round(copy_gbps, 2), "peak": PCIE5_X16_GBPS, "unit": "GB/s",
                      "frac": round(copy_gbps / PCIE5_X16_GBPS, 4),
-                     "traffic": traffic_from_profiles(args.workload),
+                     "traffic": traffic_from_profiles("miss_copy", args.workload, W, K),
                      "avg_launch_us": round(prof["copy_ms"] * 1e3 / max(calls, 1), 2),
                      "bytes_per_launch": miss_bytes // max(calls, 1),
                      "measured_link_GBps": measured_link,
@@ -669,14 +685,18 @@ def main():
                            "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                            "frac": round(state_bytes / (prof["plan_ms"] * 1e-3) / 1e9
                                          / HBM_PEAK_GBPS, 5),
+                           "traffic": traffic_from_profiles(plan_kernel, args.workload, W, K),
                            "avg_launch_us": round(prof["plan_ms"] * 1e3 / max(calls, 1), 2),
-                           "bytes_per_launch": state_bytes // max(calls, 1)},
+                           "bytes_per_launch": state_bytes // max(calls, 1),
+                           "kernel_model_bytes_per_launch": state_bytes_k // max(calls, 1),
+                           "kernel_model_GBps": round(state_bytes_k / (prof["plan_ms"] * 1e-3)
+                                                      / 1e9, 2)},
         "link": link,
     }
     if args.workload == 3:
         # the per-step path the multi-step call replaces: S single-step LRU calls
         seq_run = Runner(torch, binding, workloads, w, policy="lru", share=run)
-        seq_elapsed, _, _ = seq_run.timed(W, K)
+        seq_elapsed, _, _ = seq_run.timed(W, K, profile=False)
         seq_run.close()
         res["sequential_lru"] = {
             "ms_per_call_multistep": round(elapsed * 1e3 / (K * w.layers), 4),
@@ -690,7 +710,7 @@ def main():
                 continue
             other = Runner(torch, binding, workloads, w, admission=adm,
                            extra_rows=args.extra_rows, share=run)
-            o_el, _, o_m = other.timed(W, K)
+            o_el, _, o_m = other.timed(W, K, profile=False)
             other.close()
             cmp[adm] = {"misses_per_step": int(o_m.sum()) // K,
                         "ms_per_step": round(o_el * 1e3 / K, 4)}
