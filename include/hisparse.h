@@ -165,7 +165,29 @@ typedef struct hisparse_miss_plan {
   int32_t* miss_dst;
   int32_t* victim;
   int32_t capacity;
+  int32_t flags; /* 0 or HISPARSE_PLAN_DEFER_COPY; other bits: HISPARSE_E_INVAL */
 } hisparse_miss_plan_t;
+
+/*
+ * hisparse_miss_plan_t.flags: the swap call resolves the rows and commits the
+ * cache state (outputs, miss_count and the plan are written) but does not
+ * copy; the caller enqueues hisparse_copy_planned(layer, batch, miss_count,
+ * plan) itself, on any stream ordered after the swap call.  This splits the
+ * swap-in into the plan and the IO prefetch/replay of that plan (PR #32162
+ * report, "Risks and impact": the miss_src / miss_dst / miss_count protocol
+ * of the prefetch path), so that one layer's plan kernel can run while the
+ * previous layer's rows are still crossing the host link.  The caller owns
+ * the synchronisation the overlap needs (PR #20343 summary, review comments:
+ * a missing stream wait under overlapped scheduling crashed with an illegal
+ * address):
+ *   - nothing may read the layer's hot rows named by the plan (attention, a
+ *     copy of the buffer) before that copy has run;
+ *   - miss_count and the plan arrays must stay unchanged until it has run;
+ *   - copies of one layer must run in the order of their swap calls (a later
+ *     call may take as victim a slot an earlier call filled); later swap
+ *     calls themselves need no wait, they read and write only cache state.
+ */
+#define HISPARSE_PLAN_DEFER_COPY 1
 
 /* Accumulated kernel timings (see hisparse_profile_enable). */
 typedef struct hisparse_profile {

@@ -52,7 +52,11 @@ class HisparseConfig(ctypes.Structure):
 
 
 class HisparseMissPlan(ctypes.Structure):
-    _fields_ = [("miss_src", c_vp), ("miss_dst", c_vp), ("victim", c_vp), ("capacity", c_i32)]
+    _fields_ = [("miss_src", c_vp), ("miss_dst", c_vp), ("victim", c_vp), ("capacity", c_i32),
+                ("flags", c_i32)]
+
+
+HISPARSE_PLAN_DEFER_COPY = 1
 
 
 class HisparseTopkCall(ctypes.Structure):
@@ -363,29 +367,36 @@ class HiSparseState:
             pass
 
     @staticmethod
-    def _plan(plan):
+    def _plan(plan, defer_copy=False):
         if plan is None:
+            if defer_copy:
+                raise ValueError("defer_copy needs a plan to replay")
             return None
         src, dst, vic = plan
-        return ctypes.byref(HisparseMissPlan(_ptr(src), _ptr(dst), _ptr(vic), src.shape[-1]))
+        flags = HISPARSE_PLAN_DEFER_COPY if defer_copy else 0
+        return ctypes.byref(HisparseMissPlan(_ptr(src), _ptr(dst), _ptr(vic), src.shape[-1],
+                                             flags))
 
     def swap_in_selected(self, layer_id, req_pool_indices, seq_lens, topk_indices, out_locs,
-                         miss_count, page_table=None, num_pages=None, plan=None, stream=None):
+                         miss_count, page_table=None, num_pages=None, plan=None, stream=None,
+                         defer_copy=False):
+        """``defer_copy``: write the plan without copying; the caller runs
+        :meth:`copy_planned` on it (HISPARSE_PLAN_DEFER_COPY)."""
         batch = int(req_pool_indices.shape[0])
         rc = hisparse_swap_in_selected(
             self.handle, layer_id, batch, _ptr(req_pool_indices), _ptr(seq_lens),
             _ptr(topk_indices), _ptr(out_locs), _ptr(miss_count), _ptr(page_table),
-            _ptr(num_pages), self._plan(plan), _stream(stream))
+            _ptr(num_pages), self._plan(plan, defer_copy), _stream(stream))
         return _check(rc, "hisparse_swap_in_selected")
 
     def swap_in_spec_multistep(self, layer_id, req_pool_indices, seq_lens, topk_indices,
-                               out_locs, miss_count, plan=None, stream=None):
+                               out_locs, miss_count, plan=None, stream=None, defer_copy=False):
         batch = int(req_pool_indices.shape[0])
         num_steps = int(topk_indices.shape[1])
         rc = hisparse_swap_in_spec_multistep(
             self.handle, layer_id, batch, num_steps, _ptr(req_pool_indices), _ptr(seq_lens),
-            _ptr(topk_indices), _ptr(out_locs), _ptr(miss_count), self._plan(plan),
-            _stream(stream))
+            _ptr(topk_indices), _ptr(out_locs), _ptr(miss_count),
+            self._plan(plan, defer_copy), _stream(stream))
         return _check(rc, "hisparse_swap_in_spec_multistep")
 
     def copy_planned(self, layer_id, miss_count, plan, stream=None):

@@ -174,7 +174,17 @@ CopyArgs copy_args(const hisparse_state* st, int layer, int batch, const int32_t
   return c;
 }
 
-int run_swap(hisparse_state* st, const PlanArgs& a, bool multistep, hipStream_t s) {
+bool plan_ok(const hisparse_miss_plan_t* plan, int32_t cap) {
+  return plan == nullptr ||
+         (plan->miss_src && plan->miss_dst && plan->victim && plan->capacity >= cap &&
+          (plan->flags & ~HISPARSE_PLAN_DEFER_COPY) == 0);
+}
+
+bool defers_copy(const hisparse_miss_plan_t* plan) {
+  return plan != nullptr && (plan->flags & HISPARSE_PLAN_DEFER_COPY) != 0;
+}
+
+int run_swap(hisparse_state* st, const PlanArgs& a, bool multistep, bool defer, hipStream_t s) {
   auto* ps = static_cast<ProfiledState*>(st);
   if (st->profiling && st->events.pending.size() >= 3 * 4096) (void)drain_events(st, &ps->sums);
   // every return path keeps this call's events only as one whole triple
@@ -189,6 +199,10 @@ int run_swap(hisparse_state* st, const PlanArgs& a, bool multistep, hipStream_t 
     e = launch_lru_token_plan(a, s);
   if (e != hipSuccess) return status_of(e);
   record(st, s);
+  if (defer) {  // the caller replays the plan (the copy's interval reads zero)
+    record(st, s);
+    return HISPARSE_OK;
+  }
   const CopyArgs c = a.sort_words
                          ? copy_args(st, a.layer, a.batch, a.miss_count, a.copy_src, a.copy_dst,
                                      a.ccap)
@@ -337,8 +351,7 @@ int hisparse_swap_in_selected(hisparse_state_t st, int32_t layer_id, int32_t bat
     return HISPARSE_E_INVAL;
   const bool page = st->cfg.page_size > 1;
   if (page && (page_table == nullptr || num_pages == nullptr)) return HISPARSE_E_INVAL;
-  if (plan && (!plan->miss_src || !plan->miss_dst || !plan->victim || plan->capacity < st->cap))
-    return HISPARSE_E_INVAL;
+  if (!plan_ok(plan, st->cap)) return HISPARSE_E_INVAL;
   DeviceGuard g(st->device);
   PlanArgs a = plan_args(st, layer_id, batch, 1, req_pool_indices, seq_lens, topk_indices,
                          out_locs, miss_count, page ? page_table : nullptr,
@@ -354,7 +367,7 @@ int hisparse_swap_in_selected(hisparse_state_t st, int32_t layer_id, int32_t bat
   }
   if ((page ? lru_page_lds_bytes(a) : lru_token_lds_bytes(a)) > st->max_lds)
     return HISPARSE_E_UNSUPPORTED;
-  return run_swap(st, a, false, static_cast<hipStream_t>(stream));
+  return run_swap(st, a, false, defers_copy(plan), static_cast<hipStream_t>(stream));
 }
 
 int hisparse_swap_in_spec_multistep(hisparse_state_t st, int32_t layer_id, int32_t batch,
@@ -369,8 +382,7 @@ int hisparse_swap_in_spec_multistep(hisparse_state_t st, int32_t layer_id, int32
   if (batch == 0) return HISPARSE_OK;
   if (!req_pool_indices || !seq_lens || !topk_indices || !out_locs || !miss_count)
     return HISPARSE_E_INVAL;
-  if (plan && (!plan->miss_src || !plan->miss_dst || !plan->victim || plan->capacity < st->cap))
-    return HISPARSE_E_INVAL;
+  if (!plan_ok(plan, st->cap)) return HISPARSE_E_INVAL;
   DeviceGuard g(st->device);
   PlanArgs a = plan_args(st, layer_id, batch, num_steps, req_pool_indices, seq_lens,
                          topk_indices, out_locs, miss_count, nullptr, nullptr, plan);
@@ -378,7 +390,7 @@ int hisparse_swap_in_spec_multistep(hisparse_state_t st, int32_t layer_id, int32
   a.hash_size = std::max(64, ((3 * E / 2 + 64) + 63) / 64 * 64);
   enable_copy_sort(st, &a, clock_lds_bytes);
   if (clock_lds_bytes(a) > st->max_lds) return HISPARSE_E_UNSUPPORTED;
-  return run_swap(st, a, true, static_cast<hipStream_t>(stream));
+  return run_swap(st, a, true, defers_copy(plan), static_cast<hipStream_t>(stream));
 }
 
 int hisparse_copy_planned(hisparse_state_t st, int32_t layer_id, int32_t batch,

@@ -21,7 +21,10 @@ def short(name: str) -> str:
     return name.split("(")[0][:60]
 
 
-def summarize(db_path: str, skip: int, limit: int = 0):
+def summarize(db_path: str, skip: int, limit: int = 0, skip_for=None):
+    """Per kernel: (name, launches, mean us, timed launches, timed mean us,
+    total us); the timed launches are those after the first `skip` (or
+    skip_for[name]) of that kernel, at most `limit` of them."""
     db = sqlite3.connect(db_path)
     rows = db.execute("select name, duration from kernels order by start").fetchall()
     by = collections.OrderedDict()
@@ -29,7 +32,8 @@ def summarize(db_path: str, skip: int, limit: int = 0):
         by.setdefault(short(name), []).append(dur / 1e3)  # ns -> us
     out = []
     for k, v in by.items():
-        timed = v[skip:] if len(v) > skip else v
+        sk = next((n for pre, n in (skip_for or {}).items() if k.startswith(pre)), skip)
+        timed = v[sk:] if len(v) > sk else v
         if limit:
             timed = timed[:limit]
         out.append((k, len(v), sum(v) / len(v), len(timed), sum(timed) / len(timed), sum(v)))
@@ -43,15 +47,21 @@ def main():
     ap.add_argument("--skip", type=int, default=0)
     ap.add_argument("--limit", type=int, default=0,
                     help="use at most this many launches per kernel after the skipped ones")
+    ap.add_argument("--skip-for", action="append", default=[], metavar="KERNEL=N",
+                    help="another skip count for kernels whose short name starts with KERNEL")
     ap.add_argument("--command", default="")
     ap.add_argument("--title", default="rocprofv3 kernel trace")
     a = ap.parse_args()
     print(f"# {a.title}\n")
     if a.command:
         print(f"Command: `{a.command}`\n")
-    print(f"| kernel | launches | avg us (all) | launches timed | avg us (timed, first {a.skip} skipped) | total us |")
+    skip_for = dict((s.split("=")[0], int(s.split("=")[1])) for s in a.skip_for)
+    if skip_for:
+        print("Skipped launches per kernel: " + ", ".join(f"`{k}` {n}" for k, n in skip_for.items())
+              + f", others {a.skip}; at most {a.limit or 'all'} timed launches each.\n")
+    print(f"| kernel | launches | avg us (all) | launches timed | avg us (timed) | total us |")
     print("|---|---|---|---|---|---|")
-    for k, n, avg, nt, avg_t, tot in summarize(a.db, a.skip, a.limit):
+    for k, n, avg, nt, avg_t, tot in summarize(a.db, a.skip, a.limit, skip_for):
         print(f"| `{k}` | {n} | {avg:.2f} | {nt} | {avg_t:.2f} | {tot:.1f} |")
 
 

@@ -372,6 +372,15 @@ def test_host_side_argument_errors():
                                             topk.data_ptr(), out.data_ptr(), mc.data_ptr(),
                                             0, 0, ctypes.byref(small),
                                             0) == bd.HISPARSE_E_INVAL               # capacity
+        cap = p.gpu.capacity
+        plan_t = [torch.zeros((1, cap), **i32) for _ in range(3)]
+        bad_flags = bd.HisparseMissPlan(*(x.data_ptr() for x in plan_t), cap, 2)
+        assert bd.hisparse_swap_in_selected(h, 0, 1, req.data_ptr(), seq.data_ptr(),
+                                            topk.data_ptr(), out.data_ptr(), mc.data_ptr(),
+                                            0, 0, ctypes.byref(bad_flags),
+                                            0) == bd.HISPARSE_E_INVAL               # flags
+        with pytest.raises(ValueError):
+            p.gpu.swap_in_selected(0, req, seq, topk, out, mc, defer_copy=True)
         # a pageable host buffer is not a valid host tier
         cfg = bd.HisparseConfig(max_requests=2, num_layers=1, hot_buffer_size=64, top_k=16,
                                 max_steps=1, page_size=1, item_size_bytes=16, max_seq_len=100,
@@ -423,6 +432,93 @@ def test_copy_planned_replays_the_plan():
         assert p.gpu.error_flags() == 16
     finally:
         p.close()
+
+
+def _deferred_rows(rng, mode, B, S, K, N, P, prev):
+    if mode == "page":   # three windows of 17 pages: at most 51 distinct pages per row
+        rows = np.empty((B, K), np.int64)
+        for b in range(B):
+            centres = rng.integers(0, N, 3)
+            rows[b] = np.clip(centres[rng.integers(0, 3, K)] + rng.integers(-8 * P, 8 * P, K),
+                              0, N - 1)
+        rows[:, ::13] = -1
+        return rows.astype(np.int32)
+    rows = np.stack([make_rows(rng, B, K, N, prev=prev, reuse=0.5) for _ in range(S)], 1)
+    return rows if S > 1 else rows[:, 0]
+
+
+@pytest.mark.parametrize("mode", ["lru", "page", "clock"])
+def test_deferred_copy_pipelined_matches_eager(mode):
+    """Swap calls with HISPARSE_PLAN_DEFER_COPY on one stream and their plans
+    replayed by hisparse_copy_planned on another, the host never waiting in
+    between: layer l's copy overlaps layer l+1's plan and later steps' plans.
+    Outputs, miss counts and plans equal those of eager swap calls on a twin
+    state (itself checked against the oracle after every call), and once the
+    copies have landed the hot KV bytes are equal too."""
+    rng = np.random.default_rng([31, len(mode)])
+    R, L, K, I, B = 4, 3, 300, 32, 3
+    S = 3 if mode == "clock" else 1
+    P = 16 if mode == "page" else 1
+    N, H = (4000, 500) if P == 1 else (16 * 400, 60)
+    policy = "clock" if mode == "clock" else "lru"
+    kw = dict(R=R, L=L, H=H, K=K, N=N, I=I, S=S, P=P, policy=policy, seed=31)
+    eager, piped = Pair(**kw), Pair(**kw, shadow=False)
+    dev = torch.device("cuda", 0)
+    i32 = dict(dtype=torch.int32, device=dev)
+    try:
+        req_np = np.array([0, 1, 3], np.int32)
+        req, seq = torch.from_numpy(req_np).to(dev), torch.full((B,), N, **i32)
+        cap = piped.gpu.capacity
+        calls, prev = [], None
+        for step in range(4):                       # inputs and outputs, all allocated up front
+            for l in range(L):
+                rows = _deferred_rows(rng, mode, B, S, K, N, P, prev)
+                prev = rows[:, 0] if S > 1 else (rows if P == 1 else None)
+                c = dict(l=l, rows=rows, topk=torch.from_numpy(rows).to(dev),
+                         out=torch.full(rows.shape, -7, **i32), mc=torch.full((B,), -7, **i32),
+                         plan=tuple(torch.full((B, cap), -7, **i32) for _ in range(3)))
+                if P > 1:
+                    c["pt"], c["np"] = torch.full((B, H), -7, **i32), torch.full((B,), -7, **i32)
+                calls.append(c)
+        torch.cuda.synchronize()
+        plan_s, copy_s = torch.cuda.Stream(), torch.cuda.Stream()
+        for c in calls:
+            if S > 1:
+                piped.gpu.swap_in_spec_multistep(c["l"], req, seq, c["topk"], c["out"], c["mc"],
+                                                 plan=c["plan"], stream=plan_s, defer_copy=True)
+            else:
+                piped.gpu.swap_in_selected(c["l"], req, seq, c["topk"], c["out"], c["mc"],
+                                           page_table=c.get("pt"), num_pages=c.get("np"),
+                                           plan=c["plan"], stream=plan_s, defer_copy=True)
+            ev = torch.cuda.Event()
+            ev.record(plan_s)
+            copy_s.wait_event(ev)
+            piped.gpu.copy_planned(c["l"], c["mc"], c["plan"], stream=copy_s)
+        torch.cuda.synchronize()
+        assert piped.gpu.error_flags() == 0
+        misses = 0
+        for c in calls:
+            want_out, want_mc, want = eager.call(c["l"], req_np, [N] * B, c["rows"])
+            assert np.array_equal(c["out"].cpu().numpy(), want_out)
+            assert np.array_equal(c["mc"].cpu().numpy(), want_mc)
+            if P > 1:
+                assert np.array_equal(c["pt"].cpu().numpy(), want["page_table"])
+            src, dst, vic = (x.cpu().numpy() for x in c["plan"])
+            for b in range(B):
+                m = int(want_mc[b])
+                assert list(zip(src[b, :m].tolist(), dst[b, :m].tolist(), vic[b, :m].tolist())) \
+                    == [tuple(x) for x in want["plan"][b]]
+            misses += int(want_mc.sum())
+        for l in range(L):
+            assert torch.equal(piped.gpu.dev_kv[l], eager.gpu.dev_kv[l]), f"layer {l} KV differs"
+        for r in req_np:
+            for l in range(L):
+                a, b = piped.gpu.export(int(r), l), eager.gpu.export(int(r), l)
+                assert np.array_equal(a["slot_key"], b["slot_key"])
+        log(f"deferred copy {mode}: {len(calls)} calls, {misses} misses, equal to eager")
+    finally:
+        piped.close()
+        eager.close()
 
 
 @pytest.mark.parametrize("policy", ["lru", "clock"])
