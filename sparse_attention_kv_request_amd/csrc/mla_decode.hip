@@ -439,8 +439,15 @@ void mla_decode(MlaArgs a) {
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(raw[j + 1], a.scale_log2, -mr));
       const uint32_t pw = pack_bf16(p0, p1);
       pbits[j >> 3][(j & 7) >> 1] = pw;
-      psum += p0;  // the normaliser sums the fp32 weights, before their rounding
-      psum += p1;
+      // The normaliser sums the fp32 weights (before their bf16 rounding),
+      // each written as its rounded value plus the remainder: p - bf16(p) is
+      // exact in fp32 and so is the sum, i.e. the same value as p, but the
+      // scheduler then keeps the packed word instead of both fp32 weights
+      // live over the loop (the fp8 kernel spills registers otherwise).
+      const float b0 = __builtin_bit_cast(float, pw << 16);
+      const float b1 = __builtin_bit_cast(float, pw & 0xFFFF0000u);
+      psum += b0 + (p0 - b0);
+      psum += b1 + (p1 - b1);
     }
     psum += xor32(psum);
     l_run = fresh ? psum : l_run + psum;
