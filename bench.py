@@ -124,7 +124,8 @@ def distinct_keys(w, trace):
 def link_probes(torch, st, w, rows):
     """Host->HBM link: (i) hipMemcpyAsync of 1 GiB from pinned memory, (ii) the
     miss-copy kernel replaying a plan of consecutive host rows, (iii) the same
-    kernel over a random row order (the gather pattern of real misses)."""
+    kernel over a random row order (the gather pattern of real misses); and,
+    for the HBM roofline's context, a 1 GiB device-to-device copy."""
     dev = torch.device("cuda", 0)
     res = {}
     src = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
@@ -139,6 +140,18 @@ def link_probes(torch, st, w, rows):
         torch.cuda.synchronize()
         best = max(best, (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9)
     res["memcpy_h2d_GBps"] = round(best, 2)
+    del src
+    # HBM for reference: a 1 GiB device-to-device copy (bytes read + written)
+    src = torch.empty_like(dst).fill_(2)
+    best = 0.0
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, 2 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    res["hbm_d2d_copy_GBps"] = round(best, 1)
     del src, dst
     B, N, H = w.batch, w.seq_len // w.page_size, w.hot
     unit = w.item_bytes * w.page_size
@@ -689,7 +702,7 @@ def main():
     entries = K * w.entries_per_step
     calls = prof["calls"]
     copy_gbps = miss_bytes / (prof["copy_ms"] * 1e-3) / 1e9
-    measured_link = max(link.values(), default=None)
+    measured_link = max((v for k, v in link.items() if k != "hbm_d2d_copy_GBps"), default=None)
     dist = distinct_keys(w, run.trace[:, W:W + K])           # [L, K, B]
     pairs = list(zip(m[:, :, 0, :].transpose(1, 0, 2).reshape(-1), dist.reshape(-1)))
     state_bytes = sum(state_bytes_defined(w, int(x), int(d)) for x, d in pairs)
