@@ -47,6 +47,8 @@ def parse():
                     help="oracle seconds per worker of the CPU baseline (one worker alone, "
                          "then one per core)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--repeats", type=int, default=3,
+                    help="unprofiled timed runs on fresh states; the headline is their median")
     ap.add_argument("--no-link-probe", action="store_true")
     ap.add_argument("--attention", action="store_true",
                     help="time the sparse MLA decode attention over the swapped-in rows "
@@ -301,9 +303,16 @@ class Runner:
         durations, at the cost of the event records between launches); the
         step time of such a run is not the headline's."""
         torch = self.torch
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        c0.record()
         for s in range(W):
             self.step(s)
+            if s == 0:
+                c1.record()
         torch.cuda.synchronize()
+        # step 0 on the fresh state: every entry a miss (the cold step)
+        self.cold_s = c0.elapsed_time(c1) * 1e-3 if W > 0 else None
         self.st.profile(profile)
         self.st.profile_read()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -689,13 +698,19 @@ def main():
         log(f"link probes {link}")
     # per-launch plan and copy durations (HIP events around each launch) ...
     elapsed_prof, prof, m = run.timed(W, K)
-    # ... and the step time of the same steps without those events
-    u_run = Runner(torch, binding, workloads, w, admission=args.admission,
-                   extra_rows=args.extra_rows, share=run)
-    elapsed, _, m_u = u_run.timed(W, K, profile=False)
-    u_run.close()
-    if not (m_u == m).all():
-        raise SystemExit("the unprofiled run missed different entries than the profiled one")
+    # ... and the step time of the same steps without those events, repeated
+    # on fresh states (the median is the headline)
+    runs, colds = [], []
+    for _ in range(max(1, args.repeats)):
+        u_run = Runner(torch, binding, workloads, w, admission=args.admission,
+                       extra_rows=args.extra_rows, share=run)
+        el, _, m_u = u_run.timed(W, K, profile=False)
+        colds.append(u_run.cold_s)
+        u_run.close()
+        if not (m_u == m).all():
+            raise SystemExit("an unprofiled run missed different entries than the profiled one")
+        runs.append(el)
+    elapsed = sorted(runs)[len(runs) // 2]
 
     unit = w.item_bytes * w.page_size
     miss_bytes = int(m.sum()) * unit
@@ -731,6 +746,10 @@ def main():
         "dtype": "int32",
         "data": "synthetic",
         "config": cfg,
+        "repeats": {"ms_per_step": [round(x * 1e3 / K, 4) for x in runs],
+                    "statistic": "median", "state": "fresh per repeat, same trace"},
+        "cold_step_ms": (round(sorted(colds)[len(colds) // 2] * 1e3, 4)
+                         if colds and colds[0] is not None else None),
         "ms_per_step_profiled": round(elapsed_prof * 1e3 / K, 4),
         "step_over_copy_time": round(elapsed / (prof["copy_ms"] * 1e-3), 4),
         "miss_copy": {"GBps_per_step": round(miss_bytes / elapsed / 1e9, 2),
