@@ -564,7 +564,7 @@ def attention_bench(args, torch, binding, workloads):
     valid = int(sum(int((x >= 0).sum()) for x in locs)) // w.layers
     flops = 2.0 * (576 + 512) * H * valid
     byts = valid * item + B * H * (576 * 2 + 512 * 4 + 4) + B * w.top_k * 4
-    splits = (need // (B * H * (512 * 2 + 2 * 4))) if need else 1  # fp16 partials + fp32 max, sum
+    splits = (need // (B * H * (512 * 2 + 8 * 4))) if need else 1  # fp16 partials + m, l, exponents
     run.close()
     tflops = flops / per_call / 1e12
     gbps = byts / per_call / 1e9

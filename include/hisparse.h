@@ -335,9 +335,10 @@ int hisparse_copy_planned(hisparse_state_t st, int32_t layer_id, int32_t batch,
  * by one fp32 product and rounded to bf16); the softmax weights are rounded
  * to bf16 for the weighted sum, while their normaliser and lse sum the fp32
  * weights.  When the locations are split over several workgroups, each
- * split's normalised output is kept in fp16 (relative 2^-11) until the splits
- * are merged by their log-sum-exp, so |latent| values must stay below 65504
- * (fp16's largest finite value); a split output beyond it is not detected.
+ * split's normalised output is kept in fp16 (relative 2^-11) until the
+ * splits are merged by their log-sum-exp; a 32-dim block whose largest
+ * |value| exceeds fp16's range is kept scaled by a power of two, so fp16
+ * sets no range limit.  The softmax itself stays exact while |latent| < 2^53.
  * Enqueued on `stream`; allocates nothing.  Errors: HISPARSE_E_INVAL,
  * HISPARSE_E_UNSUPPORTED, HISPARSE_E_HIP.
  */

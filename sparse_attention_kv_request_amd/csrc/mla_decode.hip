@@ -106,7 +106,9 @@ struct MlaArgs {
   float* out;                 // [B][Hq][512]
   float* lse;                 // [B][Hq] or null
   _Float16* part_out;         // [B][splits][Hq][512] normalised split outputs (fp16)
-  float* part_ml;             // [B][splits][Hq][2]: running max (log2 units), sum
+  float* part_ml;             // [B][splits][Hq][8]: running max (log2 units), sum, 0,
+                              // 0, then 16 int8 exponents e: 32-dim block db of the
+                              // fp16 output is stored scaled by 2^-e[db]
   uint32_t* err;
 };
 
@@ -629,39 +631,63 @@ void mla_decode(MlaArgs a) {
         *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * jj) =
             f32x4{acc[db][4 * jj], acc[db][4 * jj + 1], acc[db][4 * jj + 2], acc[db][4 * jj + 3]} * inv;
   } else {
-    // a split's output is a convex combination of its values, so fp16
-    // (relative 2^-11) holds it; the split's max and sum stay fp32
+    // A split's output goes out in fp16 (relative 2^-11).  A 32-dim block
+    // whose largest |value| exceeds fp16's range is stored scaled by a power
+    // of two 2^-e that puts that value in [2^14, 2^15) (e = 0 otherwise), so
+    // no latent range overflows it.  The split's max and sum stay fp32 and
+    // the block exponents (int8) go beside them; the merge multiplies by 2^e
+    // again.  Lanes l and l ^ 32 hold the two halves of each block of one
+    // head and exchange their maxima, so both take the same e.
     const size_t ps = (static_cast<size_t>(b) * a.splits + split) * a.heads + head;
-    if (h2 == 0) {
-      a.part_ml[2 * ps] = m_ref;
-      a.part_ml[2 * ps + 1] = l_run;
-    }
+    if (h2 == 0) *reinterpret_cast<f32x4*>(a.part_ml + 8 * ps) = f32x4{m_ref, l_run, 0.f, 0.f};
+    uint32_t ebits[4] = {0u, 0u, 0u, 0u};  // e of block db in byte db % 4 of word db / 4
     // Lanes l and l ^ 32 hold alternating 4-dim groups of one head: one swap
     // of the group each lacks (the fp16 bits of 4 dims, two dwords) gives
     // lane l dims 32 db + 16 p + 8 (l/32) .. +7, one 16-byte store.
     _Float16* dst8 = a.part_out + ps * kLatent + 8 * h2;
 #pragma unroll
     for (int db = 0; db < kDimBlocks; ++db) {
+      // the block's maximum comes from the products the conversion uses (a
+      // second read of the accumulators makes the compiler spill registers
+      // of the tile loop)
+      f32x4 g[4];
+      float bm = 0.f;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        g[q4] = f32x4{acc[db][4 * q4], acc[db][4 * q4 + 1], acc[db][4 * q4 + 2],
+                      acc[db][4 * q4 + 3]} * inv;
+        bm = fmaxf(bm, fmaxf(fmaxf(fabsf(g[q4][0]), fabsf(g[q4][1])),
+                             fmaxf(fabsf(g[q4][2]), fabsf(g[q4][3]))));
+      }
+      bm = fmaxf(bm, xor32(bm));
+      if (bm > 65504.f) {
+        // frexp: bm = f * 2^x with f in [0.5, 1), so bm * 2^(15 - x) lies in
+        // [2^14, 2^15); scaling by a power of two is exact
+        const int e = __builtin_amdgcn_frexp_expf(bm) - 15;
+        const float r = __builtin_amdgcn_ldexpf(1.f, -e);
+        ebits[db >> 2] |= (static_cast<uint32_t>(e) & 0xFFu) << (8 * (db & 3));
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) g[q4] *= r;
+      }
 #pragma unroll
       for (int pr = 0; pr < 2; ++pr) {
-        const f32x4 g0 = f32x4{acc[db][8 * pr], acc[db][8 * pr + 1], acc[db][8 * pr + 2],
-                               acc[db][8 * pr + 3]} * inv;
-        const f32x4 g1 = f32x4{acc[db][8 * pr + 4], acc[db][8 * pr + 5], acc[db][8 * pr + 6],
-                               acc[db][8 * pr + 7]} * inv;
-        const u32x2 b0 = __builtin_bit_cast(u32x2, __builtin_convertvector(g0, f16x4));
-        const u32x2 b1 = __builtin_bit_cast(u32x2, __builtin_convertvector(g1, f16x4));
+        const u32x2 b0 = __builtin_bit_cast(u32x2, __builtin_convertvector(g[2 * pr], f16x4));
+        const u32x2 b1 = __builtin_bit_cast(u32x2, __builtin_convertvector(g[2 * pr + 1], f16x4));
         const u32x2 send = h2 == 0 ? b1 : b0;
         u32x2 recv;
 #pragma unroll
         for (int w = 0; w < 2; ++w) {
-          const auto r = __builtin_amdgcn_permlane32_swap(send[w], send[w], false, false);
-          recv[w] = h2 ? r[0] : r[1];
+          const auto rr = __builtin_amdgcn_permlane32_swap(send[w], send[w], false, false);
+          recv[w] = h2 ? rr[0] : rr[1];
         }
         const u32x4 out = h2 == 0 ? u32x4{b0[0], b0[1], recv[0], recv[1]}
                                   : u32x4{recv[0], recv[1], b1[0], b1[1]};
         *reinterpret_cast<u32x4*>(dst8 + 32 * db + 16 * pr) = out;
       }
     }
+    if (h2 == 0)
+      *reinterpret_cast<u32x4*>(a.part_ml + 8 * ps + 4) =
+          u32x4{ebits[0], ebits[1], ebits[2], ebits[3]};
   }
 }
 
@@ -678,22 +704,26 @@ __global__ __launch_bounds__(kCombineHeads * kWave) void mla_combine(MlaArgs a) 
   float big = -INFINITY;
   for (int s = 0; s < a.splits; ++s) {
     const size_t ps = ps0 + static_cast<size_t>(s) * a.heads;
-    const f32x2 ml = *reinterpret_cast<const f32x2*>(a.part_ml + 2 * ps);
+    const f32x4 ml = *reinterpret_cast<const f32x4*>(a.part_ml + 8 * ps);
     if (ml[1] > 0.f) big = fmaxf(big, ml[0] + log2f(ml[1]));
   }
   float wsum = 0.f;
   f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < a.splits; ++s) {
     const size_t ps = ps0 + static_cast<size_t>(s) * a.heads;
-    const f32x2 ml = *reinterpret_cast<const f32x2*>(a.part_ml + 2 * ps);
+    const f32x4 ml = *reinterpret_cast<const f32x4*>(a.part_ml + 8 * ps);  // m, l
     if (!(ml[1] > 0.f)) continue;
     const float w = exp2f(ml[0] + log2f(ml[1]) - big);
     wsum += w;
+    // this lane's 8 dims lie in 32-dim block lane / 4, stored scaled by 2^-e
+    const int e = static_cast<int8_t>(
+        reinterpret_cast<const uint8_t*>(a.part_ml + 8 * ps + 4)[lane >> 2]);
+    const float wo = __builtin_amdgcn_ldexpf(w, e);
     const u32x4 raw = *reinterpret_cast<const u32x4*>(a.part_out + ps * kLatent + 8 * lane);
     const f16x4 lo = __builtin_bit_cast(f16x4, u32x2{raw[0], raw[1]});
     const f16x4 hi = __builtin_bit_cast(f16x4, u32x2{raw[2], raw[3]});
-    o0 += w * __builtin_convertvector(lo, f32x4);
-    o1 += w * __builtin_convertvector(hi, f32x4);
+    o0 += wo * __builtin_convertvector(lo, f32x4);
+    o1 += wo * __builtin_convertvector(hi, f32x4);
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   float* dst = a.out + static_cast<size_t>(bh) * kLatent + 8 * lane;
@@ -722,7 +752,7 @@ size_t mla_workspace_bytes(int batch, int heads, int n_locs, int num_cus) {
   const int splits = mla_splits(batch, heads, n_locs, num_cus);
   if (splits == 1) return 0;
   return static_cast<size_t>(batch) * splits * heads *
-         (kLatent * sizeof(_Float16) + 2 * sizeof(float));
+         (kLatent * sizeof(_Float16) + 8 * sizeof(float));
 }
 
 hipError_t launch_mla_decode(const MlaDecodeCall& c, hipStream_t s) {

@@ -157,6 +157,17 @@ def test_mla_replay_in_two_tile_splits(item):
              boost=[(0, 40, 5000.0), (0, 97, 3000.0), (0, 255, 4000.0)])
 
 
+@pytest.mark.parametrize("item", [1152, 656])
+def test_mla_split_outputs_beyond_fp16_range(item):
+    """Split outputs far above fp16's largest finite value (65504): rows
+    whose latent is multiplied by 5e4 to 2e5 dominate the heads of their
+    batch rows, so those heads' outputs (and split partials) reach 1e5 and
+    more.  The per-(split, head) power-of-two scaling of the fp16 partials
+    keeps them finite and within the bound."""
+    run_case(R=64, B=64, H=400, K=300, N=1200, item=item, heads=128, seed=item + 17, calls=1,
+             boost=[(0, 50, 1e5), (3, 100, 2e5), (7, 250, 5e4)])
+
+
 def _random_case(case):
     """Case `case` of a seeded sweep over batch, heads, location count, hot
     size and boosted rows (which force replays at varied tiles), alternating
