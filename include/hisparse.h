@@ -295,7 +295,9 @@ int hisparse_swap_in_spec_multistep(hisparse_state_t st, int32_t layer_id, int32
  * of a swap call on its own, so a plan recorded by a swap call can be
  * replayed later or on another stream (PR #32162 report, item 2 and "Risks
  * and impact": the plan stays compatible with the prefetch replay path).
- * The victim array is not read.  Entries outside the layer's host rows
+ * The victim array and plan->flags are not read; this is the call that
+ * completes a swap call made with HISPARSE_PLAN_DEFER_COPY.  Entries outside
+ * the layer's host rows
  * ([0, R*N) tokens or [0, R*N/P) pages) or device rows are skipped and raise
  * HISPARSE_ERR_BAD_PLAN.  miss_count: device int32 [batch].  Enqueued on
  * `stream`; errors: HISPARSE_E_INVAL, HISPARSE_E_UNSUPPORTED (batch above
@@ -526,7 +528,9 @@ int hisparse_host_free(void* p_h);
 
 /*
  * Kernel timing with HIP events recorded on the call's stream around the two
- * kernels of every swap call while enabled.  hisparse_profile_read is
+ * kernels of every swap call while enabled (a call with
+ * HISPARSE_PLAN_DEFER_COPY adds a zero copy interval; its replay by
+ * hisparse_copy_planned is not timed).  hisparse_profile_read is
  * synchronous: it waits for the recorded events, returns the sums since the
  * last read and resets them.
  */
