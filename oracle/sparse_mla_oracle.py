@@ -24,7 +24,7 @@ KV row layouts (the item bytes a swap call copies):
   128-dim tile of the latent), 64 bfloat16 rope values.
 
 These layouts and the 576/512/64 split are readings (the pages name neither).
-The kernel computes with bf16 keys and values (reading R23): fp8 rows are
+The kernel computes with bf16 keys and values: fp8 rows are
 dequantised by one float32 product per value and rounded to bf16;
 ``decode_rows_bf16`` gives those values, and the GPU parity tests attend over
 them so that their tolerance covers only the kernel's accumulation and
@@ -81,7 +81,7 @@ def f32_to_bf16_rne(x: np.ndarray) -> np.ndarray:
 
 
 def decode_rows_bf16(rows: np.ndarray):
-    """The values attention computes with (reading R23): bf16 rows as stored;
+    """The values attention computes with: bf16 rows as stored;
     fp8 rows dequantised as one float32 product (code value x the tile's
     float32 scale, rounded to nearest even) and then rounded to bfloat16.
     Returns (latent [n, 512], rope [n, 64]) float64."""
@@ -130,9 +130,10 @@ def sparse_mla_decode(q_bits: np.ndarray, locs: np.ndarray, kv_rows: np.ndarray,
                       bf16_kv: bool = False):
     """q_bits: bfloat16 bits uint16 [B, H, 576]; locs: int [B, n] rows of
     kv_rows (uint8 [rows, item]), -1 skipped.  Returns (out [B, H, 512],
-    lse [B, H]) in float64.  bf16_kv: attend over the values as reading R23
-    has the kernel read them (decode_rows_bf16) instead of the exact values
-    the bytes encode (identical for bf16 rows)."""
+    lse [B, H]) in float64.  bf16_kv: attend over the rows' bf16 values
+    (decode_rows_bf16: fp8 latents dequantised in float32, then rounded to
+    bf16) instead of the exact values the bytes encode (identical for bf16
+    rows)."""
     B, H, _ = q_bits.shape
     out = np.zeros((B, H, LATENT))
     lse = np.full((B, H), -np.inf)

@@ -1,7 +1,7 @@
 """Reference and error bounds for the sparse MLA decode attention parity tests.
 
 The reference is the float64 oracle (``oracle/sparse_mla_oracle.py``) over the
-values reading R23 has the kernel compute with: bf16 queries and bf16 keys /
+values the kernel computes with: bf16 queries and bf16 keys /
 values (fp8 rows dequantised by one float32 product and rounded to bf16).
 What is left between a correct kernel and that reference is the kernel's own
 arithmetic, bounded here per (row, head) and per output element from first

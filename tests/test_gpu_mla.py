@@ -1,7 +1,7 @@
 """Sparse MLA decode attention (HIP, through the C ABI) against the float64
 oracle, on rows that a swap call placed in the hot buffer.
 
-The reference attends over the values reading R23 has the kernel compute
+The reference attends over the values the kernel computes
 with (bf16 keys and values; fp8 rows dequantised in float32 and rounded to
 bf16), and every output element and lse is held to the bound of
 ``tests/mla_check.py``: the kernel's float32 accumulation, bf16 softmax

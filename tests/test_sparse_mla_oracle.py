@@ -124,7 +124,7 @@ def test_f32_to_bf16_rne_matches_torch():
 
 
 def test_bf16_reading_of_fp8_rows_matches_torch():
-    """Reading R23 of an fp8 row: code value x float32 scale as one float32
+    """The bf16 value of an fp8 row's latent: code value x float32 scale as one float32
     product, then bfloat16 -- against torch's float8_e4m3fn decoding and
     conversions, over every code and scales of many magnitudes."""
     rng = np.random.default_rng(4)
