@@ -47,7 +47,7 @@ def parse():
                     help="oracle seconds per worker of the CPU baseline (one worker alone, "
                          "then one per core)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--repeats", type=int, default=3,
+    ap.add_argument("--repeats", type=int, default=5,
                     help="unprofiled timed runs on fresh states; the headline is their median")
     ap.add_argument("--no-link-probe", action="store_true")
     ap.add_argument("--attention", action="store_true",
