@@ -17,13 +17,23 @@ namespace hisparse {
 #ifndef HISPARSE_COPY_BLOCKS
 #define HISPARSE_COPY_BLOCKS 1024
 #endif
+#ifndef HISPARSE_COPY_ROW_BLOCKS
+#define HISPARSE_COPY_ROW_BLOCKS 256
+#endif
 #ifndef HISPARSE_COPY_NT_LOAD
 #define HISPARSE_COPY_NT_LOAD 0
 #endif
 
 constexpr int kCopyThreads = HISPARSE_COPY_THREADS;
 constexpr int kCopyUnroll = HISPARSE_COPY_UNROLL;  // 16-byte loads in flight per lane
-constexpr int kCopyBlocks = HISPARSE_COPY_BLOCKS;  // 4 workgroups per CU on 256 CUs
+// Workgroups: 4 per CU on 256 CUs for whole pages (units of 4 KiB and more),
+// one per CU for token rows.  Measured on the 64-request swap step (656-B
+// rows, alternated three times on one box): 256 workgroups copy a launch in
+// 333.6 us against 335.3 us with 1024 (128 took 351 us, 64 varied from 332
+// to 335 us); with 168-KB pages 1024 stay 0.2 % ahead.
+constexpr int kCopyBlocks = HISPARSE_COPY_BLOCKS;
+constexpr int kCopyRowBlocks = HISPARSE_COPY_ROW_BLOCKS;
+constexpr int64_t kCopyPageUnit = 4096;
 
 // Rows of `unit_bytes` from the host tier to the hot buffer.
 struct CopyArgs {

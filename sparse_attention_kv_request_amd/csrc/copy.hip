@@ -96,7 +96,8 @@ hipError_t launch_miss_copy(const CopyArgs& a, hipStream_t s) {
   static_assert((HISPARSE_MAX_BATCH + 1 + kCopyThreads / kWave + 1) * sizeof(int) <= 64 * 1024,
                 "the largest batch's prefix and the scan scratch fit the default LDS");
   const size_t lds = (static_cast<size_t>(a.batch) + 1) * sizeof(int);
-  hipLaunchKernelGGL((miss_copy<kCopyThreads, kCopyUnroll>), dim3(kCopyBlocks),
+  const int blocks = a.unit_bytes >= kCopyPageUnit ? kCopyBlocks : kCopyRowBlocks;
+  hipLaunchKernelGGL((miss_copy<kCopyThreads, kCopyUnroll>), dim3(blocks),
                      dim3(kCopyThreads), lds, s, a);
   return hipGetLastError();
 }
