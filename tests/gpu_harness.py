@@ -66,7 +66,13 @@ class Pair:
             h.free()
 
     # -- calls -------------------------------------------------------------------
-    def call(self, layer, req, seq, topk, check_bytes=True, check_state=True, plan_extra=0):
+    def call(self, layer, req, seq, topk, check_bytes=True, check_state=True, plan_extra=0,
+             defer=False):
+        """One swap call on the GPU and the oracle, compared on outputs, plan,
+        error word and (optionally) the device KV bytes and exported state.
+        defer: the GPU call runs with HISPARSE_PLAN_DEFER_COPY on a side
+        stream and its plan is replayed by hisparse_copy_planned on a second
+        stream behind an event (the comparison follows both)."""
         req = np.asarray(req, np.int32)
         seq = np.asarray(seq, np.int32)
         topk = np.asarray(topk, np.int32)
@@ -76,18 +82,27 @@ class Pair:
         out = torch.full(topk.shape, -7, dtype=torch.int32, device=DEV)
         mc = torch.full((B,), -7, dtype=torch.int32, device=DEV)
         plan = tuple(torch.full((B, cap), -7, dtype=torch.int32, device=DEV) for _ in range(3))
+        pt = nump = None
+        if self.P > 1 and not multi:
+            pt = torch.full((B, self.H), -7, dtype=torch.int32, device=DEV)
+            nump = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+        args = (layer, t32(req), t32(seq), t32(topk), out, mc)
+        s_plan = s_copy = None
+        if defer:
+            torch.cuda.synchronize()          # inputs made on the current stream
+            s_plan, s_copy = torch.cuda.Stream(), torch.cuda.Stream()
         if multi:
-            self.gpu.swap_in_spec_multistep(layer, t32(req), t32(seq), t32(topk), out, mc,
-                                            plan=plan)
+            self.gpu.swap_in_spec_multistep(*args, plan=plan, stream=s_plan, defer_copy=defer)
             want = self.cpu.swap_in_spec_multistep(layer, req, seq, topk)
         else:
-            pt = nump = None
-            if self.P > 1:
-                pt = torch.full((B, self.H), -7, dtype=torch.int32, device=DEV)
-                nump = torch.full((B,), -7, dtype=torch.int32, device=DEV)
-            self.gpu.swap_in_selected(layer, t32(req), t32(seq), t32(topk), out, mc,
-                                      page_table=pt, num_pages=nump, plan=plan)
+            self.gpu.swap_in_selected(*args, page_table=pt, num_pages=nump, plan=plan,
+                                      stream=s_plan, defer_copy=defer)
             want = self.cpu.swap_in_selected(layer, req, seq, topk)
+        if defer:
+            planned = torch.cuda.Event()
+            planned.record(s_plan)
+            s_copy.wait_event(planned)
+            self.gpu.copy_planned(layer, mc, plan, stream=s_copy)
         torch.cuda.synchronize()
         got_out = out.cpu().numpy()
         got_mc = mc.cpu().numpy()
