@@ -449,10 +449,12 @@ hipError_t launch_clock_plan(const PlanArgs& a, hipStream_t s) {
   if (E <= 2 * kPlanThreads) {
     if (a.H <= 4 * kPlanThreads) return go(clock_plan<kPlanThreads, 2, 4>);
     if (a.H <= 8 * kPlanThreads) return go(clock_plan<kPlanThreads, 2, 8>);
+    if (a.H <= 16 * kPlanThreads) return go(clock_plan<kPlanThreads, 2, 16>);
     return go(clock_plan<kPlanThreads, 2, 32>);
   }
   if (a.H <= 4 * kPlanThreads) return go(clock_plan<kPlanThreads, 8, 4>);
   if (a.H <= 8 * kPlanThreads) return go(clock_plan<kPlanThreads, 8, 8>);
+  if (a.H <= 16 * kPlanThreads) return go(clock_plan<kPlanThreads, 8, 16>);
   return go(clock_plan<kPlanThreads, 8, 32>);
 }
 

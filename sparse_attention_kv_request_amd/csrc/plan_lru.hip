@@ -570,6 +570,8 @@ size_t lru_page_lds_bytes(const PlanArgs& a) {
     return launch_plan(KERNEL<kPlanThreads, EPTV, 4>, a, lds, s);                     \
   if (a.H <= 8 * kPlanThreads)                                                        \
     return launch_plan(KERNEL<kPlanThreads, EPTV, 8>, a, lds, s);                     \
+  if (a.H <= 16 * kPlanThreads)                                                       \
+    return launch_plan(KERNEL<kPlanThreads, EPTV, 16>, a, lds, s);                    \
   return launch_plan(KERNEL<kPlanThreads, EPTV, 32>, a, lds, s);
 
 hipError_t launch_lru_token_plan(const PlanArgs& a, hipStream_t s) {
@@ -581,11 +583,11 @@ hipError_t launch_lru_token_plan(const PlanArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_lru_page_plan(const PlanArgs& a, hipStream_t s) {
+  // page mode holds at most 4096 hot pages: four order positions per thread
+  static_assert(kMaxPageModeHot <= 4 * kPlanThreads, "page-mode caches fit 4 slots per thread");
   const size_t lds = lru_page_lds_bytes(a);
-  if (a.K <= 2 * kPlanThreads) {
-    HS_DISPATCH_EPH(lru_page_plan, 2)
-  }
-  HS_DISPATCH_EPH(lru_page_plan, 8)
+  if (a.K <= 2 * kPlanThreads) return launch_plan(lru_page_plan<kPlanThreads, 2, 4>, a, lds, s);
+  return launch_plan(lru_page_plan<kPlanThreads, 8, 4>, a, lds, s);
 }
 
 }  // namespace hisparse

@@ -21,14 +21,15 @@ from tests.test_oracle_pages_shapes import build_782_case
 pytestmark = pytest.mark.gpu
 
 CLOCK_LARGE = [
-    # (H, K, N, I, S, calls, R, L, reuse, share): slots per thread 8 (H <= 8192)
-    # or 32 (H <= 32768); entries per thread 2 (S*K <= 2048) or 8.  `reuse` is
+    # (H, K, N, I, S, calls, R, L, reuse, share): slots per thread 8 (H <= 8192),
+    # 16 (H <= 16384) or 32 (H <= 32768); entries per thread 2 (S*K <= 2048) or 8.  `reuse` is
     # the fraction of a call's first step taken from the previous call,
     # `share` the fraction of the first step a later step repeats.
     (6000, 2048, 20000, 32, 4, 8, 3, 2, 0.3, 0.0),     # S*K = 8192 > H: overflow into scratch
     (6000, 1024, 20000, 32, 2, 10, 2, 1, 0.3, 0.5),    # S*K = 2048: two entries per thread
     (8192, 2048, 30000, 16, 4, 8, 3, 2, 0.3, 0.5),     # S*K = H: a call may fill the cache
-    (12000, 2048, 40000, 16, 3, 10, 2, 1, 0.3, 0.5),   # 32 slots per thread
+    (12000, 2048, 40000, 16, 3, 10, 2, 1, 0.3, 0.5),   # 16 slots per thread
+    (16384, 1024, 60000, 16, 2, 16, 2, 1, 0.0, 0.5),   # 16 slots, two entries per thread
     (32768, 2048, 65536, 16, 4, 14, 2, 1, 0.3, 0.5),   # the pages' upper bound
     (32768, 1024, 131072, 16, 2, 24, 1, 1, 0.0, 0.0),  # two entries, 32 slots per thread
 ]

@@ -339,6 +339,30 @@ def test_hot_buffer_upper_bound():
         p.close()
 
 
+SIXTEEN_SLOTS = [
+    # (H, K, N): token caches of 8193..16384 slots run 16 slots per thread;
+    # K <= 2048 two entries per thread, else eight
+    (12000, 2048, 60000),
+    (16384, 3000, 65536),
+]
+
+
+@pytest.mark.parametrize("H,K,N", SIXTEEN_SLOTS)
+def test_lru_sixteen_slots_per_thread(H, K, N):
+    log(f"LRU, 16 slots per thread: H={H} K={K} N={N}")
+    rng = np.random.default_rng([H, K])
+    p = Pair(R=2, L=1, H=H, K=K, N=N, I=16, seed=H)
+    try:
+        prev = None
+        for call in range(16):   # about K/2 fresh keys per call: the cache fills, then evicts
+            rows = make_rows(rng, 2, K, N, prev=prev, reuse=0.5)
+            prev = rows
+            p.call(0, [0, 1], [N, N], rows, check_state=(call % 4 == 3))
+        assert len(p.cpu.instance(0, 0).key_slot) == H, "the cache was meant to fill"
+    finally:
+        p.close()
+
+
 def test_host_side_argument_errors():
     p = Pair(R=2, L=1, H=64, K=16, N=100, I=16, seed=15)
     dev = torch.device("cuda", 0)
