@@ -102,15 +102,17 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
   // circular sweep positions of this thread and their slot->key words (in
   // slot order from the hand, so coalesced): the join's probe side, and the
   // victims' old keys for the plan
-  int sl_of[EPH];
+  // sweep position tid*EPH + e is slot (hand + position) mod H, -1 past H
+  const auto sl_of = [&](int e) {
+    const int k = tid * EPH + e;
+    const int s = hand + k;
+    return k < a.H ? (s >= a.H ? s - a.H : s) : -1;
+  };
   int oldk[EPH];
 #pragma unroll
   for (int e = 0; e < EPH; ++e) {
-    const int k = tid * EPH + e;
-    int s = hand + k;
-    if (s >= a.H) s -= a.H;
-    sl_of[e] = k < a.H ? s : -1;
-    oldk[e] = k < a.H ? sk[s] : kEmpty;
+    const int s = sl_of(e);
+    oldk[e] = s >= 0 ? sk[s] : kEmpty;
   }
 
   // 1. flatten [S][K] step-major.  Entries among the newest ext tokens
@@ -152,9 +154,9 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
     for (int e = 0; e < EPH; ++e) {
       const int32_t k = oldk[e];
       if (k < 0 || !bit_test(rbits, k)) continue;
-      atomicOr(&val[bitmap_rank(rbits, rwpre, k)], static_cast<uint32_t>(sl_of[e] + 1));
-      bit_set_atomic(pinned, sl_of[e]);
-      bit_set_atomic(refl, sl_of[e]);
+      atomicOr(&val[bitmap_rank(rbits, rwpre, k)], static_cast<uint32_t>(sl_of(e) + 1));
+      bit_set_atomic(pinned, sl_of(e));
+      bit_set_atomic(refl, sl_of(e));
     }
   } else {
 #pragma unroll
@@ -171,9 +173,9 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
       if (oldk[e] < 0) continue;
       const int h = hash_find(hkey, T, oldk[e]);
       if (h < 0) continue;
-      mark_hit(val, h, sl_of[e]);
-      bit_set_atomic(pinned, sl_of[e]);
-      bit_set_atomic(refl, sl_of[e]);
+      mark_hit(val, h, sl_of(e));
+      bit_set_atomic(pinned, sl_of(e));
+      bit_set_atomic(refl, sl_of(e));
     }
   }
   __syncthreads();
@@ -313,73 +315,83 @@ __global__ __launch_bounds__(NT) void clock_plan(PlanArgs a) {
     __syncthreads();
   }
 
-  // 3. CLOCK sweep over circular positions k (slot = (hand + k) mod H)
-  bool pin[EPH], rf[EPH];
-  int n1 = 0;
+  // 3. CLOCK sweep over circular positions k (slot = (hand + k) mod H).  The
+  // first lap takes unpinned slots whose reference bit is clear (mask c1),
+  // the second, if the first falls short, unpinned slots whose bit it
+  // cleared (c2); a candidate's victim rank is its lap's base plus its rank
+  // within the lap, and only ranks below ma are victims.
+  static_assert(EPH <= 32, "one mask bit per position");
+  constexpr uint32_t kAll = EPH == 32 ? ~0u : (1u << EPH) - 1u;
+  uint32_t pin = 0u, rf = 0u;
 #pragma unroll
   for (int e = 0; e < EPH; ++e) {
-    const int s = sl_of[e];
-    pin[e] = s >= 0 ? bit_test(pinned, s) : true;
-    rf[e] = s >= 0 ? bit_test(refl, s) : false;
-    n1 += (!pin[e] && !rf[e]);
+    const int s = sl_of(e);
+    if (s < 0 || bit_test(pinned, s)) pin |= 1u << e;
+    if (s >= 0 && bit_test(refl, s)) rf |= 1u << e;
   }
+  const uint32_t c1 = ~pin & ~rf & kAll;
+  uint32_t c2 = 0u;
+  const int n1 = __popc(c1);
   int e1_tot;
-  int r1 = block_exclusive_scan<NT>(n1, scan, &e1_tot);
-  int vrank[EPH];
-#pragma unroll
-  for (int e = 0; e < EPH; ++e) {
-    vrank[e] = -1;
-    if (!pin[e] && !rf[e]) {
-      if (r1 < ma) vrank[e] = r1;
-      ++r1;
-    }
-  }
+  const int r1 = block_exclusive_scan<NT>(n1, scan, &e1_tot);
+  int r2 = 0;  // second-lap rank of this thread's first c2 candidate, after e1_tot
   if (e1_tot >= ma) {
-    if (ma > 0) {
+    if (ma > 0 && r1 <= ma - 1 && ma - 1 < r1 + n1) {  // this thread holds victim ma - 1
+      int j = r1;
 #pragma unroll
-      for (int e = 0; e < EPH; ++e)
-        if (vrank[e] == ma - 1) {
+      for (int e = 0; e < EPH; ++e) {
+        if (!(c1 >> e & 1u)) continue;
+        if (j == ma - 1) {
           s_klast = tid * EPH + e;
-          s_last_slot = sl_of[e];
+          s_last_slot = sl_of(e);
         }
-    }
-    __syncthreads();
-    if (ma > 0) {
-      const int klast = s_klast;
-#pragma unroll
-      for (int e = 0; e < EPH; ++e)
-        if (!pin[e] && rf[e] && tid * EPH + e < klast) bit_clear_atomic(refl, sl_of[e]);
-    }
-  } else {
-    int n2 = 0;
-#pragma unroll
-    for (int e = 0; e < EPH; ++e) n2 += (!pin[e] && rf[e]);
-    int e2_tot;
-    int r2 = block_exclusive_scan<NT>(n2, scan, &e2_tot);
-#pragma unroll
-    for (int e = 0; e < EPH; ++e) {
-      if (!pin[e] && rf[e]) {
-        if (e1_tot + r2 < ma) vrank[e] = e1_tot + r2;
-        ++r2;
-        bit_clear_atomic(refl, sl_of[e]);
+        ++j;
       }
     }
+    __syncthreads();
+    if (ma > 0) {  // the first lap cleared the bits it passed before the last victim
+      const int klast = s_klast;
+      const uint32_t c = ~pin & rf;
 #pragma unroll
-    for (int e = 0; e < EPH; ++e)
-      if (vrank[e] == ma - 1) s_last_slot = sl_of[e];
+      for (int e = 0; e < EPH; ++e)
+        if ((c >> e & 1u) && tid * EPH + e < klast) bit_clear_atomic(refl, sl_of(e));
+    }
+  } else {
+    c2 = ~pin & rf;
+    int e2_tot;
+    r2 = e1_tot + block_exclusive_scan<NT>(__popc(c2), scan, &e2_tot);
+    int j = r2;
+#pragma unroll
+    for (int e = 0; e < EPH; ++e) {
+      if (!(c2 >> e & 1u)) continue;
+      bit_clear_atomic(refl, sl_of(e));
+      if (j == ma - 1) s_last_slot = sl_of(e);
+      ++j;
+    }
   }
   __syncthreads();
 
   // 4. commit admitted misses into their victims
+  int j1 = r1, j2 = r2;
 #pragma unroll
   for (int e = 0; e < EPH; ++e) {
-    if (vrank[e] < 0) continue;
-    const int j = vrank[e];
-    const int s = sl_of[e];
+    int j;
+    if (c1 >> e & 1u) {
+      j = j1++;
+    } else if (c2 >> e & 1u) {
+      j = j2++;
+    } else {
+      continue;
+    }
+    if (j >= ma) continue;
+    const int s = sl_of(e);
     const int h = miss_i[j];
     const int32_t key = sw ? static_cast<int32_t>(kmin[h])
                            : static_cast<int32_t>(hkey[h] & kKeyMask) - 1;
-    const int32_t old = oldk[e];  // slot_key[s], fetched at kernel start
+    // slot_key[s] as the call found it (only this thread writes slot s):
+    // fetched at kernel start, or here where 32 slots per thread leave no
+    // registers to keep it
+    const int32_t old = EPH < 32 ? oldk[e] : sk[s];
     sk[s] = key;
     bit_set_atomic(refl, s);
     val[h] = static_cast<uint32_t>(s);

@@ -50,28 +50,28 @@ __device__ void reject_row(const PlanArgs& a, int b, int entries, uint32_t code,
 }
 
 // Order positions tid*EPH .. tid*EPH+EPH-1 (slots o[e]) that this call did
-// not use (`used` holds the hit slots), and their ranks among all such
-// positions in order.  Returns the count of this thread's available positions.
+// not use (`used` holds the hit slots), as a mask over e.  A position's rank
+// among all available positions in order is the thread's base rank plus the
+// count of mask bits below it.
 template <int EPH>
-__device__ __forceinline__ int lru_available(const int (&o)[EPH], const uint32_t* used,
-                                             bool (&avail)[EPH]) {
-  int navail = 0;
+__device__ __forceinline__ uint32_t lru_available(const int (&o)[EPH], const uint32_t* used) {
+  static_assert(EPH <= 32, "one mask bit per position");
+  uint32_t avail = 0u;
 #pragma unroll
-  for (int e = 0; e < EPH; ++e) {
-    avail[e] = o[e] >= 0 && !bit_test(used, o[e]);
-    navail += avail[e];
-  }
-  return navail;
+  for (int e = 0; e < EPH; ++e)
+    if (o[e] >= 0 && !bit_test(used, o[e])) avail |= 1u << e;
+  return avail;
 }
 
 // Commit of the m misses into the first m available order positions and
 // rewrite of the order.  `o` holds order positions tid*EPH .. tid*EPH+EPH-1;
-// avail/rank come from lru_available and a scan over it.  `used` has the
+// `avail` comes from lru_available, `rank0` (the rank of this thread's first
+// available position) from a scan over its counts.  `used` has the
 // bits of the slots hit by this call; victims are added to it.  Miss j (key
 // miss_key[j]) goes to vslot[j].
 template <int NT, int EPH>
 __device__ void lru_commit(const PlanArgs& a, int b, int r, int now, int m,
-                           const int (&o)[EPH], const bool (&avail)[EPH], const int (&rank)[EPH],
+                           const int (&o)[EPH], uint32_t avail, int rank0,
                            uint32_t* used, const int32_t* miss_key, int32_t* vslot, int* scan,
                            int32_t* sk, int32_t* tsq, int16_t* ord,
                            const uint32_t* mbits, const int32_t* mwpre, const int (&oldk)[EPH]) {
@@ -80,13 +80,17 @@ __device__ void lru_commit(const PlanArgs& a, int b, int r, int now, int m,
   int32_t* msrc = a.miss_src + static_cast<size_t>(b) * a.cap;
   int32_t* mdst = a.miss_dst + static_cast<size_t>(b) * a.cap;
   int32_t* mvic = a.victim + static_cast<size_t>(b) * a.cap;
+  int j = rank0;  // rank of the next available position
 #pragma unroll
   for (int e = 0; e < EPH; ++e) {
-    if (avail[e] && rank[e] < m) {
-      const int j = rank[e];
+    if (!(avail >> e & 1u)) continue;
+    if (j < m) {
       const int s = o[e];
       const int32_t key = miss_key[j];
-      const int32_t old = oldk[e];  // slot_key[s], fetched at kernel start
+      // slot_key[s] as the call found it (no other thread writes slot s):
+      // fetched at kernel start, or here where 32 slots per thread leave no
+      // registers for it
+      const int32_t old = EPH < 32 ? oldk[e] : sk[s];
       sk[s] = key;
       tsq[s] = now;
       vslot[j] = s;
@@ -100,12 +104,17 @@ __device__ void lru_commit(const PlanArgs& a, int b, int r, int now, int m,
         a.copy_dst[c] = r * a.rows + s;
       }
     }
+    ++j;
   }
   __syncthreads();
   // untouched slots keep their relative order at the front
+  j = rank0;
 #pragma unroll
-  for (int e = 0; e < EPH; ++e)
-    if (avail[e] && rank[e] >= m) ord[rank[e] - m] = static_cast<int16_t>(o[e]);
+  for (int e = 0; e < EPH; ++e) {
+    if (!(avail >> e & 1u)) continue;
+    if (j >= m) ord[j - m] = static_cast<int16_t>(o[e]);
+    ++j;
+  }
   // slots used by this call (timestamp = now) go to the back in slot order.
   // Thread w owns bitmap word w (Hw <= NT); each wave that owns words takes
   // its prefix from wave scans over all the words (Hw / 64 of them), so no
@@ -225,8 +234,10 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
   // the resident key of every order position: the victims' old keys for the
   // plan (a gather in LRU order, only needed at the commit)
   int oldk[EPH];
+  if constexpr (EPH < 32) {
 #pragma unroll
-  for (int e = 0; e < EPH; ++e) oldk[e] = o[e] >= 0 ? sk[o[e]] : kEmpty;
+    for (int e = 0; e < EPH; ++e) oldk[e] = o[e] >= 0 ? sk[o[e]] : kEmpty;
+  }
 
   // 2. dedup and the join.  kmin takes each key's first position (atomicMin);
   // the owner of each resident slot whose key the row names writes the slot
@@ -296,8 +307,8 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
     }
   }
   if (sw) __syncthreads();  // the scan below counts the miss bitmap
-  bool avail[EPH];
-  const int navail = lru_available<EPH>(o, used, avail);
+  const uint32_t avail = lru_available<EPH>(o, used);
+  const int navail = __popc(avail);
   const int wpt = (sw + NT - 1) / NT;
   const int w0 = tid * wpt;
   int nbits = 0;
@@ -307,13 +318,7 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
                             static_cast<uint32_t>(nbits), scan, &x_pre, &y_pre, &x_tot, &y_tot);
   const int m = static_cast<int>(x_tot & 0xffffu);
   int j = static_cast<int>(x_pre & 0xffffu);
-  int rank[EPH];
-  int rk = static_cast<int>(x_pre >> 16);
-#pragma unroll
-  for (int e = 0; e < EPH; ++e) {
-    rank[e] = rk;
-    rk += avail[e];
-  }
+  const int rank0 = static_cast<int>(x_pre >> 16);
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
     if (rep[e] && slot[e] < 0) {
@@ -330,7 +335,7 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
   __syncthreads();
 
   // 4. victims, commit, new order
-  lru_commit<NT, EPH>(a, b, r, now, m, o, avail, rank, used, miss_key, vslot, scan, sk, tsq,
+  lru_commit<NT, EPH>(a, b, r, now, m, o, avail, rank0, used, miss_key, vslot, scan, sk, tsq,
                       ord, sw ? mbits : nullptr, mwpre, oldk);
   __syncthreads();
 
@@ -479,17 +484,10 @@ __global__ __launch_bounds__(NT) void lru_page_plan(PlanArgs a) {
   __syncthreads();
 
   // 4. victims, commit, new order (pages are already in ascending order)
-  bool avail[EPH];
-  const int navail = lru_available<EPH>(o, used, avail);
+  const uint32_t avail = lru_available<EPH>(o, used);
   int total_avail;
-  int rk = block_exclusive_scan<NT>(navail, scan, &total_avail);
-  int rank[EPH];
-#pragma unroll
-  for (int e = 0; e < EPH; ++e) {
-    rank[e] = rk;
-    rk += avail[e];
-  }
-  lru_commit<NT, EPH>(a, b, r, now, m, o, avail, rank, used, miss_key, vslot, scan, sk, tsq,
+  const int rank0 = block_exclusive_scan<NT>(__popc(avail), scan, &total_avail);
+  lru_commit<NT, EPH>(a, b, r, now, m, o, avail, rank0, used, miss_key, vslot, scan, sk, tsq,
                       ord, nullptr, nullptr, oldk);
   __syncthreads();
 
