@@ -238,7 +238,11 @@ class Runner:
     """One workload on the GPU: host tier, traces, state, per-step calls."""
 
     def __init__(self, torch, binding, workloads, w, policy=None, admission="recent",
-                 extra_rows=0, share=None):
+                 extra_rows=0, share=None, split=False):
+        """split: every swap call defers its copy (HISPARSE_PLAN_DEFER_COPY)
+        and the bench replays its plan at once on the same stream with the
+        separate miss-copy kernel, timed with HIP events: the lookup kernel
+        and the copy kernel of the same calls measured apart."""
         import numpy as np
 
         self.torch, self.w = torch, w
@@ -278,6 +282,12 @@ class Runner:
         calls_per_step = 1 if (multi or S == 1) else S
         self.miss = torch.zeros((w.steps, w.layers, calls_per_step, B), dtype=torch.int32,
                                 device=self.dev)
+        self.split = split
+        self.copy_ev = None
+        if split:
+            cap = self.st.capacity
+            self.plans = [tuple(torch.empty((B, cap), dtype=torch.int32, device=self.dev)
+                                for _ in range(3)) for _ in range(w.layers)]
         self.pt = self.npg = None
         if w.page_size > 1:
             self.pt = torch.empty((B, w.hot), dtype=torch.int32, device=self.dev)
@@ -285,6 +295,25 @@ class Runner:
 
     def step(self, s):
         st, w = self.st, self.w
+        if self.split:
+            for l in range(w.layers):
+                mc = self.miss[s, l, 0]
+                if self.policy == "clock":
+                    st.swap_in_spec_multistep(l, self.req, self.seq, self.topk[s, l], self.outs[l],
+                                              mc, plan=self.plans[l], defer_copy=True)
+                else:
+                    st.swap_in_selected(l, self.req, self.seq, self.topk[s, l, :, 0],
+                                        self.outs[l], mc, page_table=self.pt,
+                                        num_pages=self.npg, plan=self.plans[l], defer_copy=True)
+                if self.copy_ev is not None:
+                    ev = (self.torch.cuda.Event(enable_timing=True),
+                          self.torch.cuda.Event(enable_timing=True))
+                    ev[0].record()
+                st.copy_planned(l, mc, self.plans[l])
+                if self.copy_ev is not None:
+                    ev[1].record()
+                    self.copy_ev.append(ev)
+            return
         for l in range(w.layers):
             if self.policy == "clock":
                 st.swap_in_spec_multistep(l, self.req, self.seq, self.topk[s, l], self.outs[l],
@@ -315,6 +344,7 @@ class Runner:
         self.cold_s = c0.elapsed_time(c1) * 1e-3 if W > 0 else None
         self.st.profile(profile)
         self.st.profile_read()
+        self.copy_ev = [] if (profile and self.split) else None
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
@@ -325,6 +355,9 @@ class Runner:
         elapsed = e0.elapsed_time(e1) * 1e-3
         prof = self.st.profile_read()
         self.st.profile(False)
+        if self.copy_ev is not None:   # the separate copy kernel of the split calls
+            prof["copy_ms"] = sum(a.elapsed_time(b) for a, b in self.copy_ev)
+            self.copy_ev = None
         flags = self.st.error_flags()
         if flags:
             raise SystemExit(f"device error flags {flags} during the benchmark")
@@ -698,6 +731,17 @@ def main():
         log(f"link probes {link}")
     # per-launch plan and copy durations (HIP events around each launch) ...
     elapsed_prof, prof, m = run.timed(W, K)
+    fused = prof["calls"] > 0 and prof["fused_calls"] == prof["calls"]
+    sprof = prof
+    if fused:
+        # the calls copied inside the lookup kernel: the same calls again with
+        # the lookup kernel and the separate copy kernel timed apart
+        s_run = Runner(torch, binding, workloads, w, admission=args.admission,
+                       extra_rows=args.extra_rows, share=run, split=True)
+        _, sprof, s_m = s_run.timed(W, K)
+        s_run.close()
+        if not (s_m == m).all():
+            raise SystemExit("the split run missed different entries than the fused one")
     # ... and the step time of the same steps without those events, repeated
     # on fresh states (the median is the headline)
     runs, colds = [], []
@@ -716,7 +760,9 @@ def main():
     miss_bytes = int(m.sum()) * unit
     entries = K * w.entries_per_step
     calls = prof["calls"]
-    copy_gbps = miss_bytes / (prof["copy_ms"] * 1e-3) / 1e9
+    copy_s = sprof["copy_ms"] * 1e-3          # the separate copy kernel's summed time
+    copy_gbps = miss_bytes / copy_s / 1e9
+    plan_s = sprof["plan_ms"] * 1e-3          # the lookup kernel alone
     measured_link = max((v for k, v in link.items() if k != "hbm_d2d_copy_GBps"), default=None)
     dist = distinct_keys(w, run.trace[:, W:W + K])           # [L, K, B]
     pairs = list(zip(m[:, :, 0, :].transpose(1, 0, 2).reshape(-1), dist.reshape(-1)))
@@ -751,32 +797,50 @@ def main():
         "cold_step_ms": (round(sorted(colds)[len(colds) // 2] * 1e3, 4)
                          if colds and colds[0] is not None else None),
         "ms_per_step_profiled": round(elapsed_prof * 1e3 / K, 4),
-        "step_over_copy_time": round(elapsed / (prof["copy_ms"] * 1e-3), 4),
+        "step_over_copy_time": round(elapsed / copy_s, 4),
+        "copy_in_lookup_kernel": fused,
         "miss_copy": {"GBps_per_step": round(miss_bytes / elapsed / 1e9, 2),
                       "bytes_per_step": miss_bytes // K,
                       "misses_per_step": int(m.sum()) // K},
-        "roofline": {"bound": "pcie", "kernel": "miss_copy",
-                     "achieved": round(copy_gbps, 2), "peak": PCIE5_X16_GBPS, "unit": "GB/s",
-                     "frac": round(copy_gbps / PCIE5_X16_GBPS, 4),
-                     "traffic": traffic_from_profiles("miss_copy", args.workload, W, K),
-                     "avg_launch_us": round(prof["copy_ms"] * 1e3 / max(calls, 1), 2),
-                     "bytes_per_launch": miss_bytes // max(calls, 1),
-                     "measured_link_GBps": measured_link,
-                     "frac_of_measured_link": (round(copy_gbps / measured_link, 4)
-                                               if measured_link else None)},
-        "state_roofline": {"bound": "hbm", "kernel": plan_kernel,
-                           "achieved": round(state_bytes / (prof["plan_ms"] * 1e-3) / 1e9, 2),
-                           "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                           "frac": round(state_bytes / (prof["plan_ms"] * 1e-3) / 1e9
-                                         / HBM_PEAK_GBPS, 5),
-                           "traffic": traffic_from_profiles(plan_kernel, args.workload, W, K),
-                           "avg_launch_us": round(prof["plan_ms"] * 1e3 / max(calls, 1), 2),
-                           "bytes_per_launch": state_bytes // max(calls, 1),
-                           "kernel_model_bytes_per_launch": state_bytes_k // max(calls, 1),
-                           "kernel_model_GBps": round(state_bytes_k / (prof["plan_ms"] * 1e-3)
-                                                      / 1e9, 2)},
         "link": link,
     }
+    # the dominant kernel: the one that moves the misses over the host link
+    # (the lookup kernel itself when it copies, else the miss-copy kernel)
+    split = f"{args.workload} split" if fused else args.workload
+    copy_kernel = {"bound": "pcie", "kernel": "miss_copy",
+                   "achieved": round(copy_gbps, 2), "peak": PCIE5_X16_GBPS, "unit": "GB/s",
+                   "frac": round(copy_gbps / PCIE5_X16_GBPS, 4),
+                   "traffic": traffic_from_profiles("miss_copy", split, W, K),
+                   "avg_launch_us": round(copy_s * 1e6 / max(calls, 1), 2),
+                   "bytes_per_launch": miss_bytes // max(calls, 1),
+                   "measured_link_GBps": measured_link,
+                   "frac_of_measured_link": (round(copy_gbps / measured_link, 4)
+                                             if measured_link else None)}
+    if fused:
+        fused_s = prof["plan_ms"] * 1e-3
+        f_gbps = miss_bytes / fused_s / 1e9
+        res["roofline"] = {"bound": "pcie", "kernel": f"{plan_kernel} (lookup and copy)",
+                           "achieved": round(f_gbps, 2), "peak": PCIE5_X16_GBPS, "unit": "GB/s",
+                           "frac": round(f_gbps / PCIE5_X16_GBPS, 4),
+                           "traffic": traffic_from_profiles(plan_kernel, args.workload, W, K),
+                           "avg_launch_us": round(fused_s * 1e6 / max(calls, 1), 2),
+                           "bytes_per_launch": miss_bytes // max(calls, 1),
+                           "measured_link_GBps": measured_link,
+                           "frac_of_measured_link": (round(f_gbps / measured_link, 4)
+                                                     if measured_link else None)}
+        res["split_copy_kernel"] = copy_kernel
+    else:
+        res["roofline"] = copy_kernel
+    res["state_roofline"] = {
+        "bound": "hbm", "kernel": plan_kernel + (" (copy deferred)" if fused else ""),
+        "achieved": round(state_bytes / plan_s / 1e9, 2),
+        "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+        "frac": round(state_bytes / plan_s / 1e9 / HBM_PEAK_GBPS, 5),
+        "traffic": traffic_from_profiles(plan_kernel, split, W, K),
+        "avg_launch_us": round(plan_s * 1e6 / max(calls, 1), 2),
+        "bytes_per_launch": state_bytes // max(calls, 1),
+        "kernel_model_bytes_per_launch": state_bytes_k // max(calls, 1),
+        "kernel_model_GBps": round(state_bytes_k / plan_s / 1e9, 2)}
     # the copy deferred and replayed on a second stream: plans overlap copies
     if w.policy == "clock" or w.num_steps == 1:
         p_run = Runner(torch, binding, workloads, w, admission=args.admission,
@@ -787,7 +851,7 @@ def main():
             raise SystemExit("the pipelined run missed different entries than the eager one")
         res["pipelined"] = {"ms_per_step": round(p_elapsed * 1e3 / K, 4),
                             "entries_per_s": round(entries / p_elapsed, 1),
-                            "step_over_copy_time": round(p_elapsed / (prof["copy_ms"] * 1e-3), 4)}
+                            "step_over_copy_time": round(p_elapsed / copy_s, 4)}
     if args.workload == 3:
         # the per-step path the multi-step call replaces: S single-step LRU calls
         seq_run = Runner(torch, binding, workloads, w, policy="lru", share=run)

@@ -192,8 +192,10 @@ typedef struct hisparse_miss_plan {
 /* Accumulated kernel timings (see hisparse_profile_enable). */
 typedef struct hisparse_profile {
   int64_t calls;  /* swap calls timed */
-  double plan_ms; /* summed duration of the lookup/victim/commit kernel */
-  double copy_ms; /* summed duration of the miss-copy kernel */
+  double plan_ms; /* summed duration of the lookup/victim/commit kernel,
+                     with its copies when the call copies inside it */
+  double copy_ms; /* summed duration of the separate miss-copy kernel */
+  int64_t fused_calls; /* calls among them that copied inside the lookup kernel */
 } hisparse_profile_t;
 
 /*
@@ -251,6 +253,10 @@ void hisparse_state_destroy(hisparse_state_t st);
  * [0, N] is rejected (ERR_BAD_ROW); a request named by two rows rejects both
  * (ERR_DUP_REQUEST); page mode with more than H distinct pages rejects the row
  * (ERR_PAGE_OVERFLOW); rejected rows leave their cache untouched.
+ * Launches: token-mode calls of at least 16 rows copy inside the lookup
+ * kernel (each row's workgroup moves its own misses after its commit); page
+ * mode and smaller batches add a second, miss-copy kernel.  Either way the
+ * copies are complete when the call's work on `stream` is.
  * Errors: HISPARSE_E_INVAL (NULL pointer, range, policy mismatch, plan
  * capacity), HISPARSE_E_HIP.
  */
@@ -280,7 +286,7 @@ int hisparse_swap_in_selected(hisparse_state_t st, int32_t layer_id, int32_t bat
  * priority (default: seen in the latest steps) are admitted and the rest are
  * copied to scratch rows without entering the cache (the
  * pages call this admission approximate; the data of the call stays exact).
- * Row rejection rules and errors as for hisparse_swap_in_selected.
+ * Row rejection rules, launches and errors as for hisparse_swap_in_selected.
  */
 int hisparse_swap_in_spec_multistep(hisparse_state_t st, int32_t layer_id, int32_t batch,
                                     int32_t num_steps, const int32_t* req_pool_indices,
@@ -527,9 +533,10 @@ int hisparse_host_alloc(size_t bytes, void** out_h);
 int hisparse_host_free(void* p_h);
 
 /*
- * Kernel timing with HIP events recorded on the call's stream around the two
- * kernels of every swap call while enabled (a call with
- * HISPARSE_PLAN_DEFER_COPY adds a zero copy interval; its replay by
+ * Kernel timing with HIP events recorded on the call's stream around the
+ * kernels of every swap call while enabled: the lookup kernel, then the
+ * miss-copy kernel (a call that copies inside its lookup kernel, or one made
+ * with HISPARSE_PLAN_DEFER_COPY, adds a zero copy interval; a replay by
  * hisparse_copy_planned is not timed).  hisparse_profile_read is
  * synchronous: it waits for the recorded events, returns the sums since the
  * last read and resets them.

@@ -76,7 +76,7 @@ TOPK_CHUNK = 32768
 
 class HisparseProfile(ctypes.Structure):
     _fields_ = [("calls", ctypes.c_int64), ("plan_ms", ctypes.c_double),
-                ("copy_ms", ctypes.c_double)]
+                ("copy_ms", ctypes.c_double), ("fused_calls", ctypes.c_int64)]
 
 
 _SIGNATURES = {
@@ -261,7 +261,8 @@ def hisparse_profile_enable(st, enable: bool) -> None:
 def hisparse_profile_read(st) -> dict:
     p = HisparseProfile()
     _check(lib().hisparse_profile_read(st, ctypes.byref(p)), "hisparse_profile_read")
-    return {"calls": p.calls, "plan_ms": p.plan_ms, "copy_ms": p.copy_ms}
+    return {"calls": p.calls, "plan_ms": p.plan_ms, "copy_ms": p.copy_ms,
+            "fused_calls": p.fused_calls}
 
 
 # -- conveniences ----------------------------------------------------------------

@@ -20,6 +20,9 @@ namespace hisparse {
 #ifndef HISPARSE_COPY_ROW_BLOCKS
 #define HISPARSE_COPY_ROW_BLOCKS 256
 #endif
+#ifndef HISPARSE_FUSE_MIN_ROWS
+#define HISPARSE_FUSE_MIN_ROWS 16
+#endif
 #ifndef HISPARSE_COPY_NT_LOAD
 #define HISPARSE_COPY_NT_LOAD 0
 #endif
@@ -34,6 +37,15 @@ constexpr int kCopyUnroll = HISPARSE_COPY_UNROLL;  // 16-byte loads in flight pe
 constexpr int kCopyBlocks = HISPARSE_COPY_BLOCKS;
 constexpr int kCopyRowBlocks = HISPARSE_COPY_ROW_BLOCKS;
 constexpr int64_t kCopyPageUnit = 4096;
+// Token-row swap calls of at least this many rows copy inside the plan
+// kernel: each row's workgroup moves its own misses (8 loads in flight per
+// lane) once its commit is done, so the copy starts without a second launch.
+// Measured per step against the separate copy kernel: 64 rows x 8 layers
+// 2.681 vs 2.741 ms, 32 rows 1.403 vs 1.441, 16 rows 0.776 vs 0.785, 8 rows
+// even, one row 3x slower (one workgroup keeps too few host reads in
+// flight); whole pages 5 % slower (the copy kernel spreads a row's pages over
+// many workgroups), so pages always use it.
+constexpr int kFuseMinRows = HISPARSE_FUSE_MIN_ROWS;
 
 // Rows of `unit_bytes` from the host tier to the hot buffer.
 struct CopyArgs {

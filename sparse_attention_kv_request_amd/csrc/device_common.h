@@ -52,6 +52,12 @@ struct PlanArgs {
   int32_t* copy_dst;
   int32_t ccap;
   int32_t sort_words;   // words of the LDS miss bitmap; 0 = no copy list
+  // fused copy: the plan workgroup moves its own row's misses
+  const uint8_t* host;  // device-visible address of the layer's host tier
+  uint8_t* dev;
+  int64_t unit_bytes;
+  int32_t unit16;
+  int32_t fuse_copy;
 };
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP: four row
@@ -228,6 +234,51 @@ __device__ __forceinline__ int bitmap_rank(const uint32_t* bits, const int32_t* 
 
 __device__ __forceinline__ void raise_error(uint32_t* err, uint32_t bits) {
   atomicOr(err, bits);
+}
+
+#ifndef HISPARSE_FUSE_UNROLL
+#define HISPARSE_FUSE_UNROLL 8
+#endif
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// The fused copy of a swap call: the row's m misses, (host row, device row)
+// pairs at src[0..m) / dst[0..m) that this workgroup has just written, moved
+// by the whole workgroup in 16-byte chunks with HISPARSE_FUSE_UNROLL loads in
+// flight per lane and non-temporal stores.  Every thread must call it after
+// a barrier that follows the list's stores.
+template <int NT>
+__device__ void copy_own_row(const PlanArgs& a, const int32_t* src, const int32_t* dst, int m) {
+  constexpr int U = HISPARSE_FUSE_UNROLL;
+  const int64_t total = static_cast<int64_t>(m) * a.unit16;
+  const double inv = 1.0 / static_cast<double>(a.unit16);
+  for (int64_t c = threadIdx.x; c < total; c += static_cast<int64_t>(NT) * U) {
+    u32x4 v[U];
+    u32x4* d[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t cu = c + static_cast<int64_t>(u) * NT;
+      d[u] = nullptr;
+      if (cu >= total) continue;
+      // miss j and 16-byte offset within its row
+      int64_t j = static_cast<int64_t>(static_cast<double>(cu) * inv);
+      int64_t off = cu - j * a.unit16;
+      if (off < 0) {
+        --j;
+        off += a.unit16;
+      } else if (off >= a.unit16) {
+        ++j;
+        off -= a.unit16;
+      }
+      const int64_t srow = src[j];
+      const int64_t drow = dst[j];
+      v[u] = *(reinterpret_cast<const u32x4*>(a.host + srow * a.unit_bytes) + off);
+      d[u] = reinterpret_cast<u32x4*>(a.dev + drow * a.unit_bytes) + off;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (d[u] != nullptr) __builtin_nontemporal_store(v[u], d[u]);
+  }
 }
 
 }  // namespace hisparse

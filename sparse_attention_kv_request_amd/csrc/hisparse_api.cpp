@@ -99,7 +99,7 @@ PlanArgs plan_args(const hisparse_state* st, int32_t layer, int32_t batch, int32
 
 // Accumulated profile of drained event triples.
 struct ProfileSums {
-  int64_t calls = 0;
+  int64_t calls = 0, fused = 0;
   double plan_ms = 0, copy_ms = 0;
 };
 
@@ -184,12 +184,20 @@ bool defers_copy(const hisparse_miss_plan_t* plan) {
   return plan != nullptr && (plan->flags & HISPARSE_PLAN_DEFER_COPY) != 0;
 }
 
-int run_swap(hisparse_state* st, const PlanArgs& a, bool multistep, bool defer, hipStream_t s) {
+int run_swap(hisparse_state* st, PlanArgs a, bool multistep, bool defer, hipStream_t s) {
   auto* ps = static_cast<ProfiledState*>(st);
   if (st->profiling && st->events.pending.size() >= 3 * 4096) (void)drain_events(st, &ps->sums);
   // every return path keeps this call's events only as one whole triple
   host::TripleGuard<hipEvent_t> guard(&st->events, st->profiling);
   record(st, s);
+  if (!defer && a.batch >= kFuseMinRows && st->cfg.page_size == 1) {
+    // token rows: the plan kernel copies its rows' misses itself
+    a.fuse_copy = 1;
+    a.host = st->host_kv[a.layer];
+    a.dev = st->dev_kv[a.layer];
+    a.unit_bytes = st->cfg.item_size_bytes;
+    a.unit16 = st->cfg.item_size_bytes / 16;
+  }
   hipError_t e;
   if (multistep)
     e = launch_clock_plan(a, s);
@@ -199,8 +207,9 @@ int run_swap(hisparse_state* st, const PlanArgs& a, bool multistep, bool defer, 
     e = launch_lru_token_plan(a, s);
   if (e != hipSuccess) return status_of(e);
   record(st, s);
-  if (defer) {  // the caller replays the plan (the copy's interval reads zero)
+  if (defer || a.fuse_copy) {  // replayed by the caller, or done by the plan kernel
     record(st, s);
+    if (st->profiling && a.fuse_copy) ps->sums.fused += 1;
     return HISPARSE_OK;
   }
   const CopyArgs c = a.sort_words
@@ -656,6 +665,7 @@ int hisparse_profile_read(hisparse_state_t st, hisparse_profile_t* out_h) {
   out_h->calls = ps->sums.calls;
   out_h->plan_ms = ps->sums.plan_ms;
   out_h->copy_ms = ps->sums.copy_ms;
+  out_h->fused_calls = ps->sums.fused;
   ps->sums = ProfileSums{};
   return status_of(e);
 }

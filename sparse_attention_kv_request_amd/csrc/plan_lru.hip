@@ -357,6 +357,12 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
     a.ctrl[2 * q] = now + 1;
   }
   if (bad_index) raise_error(a.err, HISPARSE_ERR_BAD_INDEX);
+  if (a.fuse_copy) {
+    __syncthreads();  // the row's copy list, written above by this workgroup
+    const size_t lb = sw ? static_cast<size_t>(b) * a.ccap : static_cast<size_t>(b) * a.cap;
+    copy_own_row<NT>(a, (sw ? a.copy_src : a.miss_src) + lb, (sw ? a.copy_dst : a.miss_dst) + lb,
+                     m);
+  }
 }
 
 // -------------------------------------------------------------------------
