@@ -37,9 +37,13 @@ COUNTERS = ROOT / "profiles" / "traffic_counters.json"
 # helpers it uses): a counter figure applies only while these are unchanged.
 KERNEL_SOURCES = {
     "miss_copy": ("copy.hip", "copy.h", "device_common.h"),
-    "lru_token_plan": ("plan_lru.hip", "device_common.h", "internal.h", "hisparse_api.cpp"),
-    "lru_page_plan": ("plan_lru.hip", "device_common.h", "internal.h", "hisparse_api.cpp"),
-    "clock_plan": ("plan_clock.hip", "device_common.h", "internal.h", "hisparse_api.cpp"),
+    # (copy.h: the rule that lets a swap call copy inside the lookup kernel)
+    "lru_token_plan": ("plan_lru.hip", "device_common.h", "internal.h", "hisparse_api.cpp",
+                       "copy.h"),
+    "lru_page_plan": ("plan_lru.hip", "device_common.h", "internal.h", "hisparse_api.cpp",
+                      "copy.h"),
+    "clock_plan": ("plan_clock.hip", "device_common.h", "internal.h", "hisparse_api.cpp",
+                   "copy.h"),
     # one call: topk_chunk_kernel (+ topk_merge_kernel when a row spans chunks)
     "topk": ("topk.hip", "device_common.h", "internal.h"),
     # one call: mla_decode (+ mla_combine when the locations are split)
@@ -153,6 +157,9 @@ def record(args):
     else:
         sr = line.get("state_roofline") or line.get("roofline", {})   # swap / batched-state
         alg, model = sr.get("bytes_per_launch"), sr.get("kernel_model_bytes_per_launch")
+        if args.fused:   # the lookup kernel that also copied: + each miss read and written
+            copy = 2 * line["roofline"]["bytes_per_launch"]
+            alg, model = alg + copy, (model + copy if model else None)
     entry = {"kernel": args.kernel, "workload": args.workload, "warmup": args.warmup,
              "steps": args.steps, **out,
              "algorithmic_bytes_per_launch": alg,
@@ -234,6 +241,9 @@ def main():
     r.add_argument("--warmup", type=int, required=True)
     r.add_argument("--steps", type=int, required=True)
     r.add_argument("--bench-line", default="")
+    r.add_argument("--fused", action="store_true",
+                   help="the launches copied their misses too (algorithmic bytes: state + "
+                        "miss bytes read and written)")
     r.add_argument("--cmd", default="")
     sub.add_parser("table")
     q = sub.add_parser("sq")
