@@ -90,6 +90,29 @@ def test_fused_clock(B, R, H, K, N, I, S, reuse, share):
         p.close()
 
 
+@pytest.mark.parametrize("admission", ["frequent", "first"])
+def test_fused_clock_admission_and_ring(admission):
+    """Fused multi-step calls that overflow (S*K > H) under the other two
+    admission priorities, with an extra-row ring of 16 rows: the newest
+    tokens resolve to ring rows and never reach the copy list."""
+    B, R, H, K, N, I, S = 16, 18, 700, 256, 3000, 32, 4
+    rng = np.random.default_rng([16, len(admission)])
+    p = Pair(R=R, L=1, H=H, K=K, N=N, I=I, S=S, policy="clock", seed=17,
+             admission=admission, extra_rows=16)
+    try:
+        prev = None
+        for call in range(5):
+            req = rng.permutation(R)[:B]
+            base = make_rows(rng, B, K, N, prev=prev, reuse=0.3)
+            base[:, :4] = N - 1 - rng.integers(0, 16, (B, 4))   # ring tokens
+            prev = base
+            steps = [base] + [make_rows(rng, B, K, N, prev=np.where(base >= 0, base, -1),
+                                        reuse=0.0) for _ in range(1, S)]
+            p.call(0, req, np.full(B, N), np.stack(steps, axis=1))
+    finally:
+        p.close()
+
+
 def test_threshold_and_deferred_interleave():
     """One state, batches of 15 (separate copy kernel) and 16 (fused) and
     deferred calls (separate copy replayed on another stream) in turn."""

@@ -545,20 +545,21 @@ def test_deferred_copy_pipelined_matches_eager(mode):
         eager.close()
 
 
+@pytest.mark.parametrize("B", [3, 20])   # 20 rows: the copy runs inside the plan kernel
 @pytest.mark.parametrize("policy", ["lru", "clock"])
-def test_graph_capture_replays_match_eager(policy):
+def test_graph_capture_replays_match_eager(policy, B):
     """Swap calls allocate nothing and never synchronise, so a call can be
     captured in a HIP graph; each replay (inputs refreshed by eager copies in
     between) must equal the same call made eagerly on a twin state."""
-    rng = np.random.default_rng(21)
-    R, H, K, N, I = 4, 500, 300, 3000, 32
+    rng = np.random.default_rng(21 + B)
+    R, H, K, N, I = B + 1, 500, 300, 3000, 32
     S = 3 if policy == "clock" else 1
     eager = Pair(R=R, L=1, H=H, K=K, N=N, I=I, S=S, policy=policy, seed=21)
     graph = Pair(R=R, L=1, H=H, K=K, N=N, I=I, S=S, policy=policy, seed=21)
     dev = torch.device("cuda", 0)
     try:
-        B = 3
-        req = torch.tensor([0, 2, 3], dtype=torch.int32, device=dev)
+        reqs = [r for r in range(R) if r != 1]     # B requests, one left out
+        req = torch.tensor(reqs, dtype=torch.int32, device=dev)
         seq = torch.full((B,), N, dtype=torch.int32, device=dev)
         shape = (B, S, K) if S > 1 else (B, K)
         topk_buf = torch.zeros(shape, dtype=torch.int32, device=dev)
@@ -582,11 +583,11 @@ def test_graph_capture_replays_match_eager(policy):
             g.replay()
             torch.cuda.synchronize()
             got, got_mc = out_g.cpu().numpy(), mc_g.cpu().numpy()
-            want_out, want_mc, _ = eager.call(0, [0, 2, 3], [N] * B, rows)
+            want_out, want_mc, _ = eager.call(0, reqs, [N] * B, rows)
             assert np.array_equal(got, want_out), f"replay {step} differs"
             assert np.array_equal(got_mc, want_mc)
             assert torch.equal(graph.gpu.dev_kv[0], eager.gpu.dev_kv[0])
-        for r in (0, 2, 3):
+        for r in reqs:
             a, b = graph.gpu.export(r, 0, with_map=True), eager.gpu.export(r, 0, with_map=True)
             for key in ("slot_key", "ctrl", "key_slot"):
                 assert np.array_equal(a[key], b[key])
