@@ -152,3 +152,32 @@ def test_profile_counts_fused_calls():
         assert prof["plan_ms"] > 0 and prof["copy_ms"] > 0
     finally:
         p.close()
+
+
+FUSED_LARGE = [
+    # (policy, H, K, N, S): 16 and 32 slots per thread, copies inside the plan kernel
+    ("lru", 12000, 2048, 40000, 1),
+    ("lru", 32768, 3000, 65536, 1),     # 8 entries per thread
+    ("clock", 16384, 1024, 50000, 2),
+    ("clock", 32768, 2048, 65536, 4),   # 8 entries per thread, overflow on the first call
+]
+
+
+@pytest.mark.parametrize("policy,H,K,N,S", FUSED_LARGE)
+def test_fused_large_hot_buffers(policy, H, K, N, S):
+    B = R = FUSE_MIN_ROWS
+    log(f"fused large {policy} H={H} K={K} N={N} S={S} B={B}")
+    rng = np.random.default_rng([H, K, S, 16])
+    p = Pair(R=R, L=1, H=H, K=K, N=N, I=16, S=S, policy=policy, seed=H + 16)
+    prev = None
+    try:
+        for call in range(4):
+            req = rng.permutation(R)[:B]
+            base = make_rows(rng, B, K, N, prev=prev, reuse=0.5)
+            prev = base
+            rows = base if S == 1 else np.stack(
+                [base] + [make_rows(rng, B, K, N, prev=np.where(base >= 0, base, -1), reuse=0.3)
+                          for _ in range(1, S)], axis=1)
+            p.call(0, req, np.full(B, N), rows)
+    finally:
+        p.close()
