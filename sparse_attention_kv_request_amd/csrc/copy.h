@@ -43,8 +43,10 @@ constexpr int64_t kCopyPageUnit = 4096;
 // Measured per step against the separate copy kernel: 64 rows x 8 layers
 // 2.681 vs 2.741 ms, 32 rows 1.403 vs 1.441, 16 rows 0.776 vs 0.785, 8 rows
 // even, one row 3x slower (one workgroup keeps too few host reads in
-// flight); whole pages 5 % slower (the copy kernel spreads a row's pages over
-// many workgroups), so pages always use it.
+// flight); 168-KB pages 4 % slower (the copy kernel spreads a row's pages
+// over many workgroups), so page mode always uses it.  The plan kernel's
+// entries are in range by construction; the copy kernel checks each one
+// because a replayed plan comes from the caller.
 constexpr int kFuseMinRows = HISPARSE_FUSE_MIN_ROWS;
 
 // Rows of `unit_bytes` from the host tier to the hot buffer.
