@@ -181,3 +181,22 @@ def test_fused_large_hot_buffers(policy, H, K, N, S):
             p.call(0, req, np.full(B, N), rows)
     finally:
         p.close()
+
+
+def test_fused_lru_with_extra_row_ring():
+    """Fused single-step LRU calls with a 32-row ring of the newest tokens:
+    ring tokens resolve to ring rows, the rest are looked up and copied."""
+    B, R, H, K, N, I = 20, 24, 600, 300, 4000, 48
+    rng = np.random.default_rng(2032)
+    p = Pair(R=R, L=2, H=H, K=K, N=N, I=I, seed=2032, extra_rows=32)
+    try:
+        prev = {}
+        for call in range(6):
+            layer = call % 2
+            req = rng.permutation(R)[:B]
+            rows = make_rows(rng, B, K, N, prev=prev.get(layer), reuse=0.5)
+            rows[:, :6] = N - 1 - rng.integers(0, 40, (B, 6))   # in and just below the ring
+            prev[layer] = rows
+            p.call(layer, req, np.full(B, N), rows)
+    finally:
+        p.close()
