@@ -6,7 +6,9 @@ every (request, layer) an independent hot cache of 4096 slots over 32768 host
 tokens of 656 bytes (fp8 MLA layout: 512 e4m3 latent + 4 fp32 scales + 64
 bf16 rope), top-k 2048 per row and layer, 70 % step-to-step reuse with a
 Zipf(1.1) recency bias.  One step is one decode step: the 8 per-layer swap
-calls (plan kernel + miss-copy kernel each) on one stream.
+calls on one stream (one launch each: with 16 or more token rows the plan
+kernel copies its rows' misses itself; fewer rows and page mode add the
+miss-copy kernel).
 
 ``--workload 1|3|4|5`` measures the other workload shapes the same way
 (1: B=1 bf16 rows; 3: multi-step CLOCK, also against S sequential LRU calls;
