@@ -420,22 +420,24 @@ def test_host_side_argument_errors():
         p.close()
 
 
-def test_copy_planned_replays_the_plan():
+@pytest.mark.parametrize("B", [2, 18])   # 18 rows: the call itself copies inside its plan kernel
+def test_copy_planned_replays_the_plan(B):
     """Replaying the plan of a swap call reproduces its copies; an entry outside
     the buffers is skipped and flagged instead of being written."""
-    rng = np.random.default_rng(16)
-    R, H, K, N, I = 3, 200, 150, 1000, 32
+    rng = np.random.default_rng(16 + B)
+    R, H, K, N, I = B + 1, 200, 150, 1000, 32
+    reqs = [r for r in range(R) if r != 1]
     p = Pair(R=R, L=1, H=H, K=K, N=N, I=I, seed=16)
     dev = torch.device("cuda", 0)
     try:
-        p.call(0, [0, 2], [N, N], make_rows(rng, 2, K, N))
+        p.call(0, reqs, [N] * B, make_rows(rng, B, K, N))
         cap = p.gpu.capacity
-        plan = tuple(torch.full((2, cap), -1, dtype=torch.int32, device=dev) for _ in range(3))
-        mc = torch.empty(2, dtype=torch.int32, device=dev)
-        out = torch.empty((2, K), dtype=torch.int32, device=dev)
-        rows = torch.from_numpy(make_rows(rng, 2, K, N)).to(dev)
-        p.gpu.swap_in_selected(0, torch.tensor([0, 2], dtype=torch.int32, device=dev),
-                               torch.full((2,), N, dtype=torch.int32, device=dev), rows, out, mc,
+        plan = tuple(torch.full((B, cap), -1, dtype=torch.int32, device=dev) for _ in range(3))
+        mc = torch.empty(B, dtype=torch.int32, device=dev)
+        out = torch.empty((B, K), dtype=torch.int32, device=dev)
+        rows = torch.from_numpy(make_rows(rng, B, K, N)).to(dev)
+        p.gpu.swap_in_selected(0, torch.tensor(reqs, dtype=torch.int32, device=dev),
+                               torch.full((B,), N, dtype=torch.int32, device=dev), rows, out, mc,
                                plan=plan)
         torch.cuda.synchronize()
         p.gpu.dev_kv[0].zero_()
@@ -445,7 +447,8 @@ def test_copy_planned_replays_the_plan():
         flat = p.gpu.dev_kv[0].reshape(-1, I).cpu()
         src, dst = plan[0].cpu(), plan[1].cpu()
         n = mc.cpu()
-        for b in range(2):
+        assert int(n.sum()) > 0
+        for b in range(B):
             for j in range(int(n[b])):
                 assert torch.equal(flat[dst[b, j]], host[src[b, j]])
         assert p.gpu.error_flags() == 0
