@@ -32,27 +32,31 @@ def sources():
     return sorted(list(CSRC.glob("*.hip")) + list(CSRC.glob("*.cpp")))
 
 
-def _compile(src: pathlib.Path) -> pathlib.Path:
-    obj = BUILD / (src.name + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", str(src), "-o", str(obj)]
+def _compile(src: pathlib.Path, objdir: pathlib.Path, defines) -> pathlib.Path:
+    obj = objdir / (src.name + ".o")
+    cmd = [HIPCC, *FLAGS, *defines, "-c", str(src), "-o", str(obj)]
     if src.suffix == ".cpp":
         cmd[1:1] = ["-x", "hip"]
     subprocess.run(cmd, check=True)
     return obj
 
 
-def build(verbose: bool = False) -> pathlib.Path:
-    BUILD.mkdir(exist_ok=True)
+def build(verbose: bool = False, defines=(), lib: pathlib.Path = LIB) -> pathlib.Path:
+    """The library at `lib`; `defines` (``-DNAME=VALUE``) build a variant,
+    e.g. the phase-clock instrumentation, into its own object folder."""
+    objdir = BUILD if not defines else BUILD / ("variant_" + lib.parent.name)
+    objdir.mkdir(parents=True, exist_ok=True)
+    lib.parent.mkdir(parents=True, exist_ok=True)
     srcs = sources()
     with concurrent.futures.ThreadPoolExecutor(min(8, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB.with_suffix(".so.tmp")
+        objs = list(ex.map(lambda s: _compile(s, objdir, list(defines)), srcs))
+    tmp = lib.with_suffix(".so.tmp")
     subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC",
                     *[str(o) for o in objs], "-o", str(tmp)], check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":

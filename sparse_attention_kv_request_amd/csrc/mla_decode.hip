@@ -31,6 +31,23 @@
 
 #include "internal.h"
 
+// Opt-in instrumentation, a separate build (-DHISPARSE_PHASE_CLOCKS=1, see
+// phase_clocks.py): the bf16 tile loop adds up, per wave, the shader clocks
+// spent waiting for a tile's gather, at the phase barriers and in the whole
+// loop; hisparse_attention_wait_clocks() returns the sums since the library
+// was loaded (and the waves counted).  The default build records nothing.
+#ifndef HISPARSE_PHASE_CLOCKS
+#define HISPARSE_PHASE_CLOCKS 0
+#endif
+#if HISPARSE_PHASE_CLOCKS
+__device__ unsigned long long g_attn_clock[4];
+extern "C" int hisparse_attention_wait_clocks(unsigned long long* out_h) {
+  return hipMemcpyFromSymbol(out_h, HIP_SYMBOL(g_attn_clock), sizeof(g_attn_clock)) ==
+                 hipSuccess
+             ? 0 : -1;
+}
+#endif
+
 namespace hisparse {
 
 namespace {
@@ -525,10 +542,23 @@ void mla_decode(MlaArgs a) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     int it = 0;          // tile in buffer `cur`
     bool fresh = false;  // this phase starts the sums over
+#if HISPARSE_PHASE_CLOCKS
+    unsigned long long c_gather = 0, c_barrier = 0;
+    const unsigned long long c_loop = __builtin_amdgcn_s_memtime();
+#endif
     for (int phase = 0; it < ntiles; ++phase) {
       const int cur = phase & 1;
+#if HISPARSE_PHASE_CLOCKS
+      const unsigned long long c0 = __builtin_amdgcn_s_memtime();
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      const unsigned long long c1 = __builtin_amdgcn_s_memtime();
+      __syncthreads();
+      c_gather += c1 - c0;
+      c_barrier += __builtin_amdgcn_s_memtime() - c1;
+#else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();  // this phase's tile is in LDS; every wave is done with the last one
+#endif
       const bool replay = restart_at[cur ^ 1] == phase - 1;
       const int next = replay ? 0 : it + 1;
       const uint32_t valid = valid_next;  // bit t: row t of this tile is present
@@ -552,6 +582,14 @@ void mla_decode(MlaArgs a) {
         }
       }
     }
+#if HISPARSE_PHASE_CLOCKS
+    if (lane == 0) {
+      atomicAdd(&g_attn_clock[0], c_gather);
+      atomicAdd(&g_attn_clock[1], c_barrier);
+      atomicAdd(&g_attn_clock[2], __builtin_amdgcn_s_memtime() - c_loop);
+      atomicAdd(&g_attn_clock[3], 1ull);
+    }
+#endif
   } else {
     // fp8 rows: raw tiles are gathered two tiles ahead into R(0..1), and the
     // next tile is dequantised into the idle bf16 tile T(pb ^ 1) by every

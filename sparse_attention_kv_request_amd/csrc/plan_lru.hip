@@ -20,6 +20,33 @@
 //    with block scans, so the result does not depend on thread timing.
 #include "internal.h"
 
+// Opt-in instrumentation, a separate build (-DHISPARSE_PHASE_CLOCKS=1, see
+// phase_clocks.py): every workgroup of a token-mode plan launch records the
+// 100 MHz wall clock at its phase boundaries, and hisparse_phase_clocks()
+// copies the last launch's stamps out.  The default build records nothing.
+#ifndef HISPARSE_PHASE_CLOCKS
+#define HISPARSE_PHASE_CLOCKS 0
+#endif
+#if HISPARSE_PHASE_CLOCKS
+constexpr int kClockRows = 4096;   // workgroups recorded
+constexpr int kClockStamps = 10;   // per workgroup: 9 stamps, then the row's miss count
+__device__ long long g_phase_clock[kClockRows * kClockStamps];
+#define PHASE_CLOCK(i, v)                                                        \
+  do {                                                                          \
+    if (threadIdx.x == 0 && blockIdx.x < kClockRows)                            \
+      g_phase_clock[blockIdx.x * kClockStamps + (i)] = (v);                     \
+  } while (0)
+extern "C" int hisparse_phase_clocks(long long* out_h, int n) {
+  if (n < 0 || n > kClockRows * kClockStamps) return -1;
+  return hipMemcpyFromSymbol(out_h, HIP_SYMBOL(g_phase_clock), n * sizeof(long long)) == hipSuccess
+             ? 0 : -1;
+}
+#else
+#define PHASE_CLOCK(i, v) \
+  do {                    \
+  } while (0)
+#endif
+
 namespace hisparse {
 
 namespace {
@@ -171,6 +198,7 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
 
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
+  PHASE_CLOCK(0, wall_clock64());
   const int r = a.req[b];
   const int sl = a.seq[b];
   // Loads that need only the instance go out before the row checks so they
@@ -214,6 +242,7 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
     reject_row<NT>(a, b, a.K, code, false);
     return;
   }
+  PHASE_CLOCK(1, wall_clock64());
   // 1. validate every entry.  Entries among the newest ext tokens resolve to
   // their ring row instead (the extra-page lookup, before the hash lookup)
   // and stay out of the cache.
@@ -239,6 +268,7 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
     for (int e = 0; e < EPH; ++e) oldk[e] = o[e] >= 0 ? sk[o[e]] : kEmpty;
   }
 
+  PHASE_CLOCK(2, wall_clock64());
   // 2. dedup and the join.  kmin takes each key's first position (atomicMin);
   // the owner of each resident slot whose key the row names writes the slot
   // into the key's kres entry and marks the slot used now.
@@ -289,6 +319,7 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
   store_slot_words<EPH>(used, a.Hw, hitmask);
   __syncthreads();
 
+  PHASE_CLOCK(3, wall_clock64());
   // 3. representatives (first occurrences) take their key's result; misses
   // go into the miss-key bitmap.  One scan then ranks the misses (position
   // order), the available order positions (order) and the miss keys' bitmap
@@ -333,11 +364,13 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
     wp += __popc(mbits[w]);
   }
   __syncthreads();
+  PHASE_CLOCK(4, wall_clock64());
 
   // 4. victims, commit, new order
   lru_commit<NT, EPH>(a, b, r, now, m, o, avail, rank0, used, miss_key, vslot, scan, sk, tsq,
                       ord, sw ? mbits : nullptr, mwpre, oldk);
   __syncthreads();
+  PHASE_CLOCK(5, wall_clock64());
 
   // 5. outputs
   int32_t* out = a.out_locs + static_cast<size_t>(b) * a.K;
@@ -357,11 +390,18 @@ __global__ __launch_bounds__(NT) void lru_token_plan(PlanArgs a) {
     a.ctrl[2 * q] = now + 1;
   }
   if (bad_index) raise_error(a.err, HISPARSE_ERR_BAD_INDEX);
+  PHASE_CLOCK(6, wall_clock64());
+  PHASE_CLOCK(9, m);
   if (a.fuse_copy) {
     __syncthreads();  // the row's copy list, written above by this workgroup
+    PHASE_CLOCK(7, wall_clock64());
     const size_t lb = sw ? static_cast<size_t>(b) * a.ccap : static_cast<size_t>(b) * a.cap;
     copy_own_row<NT>(a, (sw ? a.copy_src : a.miss_src) + lb, (sw ? a.copy_dst : a.miss_dst) + lb,
                      m);
+#if HISPARSE_PHASE_CLOCKS
+    __syncthreads();  // every wave's last loads returned
+    PHASE_CLOCK(8, wall_clock64());
+#endif
   }
 }
 

@@ -1,0 +1,163 @@
+"""Phase clocks of the token-mode plan kernel (with the copy it does for
+calls of 16 or more rows) and the wait shares of the bf16 attention tile
+loop, from the instrumented build of the library.
+
+``python -m sparse_attention_kv_request_amd.phase_clocks build`` compiles the
+sources with ``-DHISPARSE_PHASE_CLOCKS=1`` into
+``_build/phase_clocks/libhisparse.so`` (the default library is untouched;
+that build records nothing).  ``python -m
+sparse_attention_kv_request_amd.phase_clocks run`` (on the GPU) drives that
+library and prints a markdown summary:
+
+* the 64-row, single-layer swap call of the headline workload (16 calls,
+  the first 4 skipped): per workgroup the 100 MHz wall clock at each phase
+  boundary of the plan, at the start and end of its row's copy, and the
+  row's miss count; medians over workgroups and calls, the copy end per XCD
+  (workgroup id mod 8), and the copy phase's rate;
+* the attention bench's bf16 calls: the share of each wave's tile-loop
+  clocks spent waiting for the next tile's gather and at the phase barrier.
+
+The clock reads add a few instructions per phase, so the absolute times run
+a little above the uninstrumented kernels'; the shares and the spread are
+what the summary is for.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import pathlib
+import sys
+
+ROOT = pathlib.Path(__file__).resolve().parents[1]
+VARIANT = ROOT / "_build" / "phase_clocks" / "libhisparse.so"
+TICK_US = 0.01  # wall_clock64: 100 MHz
+STAMPS = 10
+PHASES = ["request/state/top-k loads, row checks", "entry validation",
+          "join (row-key bitmap, ranks, resident-key matches, hit touch)",
+          "representatives, miss bitmap, merged scan, miss lists",
+          "victims, commit, order rewrite", "outputs"]
+
+
+def build():
+    from sparse_attention_kv_request_amd import build as b
+
+    return b.build(verbose=True, defines=["-DHISPARSE_PHASE_CLOCKS=1"], lib=VARIANT)
+
+
+def _plan_clocks(torch, binding, workloads, lib, calls=16, skip=4):
+    import numpy as np
+
+    fn = lib.hisparse_phase_clocks
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    w = workloads.config(2, layers=1, steps=calls)
+    host = [binding.HostKV(w.requests, w.seq_len, w.item_bytes)]
+    workloads.fill_host_kv(w, [h.array for h in host], threads=16)
+    trace = workloads.batch_trace(w, threads=16)
+    dev = torch.device("cuda", 0)
+    st = binding.HiSparseState(max_requests=w.requests, num_layers=1, hot_buffer_size=w.hot,
+                               top_k=w.top_k, item_size_bytes=w.item_bytes,
+                               max_seq_len=w.seq_len, host_kv=host)
+    B = w.batch
+    req = torch.arange(B, dtype=torch.int32, device=dev)
+    seq = torch.full((B,), w.seq_len, dtype=torch.int32, device=dev)
+    out = torch.empty((B, w.top_k), dtype=torch.int32, device=dev)
+    mc = torch.empty(B, dtype=torch.int32, device=dev)
+    phases, ends, xcd_end, rates, spans, plan_spans = [], [], [[] for _ in range(8)], [], [], []
+    for s in range(calls):
+        rows = torch.from_numpy(np.ascontiguousarray(trace[0, s, :, 0])).to(dev)
+        st.swap_in_selected(0, req, seq, rows, out, mc)
+        torch.cuda.synchronize()
+        if s < skip:
+            continue
+        buf = np.zeros(B * STAMPS, np.int64)
+        if fn(buf.ctypes.data, buf.size) != 0:
+            raise SystemExit("hisparse_phase_clocks failed")
+        t = buf.reshape(B, STAMPS)
+        t0 = t[:, 0].min()
+        phases.append(np.diff(t[:, :7], axis=1) * TICK_US)
+        end = (t[:, 8] - t0) * TICK_US
+        ends.append(end)
+        for b in range(B):
+            xcd_end[b % 8].append(end[b])
+        spans.append(end.max())
+        plan_spans.append((t[:, 6].max() - t0) * TICK_US)
+        copy_us = (t[:, 8].max() - t[:, 7].min()) * TICK_US
+        rates.append(t[:, 9].sum() * w.item_bytes / copy_us / 1e3)
+    st.close()
+    for h in host:
+        h.free()
+    ph = np.concatenate(phases)
+    ends = np.concatenate(ends)
+    return {"B": B, "calls": calls - skip, "phase_us": np.median(ph, axis=0),
+            "phase_sum_us": float(np.median(ph.sum(axis=1))),
+            "plan_span_us": float(np.median(plan_spans)), "span_us": float(np.median(spans)),
+            "end_median_us": float(np.median(ends)), "end_p90_us": float(np.percentile(ends, 90)),
+            "xcd_end_us": [float(np.median(x)) for x in xcd_end],
+            "copy_GBps": float(np.median(rates))}
+
+
+def _attention_waits(torch, binding, workloads, lib):
+    import bench
+
+    fn = lib.hisparse_attention_wait_clocks
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p]
+    before = (ctypes.c_ulonglong * 4)()
+    after = (ctypes.c_ulonglong * 4)()
+    if fn(ctypes.byref(before)) != 0:
+        raise SystemExit("hisparse_attention_wait_clocks failed")
+    args = argparse.Namespace(warmup=5, steps=20, workload=2, item=1152, heads=128)
+    res = bench.attention_bench(args, torch, binding, workloads)
+    if fn(ctypes.byref(after)) != 0:
+        raise SystemExit("hisparse_attention_wait_clocks failed")
+    g, b, total, waves = (after[i] - before[i] for i in range(4))
+    return {"us_per_call": res["roofline"]["us_per_call"], "waves": waves,
+            "gather_share": g / total, "barrier_share": b / total,
+            "loop_clocks_per_wave": total / waves}
+
+
+def run():
+    sys.path.insert(0, str(ROOT))
+    import torch
+
+    from sparse_attention_kv_request_amd import binding, workloads
+
+    if not VARIANT.exists():
+        raise SystemExit(f"{VARIANT} is missing: run this module's build step first")
+    binding.LIB_PATH = VARIANT
+    lib = binding.lib()
+    torch.cuda.set_device(0)
+    p = _plan_clocks(torch, binding, workloads, lib)
+    a = _attention_waits(torch, binding, workloads, lib)
+    print(f"### Plan kernel with its copies: {p['B']} rows, one layer of the headline "
+          f"workload, medians over {p['calls']} calls x {p['B']} workgroups\n")
+    print("| phase | µs per workgroup |\n|---|---|")
+    for name, v in zip(PHASES, p["phase_us"]):
+        print(f"| {name} | {v:.2f} |")
+    print(f"| sum | {p['phase_sum_us']:.2f} |\n")
+    print(f"- last row's plan done {p['plan_span_us']:.1f} µs after the first workgroup started; "
+          f"copies done: median row {p['end_median_us']:.1f} µs, 90th percentile "
+          f"{p['end_p90_us']:.1f} µs, last {p['span_us']:.1f} µs")
+    print("- copy end per XCD (workgroup id mod 8), median µs: " +
+          ", ".join(f"XCD {x} {v:.0f}" for x, v in enumerate(p["xcd_end_us"])))
+    print(f"- copy phase (first copy start to last copy end): {p['copy_GBps']:.2f} GB/s of miss "
+          f"bytes\n")
+    print("### bf16 attention tile loop (the attention bench, 8 layers x 25 calls)\n")
+    print(f"- share of a wave's loop clocks waiting for the next tile's gather: "
+          f"{100 * a['gather_share']:.2f} %; at the phase barrier: {100 * a['barrier_share']:.2f} %")
+    print(f"- {a['waves']} waves, {a['loop_clocks_per_wave']:.0f} loop clocks per wave; "
+          f"{a['us_per_call']} µs per call in this instrumented build")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("action", choices=["build", "run"])
+    if ap.parse_args().action == "build":
+        build()
+    else:
+        run()
+
+
+if __name__ == "__main__":
+    main()
