@@ -30,6 +30,13 @@ def test_library_exports_every_declared_symbol():
     assert set(declared_functions()) == set(binding.EXPORTED)
 
 
+def test_default_build_carries_no_instrumentation():
+    """The phase-clock hooks exist only in the opt-in instrumented build."""
+    lib = binding.lib()
+    for name in ("hisparse_phase_clocks", "hisparse_attention_wait_clocks"):
+        assert not hasattr(lib, name), name
+
+
 def test_strerror_and_rows_are_host_only():
     assert binding.strerror(0) == "success"
     assert binding.strerror(binding.HISPARSE_E_INVAL) == "invalid argument"
