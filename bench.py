@@ -498,8 +498,9 @@ def batched_state_bench(args, torch, binding, workloads):
     64 requests x 8 layers as 512 requests of one layer, all resolved by one
     swap call.  After the first (cold) call every later call repeats the same
     top-k rows, so every entry hits: the step is the plan kernel alone
-    (lookup, hit touch, LRU order rewrite, outputs) plus an empty copy
-    launch.  Host KV bytes are left zero (no miss reads them after call 0)."""
+    (lookup, hit touch, LRU order rewrite, outputs; the copy it does for a
+    call of this many rows has nothing to move).  Host KV bytes are left zero
+    (no miss reads them after call 0)."""
     import numpy as np
 
     W, K = args.warmup, args.steps

@@ -32,20 +32,39 @@
 #include "internal.h"
 
 // Opt-in instrumentation, a separate build (-DHISPARSE_PHASE_CLOCKS=1, see
-// phase_clocks.py): the bf16 tile loop adds up, per wave, the shader clocks
-// spent waiting for a tile's gather, at the phase barriers and in the whole
-// loop; hisparse_attention_wait_clocks() returns the sums since the library
-// was loaded (and the waves counted).  The default build records nothing.
+// phase_clocks.py): in the bf16 tile loop every wave of the last launch
+// stores the shader clocks it spent waiting for a tile's gather, at the
+// phase barriers and in the whole loop (hisparse_attention_wait_clocks()),
+// and every workgroup the 100 MHz wall clock at its start, at the first
+// tile's barrier, after the tile loop and at its end
+// (hisparse_attention_phase_clocks()).  The default build records nothing.
 #ifndef HISPARSE_PHASE_CLOCKS
 #define HISPARSE_PHASE_CLOCKS 0
 #endif
 #if HISPARSE_PHASE_CLOCKS
-__device__ unsigned long long g_attn_clock[4];
-extern "C" int hisparse_attention_wait_clocks(unsigned long long* out_h) {
-  return hipMemcpyFromSymbol(out_h, HIP_SYMBOL(g_attn_clock), sizeof(g_attn_clock)) ==
+constexpr int kAttnClockRows = 4096;
+__device__ unsigned long long g_attn_wave[kAttnClockRows * 4 * 3];
+extern "C" int hisparse_attention_wait_clocks(unsigned long long* out_h, int n) {
+  if (n < 0 || n > kAttnClockRows * 4 * 3) return -1;
+  return hipMemcpyFromSymbol(out_h, HIP_SYMBOL(g_attn_wave), n * sizeof(unsigned long long)) ==
                  hipSuccess
              ? 0 : -1;
 }
+__device__ long long g_attn_stamp[kAttnClockRows * 4];
+#define ATTN_CLOCK(i)                                                            \
+  do {                                                                          \
+    if (threadIdx.x == 0 && blockIdx.x < kAttnClockRows)                        \
+      g_attn_stamp[blockIdx.x * 4 + (i)] = wall_clock64();                      \
+  } while (0)
+extern "C" int hisparse_attention_phase_clocks(long long* out_h, int n) {
+  if (n < 0 || n > kAttnClockRows * 4) return -1;
+  return hipMemcpyFromSymbol(out_h, HIP_SYMBOL(g_attn_stamp), n * sizeof(long long)) == hipSuccess
+             ? 0 : -1;
+}
+#else
+#define ATTN_CLOCK(i) \
+  do {                \
+  } while (0)
 #endif
 
 namespace hisparse {
@@ -305,6 +324,7 @@ void mla_decode(MlaArgs a) {
   const int split = su % a.splits;
   const int b = (su / a.splits) * 8 + xcd;
   if (b >= a.batch) return;
+  ATTN_CLOCK(0);
   const int t_begin = split * a.per_split;
   const int nrows = max(0, min(a.n_locs, t_begin + a.per_split) - t_begin);
   const int tid = threadIdx.x;
@@ -555,6 +575,7 @@ void mla_decode(MlaArgs a) {
       __syncthreads();
       c_gather += c1 - c0;
       c_barrier += __builtin_amdgcn_s_memtime() - c1;
+      if (phase == 0) ATTN_CLOCK(1);
 #else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();  // this phase's tile is in LDS; every wave is done with the last one
@@ -583,11 +604,12 @@ void mla_decode(MlaArgs a) {
       }
     }
 #if HISPARSE_PHASE_CLOCKS
-    if (lane == 0) {
-      atomicAdd(&g_attn_clock[0], c_gather);
-      atomicAdd(&g_attn_clock[1], c_barrier);
-      atomicAdd(&g_attn_clock[2], __builtin_amdgcn_s_memtime() - c_loop);
-      atomicAdd(&g_attn_clock[3], 1ull);
+    ATTN_CLOCK(2);
+    if (lane == 0 && blockIdx.x < kAttnClockRows) {
+      unsigned long long* wv = g_attn_wave + (blockIdx.x * 4 + wave) * 3;
+      wv[0] = c_gather;
+      wv[1] = c_barrier;
+      wv[2] = __builtin_amdgcn_s_memtime() - c_loop;
     }
 #endif
   } else {
@@ -727,6 +749,7 @@ void mla_decode(MlaArgs a) {
       *reinterpret_cast<u32x4*>(a.part_ml + 8 * ps + 4) =
           u32x4{ebits[0], ebits[1], ebits[2], ebits[3]};
   }
+  ATTN_CLOCK(3);
 }
 
 // Merges the splits of every (row, head) by their log-sum-exp: 64 lanes per

@@ -35,6 +35,33 @@
 
 #include "internal.h"
 
+// Opt-in instrumentation, a separate build (-DHISPARSE_PHASE_CLOCKS=1, see
+// phase_clocks.py): each chunk workgroup records the 100 MHz wall clock at
+// its phase boundaries; hisparse_topk_phase_clocks() copies out the last
+// launch's stamps.  The default build records nothing.
+#ifndef HISPARSE_PHASE_CLOCKS
+#define HISPARSE_PHASE_CLOCKS 0
+#endif
+#if HISPARSE_PHASE_CLOCKS
+constexpr int kTopkClockRows = 4096;
+constexpr int kTopkStamps = 6;
+__device__ long long g_topk_clock[kTopkClockRows * kTopkStamps];
+#define TOPK_CLOCK(i)                                                            \
+  do {                                                                          \
+    if (threadIdx.x == 0 && blockIdx.x < kTopkClockRows)                        \
+      g_topk_clock[blockIdx.x * kTopkStamps + (i)] = wall_clock64();            \
+  } while (0)
+extern "C" int hisparse_topk_phase_clocks(long long* out_h, int n) {
+  if (n < 0 || n > kTopkClockRows * kTopkStamps) return -1;
+  return hipMemcpyFromSymbol(out_h, HIP_SYMBOL(g_topk_clock), n * sizeof(long long)) == hipSuccess
+             ? 0 : -1;
+}
+#else
+#define TOPK_CLOCK(i) \
+  do {                \
+  } while (0)
+#endif
+
 namespace hisparse {
 
 namespace {
@@ -383,6 +410,7 @@ void topk_chunk_kernel(TopkArgs a) {
   const int w = blockIdx.x;
   if (w >= a.plan[0]) return;
   const int tid = threadIdx.x;
+  TOPK_CLOCK(0);
   const int32_t* item = a.plan + p.items + 4 * w;
   const int row = item[0], start = item[2], len = item[3];
   const int n_chunks = a.plan[p.row_info + 2 * row + 1];
@@ -427,20 +455,25 @@ void topk_chunk_kernel(TopkArgs a) {
     }
   }
   __syncthreads();
+  TOPK_CLOCK(1);
   const int kk = min(a.k, len);
   uint32_t T = 0u, kept = 0u;
   int need = 0, offset = 0;
   if (kk > 0) {
     radix_threshold(key, kk, s, T, need);
+    TOPK_CLOCK(2);
     kept = select_word(key, T, need, s, offset);
   }
+  TOPK_CLOCK(3);
   const bool staged = kk <= kStageCap;
   if (staged) stage_kept(key, kept, offset, s);
+  TOPK_CLOCK(4);
   if (n_chunks == 1) {
     if (staged)
       emit_staged(a, row, [&](int i) { return start + i; }, s, kk);
     else
       emit_final(a, row, [&](int i) { return start + i; }, kept, offset, kk);
+    TOPK_CLOCK(5);
     return;
   }
   // a chunk of a split row: its candidates (key, position) in slot order,

@@ -14,8 +14,12 @@ library and prints a markdown summary:
   boundary of the plan, at the start and end of its row's copy, and the
   row's miss count; medians over workgroups and calls, the copy end per XCD
   (workgroup id mod 8), and the copy phase's rate;
-* the attention bench's bf16 calls: the share of each wave's tile-loop
-  clocks spent waiting for the next tile's gather and at the phase barrier.
+* the same kernel with 512 instances in one launch (the batched-state
+  bench): when its workgroups start and how long each runs;
+* the top-k chunk kernel's phases (64 rows x 32768 scores);
+* the attention bench's bf16 calls: the kernel's setup, tile loop and
+  epilogue, and the share of each wave's tile-loop clocks spent waiting for
+  the next tile's gather and at the phase barrier.
 
 The clock reads add a few instructions per phase, so the absolute times run
 a little above the uninstrumented kernels'; the shares and the spread are
@@ -97,24 +101,83 @@ def _plan_clocks(torch, binding, workloads, lib, calls=16, skip=4):
             "copy_GBps": float(np.median(rates))}
 
 
+def _batched_dispatch(torch, binding, workloads, lib):
+    """The 512-instance hit-only launch of the batched-state bench: when each
+    workgroup starts and how long it runs (stamps of the last launch)."""
+    import numpy as np
+
+    import bench
+
+    fn = lib.hisparse_phase_clocks
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    args = argparse.Namespace(warmup=5, steps=20)
+    res = bench.batched_state_bench(args, torch, binding, workloads)
+    n = res["config"]["batch"]
+    buf = np.zeros(n * STAMPS, np.int64)
+    if fn(buf.ctypes.data, buf.size) != 0:
+        raise SystemExit("hisparse_phase_clocks failed")
+    t = buf.reshape(n, STAMPS)
+    t0 = t[:, 0].min()
+    start = (t[:, 0] - t0) * TICK_US
+    run = (t[:, 8] - t[:, 0]) * TICK_US
+    first_end = (t[:, 8] - t0).min() * TICK_US
+    return {"n": n, "us_per_launch": res["roofline"]["avg_launch_us"],
+            "start_span_us": float(start.max()), "start_median_us": float(np.median(start)),
+            "run_median_us": float(np.median(run)), "first_end_us": float(first_end),
+            "started_before_first_end": int((start < first_end).sum()),
+            "wg_per_us": float(n / start.max()) if start.max() > 0 else float("inf")}
+
+
+def _topk_phases(torch, binding, workloads, lib):
+    import numpy as np
+
+    import bench
+
+    fn = lib.hisparse_topk_phase_clocks
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    args = argparse.Namespace(warmup=5, steps=20, workload=2, no_cpu_baseline=True,
+                              cpu_seconds=0)
+    res = bench.topk_bench(args, torch, binding, workloads)
+    n = res["config"]["batch"]
+    buf = np.zeros(n * 6, np.int64)
+    if fn(buf.ctypes.data, buf.size) != 0:
+        raise SystemExit("hisparse_topk_phase_clocks failed")
+    t = buf.reshape(n, 6)
+    return {"n": n, "us_per_call": res["roofline"]["us_per_call"],
+            "phase_us": np.median(np.diff(t, axis=1), axis=0) * TICK_US,
+            "span_us": float((t[:, 5].max() - t[:, 0].min()) * TICK_US)}
+
+
 def _attention_waits(torch, binding, workloads, lib):
     import bench
 
-    fn = lib.hisparse_attention_wait_clocks
-    fn.restype = ctypes.c_int
-    fn.argtypes = [ctypes.c_void_p]
-    before = (ctypes.c_ulonglong * 4)()
-    after = (ctypes.c_ulonglong * 4)()
-    if fn(ctypes.byref(before)) != 0:
-        raise SystemExit("hisparse_attention_wait_clocks failed")
+    import numpy as np
+
     args = argparse.Namespace(warmup=5, steps=20, workload=2, item=1152, heads=128)
     res = bench.attention_bench(args, torch, binding, workloads)
-    if fn(ctypes.byref(after)) != 0:
+    n = 256                                   # workgroups of a 64-row launch
+    fn = lib.hisparse_attention_wait_clocks
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    wv = np.zeros(n * 4 * 3, np.uint64)
+    if fn(wv.ctypes.data, wv.size) != 0:
         raise SystemExit("hisparse_attention_wait_clocks failed")
-    g, b, total, waves = (after[i] - before[i] for i in range(4))
+    g, b, total = (float(x) for x in wv.reshape(n * 4, 3).sum(axis=0))
+    waves = n * 4
+    st = lib.hisparse_attention_phase_clocks
+    st.restype = ctypes.c_int
+    st.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    buf = np.zeros(n * 4, np.int64)
+    if st(buf.ctypes.data, buf.size) != 0:
+        raise SystemExit("hisparse_attention_phase_clocks failed")
+    t = buf.reshape(n, 4)
     return {"us_per_call": res["roofline"]["us_per_call"], "waves": waves,
             "gather_share": g / total, "barrier_share": b / total,
-            "loop_clocks_per_wave": total / waves}
+            "loop_clocks_per_wave": total / waves,
+            "phase_us": np.median(np.diff(t, axis=1), axis=0) * TICK_US,
+            "span_us": float((t[:, 3].max() - t[:, 0].min()) * TICK_US)}
 
 
 def run():
@@ -129,6 +192,8 @@ def run():
     lib = binding.lib()
     torch.cuda.set_device(0)
     p = _plan_clocks(torch, binding, workloads, lib)
+    d = _batched_dispatch(torch, binding, workloads, lib)
+    k = _topk_phases(torch, binding, workloads, lib)
     a = _attention_waits(torch, binding, workloads, lib)
     print(f"### Plan kernel with its copies: {p['B']} rows, one layer of the headline "
           f"workload, medians over {p['calls']} calls x {p['B']} workgroups\n")
@@ -143,7 +208,27 @@ def run():
           ", ".join(f"XCD {x} {v:.0f}" for x, v in enumerate(p["xcd_end_us"])))
     print(f"- copy phase (first copy start to last copy end): {p['copy_GBps']:.2f} GB/s of miss "
           f"bytes\n")
-    print("### bf16 attention tile loop (the attention bench, 8 layers x 25 calls)\n")
+    print(f"### The same kernel with {d['n']} instances in one launch (batched-state bench, "
+          f"hit-only; stamps of the last launch)\n")
+    print(f"- workgroup start times spread over {d['start_span_us']:.1f} µs (median "
+          f"{d['start_median_us']:.1f} µs): {d['wg_per_us']:.1f} workgroups of 16 waves per µs")
+    print(f"- each workgroup runs {d['run_median_us']:.1f} µs (median); the first finishes at "
+          f"{d['first_end_us']:.1f} µs, by when {d['started_before_first_end']} have started")
+    print(f"- {d['us_per_launch']} µs per launch (HIP events) in this instrumented build\n")
+    print(f"### Top-k chunk kernel, {k['n']} rows x 32768 scores, k = 2048 (last launch)\n")
+    print("| phase | µs per workgroup |\n|---|---|")
+    for name, v in zip(["loads and first-digit histogram", "exact threshold (radix select)",
+                        "bitmap selection", "output staging", "output"], k["phase_us"]):
+        print(f"| {name} | {v:.2f} |")
+    print(f"\n- span {k['span_us']:.1f} µs; {k['us_per_call']} µs per call in this instrumented "
+          f"build\n")
+    print("### bf16 attention kernel (the attention bench's last launch: 64 rows x 128 heads x "
+          "2048 locations, 256 workgroups)\n")
+    print("| phase (workgroup, last launch) | µs |\n|---|---|")
+    for name, v in zip(["setup: locations, row table, queries, first tile landed",
+                        "tile loop", "split partials out"], a["phase_us"]):
+        print(f"| {name} | {v:.2f} |")
+    print(f"\n- kernel span {a['span_us']:.1f} µs")
     print(f"- share of a wave's loop clocks waiting for the next tile's gather: "
           f"{100 * a['gather_share']:.2f} %; at the phase barrier: {100 * a['barrier_share']:.2f} %")
     print(f"- {a['waves']} waves, {a['loop_clocks_per_wave']:.0f} loop clocks per wave; "
