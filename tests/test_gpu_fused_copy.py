@@ -51,6 +51,8 @@ def test_fused_lru_random(case):
             seq = np.full(c["B"], c["N"])
             if call == 3:
                 seq[5] = c["N"] + 1          # one rejected row inside a fused call
+            if call == 4:
+                req[7] = req[2]              # a request named twice: both rows rejected
             p.call(layer, req, seq, rows, plan_extra=3 * (call % 2))
     finally:
         p.close()
