@@ -202,3 +202,18 @@ def test_fused_lru_with_extra_row_ring():
             p.call(layer, req, np.full(B, N), rows)
     finally:
         p.close()
+
+
+def test_fused_clock_with_fewer_steps_than_max():
+    """A state made for 4 steps called with 2, 3 and 4 steps by fused calls."""
+    rng = np.random.default_rng(234)
+    B, R, H, K, N = 18, 20, 900, 200, 3000
+    p = Pair(R=R, L=1, H=H, K=K, N=N, I=16, S=4, policy="clock", seed=234)
+    try:
+        for call in range(6):
+            S = 2 + call % 3
+            req = rng.permutation(R)[:B]
+            topk = rng.integers(-1, N, (B, S, K))
+            p.call(0, req, np.full(B, N), topk)
+    finally:
+        p.close()
