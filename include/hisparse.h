@@ -62,7 +62,8 @@ extern "C" {
 #define HISPARSE_ERR_DUP_REQUEST 2u   /* one request index twice in one batch */
 #define HISPARSE_ERR_PAGE_OVERFLOW 4u /* a row needs more distinct pages than hot pages */
 #define HISPARSE_ERR_BAD_ROW 8u       /* request index or seq_len out of range */
-#define HISPARSE_ERR_BAD_PLAN 16u     /* a replayed plan entry outside the buffers */
+#define HISPARSE_ERR_BAD_PLAN 16u     /* a replayed plan entry, or a top-k plan entry,
+                                         outside the buffers */
 
 /* Replacement policies. */
 #define HISPARSE_POLICY_LRU 0   /* single-step calls (PR #20343 summary) */
@@ -434,7 +435,10 @@ size_t hisparse_topk_workspace_bytes(int32_t batch, int32_t max_len, int32_t k);
 /*
  * One layer's selection and index table (see above) on `stream`: one kernel
  * launch, plus a second one that merges the chunks of rows longer than 32768
- * positions; reads each logit once.  Allocates nothing.
+ * positions; reads each logit once.  Allocates nothing.  A plan entry that
+ * lies outside batch, max_len or the plan (a plan made for other sizes) is
+ * skipped and raises HISPARSE_ERR_BAD_PLAN; its row's outputs are then not
+ * written.
  * Errors: HISPARSE_E_INVAL (NULL pointers, bad sizes or mode, plan or
  * workspace too small), HISPARSE_E_UNSUPPORTED (k or max_len beyond the
  * limits above), HISPARSE_E_HIP.

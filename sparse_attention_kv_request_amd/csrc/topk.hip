@@ -72,7 +72,6 @@ constexpr int kWaves = kThreads / kWave;           // 16
 constexpr int kBins = 4096;                        // 12-bit digits
 constexpr int kListCap = 4096;                     // keys of the threshold bin kept in LDS
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct TopkArgs {
@@ -264,7 +263,8 @@ __device__ __forceinline__ uint32_t select_word(const uint32_t (&key)[kPer], uin
 __device__ __forceinline__ int32_t table_loc(const TopkArgs& a, int row, int32_t p) {
   if (a.mode == HISPARSE_INDEX_RAGGED) return a.row_offsets[row] + p;
   const int j = p / a.page_size;
-  const int32_t page = j < a.pt_stride ? a.page_table[static_cast<size_t>(row) * a.pt_stride + j] : -1;
+  const int32_t page =
+      p >= 0 && j < a.pt_stride ? a.page_table[static_cast<size_t>(row) * a.pt_stride + j] : -1;
   if (page < 0) {
     raise_error(a.err, HISPARSE_ERR_BAD_INDEX);
     return -1;
@@ -407,24 +407,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))
 void topk_chunk_kernel(TopkArgs a) {
   __shared__ Lds s;
   const TopkPlan p = topk_plan_layout(a.batch, a.max_items);
-  const int w = blockIdx.x;
-  if (w >= a.plan[0]) return;
+  const int w = blockIdx.x;  // < max_items: its item slot lies in the plan
   const int tid = threadIdx.x;
-  TOPK_CLOCK(0);
+  // Two rounds of dependent loads before the scores: the item count and this
+  // workgroup's item together, then the row's length and chunk count
+  // together with its scores (a rejected row has an empty item, so its
+  // score loads read nothing).  The LDS clears go out meanwhile.
+  const int n_items = a.plan[0];
   const int32_t* item = a.plan + p.items + 4 * w;
-  const int row = item[0], start = item[2], len = item[3];
-  const int n_chunks = a.plan[p.row_info + 2 * row + 1];
-  if (row_rejected(a, row)) {  // one empty chunk
-    if (tid == 0) raise_error(a.err, HISPARSE_ERR_BAD_ROW);
-    for (int i = tid; i < a.k; i += kThreads) {
-      a.indices[static_cast<size_t>(row) * a.k + i] = -1;
-      if (a.locs) a.locs[static_cast<size_t>(row) * a.k + i] = -1;
-    }
-    return;
-  }
-
-  // keys of this thread's slots (positions start + slot), first-digit
-  // histogram as they arrive
+  const int row = item[0], start = item[2], item_len = item[3];
   for (int i = tid; i < kBins; i += kThreads) {
     s.hist[i] = 0u;
     s.hist1[i] = 0u;
@@ -433,30 +424,53 @@ void topk_chunk_kernel(TopkArgs a) {
   s.gt_bits[tid] = 0u;  // one word per thread
   s.eq_bits[tid] = 0u;
   if (tid == 0) s.list_count = 0;
-  __syncthreads();
-  uint32_t key[kPer];
+  if (w >= n_items) return;
+  TOPK_CLOCK(0);
+  // an item outside these sizes (a plan made for other sizes): nothing read
+  if (row < 0 || row >= a.batch || start < 0 || start > a.max_len) {
+    if (tid == 0) raise_error(a.err, HISPARSE_ERR_BAD_PLAN);
+    return;
+  }
+  const int len = max(0, min(item_len, a.max_len - start));
+  const int seq = a.seq_lens[row];
+  const int n_chunks = a.plan[p.row_info + 2 * row + 1];
+  // This thread's scores (positions start + slot), read by buffer loads
+  // with no per-lane branch, so all of a thread's loads are in flight at
+  // once (a lane-dependent branch around each load made every one wait for
+  // the previous): the buffer covers the chunk, a dword past it reads as
+  // zero, and slots past `len` are masked.  One dword load per slot; the
+  // compiler merges each thread's four consecutive slots into one 16-byte
+  // load.
+  const float* src = a.logits + static_cast<size_t>(row) * a.max_len + start;
+  float x[kPer];
   {
-    const float* src = a.logits + static_cast<size_t>(row) * a.max_len + start;
-    const bool vec = (reinterpret_cast<uintptr_t>(src) & 15u) == 0u;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(src), 0, 4 * len, 0x00020000);
 #pragma unroll
-    for (int v = 0; v < kPer / 4; ++v) {
-      const int i0 = slot_of(4 * v);
-      if (vec && i0 + 3 < len) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(src + i0);
+    for (int e = 0; e < kPer; ++e)
+      x[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * slot_of(e), 0, 0));
+  }
+  // a chunk count no plan for these sizes has (a split row needs the
+  // candidate workspace)
+  if (n_chunks < 1 || n_chunks > kTopkMaxChunks || (n_chunks > 1 && a.cand_key == nullptr)) {
+    if (tid == 0) raise_error(a.err, HISPARSE_ERR_BAD_PLAN);
+    return;
+  }
+  // a rejected row keeps no position: its outputs are all -1
+  const bool rejected = seq < 0 || seq > a.max_len;
+  if (rejected && tid == 0) raise_error(a.err, HISPARSE_ERR_BAD_ROW);
+  const int kept_len = rejected ? 0 : len;
+  __syncthreads();  // histogram cleared
+  // keys and the first-digit histogram as the scores arrive
+  uint32_t key[kPer];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) key[4 * v + j] = score_key(x[j]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) key[4 * v + j] = i0 + j < len ? score_key(src[i0 + j]) : 0u;
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (key[4 * v + j] != 0u) atomicAdd(&s.hist[key[4 * v + j] >> 20], 1u);
-    }
+  for (int e = 0; e < kPer; ++e) {
+    key[e] = slot_of(e) < kept_len ? score_key(x[e]) : 0u;
+    if (key[e] != 0u) atomicAdd(&s.hist[key[e] >> 20], 1u);
   }
   __syncthreads();
   TOPK_CLOCK(1);
-  const int kk = min(a.k, len);
+  const int kk = min(a.k, kept_len);
   uint32_t T = 0u, kept = 0u;
   int need = 0, offset = 0;
   if (kk > 0) {
@@ -486,7 +500,6 @@ void topk_chunk_kernel(TopkArgs a) {
       cp[o] = start + static_cast<int>(s.list[o]);
     }
   } else {  // the keys of the kept slots are read again (L2)
-    const float* src = a.logits + static_cast<size_t>(row) * a.max_len + start;
     for (uint32_t r = kept; r != 0u; r &= r - 1u) {
       const int i = 32 * tid + __builtin_ctz(r);
       ck[offset] = score_key(src[i]);
@@ -505,16 +518,22 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
   const TopkPlan p = topk_plan_layout(a.batch, a.max_items);
   const int row = blockIdx.x;
   const int n_chunks = a.plan[p.row_info + 2 * row + 1];
-  if (n_chunks == 1 || row_rejected(a, row)) return;
   const int first = a.plan[p.row_info + 2 * row];
+  if (n_chunks == 1 || row_rejected(a, row)) return;
   const int tid = threadIdx.x;
+  // a row entry outside these sizes (a plan made for other sizes)
+  if (n_chunks < 1 || n_chunks > kTopkMaxChunks || n_chunks * a.k > kTopkMaxCandidates ||
+      first < 0 || first > a.max_items - n_chunks) {
+    if (tid == 0) raise_error(a.err, HISPARSE_ERR_BAD_PLAN);
+    return;
+  }
   // one barrier publishes the chunk offsets and the cleared histograms and
   // bitmaps
   if (tid == 0) {
     int acc = 0;
     for (int c = 0; c < n_chunks; ++c) {
       s.offs[c] = acc;
-      acc += a.cand_cnt[first + c];
+      acc += min(max(a.cand_cnt[first + c], 0), a.k);  // (a count is at most k)
     }
     s.offs[n_chunks] = acc;
   }

@@ -182,3 +182,36 @@ def test_rejects_bad_arguments():
     with pytest.raises(binding.HiSparseError) as e:
         b.build(lg, sl, idx, None, mode="paged")               # paged without a table
     assert e.value.code == binding.HISPARSE_E_INVAL
+
+
+def test_plan_made_for_other_sizes_is_rejected():
+    """A plan built for other sizes: its entries outside this call's batch,
+    row length or plan, and split rows without a candidate workspace, raise
+    ERR_BAD_PLAN on the device and read nothing outside the buffers."""
+    rng = np.random.default_rng(11)
+    # (a) a plan of 4 rows x 100000 handed to 2 rows x 1000 (no workspace)
+    log("topk plan for other sizes: 4x100000 plan, 2x1000 call")
+    big = binding.TopkIndexBuilder(4, 100000, 16, device=DEV)
+    big.plan(torch.full((4,), 100000, dtype=torch.int32, device=DEV))
+    small = binding.TopkIndexBuilder(2, 1000, 16, device=DEV)
+    small.plan_buf = big.plan_buf
+    lg = torch.from_numpy(rng.standard_normal((2, 1000)).astype(np.float32)).to(DEV)
+    idx = torch.empty((2, 16), dtype=torch.int32, device=DEV)
+    small.build(lg, torch.full((2,), 1000, dtype=torch.int32, device=DEV), idx)
+    torch.cuda.synchronize()
+    assert small.error_flags() & binding.ERR_BAD_PLAN
+    # (b) a plan of 2 rows x 100000 (4 chunks each) handed to 2 rows x 40000
+    # (2 chunks each): chunks past the row length and the second row's merge
+    # entry are rejected
+    log("topk plan for other sizes: 2x100000 plan, 2x40000 call")
+    big = binding.TopkIndexBuilder(2, 100000, 16, device=DEV)
+    big.plan(torch.full((2,), 100000, dtype=torch.int32, device=DEV))
+    mid = binding.TopkIndexBuilder(2, 40000, 16, device=DEV)
+    mid.plan_buf = big.plan_buf
+    lg = torch.from_numpy(rng.standard_normal((2, 40000)).astype(np.float32)).to(DEV)
+    idx = torch.empty((2, 16), dtype=torch.int32, device=DEV)
+    mid.build(lg, torch.full((2,), 40000, dtype=torch.int32, device=DEV), idx)
+    torch.cuda.synchronize()
+    assert mid.error_flags() & binding.ERR_BAD_PLAN
+    # a plan made for the call's sizes: exact again, no error
+    run(lg.cpu().numpy(), [40000, 40000], 16)
