@@ -158,20 +158,36 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
-// Token row of location `loc` of batch row b, or -1.
-__device__ __forceinline__ int64_t token_row(const MlaArgs& a, int b, int32_t loc) {
-  if (loc < 0) return -1;
-  int64_t row;
+// Token rows of this thread's locations (-1: skipped or out of range).
+// Token rows are the locations themselves; in page mode every page-table
+// load goes out before the first is used (a buffer load per location with
+// no per-lane branch: a location whose page index lies outside the row's
+// table reads past the buffer, which returns zero, and is masked), so the
+// lookups cost one round trip rather than one each.
+template <int kN>
+__device__ __forceinline__ void token_rows(const MlaArgs& a, int b, const int32_t (&loc)[kN],
+                                           int64_t (&row)[kN]) {
   if (a.page_table == nullptr) {
-    row = loc;
-  } else {
-    const int j = loc / a.page_size;
-    if (j >= a.pt_stride) return -1;
-    const int32_t page = a.page_table[static_cast<size_t>(b) * a.pt_stride + j];
-    if (page < 0) return -1;
-    row = static_cast<int64_t>(page) * a.page_size + (loc - j * a.page_size);
+#pragma unroll
+    for (int k = 0; k < kN; ++k) row[k] = loc[k] >= 0 && loc[k] < a.kv_rows ? loc[k] : -1;
+    return;
   }
-  return row < a.kv_rows ? row : -1;
+  const __amdgpu_buffer_rsrc_t pt = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(a.page_table + static_cast<size_t>(b) * a.pt_stride), 0,
+      4 * a.pt_stride, 0x00020000);
+  int32_t page[kN];
+#pragma unroll
+  for (int k = 0; k < kN; ++k) {
+    const int j = loc[k] >= 0 ? loc[k] / a.page_size : a.pt_stride;
+    page[k] = static_cast<int32_t>(__builtin_amdgcn_raw_buffer_load_b32(
+        pt, 4 * (j < a.pt_stride ? j : a.pt_stride), 0, 0));
+  }
+#pragma unroll
+  for (int k = 0; k < kN; ++k) {
+    const int j = loc[k] >= 0 ? loc[k] / a.page_size : a.pt_stride;
+    const int64_t r = static_cast<int64_t>(page[k]) * a.page_size + (loc[k] - j * a.page_size);
+    row[k] = j < a.pt_stride && page[k] >= 0 && r < a.kv_rows ? r : -1;
+  }
 }
 
 // This wave's share of the loads of tile rows [t0, t0 + 32) straight into
@@ -368,8 +384,7 @@ void mla_decode(MlaArgs a) {
   }
 
   int64_t rowv[kRowIters];
-#pragma unroll
-  for (int k = 0; k < kRowIters; ++k) rowv[k] = token_row(a, b, locv[k]);
+  token_rows(a, b, locv, rowv);
   bool bad = false;
 #pragma unroll
   for (int k = 0; k < kRowIters; ++k) {

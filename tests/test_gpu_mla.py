@@ -129,6 +129,12 @@ def test_mla_page_mode(item):
     run_case(R=3, B=3, H=40, K=200, N=16 * 64, item=item, heads=32, P=16, seed=item + 2)
 
 
+def test_mla_page_mode_full_location_table():
+    """2048 locations per row through the page table (64-token pages, 32 hot
+    pages): every page-table lookup of a workgroup's location range."""
+    run_case(R=4, B=4, H=32, K=2048, N=4096, item=1152, heads=64, P=64, seed=64)
+
+
 @pytest.mark.parametrize("item", [1152, 656])
 def test_mla_replay_after_large_score_jump(item):
     """Rows far above the first tile's scores (latent x2000, then x5000) in
