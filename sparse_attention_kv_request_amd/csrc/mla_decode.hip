@@ -769,8 +769,13 @@ void mla_decode(MlaArgs a) {
 
 // Merges the splits of every (row, head) by their log-sum-exp: 64 lanes per
 // head, 8 dims (one 16-byte fp16 load per split) per lane, 4 heads per
-// workgroup.
+// workgroup.  kMaxS > 0 (at most kMaxS splits): every split's record and
+// this lane's 16 bytes of it are loaded before any is used, with no branch
+// between the loads (split indices past the last repeat it and are then
+// skipped), so the merge waits for memory once; kMaxS = 0 loops over any
+// number of splits.  Both add the same terms in the same order.
 constexpr int kCombineHeads = 4;
+template <int kMaxS>
 __global__ __launch_bounds__(kCombineHeads * kWave) void mla_combine(MlaArgs a) {
   const int bh = blockIdx.x * kCombineHeads + static_cast<int>(threadIdx.x / kWave);
   if (bh >= a.batch * a.heads) return;
@@ -778,28 +783,52 @@ __global__ __launch_bounds__(kCombineHeads * kWave) void mla_combine(MlaArgs a) 
   const int b = bh / a.heads, h = bh - b * a.heads;
   const size_t ps0 = static_cast<size_t>(b) * a.splits * a.heads + h;  // split s: ps0 + s*heads
   float big = -INFINITY;
-  for (int s = 0; s < a.splits; ++s) {
-    const size_t ps = ps0 + static_cast<size_t>(s) * a.heads;
-    const f32x4 ml = *reinterpret_cast<const f32x4*>(a.part_ml + 8 * ps);
-    if (ml[1] > 0.f) big = fmaxf(big, ml[0] + log2f(ml[1]));
-  }
   float wsum = 0.f;
   f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < a.splits; ++s) {
-    const size_t ps = ps0 + static_cast<size_t>(s) * a.heads;
-    const f32x4 ml = *reinterpret_cast<const f32x4*>(a.part_ml + 8 * ps);  // m, l
-    if (!(ml[1] > 0.f)) continue;
+  // split s's term; e: the exponent its 32-dim block is stored scaled by
+  auto add = [&](f32x4 ml, int e, u32x4 raw) {
     const float w = exp2f(ml[0] + log2f(ml[1]) - big);
     wsum += w;
-    // this lane's 8 dims lie in 32-dim block lane / 4, stored scaled by 2^-e
-    const int e = static_cast<int8_t>(
-        reinterpret_cast<const uint8_t*>(a.part_ml + 8 * ps + 4)[lane >> 2]);
     const float wo = __builtin_amdgcn_ldexpf(w, e);
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(a.part_out + ps * kLatent + 8 * lane);
     const f16x4 lo = __builtin_bit_cast(f16x4, u32x2{raw[0], raw[1]});
     const f16x4 hi = __builtin_bit_cast(f16x4, u32x2{raw[2], raw[3]});
     o0 += wo * __builtin_convertvector(lo, f32x4);
     o1 += wo * __builtin_convertvector(hi, f32x4);
+  };
+  // this lane's 8 dims lie in 32-dim block lane / 4: byte lane / 4 of the
+  // record's exponents, i.e. byte (lane / 4) % 4 of exponent word lane / 16
+  const int ebyte = 8 * ((lane >> 2) & 3);
+  if constexpr (kMaxS > 0) {
+    f32x4 ml[kMaxS];
+    uint32_t ew[kMaxS];
+    u32x4 raw[kMaxS];
+#pragma unroll
+    for (int s = 0; s < kMaxS; ++s) {
+      const size_t ps = ps0 + static_cast<size_t>(s < a.splits ? s : a.splits - 1) * a.heads;
+      ml[s] = *reinterpret_cast<const f32x4*>(a.part_ml + 8 * ps);  // m, l
+      ew[s] = reinterpret_cast<const uint32_t*>(a.part_ml + 8 * ps + 4)[lane >> 4];
+      raw[s] = *reinterpret_cast<const u32x4*>(a.part_out + ps * kLatent + 8 * lane);
+    }
+#pragma unroll
+    for (int s = 0; s < kMaxS; ++s)
+      if (s < a.splits && ml[s][1] > 0.f) big = fmaxf(big, ml[s][0] + log2f(ml[s][1]));
+#pragma unroll
+    for (int s = 0; s < kMaxS; ++s)
+      if (s < a.splits && ml[s][1] > 0.f) add(ml[s], static_cast<int8_t>(ew[s] >> ebyte), raw[s]);
+  } else {
+    for (int s = 0; s < a.splits; ++s) {
+      const size_t ps = ps0 + static_cast<size_t>(s) * a.heads;
+      const f32x4 ml = *reinterpret_cast<const f32x4*>(a.part_ml + 8 * ps);
+      if (ml[1] > 0.f) big = fmaxf(big, ml[0] + log2f(ml[1]));
+    }
+    for (int s = 0; s < a.splits; ++s) {
+      const size_t ps = ps0 + static_cast<size_t>(s) * a.heads;
+      const f32x4 ml = *reinterpret_cast<const f32x4*>(a.part_ml + 8 * ps);
+      if (!(ml[1] > 0.f)) continue;
+      const uint32_t ew = reinterpret_cast<const uint32_t*>(a.part_ml + 8 * ps + 4)[lane >> 4];
+      add(ml, static_cast<int8_t>(ew >> ebyte),
+          *reinterpret_cast<const u32x4*>(a.part_out + ps * kLatent + 8 * lane));
+    }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   float* dst = a.out + static_cast<size_t>(bh) * kLatent + 8 * lane;
@@ -864,8 +893,13 @@ hipError_t launch_mla_decode(const MlaDecodeCall& c, hipStream_t s) {
     hipLaunchKernelGGL(mla_decode<true>, dim3(grid), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
-  hipLaunchKernelGGL(mla_combine, dim3((c.batch * c.heads + kCombineHeads - 1) / kCombineHeads),
-                     dim3(kCombineHeads * kWave), 0, s, a);
+  const dim3 cgrid((c.batch * c.heads + kCombineHeads - 1) / kCombineHeads);
+  if (a.splits <= 4)
+    hipLaunchKernelGGL(mla_combine<4>, cgrid, dim3(kCombineHeads * kWave), 0, s, a);
+  else if (a.splits <= 8)
+    hipLaunchKernelGGL(mla_combine<8>, cgrid, dim3(kCombineHeads * kWave), 0, s, a);
+  else
+    hipLaunchKernelGGL(mla_combine<0>, cgrid, dim3(kCombineHeads * kWave), 0, s, a);
   return hipGetLastError();
 }
 
