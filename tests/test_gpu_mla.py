@@ -198,7 +198,7 @@ def _random_case(case):
                 boost=boost or None)
 
 
-@pytest.mark.parametrize("case", range(16))
+@pytest.mark.parametrize("case", range(24))
 def test_mla_random_shapes(case):
     """Seeded random shapes, split counts and replays, against the oracle."""
     kw = _random_case(case)

@@ -146,7 +146,7 @@ def _random_topk_case(case):
                 layers=int(rng.integers(1, 3)))
 
 
-@pytest.mark.parametrize("case", range(12))
+@pytest.mark.parametrize("case", range(40))
 def test_random_shapes(case):
     c = _random_topk_case(case)
     log(f"topk random case {case}: {c}")
