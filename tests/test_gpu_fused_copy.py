@@ -34,7 +34,7 @@ def _lru_case(case):
                 pad=float(rng.choice([0.0, 0.02])), bad=float(rng.choice([0.0, 0.01])))
 
 
-@pytest.mark.parametrize("case", range(6))
+@pytest.mark.parametrize("case", range(16))
 def test_fused_lru_random(case):
     c = _lru_case(case)
     log(f"fused lru case {case}: {c}")

@@ -86,7 +86,7 @@ def _random_lru_case(case):
                 bad=float(rng.choice([0.0, 0.0, 0.01])))
 
 
-@pytest.mark.parametrize("case", range(12))
+@pytest.mark.parametrize("case", range(32))
 def test_lru_token_random_shapes(case):
     c = _random_lru_case(case)
     log(f"lru token random case {case}: {c}")
@@ -190,7 +190,7 @@ def _random_clock_case(case):
                 extra=int(rng.choice([0, 0, 16])))
 
 
-@pytest.mark.parametrize("case", range(10))
+@pytest.mark.parametrize("case", range(24))
 def test_clock_random_shapes(case):
     c = _random_clock_case(case)
     log(f"clock random case {case}: {c}")
@@ -225,7 +225,7 @@ def _random_page_case(case):
                 I=int(rng.choice([16, 32])), R=int(rng.integers(1, 5)))
 
 
-@pytest.mark.parametrize("case", range(8))
+@pytest.mark.parametrize("case", range(24))
 def test_lru_page_random_shapes(case):
     c = _random_page_case(case)
     log(f"page random case {case}: {c}")
