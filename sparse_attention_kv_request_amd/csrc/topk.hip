@@ -174,7 +174,8 @@ __device__ __forceinline__ void pick_bin(Lds& s, const uint32_t* hist, int bins,
 // kk >= 1, at most the number of present keys): T and the number `need` of
 // keys equal to T to keep.  The first-digit histogram is built by the
 // caller (hist0) while the keys are loaded.
-__device__ __forceinline__ void radix_threshold(const uint32_t (&key)[kPer], int kk, Lds& s,
+template <int N>
+__device__ __forceinline__ void radix_threshold(const uint32_t (&key)[N], int kk, Lds& s,
                                                 uint32_t& T, int& need) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   uint32_t b0;
@@ -188,7 +189,7 @@ __device__ __forceinline__ void radix_threshold(const uint32_t (&key)[kPer], int
   // reserves the wave's room
   uint32_t cnt = 0u;
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) cnt += key[e] != 0u && (key[e] >> 20) == b0;
+  for (int e = 0; e < N; ++e) cnt += key[e] != 0u && (key[e] >> 20) == b0;
   const uint32_t incl = wave_incl_scan(cnt);
   const uint32_t wave_total = __builtin_amdgcn_readlane(incl, kWave - 1);
   if (wave_total > 0u) {
@@ -196,7 +197,7 @@ __device__ __forceinline__ void radix_threshold(const uint32_t (&key)[kPer], int
     if (lane == kWave - 1) base = atomicAdd(reinterpret_cast<uint32_t*>(&s.list_count), wave_total);
     int at = static_cast<int>(__builtin_amdgcn_readlane(base, kWave - 1) + incl - cnt);
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) {
+    for (int e = 0; e < N; ++e) {
       if (key[e] != 0u && (key[e] >> 20) == b0) {
         if (at < kListCap) s.list[at] = key[e];
         ++at;
@@ -219,7 +220,7 @@ __device__ __forceinline__ void radix_threshold(const uint32_t (&key)[kPer], int
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < kPer; ++e)
+      for (int e = 0; e < N; ++e)
         if (key[e] != 0u && (key[e] & pm) == prefix) atomicAdd(&hist[digit(key[e], pass)], 1u);
     }
     __syncthreads();
@@ -237,12 +238,13 @@ __device__ __forceinline__ void radix_threshold(const uint32_t (&key)[kPer], int
 // (count > T, count == T) per word gives, in slot order, the output offset of
 // the word's first kept slot; ties are kept while their rank is below
 // `need`.  Returns the word's kept bits and its output offset.
-__device__ __forceinline__ uint32_t select_word(const uint32_t (&key)[kPer], uint32_t T, int need,
+template <int N>
+__device__ __forceinline__ uint32_t select_word(const uint32_t (&key)[N], uint32_t T, int need,
                                                 Lds& s, int& offset) {
   const int tid = threadIdx.x;
   // (the bitmaps were cleared at kernel start)
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) {
+  for (int e = 0; e < N; ++e) {
     if (key[e] >= T) {
       const int i = slot_of(e);
       atomicOr(key[e] > T ? &s.gt_bits[i >> 5] : &s.eq_bits[i >> 5], 1u << (i & 31));
@@ -299,14 +301,15 @@ constexpr int kStageCap = kListCap < kBins ? kListCap : kBins;
 // s.hist[o] = key of the o-th output.  Word w's kept bits and output offset
 // (thread w's select_word result) go through the bitmap arrays; each slot's
 // owner, which holds its key, places it.  kk <= kStageCap.
-__device__ __forceinline__ void stage_kept(const uint32_t (&key)[kPer], uint32_t kept, int offset,
+template <int N>
+__device__ __forceinline__ void stage_kept(const uint32_t (&key)[N], uint32_t kept, int offset,
                                            Lds& s) {
   const int tid = threadIdx.x;
   s.gt_bits[tid] = kept;
   s.eq_bits[tid] = static_cast<uint32_t>(offset);
   __syncthreads();
 #pragma unroll
-  for (int v = 0; v < kPer / 4; ++v) {  // slots i0 .. i0 + 3 share a bitmap word
+  for (int v = 0; v < N / 4; ++v) {  // slots i0 .. i0 + 3 share a bitmap word
     const int i0 = slot_of(4 * v);
     const uint32_t wv = s.gt_bits[i0 >> 5];
     const uint32_t sh = static_cast<uint32_t>(i0 & 31);
@@ -512,7 +515,11 @@ void topk_chunk_kernel(TopkArgs a) {
 
 // One workgroup per row: rows of several chunks select their top-k from the
 // chunks' candidates, which are in position order (chunk order, ascending
-// within a chunk).
+// within a chunk).  N candidate slots per thread: the launch takes the
+// smallest N in {8, 16, 32} whose N x 1024 slots hold every candidate a row
+// of max_len can have (4 chunks of top-2048: 8192 candidates, N = 8), so the
+// per-slot work scales with the candidates rather than a full chunk.
+template <int N>
 __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
   __shared__ Lds s;
   const TopkPlan p = topk_plan_layout(a.batch, a.max_items);
@@ -522,7 +529,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
   if (n_chunks == 1 || row_rejected(a, row)) return;
   const int tid = threadIdx.x;
   // a row entry outside these sizes (a plan made for other sizes)
-  if (n_chunks < 1 || n_chunks > kTopkMaxChunks || n_chunks * a.k > kTopkMaxCandidates ||
+  if (n_chunks < 1 || n_chunks > kTopkMaxChunks || n_chunks * a.k > N * kThreads ||
       first < 0 || first > a.max_items - n_chunks) {
     if (tid == 0) raise_error(a.err, HISPARSE_ERR_BAD_PLAN);
     return;
@@ -547,38 +554,38 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
   if (tid == 0) s.list_count = 0;
   __syncthreads();
   const int M = s.offs[n_chunks];
-  // candidate i sits in chunk c with offs[c] <= i < offs[c + 1]
-  auto cand_at = [&](int i) {
-    int c = 0;
-    while (c + 1 < n_chunks && s.offs[c + 1] <= i) ++c;
-    return static_cast<size_t>(first + c) * a.k + (i - s.offs[c]);
+  // candidate i sits in chunk c, the last with offs[c] <= i (binary search);
+  // its index relative to the row's first chunk
+  auto rel_at = [&](int i) {
+    int lo = 0, hi = n_chunks - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s.offs[mid] <= i) lo = mid;
+      else hi = mid - 1;
+    }
+    return lo * a.k + (i - s.offs[lo]);
   };
-  // slots i0 .. i0 + 3 usually sit in one chunk (chunk candidate counts are
-  // k or a chunk's length, multiples of 4 except at a row's end): one 16-byte
-  // load then, else one load per slot
-  uint32_t key[kPer];
-  const bool vec4 = (a.k & 3) == 0 && (reinterpret_cast<uintptr_t>(a.cand_key) & 15u) == 0u;
+  auto cand_at = [&](int i) { return static_cast<size_t>(first) * a.k + rel_at(i); };
+  // Every slot's key is loaded before any is used: buffer loads over the
+  // row's candidates with no per-lane branch; a slot past M reads past the
+  // buffer, i.e. key 0, absent.
+  uint32_t key[N];
+  {
+    const uint32_t range = 4u * static_cast<uint32_t>(n_chunks * a.k);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        a.cand_key + static_cast<size_t>(first) * a.k, 0, static_cast<int>(range), 0x00020000);
+    int off[N];
 #pragma unroll
-  for (int v = 0; v < kPer / 4; ++v) {
-    const int i0 = slot_of(4 * v);
-    if (i0 >= M) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) key[4 * v + j] = 0u;
-      continue;
-    }
-    const size_t c0 = cand_at(i0);
-    if (vec4 && i0 + 3 < M && cand_at(i0 + 3) == c0 + 3 && (c0 & 3) == 0) {
-      const u32x4 x = *reinterpret_cast<const u32x4*>(a.cand_key + c0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) key[4 * v + j] = x[j];
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) key[4 * v + j] = i0 + j < M ? a.cand_key[cand_at(i0 + j)] : 0u;
+    for (int e = 0; e < N; ++e) {
+      const int i = slot_of(e);
+      off[e] = i < M ? 4 * rel_at(i) : static_cast<int>(range);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (key[4 * v + j] != 0u) atomicAdd(&s.hist[key[4 * v + j] >> 20], 1u);
+    for (int e = 0; e < N; ++e) key[e] = __builtin_amdgcn_raw_buffer_load_b32(rs, off[e], 0, 0);
   }
+#pragma unroll
+  for (int e = 0; e < N; ++e)
+    if (key[e] != 0u) atomicAdd(&s.hist[key[e] >> 20], 1u);
   __syncthreads();
   const int kf = min(a.k, M);
   uint32_t T = 0u, w = 0u;
@@ -670,7 +677,14 @@ hipError_t launch_topk_index_build(const hisparse_topk_call_t& c, hipStream_t st
   hipLaunchKernelGGL(topk_chunk_kernel, dim3(a.max_items), dim3(kThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_items == a.batch) return e;  // no row can be split
-  hipLaunchKernelGGL(topk_merge_kernel, dim3(a.batch), dim3(kThreads), 0, st, a);
+  // candidate slots per merge thread: the most a row of max_len can have
+  const int most = topk_chunks(c.max_len) * c.k;
+  if (most <= 8 * kThreads)
+    hipLaunchKernelGGL(topk_merge_kernel<8>, dim3(a.batch), dim3(kThreads), 0, st, a);
+  else if (most <= 16 * kThreads)
+    hipLaunchKernelGGL(topk_merge_kernel<16>, dim3(a.batch), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(topk_merge_kernel<32>, dim3(a.batch), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -215,3 +215,14 @@ def test_plan_made_for_other_sizes_is_rejected():
     assert mid.error_flags() & binding.ERR_BAD_PLAN
     # a plan made for the call's sizes: exact again, no error
     run(lg.cpu().numpy(), [40000, 40000], 16)
+
+
+@pytest.mark.parametrize("N,k", [(70000, 2000), (3 * 32768 + 100, 3000), (8 * 32768, 4000)])
+def test_merge_slot_counts(N, k):
+    """Split rows whose most candidates per row (chunks x k: 6000, 12000,
+    32000) take the merge's 8, 16 and 32 slots per thread; rows of every
+    chunk count up to the longest, ties across chunks."""
+    rng = np.random.default_rng(N + k)
+    lg = logits_with_specials(rng, 3, N, ties=True)
+    log(f"topk merge slots: N={N} k={k}")
+    run(lg, [N, N // 2 + 1, 32769], k, mode="ragged", row_offsets=[0, N, 2 * N])
