@@ -119,6 +119,13 @@ def test_mla_token_rows_large_batch(item):
     run_case(R=40, B=40, H=600, K=300, N=1500, item=item, heads=64, seed=item + 1, calls=1)
 
 
+@pytest.mark.parametrize("heads,B,K", [(200, 5, 300), (256, 2, 1000), (384, 3, 130)])
+def test_mla_several_head_groups(heads, B, K):
+    """More than 128 heads: several head groups per row (the last one partial
+    for 200), split and unsplit rows."""
+    run_case(R=B + 1, B=B, H=max(K, 256), K=K, N=K + 300, item=1152, heads=heads, seed=heads + B)
+
+
 def test_mla_ragged_heads_and_locations():
     """Heads not a multiple of 16 and a location count not a multiple of 32."""
     run_case(R=4, B=3, H=128, K=77, N=500, item=1152, heads=24, seed=5)
