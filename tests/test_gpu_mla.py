@@ -126,6 +126,14 @@ def test_mla_several_head_groups(heads, B, K):
     run_case(R=B + 1, B=B, H=max(K, 256), K=K, N=K + 300, item=1152, heads=heads, seed=heads + B)
 
 
+def test_mla_long_location_lists():
+    """8000 locations per row over 128 rows: the split count comes from the
+    2048-location cap per workgroup (4 splits of 2000, not the 2 that fill the
+    CUs); sampled rows against the oracle."""
+    run_case(R=128, B=128, H=8192, K=8000, N=8300, item=1152, heads=16, seed=8000, calls=1,
+             check_rows=[0, 77, 127])
+
+
 def test_mla_ragged_heads_and_locations():
     """Heads not a multiple of 16 and a location count not a multiple of 32."""
     run_case(R=4, B=3, H=128, K=77, N=500, item=1152, heads=24, seed=5)
