@@ -35,9 +35,12 @@
 // phase_clocks.py): in the bf16 tile loop every wave of the last launch
 // stores the shader clocks it spent waiting for a tile's gather, at the
 // phase barriers and in the whole loop (hisparse_attention_wait_clocks()),
-// and every workgroup the 100 MHz wall clock at its start, at the first
-// tile's barrier, after the tile loop and at its end
-// (hisparse_attention_phase_clocks()).  The default build records nothing.
+// and every workgroup the 100 MHz wall clock at its start (stamp 0), at the
+// first tile's barrier (1), after the tile loop (2), at its end (3), and in
+// the setup once its rows are computed from the locations (6), after the row
+// table's barrier (4) and once the queries and the first tile have landed
+// in its first wave (5, bf16 rows) (hisparse_attention_phase_clocks()).  The
+// default build records nothing.
 #ifndef HISPARSE_PHASE_CLOCKS
 #define HISPARSE_PHASE_CLOCKS 0
 #endif
@@ -50,14 +53,15 @@ extern "C" int hisparse_attention_wait_clocks(unsigned long long* out_h, int n) 
                  hipSuccess
              ? 0 : -1;
 }
-__device__ long long g_attn_stamp[kAttnClockRows * 4];
+constexpr int kAttnStamps = 7;
+__device__ long long g_attn_stamp[kAttnClockRows * kAttnStamps];
 #define ATTN_CLOCK(i)                                                            \
   do {                                                                          \
     if (threadIdx.x == 0 && blockIdx.x < kAttnClockRows)                        \
-      g_attn_stamp[blockIdx.x * 4 + (i)] = wall_clock64();                      \
+      g_attn_stamp[blockIdx.x * kAttnStamps + (i)] = wall_clock64();            \
   } while (0)
 extern "C" int hisparse_attention_phase_clocks(long long* out_h, int n) {
-  if (n < 0 || n > kAttnClockRows * 4) return -1;
+  if (n < 0 || n > kAttnClockRows * kAttnStamps) return -1;
   return hipMemcpyFromSymbol(out_h, HIP_SYMBOL(g_attn_stamp), n * sizeof(long long)) == hipSuccess
              ? 0 : -1;
 }
@@ -385,6 +389,7 @@ void mla_decode(MlaArgs a) {
 
   int64_t rowv[kRowIters];
   token_rows(a, b, locv, rowv);
+  ATTN_CLOCK(6);
   bool bad = false;
 #pragma unroll
   for (int k = 0; k < kRowIters; ++k) {
@@ -398,6 +403,7 @@ void mla_decode(MlaArgs a) {
   if (bad) raise_error(a.err, HISPARSE_ERR_BAD_INDEX);
 
   __syncthreads();  // rows[] complete
+  ATTN_CLOCK(4);
 
   // O^T of the wave's 32 heads: block db holds dims 32 db + [0, 32); its
   // register j at lane l is dim 32 db + 8 (j/4) + 4 (l/32) + j%4 of head l%32
@@ -575,6 +581,7 @@ void mla_decode(MlaArgs a) {
     // and puts no waits for them inside the loop (where they would also wait
     // for the gather).
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    ATTN_CLOCK(5);
     int it = 0;          // tile in buffer `cur`
     bool fresh = false;  // this phase starts the sums over
 #if HISPARSE_PHASE_CLOCKS

@@ -37,28 +37,47 @@
 
 // Opt-in instrumentation, a separate build (-DHISPARSE_PHASE_CLOCKS=1, see
 // phase_clocks.py): each chunk workgroup records the 100 MHz wall clock at
-// its phase boundaries; hisparse_topk_phase_clocks() copies out the last
-// launch's stamps.  The default build records nothing.
+// its phase boundaries (stamps 0-5) and inside the threshold step (6: first
+// bin picked, 7: threshold-bin keys listed, 8: first list pass done), each
+// merge workgroup at its own (0: start, 1: offsets published, 2: keys and
+// histogram, 3: threshold, 4: selection, 5: staging, 6: end);
+// hisparse_topk_phase_clocks() and hisparse_topk_merge_phase_clocks() copy
+// out the last launch's stamps.  The default build records nothing.
 #ifndef HISPARSE_PHASE_CLOCKS
 #define HISPARSE_PHASE_CLOCKS 0
 #endif
 #if HISPARSE_PHASE_CLOCKS
 constexpr int kTopkClockRows = 4096;
-constexpr int kTopkStamps = 6;
+constexpr int kTopkStamps = 9;
+constexpr int kMergeStamps = 7;
 __device__ long long g_topk_clock[kTopkClockRows * kTopkStamps];
+__device__ long long g_merge_clock[kTopkClockRows * kMergeStamps];
 #define TOPK_CLOCK(i)                                                            \
   do {                                                                          \
     if (threadIdx.x == 0 && blockIdx.x < kTopkClockRows)                        \
       g_topk_clock[blockIdx.x * kTopkStamps + (i)] = wall_clock64();            \
+  } while (0)
+#define MERGE_CLOCK(i)                                                           \
+  do {                                                                          \
+    if (threadIdx.x == 0 && blockIdx.x < kTopkClockRows)                        \
+      g_merge_clock[blockIdx.x * kMergeStamps + (i)] = wall_clock64();          \
   } while (0)
 extern "C" int hisparse_topk_phase_clocks(long long* out_h, int n) {
   if (n < 0 || n > kTopkClockRows * kTopkStamps) return -1;
   return hipMemcpyFromSymbol(out_h, HIP_SYMBOL(g_topk_clock), n * sizeof(long long)) == hipSuccess
              ? 0 : -1;
 }
+extern "C" int hisparse_topk_merge_phase_clocks(long long* out_h, int n) {
+  if (n < 0 || n > kTopkClockRows * kMergeStamps) return -1;
+  return hipMemcpyFromSymbol(out_h, HIP_SYMBOL(g_merge_clock), n * sizeof(long long)) == hipSuccess
+             ? 0 : -1;
+}
 #else
 #define TOPK_CLOCK(i) \
   do {                \
+  } while (0)
+#define MERGE_CLOCK(i) \
+  do {                 \
   } while (0)
 #endif
 
@@ -174,13 +193,14 @@ __device__ __forceinline__ void pick_bin(Lds& s, const uint32_t* hist, int bins,
 // kk >= 1, at most the number of present keys): T and the number `need` of
 // keys equal to T to keep.  The first-digit histogram is built by the
 // caller (hist0) while the keys are loaded.
-template <int N>
+template <int N, class Stamp>
 __device__ __forceinline__ void radix_threshold(const uint32_t (&key)[N], int kk, Lds& s,
-                                                uint32_t& T, int& need) {
+                                                uint32_t& T, int& need, Stamp&& stamp) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   uint32_t b0;
   int above;
   pick_bin(s, s.hist, kBins, kk, b0, above);
+  stamp(6);
   int remaining = kk - above;
   uint32_t prefix = b0 << 20;
 
@@ -205,6 +225,7 @@ __device__ __forceinline__ void radix_threshold(const uint32_t (&key)[N], int kk
     }
   }
   __syncthreads();
+  stamp(7);
   const int m = s.list_count;
   const bool listed = m <= kListCap;
 #pragma unroll 1
@@ -228,6 +249,7 @@ __device__ __forceinline__ void radix_threshold(const uint32_t (&key)[N], int kk
     pick_bin(s, hist, bins, remaining, b, above);
     remaining -= above;
     prefix |= pass == 1 ? (b << 8) : b;
+    if (pass == 1) stamp(8);
   }
   T = prefix;
   need = remaining;
@@ -477,7 +499,7 @@ void topk_chunk_kernel(TopkArgs a) {
   uint32_t T = 0u, kept = 0u;
   int need = 0, offset = 0;
   if (kk > 0) {
-    radix_threshold(key, kk, s, T, need);
+    radix_threshold(key, kk, s, T, need, [](int i) { TOPK_CLOCK(i); });
     TOPK_CLOCK(2);
     kept = select_word(key, T, need, s, offset);
   }
@@ -528,6 +550,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
   const int first = a.plan[p.row_info + 2 * row];
   if (n_chunks == 1 || row_rejected(a, row)) return;
   const int tid = threadIdx.x;
+  MERGE_CLOCK(0);
   // a row entry outside these sizes (a plan made for other sizes)
   if (n_chunks < 1 || n_chunks > kTopkMaxChunks || n_chunks * a.k > N * kThreads ||
       first < 0 || first > a.max_items - n_chunks) {
@@ -553,6 +576,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
   s.eq_bits[tid] = 0u;
   if (tid == 0) s.list_count = 0;
   __syncthreads();
+  MERGE_CLOCK(1);
   const int M = s.offs[n_chunks];
   // candidate i sits in chunk c, the last with offs[c] <= i (binary search);
   // its index relative to the row's first chunk
@@ -587,19 +611,24 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(TopkArgs a) {
   for (int e = 0; e < N; ++e)
     if (key[e] != 0u) atomicAdd(&s.hist[key[e] >> 20], 1u);
   __syncthreads();
+  MERGE_CLOCK(2);
   const int kf = min(a.k, M);
   uint32_t T = 0u, w = 0u;
   int need = 0, offset = 0;
   if (kf > 0) {
-    radix_threshold(key, kf, s, T, need);
+    radix_threshold(key, kf, s, T, need, [](int) {});
+    MERGE_CLOCK(3);
     w = select_word(key, T, need, s, offset);
   }
+  MERGE_CLOCK(4);
   if (kf <= kStageCap) {
     if (kf > 0) stage_kept(key, w, offset, s);
+    MERGE_CLOCK(5);
     emit_staged(a, row, [&](int i) { return a.cand_pos[cand_at(i)]; }, s, kf);
   } else {
     emit_final(a, row, [&](int i) { return a.cand_pos[cand_at(i)]; }, w, offset, kf);
   }
+  MERGE_CLOCK(6);
 }
 
 }  // namespace

@@ -16,10 +16,14 @@ library and prints a markdown summary:
   (workgroup id mod 8), and the copy phase's rate;
 * the same kernel with 512 instances in one launch (the batched-state
   bench): when its workgroups start and how long each runs;
-* the top-k chunk kernel's phases (64 rows x 32768 scores);
-* the attention bench's bf16 calls: the kernel's setup, tile loop and
-  epilogue, and the share of each wave's tile-loop clocks spent waiting for
-  the next tile's gather and at the phase barrier.
+* the top-k chunk kernel's phases (64 rows x 32768 scores), with the
+  threshold step split into its first bin pick, the listing of that bin's
+  keys and the two list passes, and the merge kernel's phases (128 rows x
+  131072 scores);
+* the attention bench's bf16 calls: the kernel's setup (locations, row
+  table, queries and first tile), tile loop and epilogue, and the share of
+  each wave's tile-loop clocks spent waiting for the next tile's gather and
+  at the phase barrier.
 
 The clock reads add a few instructions per phase, so the absolute times run
 a little above the uninstrumented kernels'; the shares and the spread are
@@ -141,13 +145,35 @@ def _topk_phases(torch, binding, workloads, lib):
                               cpu_seconds=0)
     res = bench.topk_bench(args, torch, binding, workloads)
     n = res["config"]["batch"]
-    buf = np.zeros(n * 6, np.int64)
+    buf = np.zeros(n * 9, np.int64)
     if fn(buf.ctypes.data, buf.size) != 0:
         raise SystemExit("hisparse_topk_phase_clocks failed")
-    t = buf.reshape(n, 6)
+    # stamps in time order: 0, 1, then 6, 7, 8 inside the threshold, 2 .. 5
+    t = buf.reshape(n, 9)[:, [0, 1, 6, 7, 8, 2, 3, 4, 5]]
     return {"n": n, "us_per_call": res["roofline"]["us_per_call"],
             "phase_us": np.median(np.diff(t, axis=1), axis=0) * TICK_US,
-            "span_us": float((t[:, 5].max() - t[:, 0].min()) * TICK_US)}
+            "span_us": float((t[:, -1].max() - t[:, 0].min()) * TICK_US)}
+
+
+def _merge_phases(torch, binding, workloads, lib):
+    import numpy as np
+
+    import bench
+
+    fn = lib.hisparse_topk_merge_phase_clocks
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    args = argparse.Namespace(warmup=5, steps=20, workload=4, no_cpu_baseline=True,
+                              cpu_seconds=0)
+    res = bench.topk_bench(args, torch, binding, workloads)
+    n = res["config"]["batch"]
+    buf = np.zeros(n * 7, np.int64)
+    if fn(buf.ctypes.data, buf.size) != 0:
+        raise SystemExit("hisparse_topk_merge_phase_clocks failed")
+    t = buf.reshape(n, 7)
+    return {"n": n, "seq_len": res["config"]["seq_len"],
+            "us_per_call": res["roofline"]["us_per_call"],
+            "phase_us": np.median(np.diff(t, axis=1), axis=0) * TICK_US}
 
 
 def _attention_waits(torch, binding, workloads, lib):
@@ -169,15 +195,16 @@ def _attention_waits(torch, binding, workloads, lib):
     st = lib.hisparse_attention_phase_clocks
     st.restype = ctypes.c_int
     st.argtypes = [ctypes.c_void_p, ctypes.c_int]
-    buf = np.zeros(n * 4, np.int64)
+    buf = np.zeros(n * 7, np.int64)
     if st(buf.ctypes.data, buf.size) != 0:
         raise SystemExit("hisparse_attention_phase_clocks failed")
-    t = buf.reshape(n, 4)
+    # stamps in time order: 0, then 6, 4, 5 in the setup, 1, 2, 3
+    t = buf.reshape(n, 7)[:, [0, 6, 4, 5, 1, 2, 3]]
     return {"us_per_call": res["roofline"]["us_per_call"], "waves": waves,
             "gather_share": g / total, "barrier_share": b / total,
             "loop_clocks_per_wave": total / waves,
             "phase_us": np.median(np.diff(t, axis=1), axis=0) * TICK_US,
-            "span_us": float((t[:, 3].max() - t[:, 0].min()) * TICK_US)}
+            "span_us": float((t[:, -1].max() - t[:, 0].min()) * TICK_US)}
 
 
 def run():
@@ -194,6 +221,7 @@ def run():
     p = _plan_clocks(torch, binding, workloads, lib)
     d = _batched_dispatch(torch, binding, workloads, lib)
     k = _topk_phases(torch, binding, workloads, lib)
+    mg = _merge_phases(torch, binding, workloads, lib)
     a = _attention_waits(torch, binding, workloads, lib)
     print(f"### Plan kernel with its copies: {p['B']} rows, one layer of the headline "
           f"workload, medians over {p['calls']} calls x {p['B']} workgroups\n")
@@ -217,15 +245,30 @@ def run():
     print(f"- {d['us_per_launch']} µs per launch (HIP events) in this instrumented build\n")
     print(f"### Top-k chunk kernel, {k['n']} rows x 32768 scores, k = 2048 (last launch)\n")
     print("| phase | µs per workgroup |\n|---|---|")
-    for name, v in zip(["loads and first-digit histogram", "exact threshold (radix select)",
+    for name, v in zip(["loads and first-digit histogram",
+                        "threshold: first bin picked (4096-bin scan)",
+                        "threshold: keys of that bin listed in LDS",
+                        "threshold: first list pass (12-bit digit)",
+                        "threshold: second list pass (8-bit digit)",
                         "bitmap selection", "output staging", "output"], k["phase_us"]):
         print(f"| {name} | {v:.2f} |")
     print(f"\n- span {k['span_us']:.1f} µs; {k['us_per_call']} µs per call in this instrumented "
           f"build\n")
+    print(f"### Top-k merge kernel, {mg['n']} rows x {mg['seq_len']} scores (4 chunks of top-2048 "
+          f"per row; last launch)\n")
+    print("| phase | µs per workgroup |\n|---|---|")
+    for name, v in zip(["chunk offsets published, LDS cleared", "candidate keys and histogram",
+                        "exact threshold", "bitmap selection", "output staging", "output"],
+                       mg["phase_us"]):
+        print(f"| {name} | {v:.2f} |")
+    print(f"\n- {mg['us_per_call']} µs per call (chunk + merge kernels) in this instrumented "
+          f"build\n")
     print("### bf16 attention kernel (the attention bench's last launch: 64 rows x 128 heads x "
           "2048 locations, 256 workgroups)\n")
     print("| phase (workgroup, last launch) | µs |\n|---|---|")
-    for name, v in zip(["setup: locations, row table, queries, first tile landed",
+    for name, v in zip(["setup: locations loaded, rows computed", "setup: row table barrier",
+                        "setup: queries and first tile landed (first wave)",
+                        "setup: first phase barrier (every wave's queries and tile)",
                         "tile loop", "split partials out"], a["phase_us"]):
         print(f"| {name} | {v:.2f} |")
     print(f"\n- kernel span {a['span_us']:.1f} µs")

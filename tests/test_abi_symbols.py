@@ -33,7 +33,9 @@ def test_library_exports_every_declared_symbol():
 def test_default_build_carries_no_instrumentation():
     """The phase-clock hooks exist only in the opt-in instrumented build."""
     lib = binding.lib()
-    for name in ("hisparse_phase_clocks", "hisparse_attention_wait_clocks"):
+    for name in ("hisparse_phase_clocks", "hisparse_attention_wait_clocks",
+                 "hisparse_attention_phase_clocks", "hisparse_topk_phase_clocks",
+                 "hisparse_topk_merge_phase_clocks"):
         assert not hasattr(lib, name), name
 
 
